@@ -1,0 +1,19 @@
+"""CPU oracle for paged-KV decode (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import this package. It is never on the product path, and it shares no code with the
+HIP library: it is written from the pages' description of what PagedAttention computes.
+"""
+
+from .paged_attention import (  # noqa: F401
+    OracleInputError,
+    allocated_kv_bytes,
+    attention_one_query,
+    blocks_needed,
+    copy_blocks,
+    gather_sequence,
+    kv_cache_bytes,
+    paged_decode,
+    paged_decode_heads,
+    reshape_and_cache,
+)

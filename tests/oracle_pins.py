@@ -1,0 +1,373 @@
+"""Pins for the CPU oracle: facts fixed by the pages and by mathematics, not by the oracle.
+
+Every pin takes the oracle module ``o`` as its argument so that the mutation test can run
+the very same pins against planted mistakes (tests/test_oracle_mutations.py). A pin raises
+AssertionError when the implementation disagrees with the fact it checks.
+
+Sources of truth used here:
+  * brute force on tiny inputs: contiguous K/V scattered into a pool by a per-element loop,
+    and attention evaluated with scalar Python loops (``math.exp``);
+  * closed forms: identical keys, a dominant key, a single key, a zero scale;
+  * invariants: uniform score shift, linearity in V, GQA as replicated MHA, joint token
+    permutation, physical relabelling of blocks, block-size independence, NaN padding;
+  * a library routine: torch's CPU scaled_dot_product_attention in float64;
+  * the pages' printed numbers (tests/golden/*.json, each with its citation).
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(*key):
+    return np.random.default_rng(list(key))
+
+
+def _scatter_loop(contents, bs, ids, num_blocks, dtype=np.float32):
+    """Brute-force paging: token t of ``contents`` [L][H][d] goes to (ids[t // bs], h, t % bs)."""
+    L, H, d = contents.shape
+    pool = np.full((num_blocks, H, bs, d), np.nan, dtype)
+    for t in range(L):
+        for h in range(H):
+            for e in range(d):
+                pool[ids[t // bs], h, t % bs, e] = contents[t, h, e]
+    return pool
+
+
+def _make_case(seed, lens, Hq, Hkv, d, bs, spare=3, table_width=None, std=1.0):
+    """Tiny paged case: contiguous contents, shuffled ids, NaN-poisoned unused slots."""
+    rng = _rng(seed, bs, d)
+    lens = [int(x) for x in lens]
+    B = len(lens)
+    kc = [(rng.standard_normal((L, Hkv, d)) * std).astype(np.float32) for L in lens]
+    vc = [(rng.standard_normal((L, Hkv, d)) * std).astype(np.float32) for L in lens]
+    q = (rng.standard_normal((B, Hq, d)) * std).astype(np.float32)
+    nbs = [-(-L // bs) for L in lens]
+    num_blocks = sum(nbs) + spare
+    perm = rng.permutation(num_blocks)
+    width = table_width or max(nbs) + 1
+    table = np.full((B, width), -1, np.int32)
+    cur = 0
+    k_pool = np.full((num_blocks, Hkv, bs, d), np.nan, np.float32)
+    v_pool = np.full_like(k_pool, np.nan)
+    for b in range(B):
+        ids = perm[cur:cur + nbs[b]]
+        cur += nbs[b]
+        table[b, :nbs[b]] = ids
+        for t in range(lens[b]):
+            k_pool[ids[t // bs], :, t % bs, :] = kc[b][t]
+            v_pool[ids[t // bs], :, t % bs, :] = vc[b][t]
+    return dict(q=q, k_pool=k_pool, v_pool=v_pool, table=table, lens=np.array(lens, np.int32),
+                kc=kc, vc=vc, Hq=Hq, Hkv=Hkv, d=d, bs=bs)
+
+
+def _brute_decode(q, kc, vc, lens, scale, Hq, Hkv):
+    """Attention from contiguous per-sequence K/V with scalar Python arithmetic."""
+    B = len(lens)
+    d = q.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s = []
+            for t in range(int(lens[b])):
+                acc = 0.0
+                for e in range(d):
+                    acc += float(q[b, h, e]) * float(kc[b][t, g, e])
+                s.append(scale * acc)
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            den = sum(w)
+            for e in range(d):
+                out[b, h, e] = sum(w[t] * float(vc[b][t, g, e]) for t in range(len(w))) / den
+    return out
+
+
+def _decode(o, c, scale, **over):
+    a = dict(q=c["q"], k_pool=c["k_pool"], v_pool=c["v_pool"], table=c["table"], lens=c["lens"])
+    a.update(over)
+    return o.paged_decode(a["q"], a["k_pool"], a["v_pool"], a["table"], a["lens"], scale)
+
+
+def _close(a, b, tol, what):
+    err = float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+    assert np.all(np.isfinite(a)), f"{what}: non-finite output"
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_gather_roundtrip(o):
+    """Gathering through a random table returns the contiguous rows bit for bit."""
+    for i, (bs, L, H, d) in enumerate([(4, 1, 2, 3), (4, 4, 1, 2), (4, 11, 2, 3), (8, 17, 3, 2),
+                                       (16, 16, 1, 4), (2, 9, 2, 2), (1, 5, 2, 2)]):
+        rng = _rng(100 + i)
+        contents = rng.standard_normal((L, H, d)).astype(np.float32)
+        nb = -(-L // bs)
+        ids = rng.permutation(nb + 5)[:nb]
+        pool = _scatter_loop(contents, bs, ids, nb + 5)
+        row = np.full(nb + 2, -1, np.int32)
+        row[:nb] = ids
+        for h in range(H):
+            got = o.gather_sequence(pool, row, L, h)
+            assert got.dtype == np.float64, "gather must upcast to float64"
+            assert got.shape == (L, d), f"gather shape {got.shape} != {(L, d)}"
+            assert np.array_equal(got, contents[:, h].astype(np.float64)), \
+                f"gather mismatch bs={bs} L={L} head={h}"
+
+
+def pin_worked_example(o):
+    """[BlockManager essay] section 2: lengths [32,128,64,96] in 16-token blocks."""
+    g = _golden("worked_example_blockmanager_s2.json")
+    bs = g["block_size"]
+    counts = [o.blocks_needed(L, bs) for L in g["context_lens"]]
+    assert sum(g["context_lens"]) == g["total_tokens"]
+    assert counts[g["request_index_128_tokens"]] == g["request_128_num_blocks"]
+    assert counts == [2, 8, 4, 6] and sum(counts) == 20, f"block counts {counts}"
+    ids = np.array(g["request_128_block_ids"], np.int32)
+    rng = _rng(7)
+    contents = rng.standard_normal((128, 2, 4)).astype(np.float32)
+    pool = _scatter_loop(contents, bs, ids, 100)  # every other block stays NaN
+    for h in range(2):
+        got = o.gather_sequence(pool, ids, 128, h)
+        assert np.array_equal(got, contents[:, h].astype(np.float64)), "worked-example gather"
+
+
+def pin_memory_formula(o):
+    """Closed-form sizes printed by the pages (tests/golden/kv_sizes.json)."""
+    g = _golden("kv_sizes.json")
+    t = g["per_token"]
+    assert o.kv_cache_bytes(t["num_kv_heads"], t["head_dim"], t["dtype_bytes"], [1]) == t["bytes"]
+    b = g["per_block"]
+    assert o.kv_cache_bytes(b["num_kv_heads"], b["head_dim"], b["dtype_bytes"], [b["block_size"]],
+                            num_layers=b["num_layers"]) == b["bytes"]
+    w = g["worked_example_fp32"]
+    assert o.kv_cache_bytes(w["num_kv_heads"], w["head_dim"], w["dtype_bytes"],
+                            w["context_lens"]) == w["bytes"]
+    p = g["preallocation_7b"]
+    assert o.kv_cache_bytes(p["num_kv_heads"], p["head_dim"], p["dtype_bytes"],
+                            [p["tokens_per_seq"]] * p["batch"], num_layers=p["num_layers"]) == p["bytes"]
+    # sum over sequences, and whole blocks for the allocated figure
+    lens = [33, 16, 1]
+    assert o.kv_cache_bytes(8, 64, 4, lens) == sum(o.kv_cache_bytes(8, 64, 4, [L]) for L in lens)
+    assert o.allocated_kv_bytes(8, 64, 4, lens, 16) == 2 * 8 * 64 * 4 * 16 * (3 + 1 + 1)
+
+
+def pin_bruteforce(o):
+    """Paged decode equals scalar-loop attention over the contiguous K/V (tiny inputs)."""
+    for seed, lens, Hq, Hkv, d, bs in [(1, [1, 7, 12], 4, 2, 5, 4), (2, [5, 2], 3, 3, 4, 2),
+                                       (3, [9, 16], 4, 1, 3, 8), (4, [3], 2, 2, 2, 1)]:
+        c = _make_case(seed, lens, Hq, Hkv, d, bs)
+        scale = 1.0 / math.sqrt(d)
+        got = _decode(o, c, scale)
+        ref = _brute_decode(c["q"], c["kc"], c["vc"], c["lens"], scale, Hq, Hkv)
+        _close(got, ref, 1e-12, f"brute force seed={seed}")
+
+
+def pin_closed_forms(o):
+    d, L, bs = 6, 13, 4
+    c = _make_case(11, [L], 2, 2, d, bs)
+    rng = _rng(12)
+    # (a) identical keys: equal weights, output = mean of V
+    kc = np.repeat(rng.standard_normal((1, 2, d)).astype(np.float32), L, axis=0)
+    cc = _make_case(11, [L], 2, 2, d, bs)
+    ids = cc["table"][0, :4]
+    kp = _scatter_loop(kc, bs, ids, cc["k_pool"].shape[0])
+    got = _decode(o, cc, 0.7, k_pool=kp)
+    for h in range(2):
+        _close(got[0, h], cc["vc"][0][:, h].astype(np.float64).mean(0), 1e-13, "identical keys")
+    # (b) one dominant key: score gap >= 40 returns that key's value
+    q = c["q"][0, 0].astype(np.float64)
+    j = 5
+    kc = (rng.standard_normal((L, 2, d)) * 0.01).astype(np.float32)
+    kc[j, 0] = (q * (60.0 / float(q @ q))).astype(np.float32)
+    kp = _scatter_loop(kc, bs, c["table"][0, :4], c["k_pool"].shape[0])
+    s = kc[:, 0].astype(np.float64) @ q
+    assert s[j] - np.max(np.delete(s, j)) >= 40.0
+    got = _decode(o, c, 1.0, k_pool=kp)
+    _close(got[0, 0], c["vc"][0][j, 0], 1e-12, "dominant key")
+    # (c) a single key returns its value exactly
+    c1 = _make_case(13, [1], 2, 1, d, bs)
+    got = _decode(o, c1, 0.3)
+    for h in range(2):
+        assert np.array_equal(got[0, h], c1["vc"][0][0, 0].astype(np.float64)), "L = 1"
+    # (d) zero scale: uniform weights
+    got = _decode(o, c, 0.0)
+    for h in range(2):
+        _close(got[0, h], c["vc"][0][:, h].astype(np.float64).mean(0), 1e-13, "zero scale")
+
+
+def pin_invariants(o):
+    lens, Hq, Hkv, d, bs = [6, 11, 1], 4, 2, 5, 4
+    c = _make_case(21, lens, Hq, Hkv, d, bs)
+    scale = 0.45
+    base = _decode(o, c, scale)
+    nb = c["k_pool"].shape[0]
+    rng = _rng(22)
+
+    def rescatter(kc_list, bs_=bs, table=None, num_blocks=nb, dtype=np.float32):
+        table = c["table"] if table is None else table
+        pool = np.full((num_blocks, Hkv, bs_, d), np.nan, dtype)
+        for b, L in enumerate(lens):
+            part = _scatter_loop(kc_list[b], bs_, table[b][:-(-L // bs_)], num_blocks, dtype)
+            m = ~np.isnan(part)
+            pool[m] = part[m]
+        return pool
+
+    # (a) adding one vector to every key of a head shifts all its scores equally, so the
+    # output does not move (float64 pools keep the shift exact up to fp64 rounding)
+    u = rng.standard_normal((Hkv, d))
+    shifted = [k.astype(np.float64) + u for k in c["kc"]]
+    got = _decode(o, c, scale, k_pool=rescatter(shifted, dtype=np.float64))
+    _close(got, base, 1e-12, "uniform key shift")
+    # (b) linear in V
+    v2 = [rng.standard_normal(v.shape) for v in c["vc"]]
+    comb = [2.0 * a.astype(np.float64) - 0.5 * b2 for a, b2 in zip(c["vc"], v2)]
+    out2 = _decode(o, c, scale, v_pool=rescatter(v2, dtype=np.float64))
+    outc = _decode(o, c, scale, v_pool=rescatter(comb, dtype=np.float64))
+    _close(outc, 2.0 * base - 0.5 * out2, 1e-12, "linearity in V")
+    # (c) GQA equals MHA with each kv head replicated for its query heads
+    rep_k = [np.repeat(k, Hq // Hkv, axis=1) for k in c["kc"]]
+    rep_v = [np.repeat(v, Hq // Hkv, axis=1) for v in c["vc"]]
+    kp = np.full((nb, Hq, bs, d), np.nan, np.float32)
+    vp = np.full_like(kp, np.nan)
+    for b, L in enumerate(lens):
+        ids = c["table"][b][:-(-L // bs)]
+        for t in range(L):
+            kp[ids[t // bs], :, t % bs] = rep_k[b][t]
+            vp[ids[t // bs], :, t % bs] = rep_v[b][t]
+    mha = _decode(o, c, scale, k_pool=kp, v_pool=vp)
+    assert np.array_equal(mha, base), "GQA != replicated MHA"
+    # (d) joint permutation of a sequence's tokens
+    perm = [rng.permutation(L) for L in lens]
+    pk = [k[p] for k, p in zip(c["kc"], perm)]
+    pv = [v[p] for v, p in zip(c["vc"], perm)]
+    got = _decode(o, c, scale, k_pool=rescatter(pk), v_pool=rescatter(pv))
+    _close(got, base, 1e-12, "token permutation")
+    # (e) relabelling physical blocks leaves the result bit-identical
+    pi = rng.permutation(nb)
+    kp2 = np.empty_like(c["k_pool"])
+    vp2 = np.empty_like(c["v_pool"])
+    kp2[pi] = c["k_pool"]
+    vp2[pi] = c["v_pool"]
+    t2 = np.where(c["table"] >= 0, pi[np.maximum(c["table"], 0)], -1).astype(np.int32)
+    assert np.array_equal(_decode(o, c, scale, k_pool=kp2, v_pool=vp2, table=t2), base), "relabel"
+    # (f) the same contents under other block sizes give bit-identical results
+    for bs2 in (1, 2, 8, 16):
+        nb2 = sum(-(-L // bs2) for L in lens) + 2
+        ids_all = rng.permutation(nb2)
+        table2 = np.full((len(lens), max(-(-L // bs2) for L in lens) + 1), -1, np.int32)
+        cur = 0
+        kp3 = np.full((nb2, Hkv, bs2, d), np.nan, np.float32)
+        vp3 = np.full_like(kp3, np.nan)
+        for b, L in enumerate(lens):
+            n = -(-L // bs2)
+            table2[b, :n] = ids_all[cur:cur + n]
+            cur += n
+            for t in range(L):
+                kp3[table2[b, t // bs2], :, t % bs2] = c["kc"][b][t]
+                vp3[table2[b, t // bs2], :, t % bs2] = c["vc"][b][t]
+        got = _decode(o, c, scale, k_pool=kp3, v_pool=vp3, table=table2)
+        assert np.array_equal(got, base), f"block size {bs2} changes the result"
+    # (g) garbage ids past the valid blocks and NaN padding are never read
+    t3 = c["table"].copy()
+    t3[:, -1] = 10 ** 6
+    t3[2, 1:] = -5
+    got = _decode(o, c, scale, table=t3)
+    assert np.array_equal(got, base) and np.all(np.isfinite(got)), "padding / unused ids were read"
+
+
+def pin_sdpa(o):
+    """torch CPU scaled_dot_product_attention in float64 on the contiguous K/V."""
+    import torch
+
+    lens, Hq, Hkv, d, bs = [9, 4, 17], 6, 3, 8, 4
+    c = _make_case(31, lens, Hq, Hkv, d, bs)
+    scale = 0.31
+    got = _decode(o, c, scale)
+    G = Hq // Hkv
+    for b, L in enumerate(lens):
+        q = torch.from_numpy(c["q"][b].astype(np.float64)).view(1, Hq, 1, d)
+        k = torch.from_numpy(np.repeat(c["kc"][b], G, axis=1).astype(np.float64)).permute(1, 0, 2)
+        v = torch.from_numpy(np.repeat(c["vc"][b], G, axis=1).astype(np.float64)).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q, k.unsqueeze(0).contiguous(), v.unsqueeze(0).contiguous(), scale=scale)
+        _close(got[b], ref.view(Hq, d).numpy(), 1e-12, f"sdpa seq {b}")
+
+
+def pin_reshape_and_cache(o):
+    rng = _rng(41)
+    NB, H, bs, d = 7, 2, 4, 3
+    kp = rng.standard_normal((NB, H, bs, d)).astype(np.float32)
+    vp = rng.standard_normal((NB, H, bs, d)).astype(np.float32)
+    key = rng.standard_normal((5, H, d)).astype(np.float32)
+    val = rng.standard_normal((5, H, d)).astype(np.float32)
+    slots = np.array([3, -1, 27, 8, -7], np.int32)
+    ek, ev = kp.copy(), vp.copy()
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        for h in range(H):
+            for e in range(d):
+                ek[s // bs, h, s % bs, e] = key[i, h, e]
+                ev[s // bs, h, s % bs, e] = val[i, h, e]
+    k2, v2 = o.reshape_and_cache(kp, vp, key, val, slots)
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev), "reshape_and_cache scatter"
+    assert not np.array_equal(k2, kp), "pools must be updated"
+    k3, v3 = o.reshape_and_cache(kp, vp, key, val, np.full(5, -1, np.int32))
+    assert np.array_equal(k3, kp) and np.array_equal(v3, vp), "negative slots must be skipped"
+    try:
+        o.reshape_and_cache(kp, vp, key[:1], val[:1], np.array([NB * bs], np.int32))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("slot beyond the pool must raise")
+
+
+def pin_copy_blocks(o):
+    rng = _rng(51)
+    NB = 8
+    kp = rng.standard_normal((NB, 2, 4, 3)).astype(np.float32)
+    vp = rng.standard_normal((NB, 2, 4, 3)).astype(np.float32)
+    pairs = np.array([[1, 4], [2, 6]], np.int32)
+    k2, v2 = o.copy_blocks(kp, vp, pairs)
+    ek, ev = kp.copy(), vp.copy()
+    ek[4], ev[4], ek[6], ev[6] = kp[1], vp[1], kp[2], vp[2]
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev), "copy_blocks"
+    for bad in ([1, 1], [-1, 2], [0, NB]):
+        try:
+            o.copy_blocks(kp, vp, np.array([bad], np.int32))
+        except ValueError:
+            continue
+        raise AssertionError(f"bad pair {bad} must raise")
+
+
+def pin_errors(o):
+    c = _make_case(61, [6, 9], 2, 2, 3, 4)
+    t = c["table"].copy()
+    t[1, 1] = c["k_pool"].shape[0]  # an id outside the pool inside the valid range
+    for over, what in [(dict(table=t), "bad block id"),
+                       (dict(lens=np.array([6, 0], np.int32)), "zero length"),
+                       (dict(lens=np.array([6, 4 * c["table"].shape[1] + 1], np.int32)), "over capacity")]:
+        try:
+            _decode(o, c, 0.5, **over)
+        except ValueError:
+            continue
+        raise AssertionError(f"{what} must raise")
+
+
+ALL_PINS = [pin_gather_roundtrip, pin_worked_example, pin_memory_formula, pin_bruteforce,
+            pin_closed_forms, pin_invariants, pin_sdpa, pin_reshape_and_cache, pin_copy_blocks,
+            pin_errors]

@@ -1,0 +1,167 @@
+"""Planted mistakes in the CPU oracle must each fail at least one pin.
+
+Each mutant replaces one oracle function (on the CPU, via monkeypatch) with a plausible
+bug: a dropped term, a wrong sign or index, a transposed or swapped operand. The pins of
+tests/oracle_pins.py are then run against the mutated oracle; the test passes only if
+some pin rejects it, which shows the pins constrain every step of the oracle.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.paged_attention as pa
+from tests import oracle_pins
+
+_gather = pa.gather_sequence
+_attn = pa.attention_one_query
+
+
+def m_drop_scale(q, K, V, scale):
+    return _attn(q, K, V, 1.0)
+
+
+def m_softmin(q, K, V, scale):
+    s = float(scale) * (K @ q.astype(np.float64))
+    w = np.exp(-(s - s.min()))
+    return (w @ V) / w.sum()
+
+
+def m_no_normalise(q, K, V, scale):
+    s = float(scale) * (K @ q.astype(np.float64))
+    w = np.exp(s - s.max())
+    return w @ V
+
+
+def m_weights_on_keys(q, K, V, scale):
+    s = float(scale) * (K @ q.astype(np.float64))
+    w = np.exp(s - s.max())
+    return (w @ K) / w.sum()
+
+
+def m_mask_short(pool, row, L, h):
+    full = _gather(pool, row, L, h)
+    return full[:max(int(L) - 1, 1)]
+
+
+def m_mask_long(pool, row, L, h):
+    nb, _, bs, _ = pool.shape
+    rows = []
+    for j in range(-(-(int(L) + 1) // bs)):
+        rows.append(pool[int(row[j]) % nb, h])
+    return np.concatenate(rows)[:int(L) + 1].astype(np.float64)
+
+
+def m_reverse_blocks(pool, row, L, h):
+    nb = pa.blocks_needed(L, pool.shape[2])
+    rev = np.array(row, copy=True)
+    rev[:nb] = rev[:nb][::-1]
+    return _gather(pool, rev, L, h)
+
+
+def m_head_zero(pool, row, L, h):
+    return _gather(pool, row, L, 0)
+
+
+def m_offset_swapped(pool, row, L, h):
+    nb_pool, _, bs, _ = pool.shape
+    out = []
+    for t in range(int(L)):
+        j, off = divmod(t, bs)
+        out.append(pool[int(row[j]), h, (bs - 1 - off)])
+    return np.array(out, np.float64)
+
+
+def _decode_with_head_map(head_map):
+    def paged_decode(q, k_pool, v_pool, block_table, context_lens, scale):
+        B, Hq, d = q.shape
+        Hkv = k_pool.shape[1]
+        out = np.empty((B, Hq, d))
+        for b in range(B):
+            for h in range(Hq):
+                g = head_map(h, Hq, Hkv)
+                K = _gather(k_pool, block_table[b], context_lens[b], g)
+                V = _gather(v_pool, block_table[b], context_lens[b], g)
+                out[b, h] = _attn(q[b, h], K, V, scale)
+        return out
+    return paged_decode
+
+
+def m_wrong_sequence_row(q, k_pool, v_pool, block_table, context_lens, scale):
+    B = q.shape[0]
+    rolled = np.roll(block_table, 1, axis=0) if B > 1 else block_table
+    return pa.__dict__["_orig_paged_decode"](q, k_pool, v_pool, rolled, context_lens, scale)
+
+
+def m_cache_divmod_swapped(k_pool, v_pool, key, value, slot_mapping):
+    k_new, v_new = k_pool.copy(), v_pool.copy()
+    nb, _, bs, _ = k_pool.shape
+    for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        blk, off = int(slot) % bs, int(slot) // bs  # block and offset swapped
+        if blk >= nb or off >= bs:
+            raise pa.OracleInputError("slot")
+        k_new[blk, :, off, :] = key[i]
+        v_new[blk, :, off, :] = value[i]
+    return k_new, v_new
+
+
+def m_cache_skips_value(k_pool, v_pool, key, value, slot_mapping):
+    k_new, _ = pa.__dict__["_orig_reshape_and_cache"](k_pool, v_pool, key, value, slot_mapping)
+    return k_new, v_pool.copy()
+
+
+def m_copy_only_k(k_pool, v_pool, pairs):
+    k_new, _ = pa.__dict__["_orig_copy_blocks"](k_pool, v_pool, pairs)
+    return k_new, v_pool.copy()
+
+
+def m_copy_reversed(k_pool, v_pool, pairs):
+    p = np.asarray(pairs).reshape(-1, 2)[:, ::-1]
+    return pa.__dict__["_orig_copy_blocks"](k_pool, v_pool, p)
+
+
+def m_bytes_no_factor2(num_kv_heads, head_dim, dtype_bytes, context_lens, num_layers=1):
+    return pa.__dict__["_orig_kv_cache_bytes"](num_kv_heads, head_dim, dtype_bytes, context_lens,
+                                                num_layers) // 2
+
+
+def m_blocks_floor(L, bs):
+    return int(L) // int(bs)
+
+
+MUTANTS = {
+    "drop_scale": ("attention_one_query", m_drop_scale),
+    "softmin": ("attention_one_query", m_softmin),
+    "no_normalise": ("attention_one_query", m_no_normalise),
+    "weights_on_keys": ("attention_one_query", m_weights_on_keys),
+    "mask_short": ("gather_sequence", m_mask_short),
+    "mask_long": ("gather_sequence", m_mask_long),
+    "reverse_blocks": ("gather_sequence", m_reverse_blocks),
+    "head_zero": ("gather_sequence", m_head_zero),
+    "offset_swapped": ("gather_sequence", m_offset_swapped),
+    "gqa_modulo": ("paged_decode", _decode_with_head_map(lambda h, Hq, Hkv: h % Hkv)),
+    "gqa_identity": ("paged_decode", _decode_with_head_map(lambda h, Hq, Hkv: min(h, Hkv - 1))),
+    "wrong_sequence_row": ("paged_decode", m_wrong_sequence_row),
+    "cache_divmod_swapped": ("reshape_and_cache", m_cache_divmod_swapped),
+    "cache_skips_value": ("reshape_and_cache", m_cache_skips_value),
+    "copy_only_k": ("copy_blocks", m_copy_only_k),
+    "copy_reversed": ("copy_blocks", m_copy_reversed),
+    "bytes_no_factor2": ("kv_cache_bytes", m_bytes_no_factor2),
+    "blocks_floor": ("blocks_needed", m_blocks_floor),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    for orig in ("paged_decode", "reshape_and_cache", "copy_blocks", "kv_cache_bytes"):
+        monkeypatch.setitem(pa.__dict__, "_orig_" + orig, getattr(pa, orig))
+    monkeypatch.setattr(pa, attr, fn)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(pa)
+        except Exception as e:  # noqa: BLE001 - any failure means the pin caught it
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"

@@ -1,0 +1,201 @@
+"""Seeded synthetic paged-KV workloads.
+
+Every array here is a plain numpy array. Floating-point contents are drawn in float32,
+rounded to the workload's storage dtype (round to nearest even, done by torch on the CPU)
+and kept as float32, so the values are exactly representable in the storage dtype and the
+upcast to float64 for the oracle is exact.
+
+Layout conventions (shared by the oracle and the library):
+  q                 [B][Hq][d]
+  k_pool, v_pool    [num_blocks][Hkv][block_size][d]   unwritten slots hold NaN
+  block_table       int32 [B][max_blocks_per_seq], -1 where unallocated
+  context_lens      int32 [B], tokens already in the cache before this step's append
+  new_key/new_value [B][Hkv][d], the token appended at position context_lens[b]
+  slot_mapping      int32 [B], physical slot (block * block_size + offset) of that token
+  copy_pairs        int32 [P][2], (src, dst) physical block ids for copy-on-write
+
+Random streams are split so that contents do not depend on the block size or on the
+physical placement: contents come from ``default_rng([cfg, seed, 0])``, the physical
+permutation from ``default_rng([cfg, seed, 1, block_size])`` and the lengths from
+``default_rng([cfg, seed, 2])``.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+_TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def cast_like(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to ``dtype`` (nearest even) and return them as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x
+    return torch.from_numpy(x).to(_TORCH_DTYPES[dtype]).to(torch.float32).numpy()
+
+
+def lognormal_lengths(rng: np.random.Generator, n: int, median: float, sigma: float = 1.0,
+                      lo: int = 4, hi: int = 4096) -> np.ndarray:
+    """Long-tail lengths: round(exp(ln(median) + sigma * z)) clipped to [lo, hi]."""
+    z = rng.standard_normal(n)
+    return np.clip(np.rint(np.exp(math.log(median) + sigma * z)), lo, hi).astype(np.int32)
+
+
+@dataclass
+class PagedWorkload:
+    name: str
+    dtype: str
+    block_size: int
+    num_kv_heads: int
+    num_q_heads: int
+    head_dim: int
+    scale: float
+    q: np.ndarray
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    block_table: np.ndarray
+    context_lens: np.ndarray
+    new_key: np.ndarray
+    new_value: np.ndarray
+    slot_mapping: np.ndarray
+    copy_pairs: np.ndarray = field(default_factory=lambda: np.zeros((0, 2), np.int32))
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def lens_after_append(self) -> np.ndarray:
+        return (self.context_lens + 1).astype(np.int32)
+
+
+def _allocate_tables(rng_layout: np.random.Generator, lens: np.ndarray, bs: int,
+                     num_blocks: int | None, spare: float, max_blocks_per_seq: int | None,
+                     append: bool):
+    """Hand out physical ids from one seeded permutation of the pool.
+
+    Every sequence first receives the blocks its current tokens occupy (sequence 0 first),
+    then the sequences whose append starts a new block receive one more id each, taken
+    from the ids that remain.
+    """
+    need_now = (lens + bs - 1) // bs
+    need_after = (lens + (1 if append else 0) + bs - 1) // bs
+    total = int(need_after.sum())
+    if num_blocks is None:
+        num_blocks = int(math.ceil(total * (1.0 + spare)))
+    if num_blocks < total:
+        raise ValueError(f"pool of {num_blocks} blocks cannot hold {total}")
+    mbs = int(need_after.max()) if max_blocks_per_seq is None else int(max_blocks_per_seq)
+    perm = rng_layout.permutation(num_blocks).astype(np.int32)
+    table = np.full((len(lens), mbs), -1, np.int32)
+    cur = 0
+    for b, n in enumerate(need_now):
+        table[b, :n] = perm[cur:cur + n]
+        cur += int(n)
+    for b in range(len(lens)):
+        if need_after[b] > need_now[b]:
+            table[b, need_now[b]] = perm[cur]
+            cur += 1
+    return table, num_blocks
+
+
+def _scatter(pool: np.ndarray, table: np.ndarray, lens: np.ndarray, starts: np.ndarray,
+             contents: np.ndarray, bs: int) -> None:
+    """Write contiguous per-token rows ``contents[starts[b] + t]`` to the pool slots."""
+    for b, L in enumerate(lens):
+        t = np.arange(int(L))
+        blk = table[b, t // bs]
+        off = t % bs
+        pool[blk, :, off, :] = contents[int(starts[b]) + t]
+
+
+def build_paged(name: str, cfg_id: int, seed: int, lens: np.ndarray, block_size: int,
+                num_kv_heads: int, num_q_heads: int, head_dim: int, dtype: str,
+                scale: float | None = None, std: float = 1.0, num_blocks: int | None = None,
+                spare: float = 0.10, max_blocks_per_seq: int | None = None,
+                append: bool = True) -> PagedWorkload:
+    lens = np.asarray(lens, np.int32)
+    B = len(lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    rng_c = np.random.default_rng([cfg_id, seed, 0])
+    rng_l = np.random.default_rng([cfg_id, seed, 1, block_size])
+    table, nb = _allocate_tables(rng_l, lens, block_size, num_blocks, spare,
+                                 max_blocks_per_seq, append)
+    # Contents: q, then L+1 contiguous K rows per sequence, then the same for V.
+    q = cast_like(rng_c.standard_normal((B, num_q_heads, head_dim), np.float32) * std, dtype)
+    rows = int(lens.sum()) + B
+    starts = np.concatenate([[0], np.cumsum(lens + 1)[:-1]]).astype(np.int64)
+    kc = cast_like(rng_c.standard_normal((rows, num_kv_heads, head_dim), np.float32) * std, dtype)
+    vc = cast_like(rng_c.standard_normal((rows, num_kv_heads, head_dim), np.float32) * std, dtype)
+    k_pool = np.full((nb, num_kv_heads, block_size, head_dim), np.nan, np.float32)
+    v_pool = np.full_like(k_pool, np.nan)
+    _scatter(k_pool, table, lens, starts, kc, block_size)
+    _scatter(v_pool, table, lens, starts, vc, block_size)
+    new_key = kc[starts + lens]
+    new_value = vc[starts + lens]
+    if append:
+        slot = table[np.arange(B), lens // block_size].astype(np.int64) * block_size + lens % block_size
+        slot_mapping = slot.astype(np.int32)
+    else:
+        slot_mapping = np.full(B, -1, np.int32)
+    return PagedWorkload(
+        name=name, dtype=dtype, block_size=block_size, num_kv_heads=num_kv_heads,
+        num_q_heads=num_q_heads, head_dim=head_dim, scale=float(scale), q=q,
+        k_pool=k_pool, v_pool=v_pool, block_table=table, context_lens=lens,
+        new_key=new_key, new_value=new_value, slot_mapping=slot_mapping,
+        meta={"cfg": cfg_id, "seed": seed, "std": std,
+              "contents_k": kc, "contents_v": vc, "starts": starts},
+    )
+
+
+def config_workload(cfg: int, seed: int = 0, *, block_size: int | None = None,
+                    median: float | None = None, batch: int | None = None,
+                    heads: int | None = None, sigma: float = 1.0) -> PagedWorkload:
+    """The five seeded synthetic workloads (configs 1-4 here; 5 lives in ``longctx``).
+
+    ``batch``/``heads`` shrink a configuration for quick tests while keeping its dtype,
+    head_dim, block size and length distribution.
+    """
+    rng_len = np.random.default_rng([cfg, seed, 2])
+    if cfg == 1:
+        lens = np.array([32, 128, 64, 96], np.int32)
+        return build_paged("cfg1-f32-tiny", 1, seed, lens, block_size or 16, heads or 8,
+                           heads or 8, 64, "f32", scale=1.0 / 8.0, num_blocks=64)
+    if cfg == 2:
+        B = batch or 64
+        H = heads or 32
+        lens = rng_len.integers(450, 521, size=64).astype(np.int32)[:B]
+        return build_paged("cfg2-f16-mha", 2, seed, lens, block_size or 16, H, H, 128, "f16",
+                           std=0.5)
+    if cfg == 3:
+        B = batch or 256
+        H = heads or 32
+        med = median or 87
+        lens = lognormal_lengths(rng_len, 256, med, sigma)[:B]
+        bs = block_size or 16
+        return build_paged(f"cfg3-f16-longtail-med{med:g}-bs{bs}", 3 if med == 87 else 30,
+                           seed, lens, bs, H, H, 128, "f16")
+    if cfg == 4:
+        B = batch or 32
+        hkv = heads or 8
+        lens = np.full(B, 2048, np.int32)
+        bs = block_size or 16
+        return build_paged(f"cfg4-bf16-gqa-bs{bs}", 4, seed, lens, bs, hkv, hkv * 8, 128,
+                           "bf16")
+    raise ValueError(f"unknown config {cfg}")
