@@ -1,0 +1,178 @@
+"""Paged-KV decode benchmark on one MI355X.
+
+One step = the whole hot path over one batch: copy-on-write of shared blocks (when the
+workload has any), append of one new token per sequence through its slot (pa_reshape_and_
+cache), then decode over the grown context (pa_decode). Inputs are seeded synthetic tensors
+already resident in HBM. Pools are replicated R times and step i uses replica i % R, so the
+bytes touched between two reads of a replica exceed the 256 MB Infinity Cache and the
+per-XCD L2 (a cold-cache measurement).
+
+Prints one JSON line: effective KV GB/s of the whole step (algorithmic K+V bytes of the
+decode, 2 x kv_heads x head_dim x dtype_bytes x sum(context_len), over the step time),
+plus the decode kernel's roofline figure timed with HIP events and the CPU oracle's rate.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def _workload(cfg: int, block_size: int | None, median: float | None):
+    from workloads import config_workload
+
+    return config_workload(cfg, seed=0, block_size=block_size, median=median)
+
+
+def _describe(w) -> dict:
+    L = w.lens_after_append
+    return {"workload": w.name, "dtype": w.dtype, "batch": w.batch,
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size, "num_blocks": w.num_blocks,
+            "context_len_min": int(L.min()), "context_len_max": int(L.max()),
+            "context_len_sum": int(L.sum()), "step": "append 1 token/seq + decode"}
+
+
+def _cpu_baseline(w, budget_s: float) -> dict:
+    """The float64 oracle on the host copy of the same step: its append over the whole batch,
+    then single-sequence decodes in order until the whole batch is done or ~budget_s passed."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    per_tok = 2 * w.num_kv_heads * w.head_dim * {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    L = w.lens_after_append
+    t0 = time.perf_counter()
+    ek, ev = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.new_key, w.new_value, w.slot_mapping)
+    seqs = done = 0
+    while seqs < w.batch and (seqs == 0 or time.perf_counter() - t0 < budget_s):
+        sl = slice(seqs, seqs + 1)
+        oracle.paged_decode(w.q[sl], ek, ev, w.block_table[sl], L[sl], w.scale)
+        done += per_tok * int(L[seqs])
+        seqs += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle append of all {w.batch} tokens + float64 decode of sequences "
+                      f"0..{seqs - 1} (all heads, {done / 1e6:.1f} MB of KV) in {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload 1-4 (default 2)")
+    ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--median", type=float, default=None)
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--replica-bytes", type=float, default=1.5 * 2 ** 30,
+                    help="pool bytes touched between reuses of one replica")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from paged_kv_cache_indexed_amd import _lib, ops
+
+    _lib.load()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda", 0)
+    w = _workload(args.config, args.block_size, args.median)
+    t = w.to_device(dev)
+    pool_bytes = 2 * t["k_pool"].numel() * t["k_pool"].element_size()
+    R = max(2, math.ceil(args.replica_bytes / pool_bytes))
+    kps = [t["k_pool"]] + [t["k_pool"].clone() for _ in range(R - 1)]
+    vps = [t["v_pool"]] + [t["v_pool"].clone() for _ in range(R - 1)]
+    lens = t["lens_after"]
+    max_len = int(w.lens_after_append.max())
+    P = args.partition_size
+    ws = ops.workspace_for(t["k_pool"], w.batch, w.num_q_heads, max_len, P)
+    out = torch.empty_like(t["q"])
+    pairs = t["copy_pairs"]
+    esize = t["k_pool"].element_size()
+    kv_bytes = 2 * w.num_kv_heads * w.head_dim * esize * int(w.lens_after_append.sum())
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        r = i % R
+        if pairs.shape[0]:
+            ops.copy_blocks(kps[r], vps[r], pairs)
+        ops.reshape_and_cache(t["new_key"], t["new_value"], kps[r], vps[r], t["slot_mapping"])
+        if ev is not None:
+            ev[0].record(stream)
+        ops.decode(t["q"], kps[r], vps[r], t["block_table"], lens, max_len, w.scale,
+                   partition_size=P, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_step = wall * 1e3 / args.steps
+    dec_avg = float(dec_ms.mean())
+    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    part = _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, w.num_q_heads,
+                                         max_len, P)
+    cfg = _describe(w)
+    cfg.update({"partition_size": part, "replicas": R, "tokens_per_step": w.batch})
+    result = {
+        "metric": "paged-decode KV GB/s (% of HBM peak) and decode tokens/s at 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) contents, shuffled physical pool, NaN-filled padding)",
+        "config": cfg,
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "decode_kernel_ms": {"mean": round(dec_avg, 5), "p10": round(float(np.percentile(dec_ms, 10)), 5),
+                             "p50": round(float(np.percentile(dec_ms, 50)), 5),
+                             "p90": round(float(np.percentile(dec_ms, 90)), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

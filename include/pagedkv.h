@@ -1,0 +1,159 @@
+/*
+ * pagedkv.h - C ABI of libpagedkv: paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [BlockManager essay]  "KV Cache & BlockManager", dpshk.com/news/5906718
+ *   [KV Block course]     vLLM memory-management course, ch. 3 "KV Block design"
+ *   [Valid-length essay]  KV-cache valid length and padding-KV bug, dpshk.com/news/5937191
+ *   [CANN paging article] "KV Cache paging optimisation in LLM inference", intelliparadigm.com
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is device memory owned by the caller (allocated, for
+ *     instance, by torch). The library allocates nothing, keeps no state between calls
+ *     and never synchronises: each call enqueues kernels on `stream` and returns.
+ *   - Argument errors are found on the host before anything is launched and come back as
+ *     a status other than PA_OK. A failed launch returns PA_ERR_LAUNCH.
+ *   - Data errors that only the device can see (a bad block id, length or slot) never
+ *     cause an out-of-bounds access: the affected item is skipped or its output set to
+ *     NaN, and a bit (PA_FLAG_*) is OR-ed into *err_flag when err_flag is not NULL
+ *     (reject, do not corrupt: [BlockManager essay] §4.1). The flag is never cleared by
+ *     the library.
+ *   - Layouts (row-major, contiguous):
+ *       q, out             [batch][num_q_heads][head_dim]
+ *       k_pool, v_pool     [num_blocks][num_kv_heads][block_size][head_dim]
+ *                          (one block holds heads x block_size x head_dim for K and the
+ *                          same for V: [BlockManager essay] §5.1, [KV Block course] §3.2)
+ *       key, value         [num_tokens][num_kv_heads][head_dim]
+ *       block_table        int32 [batch][max_blocks_per_seq], logical -> physical block
+ *                          id, entries past the valid blocks are never read and may be -1
+ *                          ([BlockManager essay] §2)
+ *       context_lens       int32 [batch], number of valid tokens ([Valid-length essay] §4.1)
+ *       slot_mapping       int32 [num_tokens], physical slot = block * block_size + offset
+ *       pairs              int32 [num_pairs][2] = (src, dst) physical block ids
+ *   - q, out, key, value, k_pool and v_pool must be 16-byte aligned
+ *     ([KV Block course] §3.7 on aligned block starts).
+ *   - Supported: dtype f32/f16/bf16; head_dim 64, 128, 256; block_size a power of two in
+ *     [8, 512]; num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t; NULL is the default stream. */
+typedef struct ihipStream_t* pa_stream_t;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, workspace too small */
+    PA_ERR_UNSUPPORTED = 2,      /* dtype, head_dim, block_size or group not built */
+    PA_ERR_LAUNCH = 3            /* the HIP runtime refused a launch */
+} pa_status_t;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
+
+/* Device-side data error bits OR-ed into *err_flag. */
+#define PA_FLAG_BAD_BLOCK_ID   1  /* a table entry inside the valid range is outside [0, num_blocks) */
+#define PA_FLAG_BAD_LENGTH     2  /* context_len > max_context_len or > max_blocks_per_seq * block_size */
+#define PA_FLAG_EMPTY_CONTEXT  4  /* context_len <= 0 */
+#define PA_FLAG_BAD_SLOT       8  /* slot >= num_blocks * block_size */
+#define PA_FLAG_BAD_COPY_PAIR 16  /* src or dst outside [0, num_blocks), or src == dst */
+
+/* Shape of one physical pool pair (K and V have the same shape). */
+typedef struct {
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype; /* pa_dtype_t */
+} pa_cache_desc_t;
+
+/*
+ * pa_reshape_and_cache - write new tokens' K and V into their pool slots.
+ *
+ * Token i's rows key[i] and value[i] ([num_kv_heads][head_dim]) are copied bit for bit to
+ * block slot_mapping[i] / block_size, offset slot_mapping[i] % block_size, of every kv head,
+ * so the physical order inside a block equals the logical order ([BlockManager essay] §4.4;
+ * new K/V land at the valid length, [Valid-length essay] §4.1). A negative slot marks a
+ * padding token and is skipped, so padding KV never enters the cache ([Valid-length essay]
+ * §2.3). A slot >= num_blocks * block_size is skipped and sets PA_FLAG_BAD_SLOT.
+ * num_tokens == 0 launches nothing. Two tokens with the same slot race (caller error).
+ */
+pa_status_t pa_reshape_and_cache(const pa_cache_desc_t* cache, const void* key, const void* value,
+                                 void* k_pool, void* v_pool, const int32_t* slot_mapping,
+                                 int32_t num_tokens, int32_t* err_flag, pa_stream_t stream);
+
+/*
+ * pa_copy_blocks - copy-on-write of shared blocks.
+ *
+ * For every pair, physical block dst becomes a bitwise copy of block src, for K and V and
+ * all kv heads. A block shared by several sequences (beams) is copied before one of them
+ * writes into it ([BlockManager essay] §2, §4.2; [KV Block course] §3.4). Pairs run in
+ * parallel: every dst must be distinct and no dst may be a src (a fresh block is always the
+ * target of copy-on-write). A pair with an id outside [0, num_blocks) or src == dst is
+ * skipped and sets PA_FLAG_BAD_COPY_PAIR. num_pairs == 0 launches nothing.
+ */
+pa_status_t pa_copy_blocks(const pa_cache_desc_t* cache, void* k_pool, void* v_pool,
+                           const int32_t* pairs, int32_t num_pairs, int32_t* err_flag,
+                           pa_stream_t stream);
+
+/*
+ * pa_decode_partition_size - the context-partition length pa_decode will use.
+ *
+ * `requested` > 0 must be a multiple of block_size and of 64 (else returns -1). 0 picks a
+ * default from the batch, head and length shape. A result >= max_context_len means one
+ * partition per sequence (no reduce pass).
+ */
+int32_t pa_decode_partition_size(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_heads,
+                                 int32_t max_context_len, int32_t requested);
+
+/*
+ * pa_decode_workspace_bytes - bytes of device workspace pa_decode needs (0 if none).
+ *
+ * The workspace holds one (max, sum, normalised output) record per sequence, query head
+ * and context partition when some sequence spans more than one partition.
+ */
+size_t pa_decode_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_heads,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode - one query per sequence attends over its paged K/V cache.
+ *
+ * out[b][h] = sum_t softmax_t(scale * q[b][h] . K_b[t]) V_b[t] over the context_lens[b]
+ * valid tokens of sequence b, where token t of kv head g = h / (num_q_heads / num_kv_heads)
+ * is read from physical block block_table[b][t / block_size] at offset t % block_size
+ * ([BlockManager essay] §2, §5.2; [KV Block course] §3.3; [Valid-length essay] §3.1, §4.2;
+ * [CANN paging article] §2.2). Tokens at or past context_len are never loaded.
+ * Scores, the running max and sum, and the accumulators are fp32; out has the pool dtype.
+ *
+ * max_context_len bounds every context_lens[b] and sizes the launch; it must not exceed
+ * max_blocks_per_seq * block_size. A sequence whose length is <= 0 or above either bound
+ * gets NaN outputs and sets PA_FLAG_EMPTY_CONTEXT / PA_FLAG_BAD_LENGTH; a sequence with a
+ * bad block id in its valid range gets NaN outputs and sets PA_FLAG_BAD_BLOCK_ID. Other
+ * sequences are unaffected.
+ *
+ * partition_size: 0 = default, else as pa_decode_partition_size. When a sequence spans
+ * several partitions, each writes (max, sum, output) to `workspace` and a second kernel
+ * combines them with a log-sum-exp weighting; workspace_bytes must be at least
+ * pa_decode_workspace_bytes(...) (the workspace may be NULL when that is 0).
+ */
+pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t max_context_len, float scale, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                      pa_stream_t stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* pa_status_string(pa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,156 @@
+"""ctypes binding of libpagedkv (include/pagedkv.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls. Tensors are torch tensors on the
+GPU; only their data pointers, shapes and the current HIP stream cross the boundary. All
+computation happens in the library's HIP kernels. If libpagedkv.so is missing the first
+call raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpagedkv.so")
+
+PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, 1, 2, 3
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_FLAG_BAD_BLOCK_ID = 1
+PA_FLAG_BAD_LENGTH = 2
+PA_FLAG_EMPTY_CONTEXT = 4
+PA_FLAG_BAD_SLOT = 8
+PA_FLAG_BAD_COPY_PAIR = 16
+
+EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_size",
+            "pa_decode_workspace_bytes", "pa_decode", "pa_status_string")
+
+_DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+
+class pa_cache_desc_t(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class CacheDesc:
+    num_blocks: int
+    block_size: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: int
+
+    @staticmethod
+    def of(k_pool: torch.Tensor) -> "CacheDesc":
+        """Describe a [num_blocks][kv_heads][block_size][head_dim] pool tensor."""
+        nb, hkv, bs, d = k_pool.shape
+        return CacheDesc(int(nb), int(bs), int(hkv), int(d), _DTYPE_CODE[k_pool.dtype])
+
+    def c(self) -> pa_cache_desc_t:
+        return pa_cache_desc_t(self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim,
+                               self.dtype)
+
+
+class PagedKVError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpagedkv.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise PagedKVError(f"{path} is missing: build it with python -m paged_kv_cache_indexed_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    D = ctypes.POINTER(pa_cache_desc_t)
+    lib.pa_reshape_and_cache.argtypes = [D, P, P, P, P, P, I32, P, P]
+    lib.pa_reshape_and_cache.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [D, P, P, P, I32, P, P]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_decode_partition_size.argtypes = [D, I32, I32, I32, I32]
+    lib.pa_decode_partition_size.restype = I32
+    lib.pa_decode_workspace_bytes.argtypes = [D, I32, I32, I32, I32]
+    lib.pa_decode_workspace_bytes.restype = SZ
+    lib.pa_decode.argtypes = [D, P, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, SZ, P, P]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise PagedKVError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise PagedKVError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        raise PagedKVError(pa_status_string(status))
+
+
+def pa_status_string(status: int) -> str:
+    return load().pa_status_string(int(status)).decode()
+
+
+def pa_reshape_and_cache(cache: CacheDesc, key, value, k_pool, v_pool, slot_mapping,
+                         err_flag=None, stream=None) -> None:
+    n = int(slot_mapping.numel())
+    desc = cache.c()
+    _check(load().pa_reshape_and_cache(ctypes.byref(desc), _ptr(key), _ptr(value), _ptr(k_pool),
+                                       _ptr(v_pool), _ptr(slot_mapping), n, _ptr(err_flag),
+                                       _stream(stream)))
+
+
+def pa_copy_blocks(cache: CacheDesc, k_pool, v_pool, pairs, err_flag=None, stream=None) -> None:
+    n = int(pairs.shape[0]) if pairs is not None else 0
+    desc = cache.c()
+    _check(load().pa_copy_blocks(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(pairs) if n else None, n, _ptr(err_flag), _stream(stream)))
+
+
+def pa_decode_partition_size(cache: CacheDesc, batch: int, num_q_heads: int, max_context_len: int,
+                             requested: int = 0) -> int:
+    desc = cache.c()
+    return int(load().pa_decode_partition_size(ctypes.byref(desc), batch, num_q_heads,
+                                               max_context_len, requested))
+
+
+def pa_decode_workspace_bytes(cache: CacheDesc, batch: int, num_q_heads: int, max_context_len: int,
+                              partition_size: int = 0) -> int:
+    desc = cache.c()
+    return int(load().pa_decode_workspace_bytes(ctypes.byref(desc), batch, num_q_heads,
+                                                max_context_len, partition_size))
+
+
+def pa_decode(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_lens,
+              max_context_len: int, scale: float, partition_size: int = 0, workspace=None,
+              err_flag=None, stream=None) -> None:
+    batch, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    desc = cache.c()
+    _check(load().pa_decode(ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                            _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens),
+                            batch, num_q_heads, int(max_context_len), float(scale),
+                            int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag),
+                            _stream(stream)))

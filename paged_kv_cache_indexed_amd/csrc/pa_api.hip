@@ -1,0 +1,172 @@
+// C ABI of libpagedkv: argument checks, launch-shape policy and kernel dispatch.
+// No compute happens here; every step of the path runs in the HIP kernels.
+#include <math.h>
+
+#include "pa_kernels.h"
+
+using namespace pagedkv;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_exact(int x) {
+    if (x <= 0 || (x & (x - 1))) return -1;
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
+int dtype_bytes(int dtype) {
+    switch (dtype) {
+        case PA_F32: return 4;
+        case PA_F16:
+        case PA_BF16: return 2;
+        default: return 0;
+    }
+}
+
+pa_status_t check_cache(const pa_cache_desc_t* c) {
+    if (!c) return PA_ERR_INVALID_ARGUMENT;
+    if (dtype_bytes(c->dtype) == 0) return PA_ERR_UNSUPPORTED;
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return PA_ERR_UNSUPPORTED;
+    const int lbs = log2_exact(c->block_size);
+    if (lbs < 3 || lbs > 9) return PA_ERR_UNSUPPORTED;  // 8 .. 512 tokens per block
+    if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->num_kv_heads > 65535) return PA_ERR_INVALID_ARGUMENT;
+    // one pool must be addressable with the kernels' 64-bit byte offsets and 32-bit slots
+    if ((int64_t)c->num_blocks * c->block_size > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
+    return PA_OK;
+}
+
+pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status_t s) {
+    switch (s) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT: bad pointer, size or workspace";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: dtype, head_dim, block_size or group not built";
+        case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime refused a kernel launch";
+        default: return "unknown pa_status_t";
+    }
+}
+
+pa_status_t pa_reshape_and_cache(const pa_cache_desc_t* cache, const void* key, const void* value,
+                                 void* k_pool, void* v_pool, const int32_t* slot_mapping,
+                                 int32_t num_tokens, int32_t* err_flag, pa_stream_t stream) {
+    pa_status_t st = check_cache(cache);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_INVALID_ARGUMENT;
+    CacheArgs a{k_pool, v_pool, err_flag, cache->num_blocks, log2_exact(cache->block_size),
+                cache->num_kv_heads, cache->head_dim * dtype_bytes(cache->dtype) / 16};
+    return from_hip(launch_reshape_and_cache(a, key, value, slot_mapping, num_tokens, (hipStream_t)stream));
+}
+
+pa_status_t pa_copy_blocks(const pa_cache_desc_t* cache, void* k_pool, void* v_pool, const int32_t* pairs,
+                           int32_t num_pairs, int32_t* err_flag, pa_stream_t stream) {
+    pa_status_t st = check_cache(cache);
+    if (st != PA_OK) return st;
+    if (num_pairs < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_pool || !v_pool || !pairs) return PA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARGUMENT;
+    CacheArgs a{k_pool, v_pool, err_flag, cache->num_blocks, log2_exact(cache->block_size),
+                cache->num_kv_heads, cache->head_dim * dtype_bytes(cache->dtype) / 16};
+    return from_hip(launch_copy_blocks(a, pairs, num_pairs, (hipStream_t)stream));
+}
+
+int32_t pa_decode_partition_size(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_heads,
+                                 int32_t max_context_len, int32_t requested) {
+    (void)num_q_heads;
+    if (check_cache(cache) != PA_OK || batch < 0 || max_context_len <= 0) return -1;
+    const int bs = cache->block_size;
+    const int64_t max_p = (int64_t)kMaxIdsPerPartition * bs;
+    if (requested > 0) {
+        if (requested % bs != 0 || requested > max_p) return -1;
+        return requested;
+    }
+    // Default: one workgroup per (sequence, kv head) when contexts are short and there are
+    // enough of them to fill the chip; otherwise 512-token partitions, shortened until the
+    // launch has about 2048 workgroups (8 per compute unit).
+    const int64_t wgs = (int64_t)batch * cache->num_kv_heads;
+    const int64_t whole = ceil_div(max_context_len, bs) * bs;
+    if (max_context_len <= 1024 && wgs >= 1024 && whole <= max_p) return (int32_t)whole;
+    int64_t P = ceil_div(512 > bs ? 512 : bs, bs) * bs;
+    if (wgs * ceil_div(max_context_len, P) < 2048) {
+        int64_t want = ceil_div((int64_t)max_context_len * wgs, 2048);
+        const int64_t floor_p = bs > 64 ? bs : 64;
+        if (want < floor_p) want = floor_p;
+        P = ceil_div(want, bs) * bs;
+    }
+    if (P > max_p) P = max_p;
+    return (int32_t)P;
+}
+
+size_t pa_decode_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_heads,
+                                 int32_t max_context_len, int32_t partition_size) {
+    const int32_t P = pa_decode_partition_size(cache, batch, num_q_heads, max_context_len, partition_size);
+    if (P <= 0 || num_q_heads <= 0) return 0;
+    const int64_t parts = ceil_div(max_context_len, P);
+    if (parts <= 1) return 0;
+    return (size_t)batch * num_q_heads * parts * (cache->head_dim + 2) * sizeof(float);
+}
+
+pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream) {
+    pa_status_t st = check_cache(cache);
+    if (st != PA_OK) return st;
+    if (batch < 0 || batch > 65535) return PA_ERR_INVALID_ARGUMENT;
+    if (batch == 0) return PA_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_INVALID_ARGUMENT;
+    if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+    const int group = num_q_heads / cache->num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return PA_ERR_UNSUPPORTED;
+    if (group == 16 && cache->head_dim > 128) return PA_ERR_UNSUPPORTED;
+    if (max_blocks_per_seq <= 0 || max_context_len <= 0) return PA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * cache->block_size) return PA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+    const int32_t P = pa_decode_partition_size(cache, batch, num_q_heads, max_context_len, partition_size);
+    if (P <= 0) return PA_ERR_INVALID_ARGUMENT;
+    const int64_t parts = ceil_div(max_context_len, P);
+    if (parts > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
+    const size_t need = pa_decode_workspace_bytes(cache, batch, num_q_heads, max_context_len, partition_size);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_INVALID_ARGUMENT;
+
+    DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = need > 0 ? a.ws_o + (size_t)batch * num_q_heads * parts * cache->head_dim : nullptr;
+    a.err_flag = err_flag;
+    a.num_blocks = cache->num_blocks;
+    a.log2_block_size = log2_exact(cache->block_size);
+    a.num_kv_heads = cache->num_kv_heads;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.partition_size = P;
+    a.max_partitions = (int32_t)parts;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return from_hip(launch_decode(a, cache->dtype, cache->head_dim, group, batch, cache->num_kv_heads,
+                                  (hipStream_t)stream));
+}
+
+}  // extern "C"

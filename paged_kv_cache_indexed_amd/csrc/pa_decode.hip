@@ -1,0 +1,336 @@
+// Paged-KV decode attention for gfx950: one workgroup per (context partition, kv head,
+// sequence), a log-sum-exp reduce kernel across partitions.
+//
+// Work decomposition (VALU path, used for every group size):
+//   * A workgroup is 4 wave64s. It owns the tokens [p*P, min(L, (p+1)*P)) of one kv head of
+//     one sequence and the G = Hq/Hkv query heads that read that kv head.
+//   * The partition's slice of the block table is staged in LDS once and checked, so the
+//     per-load address translation is an LDS broadcast read plus scalar arithmetic
+//     ([BlockManager essay] §2 on caching the mapping table on chip).
+//   * A K or V row of one token is head_dim * bytes long and is covered by LPR lanes with
+//     one 16-byte load each; a wave load covers RPL = 64 / LPR consecutive tokens of one
+//     block, 1 KiB of contiguous memory. Token groups of RPL rows are dealt round-robin to
+//     the 4 waves, so the waves of a workgroup stream adjacent KiB of the same block.
+//   * Each group of LPR lanes runs its own online softmax (running max and sum in fp32,
+//     base-2 exponent with the scale folded into q . k) over the tokens it loads, so the
+//     inner loop needs no cross-row traffic; rows are merged with lane shuffles and waves
+//     through LDS at the end.
+//   * Tokens at or past the valid length are never loaded ([Valid-length essay] §4.1-4.2):
+//     their lanes are masked off and contribute exp2(-inf) = 0 with zeroed V.
+//   * Loads for the next UNROLL groups are issued before the current ones are used
+//     (two register buffers), so each lane keeps 2 * 2 * UNROLL 16-byte loads in flight.
+#include "pa_kernels.h"
+
+namespace pagedkv {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+
+template <typename T>
+__device__ __forceinline__ void store_nan_heads(void* out, size_t base, int count) {
+    for (int i = threadIdx.x; i < count; i += kThreads) store_elem(T{}, out, base + i, __builtin_nanf(""));
+}
+
+template <typename T, int D, int G, int UNROLL>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
+    constexpr int E = VecInfo<T>::kElems;  // elements per 16-byte vector
+    constexpr int LPR = D / E;             // lanes per token row
+    constexpr int RPL = 64 / LPR;          // token rows per wave load
+    static_assert(LPR >= 1 && LPR <= 64 && RPL * LPR == 64, "row shape");
+
+    __shared__ int s_ids[kMaxIdsPerPartition];
+    __shared__ int s_bad;
+    __shared__ float s_m[kWaves][G];
+    __shared__ float s_l[kWaves][G];
+    __shared__ float s_acc[kWaves][G][D];
+
+    const int p = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int row = lane / LPR;
+    const int col = lane % LPR;
+    const int h0 = kvh * G;
+    const int lbs = a.log2_block_size;
+    const int bs = 1 << lbs;
+
+    // ---- sequence length checks (never read past what the table can address) ----
+    const int L = a.context_lens[b];
+    int flag = 0;
+    if (L <= 0) flag = PA_FLAG_EMPTY_CONTEXT;
+    else if (L > a.max_context_len || (L - 1) >> lbs >= a.max_blocks_per_seq) flag = PA_FLAG_BAD_LENGTH;
+    if (flag) {
+        if (p == 0) {
+            if (tid == 0 && a.err_flag) atomicOr(a.err_flag, flag);
+            store_nan_heads<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, G * D);
+        }
+        return;
+    }
+    const int P = a.partition_size;
+    const int nparts = (L + P - 1) / P;
+    if (p >= nparts) return;
+    const int t0 = p * P;
+    const int t1 = min(L, t0 + P);
+    const int j0 = t0 >> lbs;
+    const int nids = ((t1 - 1) >> lbs) - j0 + 1;
+
+    // ---- stage and check this partition's block ids ----
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq + j0;
+    for (int i = tid; i < nids; i += kThreads) {
+        int id = trow[i];
+        if ((unsigned)id >= (unsigned)a.num_blocks) {
+            s_bad = 1;
+            id = 0;
+        }
+        s_ids[i] = id;
+    }
+    __syncthreads();
+    if (s_bad) {
+        if (tid == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_BLOCK_ID);
+        if (nparts == 1) {
+            store_nan_heads<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, G * D);
+        } else {
+            for (int i = tid; i < G * (D + 2); i += kThreads) {
+                const int g = i / (D + 2), e = i % (D + 2);
+                const size_t rec = ((size_t)b * a.num_q_heads + h0 + g) * a.max_partitions + p;
+                if (e < D) a.ws_o[rec * D + e] = __builtin_nanf("");
+                else a.ws_ml[rec * 2 + (e - D)] = (e == D) ? -INFINITY : __builtin_nanf("");
+            }
+        }
+        return;
+    }
+
+    // ---- q slices of the G heads, kept in storage form ----
+    u32x4 qv[G];
+    const char* qbase = static_cast<const char*>(a.q) + (((size_t)b * a.num_q_heads + h0) * D + col * E) * T::kBytes;
+#pragma unroll
+    for (int g = 0; g < G; ++g) qv[g] = load16(qbase + (size_t)g * D * T::kBytes);
+
+    // ---- main loop ----
+    const size_t head_bytes = (size_t)bs * D * T::kBytes;
+    const size_t block_bytes = head_bytes * a.num_kv_heads;
+    const size_t lane_off = (size_t)kvh * head_bytes + ((size_t)row * D + col * E) * T::kBytes;
+    const char* kbase = static_cast<const char*>(a.k_pool) + lane_off;
+    const char* vbase = static_cast<const char*>(a.v_pool) + lane_off;
+    const int ntok = t1 - t0;
+    constexpr int kTokPerIter = UNROLL * kWaves * RPL;
+    const int niters = (ntok + kTokPerIter - 1) / kTokPerIter;
+
+    float m[G], l[G], acc[G][E];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+    }
+
+    auto issue = [&](int it, u32x4* kk, u32x4* vv) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int rel = ((it * UNROLL + u) * kWaves + wave) * RPL;  // wave-uniform
+            kk[u] = u32x4{0, 0, 0, 0};
+            vv[u] = u32x4{0, 0, 0, 0};
+            if (rel < ntok) {
+                const int tb = t0 + rel;
+                const int id = __builtin_amdgcn_readfirstlane(s_ids[(tb >> lbs) - j0]);
+                const size_t off = (size_t)id * block_bytes + (size_t)(tb & (bs - 1)) * D * T::kBytes;
+                if (rel + row < ntok) {
+                    kk[u] = load16(kbase + off);
+                    vv[u] = load16(vbase + off);
+                }
+            }
+        }
+    };
+
+    auto compute = [&](int it, const u32x4* kk, const u32x4* vv) {
+        float s[G][UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int rel = ((it * UNROLL + u) * kWaves + wave) * RPL + row;
+            const bool valid = rel < ntok;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float d = group_sum<LPR>(dot16(T{}, qv[g], kk[u]));
+                s[g][u] = valid ? d * a.scale_log2 : -INFINITY;
+            }
+        }
+        float vf[UNROLL][E];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) unpack(T{}, vv[u], vf[u]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float cm = s[g][0];
+#pragma unroll
+            for (int u = 1; u < UNROLL; ++u) cm = fmaxf(cm, s[g][u]);
+            const float mn = fmaxf(m[g], cm);
+            const float ms = (mn == -INFINITY) ? 0.f : mn;
+            const float alpha = fast_exp2(m[g] - ms);
+            m[g] = mn;
+            l[g] *= alpha;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const float pr = fast_exp2(s[g][u] - ms);
+                l[g] += pr;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pr, vf[u][e], acc[g][e]);
+            }
+        }
+    };
+
+    u32x4 ka[UNROLL], va[UNROLL], kb[UNROLL], vb[UNROLL];
+    issue(0, ka, va);
+    for (int it = 0; it < niters; it += 2) {
+        issue(it + 1, kb, vb);
+        compute(it, ka, va);
+        if (it + 1 >= niters) break;
+        issue(it + 2, ka, va);
+        compute(it + 1, kb, vb);
+    }
+
+    // ---- merge the RPL row streams of this wave ----
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mo = shfl_xor(m[g], off);
+            const float lo = shfl_xor(l[g], off);
+            const float mn = fmaxf(m[g], mo);
+            const float ms = (mn == -INFINITY) ? 0.f : mn;
+            const float fa = fast_exp2(m[g] - ms);
+            const float fb = fast_exp2(mo - ms);
+            l[g] = l[g] * fa + lo * fb;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[g][e] = acc[g][e] * fa + shfl_xor(acc[g][e], off) * fb;
+            m[g] = mn;
+        }
+    }
+    if (row == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) s_acc[wave][g][col * E + e] = acc[g][e];
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            s_m[wave][g] = m[g];
+            s_l[wave][g] = l[g];
+        }
+    }
+    __syncthreads();
+
+    // ---- merge the waves and write ----
+    for (int i = tid; i < G * D; i += kThreads) {
+        const int g = i / D;
+        const int e = i % D;
+        float M = s_m[0][g];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
+        const float Ms = (M == -INFINITY) ? 0.f : M;
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = fast_exp2(s_m[w][g] - Ms);
+            num = fmaf(s_acc[w][g][e], f, num);
+            den = fmaf(s_l[w][g], f, den);
+        }
+        const float o = num / den;
+        const size_t hrow = (size_t)b * a.num_q_heads + h0 + g;
+        if (nparts == 1) {
+            store_elem(T{}, a.out, hrow * D + e, o);
+        } else {
+            const size_t rec = hrow * a.max_partitions + p;
+            a.ws_o[rec * D + e] = o;
+            if (e == 0) {
+                a.ws_ml[rec * 2] = M;
+                a.ws_ml[rec * 2 + 1] = den;
+            }
+        }
+    }
+}
+
+// Log-sum-exp combine of the per-partition records of one (sequence, query head):
+//   out = sum_p w_p o_p / sum_p w_p,  w_p = l_p * 2^(m_p - max_p m_p),
+// where o_p is the partition's normalised output and (m_p, l_p) its base-2 running max and
+// sum. A NaN sum (bad block in that partition) makes the whole output NaN.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
+    const int h = blockIdx.x;
+    const int b = blockIdx.y;
+    const int e = threadIdx.x;
+    const int L = a.context_lens[b];
+    if (L <= 0 || L > a.max_context_len || (L - 1) >> a.log2_block_size >= a.max_blocks_per_seq) return;
+    const int nparts = (L + a.partition_size - 1) / a.partition_size;
+    if (nparts <= 1) return;
+    const size_t rec0 = ((size_t)b * a.num_q_heads + h) * a.max_partitions;
+    const float* ml = a.ws_ml + rec0 * 2;
+    float M = -INFINITY;
+    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
+    float num = 0.f, den = 0.f;
+    for (int p = 0; p < nparts; ++p) {
+        const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+        den += w;
+        num = fmaf(w, a.ws_o[(rec0 + p) * D + e], num);
+    }
+    store_elem(T{}, a.out, ((size_t)b * a.num_q_heads + h) * D + e, num / den);
+}
+
+template <typename T, int D, int G>
+hipError_t launch_decode_tgd(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
+    constexpr int UNROLL = G <= 2 ? 4 : (G <= 4 ? 2 : 1);
+    dim3 grid(a.max_partitions, num_kv_heads, batch);
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, G, UNROLL>), grid, dim3(kThreads), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || a.max_partitions <= 1) return err;
+    hipLaunchKernelGGL((reduce_kernel<T, D>), dim3(a.num_q_heads, batch), dim3(D), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_decode_td(const DecodeArgs& a, int group, int batch, int num_kv_heads, hipStream_t s) {
+    switch (group) {
+        case 1: return launch_decode_tgd<T, D, 1>(a, batch, num_kv_heads, s);
+        case 2: return launch_decode_tgd<T, D, 2>(a, batch, num_kv_heads, s);
+        case 4: return launch_decode_tgd<T, D, 4>(a, batch, num_kv_heads, s);
+        case 8: return launch_decode_tgd<T, D, 8>(a, batch, num_kv_heads, s);
+        case 16:
+            if constexpr (D <= 128) return launch_decode_tgd<T, D, 16>(a, batch, num_kv_heads, s);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_decode_t(const DecodeArgs& a, int head_dim, int group, int batch, int num_kv_heads,
+                           hipStream_t s) {
+    switch (head_dim) {
+        case 64: return launch_decode_td<T, 64>(a, group, batch, num_kv_heads, s);
+        case 128: return launch_decode_td<T, 128>(a, group, batch, num_kv_heads, s);
+        case 256: return launch_decode_td<T, 256>(a, group, batch, num_kv_heads, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
+                         int num_kv_heads, hipStream_t stream) {
+    switch (dtype) {
+        case PA_F32: return launch_decode_t<F32>(a, head_dim, group, batch, num_kv_heads, stream);
+        case PA_F16: return launch_decode_t<F16>(a, head_dim, group, batch, num_kv_heads, stream);
+        case PA_BF16: return launch_decode_t<BF16>(a, head_dim, group, batch, num_kv_heads, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pagedkv

@@ -1,0 +1,126 @@
+// Device helpers for the gfx950 (CDNA4) paged-KV kernels: storage types, 16-byte vector
+// access, conversions and wave64 cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pagedkv {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Storage tags. Every element type is moved as raw 16-byte vectors; the tag says how the
+// lanes of a vector unpack to fp32 and how fp32 results round back.
+struct F32 {
+    static constexpr int kBytes = 4;
+};
+struct F16 {
+    static constexpr int kBytes = 2;
+};
+struct BF16 {
+    static constexpr int kBytes = 2;
+};
+
+template <typename T>
+struct VecInfo {
+    static constexpr int kElems = 16 / T::kBytes;  // elements per 16-byte vector
+};
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ---- unpack 16 bytes to fp32 -------------------------------------------------------------
+__device__ __forceinline__ void unpack(F32, u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+}
+__device__ __forceinline__ void unpack(F16, u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f16x2 h = __builtin_bit_cast(f16x2, v[i]);
+        f[2 * i] = (float)h.x;
+        f[2 * i + 1] = (float)h.y;
+    }
+}
+__device__ __forceinline__ void unpack(BF16, u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(v[i] << 16);
+        f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+}
+
+// ---- partial dot product of one 16-byte vector of K with the matching slice of q ---------
+// q is kept in its storage form; products are exact in fp32 and accumulate in fp32.
+__device__ __forceinline__ float dot16(F32, u32x4 q, u32x4 k) {
+    float s = __uint_as_float(q[0]) * __uint_as_float(k[0]);
+    s = fmaf(__uint_as_float(q[1]), __uint_as_float(k[1]), s);
+    s = fmaf(__uint_as_float(q[2]), __uint_as_float(k[2]), s);
+    s = fmaf(__uint_as_float(q[3]), __uint_as_float(k[3]), s);
+    return s;
+}
+__device__ __forceinline__ float dot16(F16, u32x4 q, u32x4 k) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q[i]), __builtin_bit_cast(f16x2, k[i]), s, false);
+    return s;
+}
+__device__ __forceinline__ float dot16(BF16, u32x4 q, u32x4 k) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[i]), __builtin_bit_cast(bf16x2, k[i]), s, false);
+    return s;
+}
+
+// ---- fp32 -> storage (round to nearest even) ---------------------------------------------
+__device__ __forceinline__ void store_elem(F32, void* base, size_t i, float x) {
+    reinterpret_cast<float*>(base)[i] = x;
+}
+__device__ __forceinline__ void store_elem(F16, void* base, size_t i, float x) {
+    reinterpret_cast<_Float16*>(base)[i] = (_Float16)x;
+}
+__device__ __forceinline__ void store_elem(BF16, void* base, size_t i, float x) {
+    reinterpret_cast<__bf16*>(base)[i] = (__bf16)x;
+}
+
+// ---- wave64 cross-lane helpers -------------------------------------------------------------
+// DPP control words (GCN/CDNA encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm:[1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm:[2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) {
+    const int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+// Sum over aligned groups of N lanes; every lane of a group receives the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group");
+    if constexpr (N >= 2) x += dpp<kDppQuadXor1>(x);
+    if constexpr (N >= 4) x += dpp<kDppQuadXor2>(x);
+    if constexpr (N >= 8) x += dpp<kDppRowHalfMirror>(x);
+    if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
+    if constexpr (N >= 32) x += shfl_xor(x, 16);
+    if constexpr (N >= 64) x += shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pagedkv

@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI layer (pa_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+#include "pa_device.h"
+
+namespace pagedkv {
+
+// Largest number of block-table entries one decode partition stages in LDS.
+constexpr int kMaxIdsPerPartition = 1024;
+
+struct DecodeArgs {
+    void* out;
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    float* ws_o;   // [batch][num_q_heads][max_partitions][head_dim]
+    float* ws_ml;  // [batch][num_q_heads][max_partitions][2] = (base-2 max, sum)
+    int32_t* err_flag;
+    int32_t num_blocks;
+    int32_t log2_block_size;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;
+    int32_t partition_size;
+    int32_t max_partitions;
+    float scale_log2;  // scale * log2(e): scores live in the base-2 exponent domain
+};
+
+struct CacheArgs {
+    void* k_pool;
+    void* v_pool;
+    int32_t* err_flag;
+    int32_t num_blocks;
+    int32_t log2_block_size;
+    int32_t num_kv_heads;
+    int32_t row_vecs;  // 16-byte vectors per [head_dim] row
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
+                         int num_kv_heads, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const CacheArgs& a, const void* key, const void* value,
+                                    const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
+
+hipError_t launch_copy_blocks(const CacheArgs& a, const int32_t* pairs, int32_t num_pairs,
+                              hipStream_t stream);
+
+}  // namespace pagedkv

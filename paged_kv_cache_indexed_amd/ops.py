@@ -1,0 +1,42 @@
+"""Torch-facing helpers over the C ABI: allocate outputs and workspaces, then call the library.
+
+Allocation is torch's; every arithmetic step runs in libpagedkv's HIP kernels.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from ._lib import (CacheDesc, pa_copy_blocks, pa_decode, pa_decode_workspace_bytes,
+                   pa_reshape_and_cache)
+
+
+def workspace_for(k_pool: torch.Tensor, batch: int, num_q_heads: int, max_context_len: int,
+                  partition_size: int = 0):
+    """A float32 workspace tensor of the size pa_decode needs, or None if it needs none."""
+    n = pa_decode_workspace_bytes(CacheDesc.of(k_pool), batch, num_q_heads, max_context_len,
+                                  partition_size)
+    if n == 0:
+        return None
+    return torch.empty((n + 3) // 4, dtype=torch.float32, device=k_pool.device)
+
+
+def decode(q, k_pool, v_pool, block_table, context_lens, max_context_len: int, scale: float,
+           partition_size: int = 0, out=None, workspace=None, err_flag=None, stream=None):
+    """Paged decode attention; returns ``out`` [batch][num_q_heads][head_dim] in q's dtype."""
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = workspace_for(k_pool, q.shape[0], q.shape[1], max_context_len, partition_size)
+    pa_decode(CacheDesc.of(k_pool), out, q, k_pool, v_pool, block_table, context_lens,
+              max_context_len, scale, partition_size, workspace, err_flag, stream)
+    return out
+
+
+def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, err_flag=None, stream=None):
+    pa_reshape_and_cache(CacheDesc.of(k_pool), key, value, k_pool, v_pool, slot_mapping, err_flag,
+                         stream)
+
+
+def copy_blocks(k_pool, v_pool, pairs, err_flag=None, stream=None):
+    pa_copy_blocks(CacheDesc.of(k_pool), k_pool, v_pool, pairs, err_flag, stream)

@@ -1,0 +1,85 @@
+"""C ABI: libpagedkv.so loads, exports every function include/pagedkv.h declares, and its
+host-only helpers (status text, partition policy, workspace size) behave. No kernels run."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_indexed_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from paged_kv_cache_indexed_amd.build import build
+        build()
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    assert _lib.pa_status_string(0) == "PA_OK"
+    assert "INVALID" in _lib.pa_status_string(1)
+    assert "UNSUPPORTED" in _lib.pa_status_string(2)
+    assert "LAUNCH" in _lib.pa_status_string(3)
+
+
+def _desc(bs=16, hkv=32, d=128, dtype=_lib.PA_F16, nb=1000):
+    return _lib.CacheDesc(nb, bs, hkv, d, dtype)
+
+
+def test_partition_policy(lib):
+    c = _desc()
+    # short contexts with enough (sequence, kv head) pairs: one partition, whole length
+    assert _lib.pa_decode_partition_size(c, 64, 32, 521, 0) == 528
+    assert _lib.pa_decode_workspace_bytes(c, 64, 32, 521, 0) == 0
+    # long contexts: 512-token partitions
+    assert _lib.pa_decode_partition_size(_desc(bs=32), 32, 32, 32769, 0) == 512
+    assert _lib.pa_decode_workspace_bytes(_desc(bs=32), 32, 32, 32769, 0) == 32 * 32 * 65 * 130 * 4
+    # few workgroups: partitions shrink toward ~2048 workgroups
+    p = _lib.pa_decode_partition_size(_desc(hkv=8, dtype=_lib.PA_BF16), 32, 64, 2049, 0)
+    assert p % 16 == 0 and 32 * 8 * -(-2049 // p) >= 2048 - 256
+    # explicit sizes must be block multiples and fit the LDS id table
+    assert _lib.pa_decode_partition_size(c, 4, 32, 100, 24) == -1
+    assert _lib.pa_decode_partition_size(c, 4, 32, 100, 64) == 64
+    assert _lib.pa_decode_partition_size(_desc(bs=8), 4, 32, 100, 8192) == 8192
+    assert _lib.pa_decode_partition_size(_desc(bs=8), 4, 32, 100, 8200) == -1
+
+
+def test_unsupported_and_invalid_caches(lib):
+    assert _lib.pa_decode_partition_size(_desc(bs=12), 4, 32, 100, 0) == -1
+    assert _lib.pa_decode_partition_size(_desc(d=96), 4, 32, 100, 0) == -1
+    assert _lib.pa_decode_partition_size(_desc(dtype=7), 4, 32, 100, 0) == -1
+    # argument errors come back before any launch (null pointers; batch 0 is a no-op)
+    d = _desc().c()
+    st = lib.pa_decode(ctypes.byref(d), None, None, None, None, None, 4, None, 2, 32, 10, 1.0,
+                       0, None, 0, None, None)
+    assert st == _lib.PA_ERR_INVALID_ARGUMENT
+    st = lib.pa_decode(ctypes.byref(d), None, None, None, None, None, 4, None, 0, 32, 10, 1.0,
+                       0, None, 0, None, None)
+    assert st == _lib.PA_OK
+    st = lib.pa_reshape_and_cache(ctypes.byref(d), None, None, None, None, None, 0, None, None)
+    assert st == _lib.PA_OK
+    st = lib.pa_copy_blocks(ctypes.byref(d), None, None, None, -1, None, None)
+    assert st == _lib.PA_ERR_INVALID_ARGUMENT
+    bad = _desc(bs=1024).c()
+    st = lib.pa_copy_blocks(ctypes.byref(bad), None, None, None, 0, None, None)
+    assert st == _lib.PA_ERR_UNSUPPORTED

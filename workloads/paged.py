@@ -83,6 +83,27 @@ class PagedWorkload:
     def lens_after_append(self) -> np.ndarray:
         return (self.context_lens + 1).astype(np.int32)
 
+    @property
+    def torch_dtype(self):
+        return _TORCH_DTYPES[self.dtype]
+
+    def to_device(self, device="cuda") -> dict:
+        """Upload every array (floats in the storage dtype, ints as int32)."""
+        dt = _TORCH_DTYPES[self.dtype]
+
+        def f(x):
+            # cast on the CPU first so NaN payloads match a CPU-side cast bit for bit
+            return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dt).to(device)
+
+        def i(x):
+            return torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(device)
+
+        return dict(q=f(self.q), k_pool=f(self.k_pool), v_pool=f(self.v_pool),
+                    block_table=i(self.block_table), context_lens=i(self.context_lens),
+                    lens_after=i(self.lens_after_append), new_key=f(self.new_key),
+                    new_value=f(self.new_value), slot_mapping=i(self.slot_mapping),
+                    copy_pairs=i(self.copy_pairs.reshape(-1, 2)))
+
 
 def _allocate_tables(rng_layout: np.random.Generator, lens: np.ndarray, bs: int,
                      num_blocks: int | None, spare: float, max_blocks_per_seq: int | None,
