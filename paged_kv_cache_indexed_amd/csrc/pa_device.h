@@ -9,7 +9,13 @@ namespace pagedkv {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Note: every reinterpretation below bit-casts the whole 16-byte vector and then takes
+// constant swizzles. Bit-casting single elements of a u32x4 (bit_cast<f16x2>(v[i]))
+// miscompiles with this toolchain: every i reads element 0.
 
 // Storage tags. Every element type is moved as raw 16-byte vectors; the tag says how the
 // lanes of a vector unpack to fp32 and how fp32 results round back.
@@ -41,12 +47,9 @@ __device__ __forceinline__ void unpack(F32, u32x4 v, float* f) {
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
 }
 __device__ __forceinline__ void unpack(F16, u32x4 v, float* f) {
+    const f16x8 h = __builtin_bit_cast(f16x8, v);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f16x2 h = __builtin_bit_cast(f16x2, v[i]);
-        f[2 * i] = (float)h.x;
-        f[2 * i + 1] = (float)h.y;
-    }
+    for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
 }
 __device__ __forceinline__ void unpack(BF16, u32x4 v, float* f) {
 #pragma unroll
@@ -66,18 +69,20 @@ __device__ __forceinline__ float dot16(F32, u32x4 q, u32x4 k) {
     return s;
 }
 __device__ __forceinline__ float dot16(F16, u32x4 q, u32x4 k) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q[i]), __builtin_bit_cast(f16x2, k[i]), s, false);
-    return s;
+    const f16x8 a = __builtin_bit_cast(f16x8, q);
+    const f16x8 b = __builtin_bit_cast(f16x8, k);
+    float s = __builtin_amdgcn_fdot2(a.s01, b.s01, 0.f, false);
+    s = __builtin_amdgcn_fdot2(a.s23, b.s23, s, false);
+    s = __builtin_amdgcn_fdot2(a.s45, b.s45, s, false);
+    return __builtin_amdgcn_fdot2(a.s67, b.s67, s, false);
 }
 __device__ __forceinline__ float dot16(BF16, u32x4 q, u32x4 k) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[i]), __builtin_bit_cast(bf16x2, k[i]), s, false);
-    return s;
+    const bf16x8 a = __builtin_bit_cast(bf16x8, q);
+    const bf16x8 b = __builtin_bit_cast(bf16x8, k);
+    float s = __builtin_amdgcn_fdot2_f32_bf16(a.s01, b.s01, 0.f, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(a.s23, b.s23, s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(a.s45, b.s45, s, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(a.s67, b.s67, s, false);
 }
 
 // ---- fp32 -> storage (round to nearest even) ---------------------------------------------
