@@ -15,7 +15,8 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libpagedkv.so")
+# PAGEDKV_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_PKG, "libpagedkv.so")
 
 PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, 1, 2, 3
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2

@@ -86,28 +86,42 @@ pa_status_t pa_copy_blocks(const pa_cache_desc_t* cache, void* k_pool, void* v_p
 
 int32_t pa_decode_partition_size(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_heads,
                                  int32_t max_context_len, int32_t requested) {
-    (void)num_q_heads;
-    if (check_cache(cache) != PA_OK || batch < 0 || max_context_len <= 0) return -1;
+    if (check_cache(cache) != PA_OK || batch < 0 || max_context_len <= 0 || num_q_heads <= 0) return -1;
     const int bs = cache->block_size;
     const int64_t max_p = (int64_t)kMaxIdsPerPartition * bs;
     if (requested > 0) {
         if (requested % bs != 0 || requested > max_p) return -1;
         return requested;
     }
-    // Default: one workgroup per (sequence, kv head) when contexts are short and there are
-    // enough of them to fill the chip; otherwise 512-token partitions, shortened until the
-    // launch has about 2048 workgroups (8 per compute unit).
+    // Defaults, from measurements on MI355X. Each workgroup pays a fixed prologue (length,
+    // table and q loads) and epilogue, and splitting a sequence adds the reduce pass, so
+    // partitions are as long as the launch shape allows.
     const int64_t wgs = (int64_t)batch * cache->num_kv_heads;
     const int64_t whole = ceil_div(max_context_len, bs) * bs;
-    if (max_context_len <= 1024 && wgs >= 1024 && whole <= max_p) return (int32_t)whole;
-    int64_t P = ceil_div(512 > bs ? 512 : bs, bs) * bs;
-    if (wgs * ceil_div(max_context_len, P) < 2048) {
-        int64_t want = ceil_div((int64_t)max_context_len * wgs, 2048);
-        const int64_t floor_p = bs > 64 ? bs : 64;
-        if (want < floor_p) want = floor_p;
-        P = ceil_div(want, bs) * bs;
+    const int group = num_q_heads % cache->num_kv_heads == 0 ? num_q_heads / cache->num_kv_heads : 1;
+    int64_t P;
+    if (decode_mfma_supported(cache->dtype, cache->head_dim, group, bs)) {
+        // Matrix-core path: one 4-wave workgroup per compute unit already streams at its
+        // best; split only to reach 256 workgroups or to cap a partition at 4096 tokens.
+        int64_t parts = wgs >= 256 ? 1 : ceil_div(256, wgs > 0 ? wgs : 1);
+        if (parts < ceil_div(max_context_len, 4096)) parts = ceil_div(max_context_len, 4096);
+        P = ceil_div(ceil_div(max_context_len, parts), bs) * bs;
+    } else if (max_context_len <= 1024 && wgs >= 1024) {
+        // VALU path, short contexts and enough (sequence, kv head) pairs: no split.
+        P = whole;
+    } else {
+        // VALU path: 512-token partitions, shortened until the launch has about 2048
+        // workgroups (8 per compute unit).
+        P = ceil_div(512 > bs ? 512 : bs, bs) * bs;
+        if (wgs * ceil_div(max_context_len, P) < 2048) {
+            int64_t want = ceil_div((int64_t)max_context_len * wgs, 2048);
+            const int64_t floor_p = bs > 64 ? bs : 64;
+            if (want < floor_p) want = floor_p;
+            P = ceil_div(want, bs) * bs;
+        }
     }
     if (P > max_p) P = max_p;
+    if (P > whole) P = whole;
     return (int32_t)P;
 }
 
@@ -165,8 +179,12 @@ pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, co
     a.partition_size = P;
     a.max_partitions = (int32_t)parts;
     a.scale_log2 = scale * 1.4426950408889634f;
-    return from_hip(launch_decode(a, cache->dtype, cache->head_dim, group, batch, cache->num_kv_heads,
-                                  (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = decode_mfma_supported(cache->dtype, cache->head_dim, group, cache->block_size)
+                       ? launch_decode_mfma(a, cache->dtype, cache->head_dim, group, batch, cache->num_kv_heads, s)
+                       : launch_decode_valu(a, cache->dtype, cache->head_dim, group, batch, cache->num_kv_heads, s);
+    if (e == hipSuccess && parts > 1) e = launch_reduce(a, cache->dtype, cache->head_dim, batch, s);
+    return from_hip(e);
 }
 
 }  // extern "C"

@@ -16,22 +16,19 @@
 //     inner loop needs no cross-row traffic; rows are merged with lane shuffles and waves
 //     through LDS at the end.
 //   * Tokens at or past the valid length are never loaded ([Valid-length essay] §4.1-4.2):
-//     their lanes are masked off and contribute exp2(-inf) = 0 with zeroed V.
-//   * Loads for the next UNROLL groups are issued before the current ones are used
-//     (two register buffers), so each lane keeps 2 * 2 * UNROLL 16-byte loads in flight.
-#include "pa_kernels.h"
+//     K/V are read with buffer loads whose resource spans one (block, kv head) slab, and a
+//     masked lane's offset is out of range, so the hardware returns zeros without a memory
+//     access; the lane's score is -inf and its weight exp2(-inf) = 0.
+//   * Two register buffers of UNROLL groups are kept loading: while one is consumed the
+//     other's loads are in flight, so each lane has 2 * UNROLL K+V loads outstanding.
+#include "pa_decode_common.h"
 
 namespace pagedkv {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-
-template <typename T>
-__device__ __forceinline__ void store_nan_heads(void* out, size_t base, int count) {
-    for (int i = threadIdx.x; i < count; i += kThreads) store_elem(T{}, out, base + i, __builtin_nanf(""));
-}
+constexpr int kWaves = kDecodeWaves;
+constexpr int kThreads = kDecodeThreads;
 
 template <typename T, int D, int G, int UNROLL>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
@@ -58,53 +55,11 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     const int lbs = a.log2_block_size;
     const int bs = 1 << lbs;
 
-    // ---- sequence length checks (never read past what the table can address) ----
-    const int L = a.context_lens[b];
-    int flag = 0;
-    if (L <= 0) flag = PA_FLAG_EMPTY_CONTEXT;
-    else if (L > a.max_context_len || (L - 1) >> lbs >= a.max_blocks_per_seq) flag = PA_FLAG_BAD_LENGTH;
-    if (flag) {
-        if (p == 0) {
-            if (tid == 0 && a.err_flag) atomicOr(a.err_flag, flag);
-            store_nan_heads<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, G * D);
-        }
-        return;
-    }
-    const int P = a.partition_size;
-    const int nparts = (L + P - 1) / P;
-    if (p >= nparts) return;
-    const int t0 = p * P;
-    const int t1 = min(L, t0 + P);
-    const int j0 = t0 >> lbs;
-    const int nids = ((t1 - 1) >> lbs) - j0 + 1;
-
-    // ---- stage and check this partition's block ids ----
-    if (tid == 0) s_bad = 0;
-    __syncthreads();
-    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq + j0;
-    for (int i = tid; i < nids; i += kThreads) {
-        int id = trow[i];
-        if ((unsigned)id >= (unsigned)a.num_blocks) {
-            s_bad = 1;
-            id = 0;
-        }
-        s_ids[i] = id;
-    }
-    __syncthreads();
-    if (s_bad) {
-        if (tid == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_BLOCK_ID);
-        if (nparts == 1) {
-            store_nan_heads<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, G * D);
-        } else {
-            for (int i = tid; i < G * (D + 2); i += kThreads) {
-                const int g = i / (D + 2), e = i % (D + 2);
-                const size_t rec = ((size_t)b * a.num_q_heads + h0 + g) * a.max_partitions + p;
-                if (e < D) a.ws_o[rec * D + e] = __builtin_nanf("");
-                else a.ws_ml[rec * 2 + (e - D)] = (e == D) ? -INFINITY : __builtin_nanf("");
-            }
-        }
-        return;
-    }
+    Partition part;
+    if (!partition_prologue<T, D, G>(a, p, kvh, b, s_ids, &s_bad, part)) return;
+    const int t0 = part.t0;
+    const int j0 = part.j0;
+    const int ntok = part.ntok;
 
     // ---- q slices of the G heads, kept in storage form ----
     u32x4 qv[G];
@@ -115,10 +70,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     // ---- main loop ----
     const size_t head_bytes = (size_t)bs * D * T::kBytes;
     const size_t block_bytes = head_bytes * a.num_kv_heads;
-    const size_t lane_off = (size_t)kvh * head_bytes + ((size_t)row * D + col * E) * T::kBytes;
-    const char* kbase = static_cast<const char*>(a.k_pool) + lane_off;
-    const char* vbase = static_cast<const char*>(a.v_pool) + lane_off;
-    const int ntok = t1 - t0;
+    const char* kpool = static_cast<const char*>(a.k_pool);
+    const char* vpool = static_cast<const char*>(a.v_pool);
     constexpr int kTokPerIter = UNROLL * kWaves * RPL;
     const int niters = (ntok + kTokPerIter - 1) / kTokPerIter;
 
@@ -131,21 +84,28 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
     }
 
+    // Branch-free loads: every lane issues its loads; a lane whose token is at or past the
+    // partition end gets an out-of-range offset and reads zeros without a memory access.
+    // The buffer resource spans only this (block, kv head) slab.
+    const uint32_t slab_bytes = (uint32_t)head_bytes;
+    const uint32_t lane_bytes = (uint32_t)(((size_t)row * D + col * E) * T::kBytes);
     auto issue = [&](int it, u32x4* kk, u32x4* vv) {
+        int idv[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int rel = ((it * UNROLL + u) * kWaves + wave) * RPL;  // wave-uniform
-            kk[u] = u32x4{0, 0, 0, 0};
-            vv[u] = u32x4{0, 0, 0, 0};
-            if (rel < ntok) {
-                const int tb = t0 + rel;
-                const int id = __builtin_amdgcn_readfirstlane(s_ids[(tb >> lbs) - j0]);
-                const size_t off = (size_t)id * block_bytes + (size_t)(tb & (bs - 1)) * D * T::kBytes;
-                if (rel + row < ntok) {
-                    kk[u] = load16(kbase + off);
-                    vv[u] = load16(vbase + off);
-                }
-            }
+            idv[u] = s_ids[((t0 + (rel < ntok ? rel : 0)) >> lbs) - j0];
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int rel = ((it * UNROLL + u) * kWaves + wave) * RPL;
+            const int id = __builtin_amdgcn_readfirstlane(idv[u]);
+            const size_t slab = (size_t)id * block_bytes + (size_t)kvh * head_bytes;
+            const uint32_t off = (rel + row < ntok)
+                                     ? (uint32_t)((rel & (bs - 1)) * D * T::kBytes) + lane_bytes
+                                     : kOutOfRange;
+            kk[u] = buffer_load16(make_rsrc(kpool + slab, slab_bytes), off);
+            vv[u] = buffer_load16(make_rsrc(vpool + slab, slab_bytes), off);
         }
     };
 
@@ -186,15 +146,27 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         }
     };
 
+    // Two register buffers, each refilled right after it is consumed, so two groups of
+    // loads are in flight at all times and every wait before a compute covers only the older
+    // group. Refills past the last group get out-of-range offsets: they return zeros and move
+    // no data. The scheduling barriers keep the compiler from sinking a refill below the next
+    // compute, which would drain the load queue.
     u32x4 ka[UNROLL], va[UNROLL], kb[UNROLL], vb[UNROLL];
     issue(0, ka, va);
-    for (int it = 0; it < niters; it += 2) {
-        issue(it + 1, kb, vb);
+    issue(1, kb, vb);
+    int it = 0;
+    for (; it + 1 < niters; it += 2) {  // one latch: the wait state is the same on every entry
+        __builtin_amdgcn_sched_barrier(0);
         compute(it, ka, va);
-        if (it + 1 >= niters) break;
+        __builtin_amdgcn_sched_barrier(0);
         issue(it + 2, ka, va);
+        __builtin_amdgcn_sched_barrier(0);
         compute(it + 1, kb, vb);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(it + 3, kb, vb);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (it < niters) compute(it, ka, va);
 
     // ---- merge the RPL row streams of this wave ----
 #pragma unroll
@@ -229,34 +201,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // ---- merge the waves and write ----
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int g = i / D;
-        const int e = i % D;
-        float M = s_m[0][g];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
-        const float Ms = (M == -INFINITY) ? 0.f : M;
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = fast_exp2(s_m[w][g] - Ms);
-            num = fmaf(s_acc[w][g][e], f, num);
-            den = fmaf(s_l[w][g], f, den);
-        }
-        const float o = num / den;
-        const size_t hrow = (size_t)b * a.num_q_heads + h0 + g;
-        if (nparts == 1) {
-            store_elem(T{}, a.out, hrow * D + e, o);
-        } else {
-            const size_t rec = hrow * a.max_partitions + p;
-            a.ws_o[rec * D + e] = o;
-            if (e == 0) {
-                a.ws_ml[rec * 2] = M;
-                a.ws_ml[rec * 2 + 1] = den;
-            }
-        }
-    }
+    partition_epilogue<T, D, G>(a, p, kvh, b, part, s_m, s_l, s_acc);
 }
 
 // Log-sum-exp combine of the per-partition records of one (sequence, query head):
@@ -285,15 +230,24 @@ __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
     store_elem(T{}, a.out, ((size_t)b * a.num_q_heads + h) * D + e, num / den);
 }
 
-template <typename T, int D, int G>
-hipError_t launch_decode_tgd(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
-    constexpr int UNROLL = G <= 2 ? 4 : (G <= 4 ? 2 : 1);
+template <typename T, int D, int G, int UNROLL>
+hipError_t launch_decode_tgdu(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     dim3 grid(a.max_partitions, num_kv_heads, batch);
     hipLaunchKernelGGL((decode_valu_kernel<T, D, G, UNROLL>), grid, dim3(kThreads), 0, stream, a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || a.max_partitions <= 1) return err;
-    hipLaunchKernelGGL((reduce_kernel<T, D>), dim3(a.num_q_heads, batch), dim3(D), 0, stream, a);
     return hipGetLastError();
+}
+
+// Groups per iteration per wave: 4 for long partitions; 2 for short ones (<= 384 tokens),
+// where a 4-deep iteration would leave most lanes idle and the smaller register footprint
+// lets 8 waves share a SIMD. Grouped-query heads multiply the registers per group.
+template <typename T, int D, int G>
+hipError_t launch_decode_tgd(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
+    if constexpr (G <= 2) {
+        if (a.partition_size <= 384) return launch_decode_tgdu<T, D, G, 2>(a, batch, num_kv_heads, stream);
+        return launch_decode_tgdu<T, D, G, 4>(a, batch, num_kv_heads, stream);
+    } else {
+        return launch_decode_tgdu<T, D, G, (G <= 4 ? 2 : 1)>(a, batch, num_kv_heads, stream);
+    }
 }
 
 template <typename T, int D>
@@ -321,10 +275,35 @@ hipError_t launch_decode_t(const DecodeArgs& a, int head_dim, int group, int bat
     }
 }
 
+template <typename T, int D>
+hipError_t launch_reduce_td(const DecodeArgs& a, int batch, hipStream_t stream) {
+    hipLaunchKernelGGL((reduce_kernel<T, D>), dim3(a.num_q_heads, batch), dim3(D), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_reduce_t(const DecodeArgs& a, int head_dim, int batch, hipStream_t s) {
+    switch (head_dim) {
+        case 64: return launch_reduce_td<T, 64>(a, batch, s);
+        case 128: return launch_reduce_td<T, 128>(a, batch, s);
+        case 256: return launch_reduce_td<T, 256>(a, batch, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
-                         int num_kv_heads, hipStream_t stream) {
+hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, int batch, hipStream_t stream) {
+    switch (dtype) {
+        case PA_F32: return launch_reduce_t<F32>(a, head_dim, batch, stream);
+        case PA_F16: return launch_reduce_t<F16>(a, head_dim, batch, stream);
+        case PA_BF16: return launch_reduce_t<BF16>(a, head_dim, batch, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
+                              int num_kv_heads, hipStream_t stream) {
     switch (dtype) {
         case PA_F32: return launch_decode_t<F32>(a, head_dim, group, batch, num_kv_heads, stream);
         case PA_F16: return launch_decode_t<F16>(a, head_dim, group, batch, num_kv_heads, stream);

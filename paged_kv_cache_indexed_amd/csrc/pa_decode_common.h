@@ -1,0 +1,121 @@
+// Pieces shared by the decode kernels: the per-partition prologue (length checks, block-id
+// staging in LDS) and the epilogue (merge of per-wave softmax states, output or partition
+// record). Every function here is called by all threads of the workgroup.
+#pragma once
+
+#include "pa_kernels.h"
+
+namespace pagedkv {
+
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = kDecodeWaves * 64;
+
+struct Partition {
+    int nparts;  // partitions of this sequence
+    int t0;      // first token of this partition
+    int ntok;    // tokens in this partition
+    int j0;      // first logical block of this partition
+};
+
+template <typename T>
+__device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
+    for (int i = threadIdx.x; i < count; i += blockDim.x) store_elem(T{}, out, base + i, __builtin_nanf(""));
+}
+
+// Checks the sequence length, stages the partition's block ids in s_ids and validates
+// them. Returns false when the workgroup has nothing more to do: the partition is past the
+// end of the sequence, or the sequence is invalid (its outputs, or this partition's record,
+// are set to NaN and the error bit is raised). Never reads a table entry or a pool byte
+// that the checks have not cleared.
+template <typename T, int D, int G>
+__device__ bool partition_prologue(const DecodeArgs& a, int p, int kvh, int b, int* s_ids, int* s_bad,
+                                   Partition& part) {
+    const int tid = threadIdx.x;
+    const int lbs = a.log2_block_size;
+    const int h0 = kvh * G;
+    const int L = a.context_lens[b];
+    int flag = 0;
+    if (L <= 0) flag = PA_FLAG_EMPTY_CONTEXT;
+    else if (L > a.max_context_len || ((L - 1) >> lbs) >= a.max_blocks_per_seq) flag = PA_FLAG_BAD_LENGTH;
+    if (flag) {
+        if (p == 0) {
+            if (tid == 0 && a.err_flag) atomicOr(a.err_flag, flag);
+            store_nan<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, G * D);
+        }
+        return false;
+    }
+    const int P = a.partition_size;
+    part.nparts = (L + P - 1) / P;
+    if (p >= part.nparts) return false;
+    part.t0 = p * P;
+    const int t1 = min(L, part.t0 + P);
+    part.ntok = t1 - part.t0;
+    part.j0 = part.t0 >> lbs;
+    const int nids = ((t1 - 1) >> lbs) - part.j0 + 1;
+
+    if (tid == 0) *s_bad = 0;
+    __syncthreads();
+    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq + part.j0;
+    for (int i = tid; i < nids; i += blockDim.x) {
+        int id = trow[i];
+        if ((unsigned)id >= (unsigned)a.num_blocks) {
+            *s_bad = 1;
+            id = 0;
+        }
+        s_ids[i] = id;
+    }
+    __syncthreads();
+    if (*s_bad) {
+        if (tid == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_BLOCK_ID);
+        if (part.nparts == 1) {
+            store_nan<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, G * D);
+        } else {
+            for (int i = tid; i < G * (D + 2); i += blockDim.x) {
+                const int g = i / (D + 2), e = i % (D + 2);
+                const size_t rec = ((size_t)b * a.num_q_heads + h0 + g) * a.max_partitions + p;
+                if (e < D) a.ws_o[rec * D + e] = __builtin_nanf("");
+                else a.ws_ml[rec * 2 + (e - D)] = (e == D) ? -INFINITY : __builtin_nanf("");
+            }
+        }
+        return false;
+    }
+    return true;
+}
+
+// Merges the per-wave states (s_m, s_l: base-2 running max and sum; s_acc: unnormalised
+// weighted sums) of G heads and writes either the final output (single partition) or the
+// partition's record (normalised output, max, sum) for the log-sum-exp reduce.
+template <typename T, int D, int G, int NW = kDecodeWaves>
+__device__ void partition_epilogue(const DecodeArgs& a, int p, int kvh, int b, const Partition& part,
+                                   const float (*s_m)[G], const float (*s_l)[G], const float (*s_acc)[G][D]) {
+    const int h0 = kvh * G;
+    for (int i = threadIdx.x; i < G * D; i += NW * 64) {
+        const int g = i / D;
+        const int e = i % D;
+        float M = s_m[0][g];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+        const float Ms = (M == -INFINITY) ? 0.f : M;
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = __builtin_amdgcn_exp2f(s_m[w][g] - Ms);
+            num = fmaf(s_acc[w][g][e], f, num);
+            den = fmaf(s_l[w][g], f, den);
+        }
+        const float o = num / den;
+        const size_t hrow = (size_t)b * a.num_q_heads + h0 + g;
+        if (part.nparts == 1) {
+            store_elem(T{}, a.out, hrow * D + e, o);
+        } else {
+            const size_t rec = hrow * a.max_partitions + p;
+            a.ws_o[rec * D + e] = o;
+            if (e == 0) {
+                a.ws_ml[rec * 2] = M;
+                a.ws_ml[rec * 2 + 1] = den;
+            }
+        }
+    }
+}
+
+}  // namespace pagedkv

@@ -34,6 +34,23 @@ struct VecInfo {
     static constexpr int kElems = 16 / T::kBytes;  // elements per 16-byte vector
 };
 
+// Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0). An offset at or
+// past `bytes` reads zeros without touching memory, which is how masked lanes skip padding.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+// Cache policy of the K/V stream loads: 2 = non-temporal (each byte is read once).
+#ifndef PA_KV_LOAD_POLICY
+#define PA_KV_LOAD_POLICY 2
+#endif
+template <int kPolicy = PA_KV_LOAD_POLICY>
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, kPolicy));
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }

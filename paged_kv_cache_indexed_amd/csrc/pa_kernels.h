@@ -44,8 +44,15 @@ struct CacheArgs {
     int32_t row_vecs;  // 16-byte vectors per [head_dim] row
 };
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
-                         int num_kv_heads, hipStream_t stream);
+// VALU decode (every dtype and group size).
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
+                              int num_kv_heads, hipStream_t stream);
+// Matrix-core decode for grouped-query heads (fp16/bf16, group 4/8/16, block_size >= 16).
+bool decode_mfma_supported(int dtype, int head_dim, int group, int block_size);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
+                              int num_kv_heads, hipStream_t stream);
+// Log-sum-exp combine of partition records (only when some sequence has > 1 partition).
+hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, int batch, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const CacheArgs& a, const void* key, const void* value,
                                     const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream);

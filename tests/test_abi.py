@@ -54,9 +54,15 @@ def test_partition_policy(lib):
     # long contexts: 512-token partitions
     assert _lib.pa_decode_partition_size(_desc(bs=32), 32, 32, 32769, 0) == 512
     assert _lib.pa_decode_workspace_bytes(_desc(bs=32), 32, 32, 32769, 0) == 32 * 32 * 65 * 130 * 4
-    # few workgroups: partitions shrink toward ~2048 workgroups
-    p = _lib.pa_decode_partition_size(_desc(hkv=8, dtype=_lib.PA_BF16), 32, 64, 2049, 0)
+    # VALU path with few workgroups: partitions shrink toward ~2048 workgroups
+    p = _lib.pa_decode_partition_size(_desc(hkv=8, dtype=_lib.PA_F32), 32, 64, 2049, 0)
     assert p % 16 == 0 and 32 * 8 * -(-2049 // p) >= 2048 - 256
+    # matrix-core path (bf16, 8 query heads per kv head): one partition for 256 pairs
+    assert _lib.pa_decode_partition_size(_desc(hkv=8, dtype=_lib.PA_BF16), 32, 64, 2049, 0) == 2064
+    # ... split to reach 256 workgroups, and at most 4096 tokens per partition
+    assert _lib.pa_decode_partition_size(_desc(hkv=8, dtype=_lib.PA_BF16), 4, 64, 2049, 0) == 272  # 8 parts
+    p = _lib.pa_decode_partition_size(_desc(hkv=8, dtype=_lib.PA_BF16), 32, 64, 32769, 0)
+    assert p <= 4096 and p % 16 == 0 and -(-32769 // p) == 9
     # explicit sizes must be block multiples and fit the LDS id table
     assert _lib.pa_decode_partition_size(c, 4, 32, 100, 24) == -1
     assert _lib.pa_decode_partition_size(c, 4, 32, 100, 64) == 64
