@@ -29,6 +29,39 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hbm_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources and the ABI header; recorded next to every counter figure."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "paged_kv_cache_indexed_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    files.append(os.path.join(ROOT, "include", "pagedkv.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per decode launch measured with rocprofv3 for this workload, if the table in
+    profiles/ was taken from the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    cur = kernel_source_hash()
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 5 and cells[0] == workload and cells[1] == cur:
+                try:
+                    return int(cells[4])
+                except ValueError:
+                    return None
+    return None
 
 
 def _workload(cfg: int, block_size: int | None, median: float | None):
@@ -110,6 +143,8 @@ def main() -> int:
                     help="pool bytes touched between reuses of one replica")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -160,6 +195,14 @@ def main() -> int:
         if ev is not None:
             ev[1].record(stream)
 
+    if args.calib_copy_mb > 0:
+        nbytes = args.calib_copy_mb << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -204,7 +247,9 @@ def main() -> int:
                              "p50": round(float(np.percentile(dec_ms, 50)), 5),
                              "p90": round(float(np.percentile(dec_ms, 90)), 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(w.name)},
+        "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (_cpu_baseline_beams(w, host_sample, args.cpu_budget) if host_sample

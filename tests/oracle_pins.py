@@ -174,6 +174,9 @@ def pin_bruteforce(o):
         got = _decode(o, c, scale)
         ref = _brute_decode(c["q"], c["kc"], c["vc"], c["lens"], scale, Hq, Hkv)
         _close(got, ref, 1e-12, f"brute force seed={seed}")
+        pairs = [(b, h) for b in range(len(lens)) for h in range(Hq)][::3]
+        sub = o.paged_decode_heads(c["q"], c["k_pool"], c["v_pool"], c["table"], c["lens"], scale, pairs)
+        _close(sub, np.array([ref[b, h] for b, h in pairs]), 1e-12, f"listed heads seed={seed}")
 
 
 def pin_closed_forms(o):

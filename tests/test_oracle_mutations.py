@@ -92,6 +92,16 @@ def m_wrong_sequence_row(q, k_pool, v_pool, block_table, context_lens, scale):
     return pa.__dict__["_orig_paged_decode"](q, k_pool, v_pool, rolled, context_lens, scale)
 
 
+def m_heads_gqa_modulo(q, k_pool, v_pool, block_table, context_lens, scale, pairs):
+    Hkv = k_pool.shape[1]
+    out = np.empty((len(pairs), q.shape[2]))
+    for i, (b, h) in enumerate(pairs):
+        K = _gather(k_pool, block_table[b], context_lens[b], h % Hkv)
+        V = _gather(v_pool, block_table[b], context_lens[b], h % Hkv)
+        out[i] = _attn(q[b, h], K, V, scale)
+    return out
+
+
 def m_cache_divmod_swapped(k_pool, v_pool, key, value, slot_mapping):
     k_new, v_new = k_pool.copy(), v_pool.copy()
     nb, _, bs, _ = k_pool.shape
@@ -143,6 +153,7 @@ MUTANTS = {
     "gqa_modulo": ("paged_decode", _decode_with_head_map(lambda h, Hq, Hkv: h % Hkv)),
     "gqa_identity": ("paged_decode", _decode_with_head_map(lambda h, Hq, Hkv: min(h, Hkv - 1))),
     "wrong_sequence_row": ("paged_decode", m_wrong_sequence_row),
+    "heads_gqa_modulo": ("paged_decode_heads", m_heads_gqa_modulo),
     "cache_divmod_swapped": ("reshape_and_cache", m_cache_divmod_swapped),
     "cache_skips_value": ("reshape_and_cache", m_cache_skips_value),
     "copy_only_k": ("copy_blocks", m_copy_only_k),
