@@ -30,52 +30,42 @@ namespace {
 constexpr int kWaves = kDecodeWaves;
 constexpr int kThreads = kDecodeThreads;
 
-template <typename T, int D, int G, int UNROLL>
-__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
-    constexpr int E = VecInfo<T>::kElems;  // elements per 16-byte vector
-    constexpr int LPR = D / E;             // lanes per token row
-    constexpr int RPL = 64 / LPR;          // token rows per wave load
+template <typename T, int D>
+struct RowShape {
+    static constexpr int E = VecInfo<T>::kElems;  // elements per 16-byte vector
+    static constexpr int LPR = D / E;             // lanes per token row
+    static constexpr int RPL = 64 / LPR;          // token rows per wave load
     static_assert(LPR >= 1 && LPR <= 64 && RPL * LPR == 64, "row shape");
+};
 
-    __shared__ int s_ids[kMaxIdsPerPartition];
-    __shared__ int s_bad;
-    __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[kWaves][G];
-    __shared__ float s_acc[kWaves][G][D];
-
-    const int p = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+// Streams this lane's share of a partition of kv head `kvh` and leaves the wave's merged
+// online-softmax state of the G query heads in every lane (m, l, and the E accumulators of
+// the lane's column). Row groups of RPL tokens are taken in the order
+// slot, slot + STRIDE, slot + 2 STRIDE, ...: STRIDE waves cooperate on one head, or one
+// wave (STRIDE = 1) owns it. All lanes must be active.
+template <typename T, int D, int G, int UNROLL, int STRIDE>
+__device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int* s_ids, const Partition& part,
+                                                 int kvh, int slot, const u32x4* qv, float* m, float* l,
+                                                 float (*acc)[RowShape<T, D>::E]) {
+    constexpr int E = RowShape<T, D>::E;
+    constexpr int LPR = RowShape<T, D>::LPR;
+    constexpr int RPL = RowShape<T, D>::RPL;
+    const int lane = threadIdx.x & 63;
     const int row = lane / LPR;
     const int col = lane % LPR;
-    const int h0 = kvh * G;
     const int lbs = a.log2_block_size;
     const int bs = 1 << lbs;
-
-    Partition part;
-    if (!partition_prologue<T, D, G>(a, p, kvh, b, s_ids, &s_bad, part)) return;
     const int t0 = part.t0;
     const int j0 = part.j0;
     const int ntok = part.ntok;
 
-    // ---- q slices of the G heads, kept in storage form ----
-    u32x4 qv[G];
-    const char* qbase = static_cast<const char*>(a.q) + (((size_t)b * a.num_q_heads + h0) * D + col * E) * T::kBytes;
-#pragma unroll
-    for (int g = 0; g < G; ++g) qv[g] = load16(qbase + (size_t)g * D * T::kBytes);
-
-    // ---- main loop ----
     const size_t head_bytes = (size_t)bs * D * T::kBytes;
     const size_t block_bytes = head_bytes * a.num_kv_heads;
     const char* kpool = static_cast<const char*>(a.k_pool);
     const char* vpool = static_cast<const char*>(a.v_pool);
-    constexpr int kTokPerIter = UNROLL * kWaves * RPL;
+    constexpr int kTokPerIter = UNROLL * STRIDE * RPL;
     const int niters = (ntok + kTokPerIter - 1) / kTokPerIter;
 
-    float m[G], l[G], acc[G][E];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         m[g] = -INFINITY;
@@ -93,12 +83,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         int idv[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int rel = ((it * UNROLL + u) * kWaves + wave) * RPL;  // wave-uniform
+            const int rel = ((it * UNROLL + u) * STRIDE + slot) * RPL;  // wave-uniform
             idv[u] = s_ids[((t0 + (rel < ntok ? rel : 0)) >> lbs) - j0];
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int rel = ((it * UNROLL + u) * kWaves + wave) * RPL;
+            const int rel = ((it * UNROLL + u) * STRIDE + slot) * RPL;
             const int id = __builtin_amdgcn_readfirstlane(idv[u]);
             const size_t slab = (size_t)id * block_bytes + (size_t)kvh * head_bytes;
             const uint32_t off = (rel + row < ntok)
@@ -113,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         float s[G][UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int rel = ((it * UNROLL + u) * kWaves + wave) * RPL + row;
+            const int rel = ((it * UNROLL + u) * STRIDE + slot) * RPL + row;
             const bool valid = rel < ntok;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -185,12 +175,49 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
             m[g] = mn;
         }
     }
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int h0, u32x4* qv) {
+    constexpr int E = RowShape<T, D>::E;
+    const int col = (threadIdx.x & 63) % RowShape<T, D>::LPR;
+    const char* qbase = static_cast<const char*>(a.q) + (((size_t)b * a.num_q_heads + h0) * D + col * E) * T::kBytes;
+#pragma unroll
+    for (int g = 0; g < G; ++g) qv[g] = load16(qbase + (size_t)g * D * T::kBytes);
+}
+
+// Split mode: the 4 waves of a workgroup share one kv head's partition (groups of RPL rows
+// dealt round-robin), and their states merge through LDS.
+template <typename T, int D, int G, int UNROLL>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
+    constexpr int E = RowShape<T, D>::E;
+    constexpr int LPR = RowShape<T, D>::LPR;
+    __shared__ int s_ids[kMaxIdsPerPartition];
+    __shared__ float s_m[kWaves][G];
+    __shared__ float s_l[kWaves][G];
+    __shared__ float s_acc[kWaves][G][D];
+
+    const int p = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = lane / LPR;
+    const int col = lane % LPR;
+
+    // q before the prologue, so its load overlaps the length and table round trip
+    u32x4 qv[G];
+    load_q<T, D, G>(a, b, kvh * G, qv);
+    Partition part;
+    if (!partition_prologue<T, D, G, kThreads>(a, p, kvh, b, s_ids, part)) return;
+
+    float m[G], l[G], acc[G][E];
+    stream_partition<T, D, G, UNROLL, kWaves>(a, s_ids, part, kvh, wave, qv, m, l, acc);
     if (row == 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int e = 0; e < E; ++e) s_acc[wave][g][col * E + e] = acc[g][e];
-        }
     }
     if (lane == 0) {
 #pragma unroll
@@ -200,8 +227,57 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-
     partition_epilogue<T, D, G>(a, p, kvh, b, part, s_m, s_l, s_acc);
+}
+
+// Head mode, for short partitions: a workgroup owns one (partition, sequence) and 4
+// consecutive kv heads that share the staged table slice; wave w streams kv head
+// 4 * blockIdx.y + w alone and writes its result without any cross-wave merge.
+template <typename T, int D, int G, int UNROLL>
+__global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs a) {
+    constexpr int E = RowShape<T, D>::E;
+    constexpr int LPR = RowShape<T, D>::LPR;
+    __shared__ int s_ids[kMaxIdsPerPartition];
+
+    const int p = blockIdx.x;
+    const int b = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = lane / LPR;
+    const int col = lane % LPR;
+    const int kvh0 = blockIdx.y * kWaves;
+    const int nkv = min(kWaves, a.num_kv_heads - kvh0);
+    const bool active = wave < nkv;
+    const int kvh = active ? kvh0 + wave : kvh0;
+    const int h0 = kvh * G;
+
+    u32x4 qv[G];
+    load_q<T, D, G>(a, b, h0, qv);
+    Partition part;
+    if (!partition_prologue_heads<T, D, kThreads>(a, p, kvh0 * G, nkv * G, b, s_ids, part)) return;
+    if (!active) return;  // no barrier follows
+
+    float m[G], l[G], acc[G][E];
+    stream_partition<T, D, G, UNROLL, 1>(a, s_ids, part, kvh, 0, qv, m, l, acc);
+    if (row == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const size_t hrow = (size_t)b * a.num_q_heads + h0 + g;
+            const float inv = 1.f / l[g];
+            if (part.nparts == 1) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) store_elem(T{}, a.out, hrow * D + col * E + e, acc[g][e] * inv);
+            } else {
+                const size_t rec = hrow * a.max_partitions + p;
+#pragma unroll
+                for (int e = 0; e < E; ++e) a.ws_o[rec * D + col * E + e] = acc[g][e] * inv;
+                if (col == 0) {
+                    a.ws_ml[rec * 2] = m[g];
+                    a.ws_ml[rec * 2 + 1] = l[g];
+                }
+            }
+        }
+    }
 }
 
 // Log-sum-exp combine of the per-partition records of one (sequence, query head):
@@ -230,20 +306,32 @@ __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
     store_elem(T{}, a.out, ((size_t)b * a.num_q_heads + h) * D + e, num / den);
 }
 
+// Partitions of at most this many tokens run in head mode.
+#ifndef PA_HEAD_MODE_MAX_P
+#define PA_HEAD_MODE_MAX_P 128
+#endif
+
 template <typename T, int D, int G, int UNROLL>
 hipError_t launch_decode_tgdu(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
-    dim3 grid(a.max_partitions, num_kv_heads, batch);
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, G, UNROLL>), grid, dim3(kThreads), 0, stream, a);
+    if (a.partition_size <= PA_HEAD_MODE_MAX_P) {
+        dim3 grid(a.max_partitions, (num_kv_heads + kWaves - 1) / kWaves, batch);
+        hipLaunchKernelGGL((decode_valu_heads_kernel<T, D, G, UNROLL>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        dim3 grid(a.max_partitions, num_kv_heads, batch);
+        hipLaunchKernelGGL((decode_valu_kernel<T, D, G, UNROLL>), grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
-// Groups per iteration per wave: 4 for long partitions; 2 for short ones (<= 384 tokens),
-// where a 4-deep iteration would leave most lanes idle and the smaller register footprint
-// lets 8 waves share a SIMD. Grouped-query heads multiply the registers per group.
+// Groups per iteration per wave: 4 for long partitions (and for head mode, where one wave
+// streams a whole partition); 2 for short split-mode partitions (<= 384 tokens), where a
+// 4-deep iteration would leave most lanes idle and the smaller register footprint lets 8
+// waves share a SIMD. Grouped-query heads multiply the registers per group.
 template <typename T, int D, int G>
 hipError_t launch_decode_tgd(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     if constexpr (G <= 2) {
-        if (a.partition_size <= 384) return launch_decode_tgdu<T, D, G, 2>(a, batch, num_kv_heads, stream);
+        if (a.partition_size > PA_HEAD_MODE_MAX_P && a.partition_size <= 384)
+            return launch_decode_tgdu<T, D, G, 2>(a, batch, num_kv_heads, stream);
         return launch_decode_tgdu<T, D, G, 4>(a, batch, num_kv_heads, stream);
     } else {
         return launch_decode_tgdu<T, D, G, (G <= 4 ? 2 : 1)>(a, batch, num_kv_heads, stream);

@@ -27,12 +27,29 @@ __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
 // end of the sequence, or the sequence is invalid (its outputs, or this partition's record,
 // are set to NaN and the error bit is raised). Never reads a table entry or a pool byte
 // that the checks have not cleared.
-template <typename T, int D, int G>
-__device__ bool partition_prologue(const DecodeArgs& a, int p, int kvh, int b, int* s_ids, int* s_bad,
-                                   Partition& part) {
+//
+// The table slice of partition p starts at logical block p * P / block_size whatever the
+// length is, so it is loaded in the same round trip as the length (entries past the valid
+// blocks are read from inside the row but never used); one barrier then publishes the ids
+// and the OR of their range checks.
+//
+// The workgroup covers query heads [h0, h0 + nq): its NaN outputs cover exactly those.
+template <typename T, int D, int NT>
+__device__ bool partition_prologue_heads(const DecodeArgs& a, int p, int h0, int nq, int b, int* s_ids,
+                                         Partition& part) {
+    constexpr int kPerThread = (kMaxIdsPerPartition + NT - 1) / NT;
     const int tid = threadIdx.x;
     const int lbs = a.log2_block_size;
-    const int h0 = kvh * G;
+    const int P = a.partition_size;
+    const int j0 = (p * P) >> lbs;
+    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq + j0;
+    const int lim = min(P >> lbs, a.max_blocks_per_seq - j0);
+    int idv[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int i = tid + k * NT;
+        idv[k] = (i < lim) ? trow[i] : 0;
+    }
     const int L = a.context_lens[b];
     int flag = 0;
     if (L <= 0) flag = PA_FLAG_EMPTY_CONTEXT;
@@ -40,37 +57,36 @@ __device__ bool partition_prologue(const DecodeArgs& a, int p, int kvh, int b, i
     if (flag) {
         if (p == 0) {
             if (tid == 0 && a.err_flag) atomicOr(a.err_flag, flag);
-            store_nan<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, G * D);
+            store_nan<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, nq * D);
         }
         return false;
     }
-    const int P = a.partition_size;
     part.nparts = (L + P - 1) / P;
     if (p >= part.nparts) return false;
     part.t0 = p * P;
     const int t1 = min(L, part.t0 + P);
     part.ntok = t1 - part.t0;
-    part.j0 = part.t0 >> lbs;
-    const int nids = ((t1 - 1) >> lbs) - part.j0 + 1;
-
-    if (tid == 0) *s_bad = 0;
-    __syncthreads();
-    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq + part.j0;
-    for (int i = tid; i < nids; i += blockDim.x) {
-        int id = trow[i];
-        if ((unsigned)id >= (unsigned)a.num_blocks) {
-            *s_bad = 1;
-            id = 0;
+    part.j0 = j0;
+    const int nids = ((t1 - 1) >> lbs) - j0 + 1;
+    int bad = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int i = tid + k * NT;
+        if (i < nids) {
+            int id = idv[k];
+            if ((unsigned)id >= (unsigned)a.num_blocks) {
+                bad = 1;
+                id = 0;
+            }
+            s_ids[i] = id;
         }
-        s_ids[i] = id;
     }
-    __syncthreads();
-    if (*s_bad) {
+    if (__syncthreads_or(bad)) {
         if (tid == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_BLOCK_ID);
         if (part.nparts == 1) {
-            store_nan<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, G * D);
+            store_nan<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, nq * D);
         } else {
-            for (int i = tid; i < G * (D + 2); i += blockDim.x) {
+            for (int i = tid; i < nq * (D + 2); i += NT) {
                 const int g = i / (D + 2), e = i % (D + 2);
                 const size_t rec = ((size_t)b * a.num_q_heads + h0 + g) * a.max_partitions + p;
                 if (e < D) a.ws_o[rec * D + e] = __builtin_nanf("");
@@ -80,6 +96,12 @@ __device__ bool partition_prologue(const DecodeArgs& a, int p, int kvh, int b, i
         return false;
     }
     return true;
+}
+
+template <typename T, int D, int G, int NT>
+__device__ __forceinline__ bool partition_prologue(const DecodeArgs& a, int p, int kvh, int b, int* s_ids,
+                                                   Partition& part) {
+    return partition_prologue_heads<T, D, NT>(a, p, kvh * G, G, b, s_ids, part);
 }
 
 // Merges the per-wave states (s_m, s_l: base-2 running max and sum; s_acc: unnormalised

@@ -101,7 +101,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     using M = Mma<T>;
 
     __shared__ int s_ids[kMaxIdsPerPartition];
-    __shared__ int s_bad;
     __shared__ float s_m[NW][G];
     __shared__ float s_l[NW][G];
     __shared__ float s_acc[NW][G][D];
@@ -116,12 +115,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int lbs = a.log2_block_size;
     const int bs = 1 << lbs;
 
-    Partition part;
-    if (!partition_prologue<T, D, G>(a, p, kvh, b, s_ids, &s_bad, part)) return;
-    const int t0 = part.t0;
-    const int j0 = part.j0;
-    const int ntok = part.ntok;
-
     // Q as the B operand of S^T = K Q^T: column n is head h0 + n (zero past G); k-block c
     // of lane group g holds dims 32c + 8g .. +7, the same dims the K loads below give.
     u32x4 qb[NC];
@@ -131,6 +124,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) qb[c] = (n < G) ? load16(qrow + 64 * c) : u32x4{0, 0, 0, 0};
     }
+    Partition part;
+    if (!partition_prologue<T, D, G, NW * 64>(a, p, kvh, b, s_ids, part)) return;
+    const int t0 = part.t0;
+    const int j0 = part.j0;
+    const int ntok = part.ntok;
+
     // Identity B operand of the 16x16x16 transpose: k-slot (g, i) is 1 in column 4g + i.
     u32x2 ident;
     ident.x = ((4 * g + 0 == n) ? M::kOne : 0u) | (((4 * g + 1 == n) ? M::kOne : 0u) << 16);
