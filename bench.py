@@ -11,7 +11,10 @@ Prints one JSON line: effective KV GB/s of the whole step (algorithmic K+V bytes
 decode, 2 x kv_heads x head_dim x dtype_bytes x sum(context_len), over the step time),
 plus the decode kernel's roofline figure timed with HIP events and the CPU oracle's rate.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2] [--window W]
+
+With --window W the decode attends to the last W tokens of each sequence only
+(pa_decode_sliding_window) and the algorithmic bytes count min(context_len, W) tokens.
 """
 
 from __future__ import annotations
@@ -79,7 +82,7 @@ def _describe(w) -> dict:
             "context_len_sum": int(L.sum()), "step": "append 1 token/seq + decode"}
 
 
-def _cpu_baseline(w, budget_s: float) -> dict:
+def _cpu_baseline(w, budget_s: float, window: int = 0) -> dict:
     """The float64 oracle on the host copy of the same step: its append over the whole batch,
     then single-sequence decodes in order until the whole batch is done or ~budget_s passed."""
     import oracle
@@ -96,16 +99,21 @@ def _cpu_baseline(w, budget_s: float) -> dict:
     seqs = done = 0
     while seqs < w.batch and (seqs == 0 or time.perf_counter() - t0 < budget_s):
         sl = slice(seqs, seqs + 1)
-        oracle.paged_decode(w.q[sl], ek, ev, w.block_table[sl], L[sl], w.scale)
-        done += per_tok * int(L[seqs])
+        if window > 0:
+            oracle.paged_decode_window(w.q[sl], ek, ev, w.block_table[sl], L[sl], w.scale, window)
+            done += per_tok * min(int(L[seqs]), window)
+        else:
+            oracle.paged_decode(w.q[sl], ek, ev, w.block_table[sl], L[sl], w.scale)
+            done += per_tok * int(L[seqs])
         seqs += 1
     dt = time.perf_counter() - t0
     return {"value": round(done / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"oracle append of all {w.batch} tokens + float64 decode of sequences "
+            "sample": f"oracle append of all {w.batch} tokens + float64 "
+                      f"{'window-' + str(window) + ' ' if window > 0 else ''}decode of sequences "
                       f"0..{seqs - 1} (all heads, {done / 1e6:.1f} MB of KV) in {dt:.1f} s"}
 
 
-def _cpu_baseline_beams(w, host, budget_s: float) -> dict:
+def _cpu_baseline_beams(w, host, budget_s: float, window: int = 0) -> dict:
     """The float64 oracle on a host snapshot of one beam (all heads) of the 32K workload:
     its copy-on-write, its append and its decode, repeated until ~budget_s passed."""
     import oracle
@@ -116,17 +124,21 @@ def _cpu_baseline_beams(w, host, budget_s: float) -> dict:
     except Exception:  # noqa: BLE001
         threads = 1
     L = np.full(1, w.context + 1, np.int32)
-    per_seq = 2 * w.num_kv_heads * w.head_dim * 2 * int(L[0])
+    per_seq = 2 * w.num_kv_heads * w.head_dim * 2 * (min(int(L[0]), window) if window > 0 else int(L[0]))
     t0 = time.perf_counter()
     reps = 0
     while reps == 0 or time.perf_counter() - t0 < budget_s:
         k1, v1 = oracle.copy_blocks(host["k_pool"], host["v_pool"], host["copy_pairs"])
         k2, v2 = oracle.reshape_and_cache(k1, v1, host["new_key"], host["new_value"], host["slot_mapping"])
-        oracle.paged_decode(host["q"], k2, v2, host["table"], L, w.scale)
+        if window > 0:
+            oracle.paged_decode_window(host["q"], k2, v2, host["table"], L, w.scale, window)
+        else:
+            oracle.paged_decode(host["q"], k2, v2, host["table"], L, w.scale)
         reps += 1
     dt = time.perf_counter() - t0
     return {"value": round(reps * per_seq / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} x (copy-on-write + append + float64 decode) of beam 0, all "
+            "sample": f"{reps} x (copy-on-write + append + float64 "
+                      f"{'window-' + str(window) + ' ' if window > 0 else ''}decode) of beam 0, all "
                       f"{w.num_kv_heads} heads, L={int(L[0])} ({per_seq / 1e6:.0f} MB of KV each) in {dt:.1f} s"}
 
 
@@ -139,6 +151,8 @@ def main() -> int:
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--median", type=float, default=None)
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window: attend to the last W tokens only (0: whole context)")
     ap.add_argument("--replica-bytes", type=float, default=1.5 * 2 ** 30,
                     help="pool bytes touched between reuses of one replica")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -176,11 +190,13 @@ def main() -> int:
     lens = t["lens_after"]
     max_len = int(w.lens_after_append.max())
     P = args.partition_size
-    ws = ops.workspace_for(t["k_pool"], w.batch, w.num_q_heads, max_len, P)
+    W = max(0, args.window)
+    ws = ops.workspace_for(t["k_pool"], w.batch, w.num_q_heads, max_len, P, window=W)
     out = torch.empty_like(t["q"])
     pairs = t["copy_pairs"]
     esize = t["k_pool"].element_size()
-    kv_bytes = 2 * w.num_kv_heads * w.head_dim * esize * int(w.lens_after_append.sum())
+    attended = np.minimum(w.lens_after_append, W) if W > 0 else w.lens_after_append
+    kv_bytes = 2 * w.num_kv_heads * w.head_dim * esize * int(attended.sum())
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
@@ -191,7 +207,7 @@ def main() -> int:
         if ev is not None:
             ev[0].record(stream)
         ops.decode(t["q"], kps[r], vps[r], t["block_table"], lens, max_len, w.scale,
-                   partition_size=P, out=out, workspace=ws)
+                   partition_size=P, out=out, workspace=ws, window=W)
         if ev is not None:
             ev[1].record(stream)
 
@@ -219,9 +235,14 @@ def main() -> int:
     dec_avg = float(dec_ms.mean())
     achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
+    span = min(max_len, W + w.block_size - 1) if W > 0 else max_len
     part = _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, w.num_q_heads,
-                                         max_len, P)
+                                         span, P)
     cfg = _describe(w)
+    if W > 0:
+        cfg["workload"] = f"{w.name}-window{W}"
+        cfg["window"] = W
+        cfg["attended_tokens_sum"] = int(attended.sum())
     cfg.update({"partition_size": part, "replicas": R, "tokens_per_step": w.batch,
                 "copy_pairs_per_step": int(pairs.shape[0]),
                 "step": ("copy-on-write + " if pairs.shape[0] else "") + "append 1 token/seq + decode"})
@@ -248,12 +269,12 @@ def main() -> int:
                              "p90": round(float(np.percentile(dec_ms, 90)), 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(w.name)},
+                     "traffic": recorded_traffic(cfg["workload"])},
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = (_cpu_baseline_beams(w, host_sample, args.cpu_budget) if host_sample
-                                  else _cpu_baseline(w, args.cpu_budget))
+        result["cpu_baseline"] = (_cpu_baseline_beams(w, host_sample, args.cpu_budget, W) if host_sample
+                                  else _cpu_baseline(w, args.cpu_budget, W))
     print(json.dumps(result), flush=True)
     return 0
 

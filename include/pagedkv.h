@@ -105,9 +105,9 @@ pa_status_t pa_copy_blocks(const pa_cache_desc_t* cache, void* k_pool, void* v_p
 /*
  * pa_decode_partition_size - the context-partition length pa_decode will use.
  *
- * `requested` > 0 must be a multiple of block_size and of 64 (else returns -1). 0 picks a
- * default from the batch, head and length shape. A result >= max_context_len means one
- * partition per sequence (no reduce pass).
+ * `requested` > 0 must be a multiple of block_size covering at most 1024 blocks (else
+ * returns -1). 0 picks a default from the batch, head and length shape. A result >=
+ * max_context_len means one partition per sequence (no reduce pass).
  */
 int32_t pa_decode_partition_size(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_heads,
                                  int32_t max_context_len, int32_t requested);
@@ -148,6 +148,38 @@ pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, co
                       int32_t max_context_len, float scale, int32_t partition_size,
                       void* workspace, size_t workspace_bytes, int32_t* err_flag,
                       pa_stream_t stream);
+
+/*
+ * pa_decode_sliding_window - decode over the last `window` tokens only.
+ *
+ * As pa_decode, but sequence b attends to tokens [max(0, L - window), L) where L =
+ * context_lens[b]: the sliding-window cache policy that keeps only the most recent tokens
+ * ([Valid-length essay] §3.3, §5.3). Blocks that lie wholly before the window are never read
+ * or checked, so their table entries may already be released (-1). window >= L gives the
+ * same result as pa_decode, bit for bit. window must be > 0 (else PA_ERR_INVALID_ARGUMENT).
+ *
+ * Partitions of a sequence start at the block that holds its first attended token, so the
+ * launch and the workspace scale with the window, not with max_context_len: they are those
+ * of pa_decode with max_context_len replaced by span = min(max_context_len, window +
+ * block_size - 1). partition_size = 0 picks pa_decode_partition_size(cache, batch,
+ * num_q_heads, span, 0); the workspace must hold
+ * pa_decode_sliding_window_workspace_bytes(...) bytes (0: none needed).
+ */
+pa_status_t pa_decode_sliding_window(const pa_cache_desc_t* cache, void* out, const void* q,
+                                     const void* k_pool, const void* v_pool, const int32_t* block_table,
+                                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                                     int32_t num_q_heads, int32_t max_context_len, float scale,
+                                     int32_t window, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream);
+
+/*
+ * pa_decode_sliding_window_workspace_bytes - workspace bytes pa_decode_sliding_window needs
+ * for these sizes and this partition_size (0 = the default policy); 0 when it needs none or
+ * when an argument is invalid (then the decode call itself reports the error).
+ */
+size_t pa_decode_sliding_window_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch,
+                                                int32_t num_q_heads, int32_t max_context_len, int32_t window,
+                                                int32_t partition_size);
 
 /* Human-readable text for a status code (static storage). */
 const char* pa_status_string(pa_status_t status);

@@ -11,9 +11,12 @@ from .paged_attention import (  # noqa: F401
     attention_one_query,
     blocks_needed,
     copy_blocks,
+    gather_range,
     gather_sequence,
     kv_cache_bytes,
     paged_decode,
     paged_decode_heads,
+    paged_decode_window,
+    window_start,
     reshape_and_cache,
 )

@@ -61,28 +61,38 @@ def allocated_kv_bytes(num_kv_heads: int, head_dim: int, dtype_bytes: int, conte
     return 2 * int(num_layers) * int(num_kv_heads) * nb * int(block_size) * int(head_dim) * int(dtype_bytes)
 
 
-def gather_sequence(pool: np.ndarray, table_row: np.ndarray, context_len: int, kv_head: int) -> np.ndarray:
-    """Contiguous [context_len][head_dim] float64 rows of one sequence and kv head.
+def gather_range(pool: np.ndarray, table_row: np.ndarray, start: int, stop: int, kv_head: int) -> np.ndarray:
+    """Contiguous float64 rows [start, stop) of one sequence and kv head.
 
-    Walks the sequence's logical blocks in order, reads physical block table_row[j]
-    ([BlockManager essay] §2, §5.2; [KV Block course] §3.3), concatenates the per-block
-    [block_size][head_dim] slabs and keeps the first context_len rows, so padding and
-    unallocated entries are never read ([Valid-length essay] §4.1).
+    Walks the logical blocks that hold those tokens in order, reads physical block
+    table_row[j] ([BlockManager essay] §2, §5.2; [KV Block course] §3.3), concatenates the
+    per-block [block_size][head_dim] slabs and keeps exactly the requested rows. Blocks
+    outside the range are never read, so padding, unallocated entries and blocks released
+    before a window are never touched ([Valid-length essay] §4.1).
     """
     num_blocks, _, block_size, _ = pool.shape
-    L = int(context_len)
-    if L <= 0:
-        raise OracleInputError(f"context_len {L} <= 0")
-    nb = blocks_needed(L, block_size)
+    start, stop = int(start), int(stop)
+    if stop <= 0:
+        raise OracleInputError(f"context_len {stop} <= 0")
+    if not 0 <= start < stop:
+        raise OracleInputError(f"empty token range [{start}, {stop})")
+    nb = blocks_needed(stop, block_size)
     if nb > len(table_row):
-        raise OracleInputError(f"context_len {L} needs {nb} blocks > table width {len(table_row)}")
+        raise OracleInputError(f"context_len {stop} needs {nb} blocks > table width {len(table_row)}")
+    j0 = start // block_size
     slabs = []
-    for j in range(nb):
+    for j in range(j0, nb):
         pid = int(table_row[j])
         if not 0 <= pid < num_blocks:
             raise OracleInputError(f"block id {pid} at logical block {j} outside [0, {num_blocks})")
         slabs.append(pool[pid, kv_head])
-    return np.concatenate(slabs, axis=0)[:L].astype(np.float64)
+    rows = np.concatenate(slabs, axis=0)
+    return rows[start - j0 * block_size: stop - j0 * block_size].astype(np.float64)
+
+
+def gather_sequence(pool: np.ndarray, table_row: np.ndarray, context_len: int, kv_head: int) -> np.ndarray:
+    """Contiguous [context_len][head_dim] float64 rows of one sequence and kv head (all its tokens)."""
+    return gather_range(pool, table_row, 0, context_len, kv_head)
 
 
 def attention_one_query(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
@@ -128,6 +138,36 @@ def paged_decode(q, k_pool, v_pool, block_table, context_lens, scale) -> np.ndar
         for g in range(Hkv):
             K = gather_sequence(k_pool, block_table[b], context_lens[b], g)
             V = gather_sequence(v_pool, block_table[b], context_lens[b], g)
+            for h in range(g * group, (g + 1) * group):
+                out[b, h] = attention_one_query(q[b, h], K, V, scale)
+    return out
+
+
+def window_start(context_len: int, window: int) -> int:
+    """First attended token of a sliding window of the last ``window`` tokens.
+
+    [Valid-length essay] §3.3 and §5.3: the sliding-window policy keeps only the most recent
+    N tokens' K/V.
+    """
+    return max(0, int(context_len) - int(window))
+
+
+def paged_decode_window(q, k_pool, v_pool, block_table, context_lens, scale, window) -> np.ndarray:
+    """Decode over the last ``window`` tokens of every sequence: float64 [B][Hq][d]."""
+    if int(window) <= 0:
+        raise OracleInputError("window must be positive")
+    B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    if Hq % Hkv:
+        raise OracleInputError(f"num_q_heads {Hq} not a multiple of num_kv_heads {Hkv}")
+    group = Hq // Hkv
+    out = np.empty((B, Hq, d), np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        lo = window_start(L, window)
+        for g in range(Hkv):
+            K = gather_range(k_pool, block_table[b], lo, L, g)
+            V = gather_range(v_pool, block_table[b], lo, L, g)
             for h in range(g * group, (g + 1) * group):
                 out[b, h] = attention_one_query(q[b, h], K, V, scale)
     return out

@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     pa_copy_blocks,
     pa_decode,
     pa_decode_partition_size,
+    pa_decode_sliding_window,
+    pa_decode_sliding_window_workspace_bytes,
     pa_decode_workspace_bytes,
     pa_reshape_and_cache,
     pa_status_string,

@@ -27,7 +27,8 @@ PA_FLAG_BAD_SLOT = 8
 PA_FLAG_BAD_COPY_PAIR = 16
 
 EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_size",
-            "pa_decode_workspace_bytes", "pa_decode", "pa_status_string")
+            "pa_decode_workspace_bytes", "pa_decode", "pa_decode_sliding_window",
+            "pa_decode_sliding_window_workspace_bytes", "pa_status_string")
 
 _DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
@@ -84,6 +85,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_workspace_bytes.restype = SZ
     lib.pa_decode.argtypes = [D, P, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, SZ, P, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_sliding_window.argtypes = [D, P, P, P, P, P, I32, P, I32, I32, I32, F, I32, I32, P, SZ, P, P]
+    lib.pa_decode_sliding_window.restype = ctypes.c_int
+    lib.pa_decode_sliding_window_workspace_bytes.argtypes = [D, I32, I32, I32, I32, I32]
+    lib.pa_decode_sliding_window_workspace_bytes.restype = SZ
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -144,6 +149,14 @@ def pa_decode_workspace_bytes(cache: CacheDesc, batch: int, num_q_heads: int, ma
                                                 max_context_len, partition_size))
 
 
+def pa_decode_sliding_window_workspace_bytes(cache: CacheDesc, batch: int, num_q_heads: int,
+                                             max_context_len: int, window: int,
+                                             partition_size: int = 0) -> int:
+    desc = cache.c()
+    return int(load().pa_decode_sliding_window_workspace_bytes(
+        ctypes.byref(desc), batch, num_q_heads, max_context_len, window, partition_size))
+
+
 def pa_decode(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_lens,
               max_context_len: int, scale: float, partition_size: int = 0, workspace=None,
               err_flag=None, stream=None) -> None:
@@ -155,3 +168,16 @@ def pa_decode(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_len
                             batch, num_q_heads, int(max_context_len), float(scale),
                             int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag),
                             _stream(stream)))
+
+
+def pa_decode_sliding_window(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_lens,
+                             max_context_len: int, scale: float, window: int, partition_size: int = 0,
+                             workspace=None, err_flag=None, stream=None) -> None:
+    batch, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    desc = cache.c()
+    _check(load().pa_decode_sliding_window(
+        ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+        int(block_table.shape[1]), _ptr(context_lens), batch, num_q_heads, int(max_context_len),
+        float(scale), int(window), int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag),
+        _stream(stream)))

@@ -42,6 +42,14 @@ pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAU
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Tokens a sequence's partitions cover: everything without a window; with one, the window
+// plus at most block_size - 1 tokens before it in the block where it starts.
+int32_t window_span(const pa_cache_desc_t* c, int32_t max_context_len, int32_t window) {
+    if (window <= 0) return max_context_len;
+    const int64_t span = (int64_t)window + c->block_size - 1;
+    return span < max_context_len ? (int32_t)span : max_context_len;
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,11 +142,24 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, in
     return (size_t)batch * num_q_heads * parts * (cache->head_dim + 2) * sizeof(float);
 }
 
-pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, const void* k_pool,
-                      const void* v_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
-                      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
-                      int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
-                      size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream) {
+size_t pa_decode_sliding_window_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch,
+                                                int32_t num_q_heads, int32_t max_context_len, int32_t window,
+                                                int32_t partition_size) {
+    if (check_cache(cache) != PA_OK || window <= 0 || max_context_len <= 0) return 0;
+    return pa_decode_workspace_bytes(cache, batch, num_q_heads, window_span(cache, max_context_len, window),
+                                     partition_size);
+}
+
+}  // extern "C"
+
+namespace {
+
+pa_status_t decode_impl(const pa_cache_desc_t* cache, void* out, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                        int32_t max_context_len, float scale, int32_t partition_size, int32_t window,
+                        void* workspace, size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream) {
+    if (window < 0) return PA_ERR_INVALID_ARGUMENT;
     pa_status_t st = check_cache(cache);
     if (st != PA_OK) return st;
     if (batch < 0 || batch > 65535) return PA_ERR_INVALID_ARGUMENT;
@@ -153,11 +174,13 @@ pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, co
     if (max_blocks_per_seq <= 0 || max_context_len <= 0) return PA_ERR_INVALID_ARGUMENT;
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * cache->block_size) return PA_ERR_INVALID_ARGUMENT;
     if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
-    const int32_t P = pa_decode_partition_size(cache, batch, num_q_heads, max_context_len, partition_size);
+    // Partitions tile [start of the window's first block, L): at most `span` tokens.
+    const int32_t span = window_span(cache, max_context_len, window);
+    const int32_t P = pa_decode_partition_size(cache, batch, num_q_heads, span, partition_size);
     if (P <= 0) return PA_ERR_INVALID_ARGUMENT;
-    const int64_t parts = ceil_div(max_context_len, P);
+    const int64_t parts = ceil_div(span, P);
     if (parts > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
-    const size_t need = pa_decode_workspace_bytes(cache, batch, num_q_heads, max_context_len, partition_size);
+    const size_t need = pa_decode_workspace_bytes(cache, batch, num_q_heads, span, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_INVALID_ARGUMENT;
 
     DecodeArgs a{};
@@ -178,6 +201,7 @@ pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, co
     a.max_context_len = max_context_len;
     a.partition_size = P;
     a.max_partitions = (int32_t)parts;
+    a.window = window;
     a.scale_log2 = scale * 1.4426950408889634f;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = decode_mfma_supported(cache->dtype, cache->head_dim, group, cache->block_size)
@@ -185,6 +209,32 @@ pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, co
                        : launch_decode_valu(a, cache->dtype, cache->head_dim, group, batch, cache->num_kv_heads, s);
     if (e == hipSuccess && parts > 1) e = launch_reduce(a, cache->dtype, cache->head_dim, batch, s);
     return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream) {
+    return decode_impl(cache, out, q, k_pool, v_pool, block_table, max_blocks_per_seq, context_lens, batch,
+                       num_q_heads, max_context_len, scale, partition_size, 0, workspace, workspace_bytes,
+                       err_flag, stream);
+}
+
+pa_status_t pa_decode_sliding_window(const pa_cache_desc_t* cache, void* out, const void* q,
+                                     const void* k_pool, const void* v_pool, const int32_t* block_table,
+                                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                                     int32_t num_q_heads, int32_t max_context_len, float scale,
+                                     int32_t window, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream) {
+    if (window <= 0) return PA_ERR_INVALID_ARGUMENT;
+    return decode_impl(cache, out, q, k_pool, v_pool, block_table, max_blocks_per_seq, context_lens, batch,
+                       num_q_heads, max_context_len, scale, partition_size, window, workspace, workspace_bytes,
+                       err_flag, stream);
 }
 
 }  // extern "C"

@@ -55,16 +55,16 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
     const int col = lane % LPR;
     const int lbs = a.log2_block_size;
     const int bs = 1 << lbs;
-    const int t0 = part.t0;
-    const int j0 = part.j0;
     const int ntok = part.ntok;
+    const int rel_lo = part.rel_lo;
+    const int g0 = rel_lo / RPL;  // first row group holding an attended token
 
     const size_t head_bytes = (size_t)bs * D * T::kBytes;
     const size_t block_bytes = head_bytes * a.num_kv_heads;
     const char* kpool = static_cast<const char*>(a.k_pool);
     const char* vpool = static_cast<const char*>(a.v_pool);
     constexpr int kTokPerIter = UNROLL * STRIDE * RPL;
-    const int niters = (ntok + kTokPerIter - 1) / kTokPerIter;
+    const int niters = (ntok - g0 * RPL + kTokPerIter - 1) / kTokPerIter;
 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -83,15 +83,15 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
         int idv[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int rel = ((it * UNROLL + u) * STRIDE + slot) * RPL;  // wave-uniform
-            idv[u] = s_ids[((t0 + (rel < ntok ? rel : 0)) >> lbs) - j0];
+            const int rel = (g0 + (it * UNROLL + u) * STRIDE + slot) * RPL;  // wave-uniform
+            idv[u] = s_ids[(rel < ntok ? rel : 0) >> lbs];  // partitions start on a block
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int rel = ((it * UNROLL + u) * STRIDE + slot) * RPL;
+            const int rel = (g0 + (it * UNROLL + u) * STRIDE + slot) * RPL;
             const int id = __builtin_amdgcn_readfirstlane(idv[u]);
             const size_t slab = (size_t)id * block_bytes + (size_t)kvh * head_bytes;
-            const uint32_t off = (rel + row < ntok)
+            const uint32_t off = (rel + row < ntok && rel + row >= rel_lo)
                                      ? (uint32_t)((rel & (bs - 1)) * D * T::kBytes) + lane_bytes
                                      : kOutOfRange;
             kk[u] = buffer_load16(make_rsrc(kpool + slab, slab_bytes), off);
@@ -103,8 +103,8 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
         float s[G][UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int rel = ((it * UNROLL + u) * STRIDE + slot) * RPL + row;
-            const bool valid = rel < ntok;
+            const int rel = (g0 + (it * UNROLL + u) * STRIDE + slot) * RPL + row;
+            const bool valid = rel < ntok && rel >= rel_lo;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const float d = group_sum<LPR>(dot16(T{}, qv[g], kk[u]));
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
     const int e = threadIdx.x;
     const int L = a.context_lens[b];
     if (L <= 0 || L > a.max_context_len || (L - 1) >> a.log2_block_size >= a.max_blocks_per_seq) return;
-    const int nparts = (L + a.partition_size - 1) / a.partition_size;
+    const int nparts = (L - partition_base(a, L) + a.partition_size - 1) / a.partition_size;
     if (nparts <= 1) return;
     const size_t rec0 = ((size_t)b * a.num_q_heads + h) * a.max_partitions;
     const float* ml = a.ws_ml + rec0 * 2;

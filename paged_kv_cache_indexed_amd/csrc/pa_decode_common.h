@@ -12,10 +12,23 @@ constexpr int kDecodeThreads = kDecodeWaves * 64;
 
 struct Partition {
     int nparts;  // partitions of this sequence
-    int t0;      // first token of this partition
-    int ntok;    // tokens in this partition
-    int j0;      // first logical block of this partition
+    int t0;      // first position of this partition (a block multiple)
+    int rel_lo;  // first attended token, relative to t0 (< block_size; 0 unless a window starts inside)
+    int ntok;    // end of the attended tokens, relative to t0
+    int j0;      // logical block of t0: s_ids[i] is the id of block j0 + i
 };
+
+// First attended position of a sequence of length L: a sliding window keeps the last
+// `window` tokens ([Valid-length essay] §3.3, §5.3), otherwise everything.
+__device__ __forceinline__ int window_start(const DecodeArgs& a, int L) {
+    return (a.window > 0 && L > a.window) ? L - a.window : 0;
+}
+
+// Position at which partition 0 of a sequence of length L starts: the start of the block
+// holding the first attended token (0 without a window). Partitions tile [base, L).
+__device__ __forceinline__ int partition_base(const DecodeArgs& a, int L) {
+    return (window_start(a, L) >> a.log2_block_size) << a.log2_block_size;
+}
 
 template <typename T>
 __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
@@ -28,10 +41,11 @@ __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
 // are set to NaN and the error bit is raised). Never reads a table entry or a pool byte
 // that the checks have not cleared.
 //
-// The table slice of partition p starts at logical block p * P / block_size whatever the
-// length is, so it is loaded in the same round trip as the length (entries past the valid
-// blocks are read from inside the row but never used); one barrier then publishes the ids
-// and the OR of their range checks.
+// Without a window the table slice of partition p starts at logical block p * P / block_size
+// whatever the length is, so it is loaded in the same round trip as the length (entries past
+// the valid blocks are read from inside the row but never used); one barrier then publishes
+// the ids and the OR of their range checks. With a window the slice starts at the block of
+// the window start, so the length is read first.
 //
 // The workgroup covers query heads [h0, h0 + nq): its NaN outputs cover exactly those.
 template <typename T, int D, int NT>
@@ -41,16 +55,21 @@ __device__ bool partition_prologue_heads(const DecodeArgs& a, int p, int h0, int
     const int tid = threadIdx.x;
     const int lbs = a.log2_block_size;
     const int P = a.partition_size;
-    const int j0 = (p * P) >> lbs;
-    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq + j0;
-    const int lim = min(P >> lbs, a.max_blocks_per_seq - j0);
+    int L = 0, base = 0;
+    if (a.window > 0) {
+        L = a.context_lens[b];
+        if (L <= a.max_context_len) base = partition_base(a, L);
+    }
+    const int jp = (base + p * P) >> lbs;  // first block of the partition
+    const int32_t* trow = a.block_table + (size_t)b * a.max_blocks_per_seq;
+    const int lim = min(P >> lbs, a.max_blocks_per_seq - jp);
     int idv[kPerThread];
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const int i = tid + k * NT;
-        idv[k] = (i < lim) ? trow[i] : 0;
+        idv[k] = (i < lim) ? trow[jp + i] : 0;
     }
-    const int L = a.context_lens[b];
+    if (a.window <= 0) L = a.context_lens[b];
     int flag = 0;
     if (L <= 0) flag = PA_FLAG_EMPTY_CONTEXT;
     else if (L > a.max_context_len || ((L - 1) >> lbs) >= a.max_blocks_per_seq) flag = PA_FLAG_BAD_LENGTH;
@@ -61,13 +80,16 @@ __device__ bool partition_prologue_heads(const DecodeArgs& a, int p, int h0, int
         }
         return false;
     }
-    part.nparts = (L + P - 1) / P;
+    part.nparts = (L - base + P - 1) / P;
     if (p >= part.nparts) return false;
-    part.t0 = p * P;
+    part.t0 = base + p * P;
+    part.rel_lo = max(window_start(a, L) - part.t0, 0);
     const int t1 = min(L, part.t0 + P);
     part.ntok = t1 - part.t0;
-    part.j0 = j0;
-    const int nids = ((t1 - 1) >> lbs) - j0 + 1;
+    part.j0 = jp;
+    // only the blocks overlapping [t0, t1) are staged and checked: blocks before a window
+    // may already be released (-1)
+    const int nids = ((t1 - 1) >> lbs) - jp + 1;
     int bad = 0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {

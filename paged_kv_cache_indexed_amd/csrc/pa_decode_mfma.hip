@@ -126,9 +126,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
     Partition part;
     if (!partition_prologue<T, D, G, NW * 64>(a, p, kvh, b, s_ids, part)) return;
-    const int t0 = part.t0;
-    const int j0 = part.j0;
     const int ntok = part.ntok;
+    const int rel_lo = part.rel_lo;
+    const int c0 = rel_lo / kChunk;  // first chunk holding an attended token
 
     // Identity B operand of the 16x16x16 transpose: k-slot (g, i) is 1 in column 4g + i.
     u32x2 ident;
@@ -141,17 +141,19 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const char* vpool = static_cast<const char*>(a.v_pool);
     const uint32_t slab_bytes = (uint32_t)head_bytes;
     const uint32_t seg = 16u * g;  // lane group g reads bytes 64c + 16g .. +15 of a row
-    const int niters = (ntok + kChunk * NW - 1) / (kChunk * NW);
+    const int niters = (ntok - c0 * kChunk + kChunk * NW - 1) / (kChunk * NW);
 
     // Loads of one chunk: tile t rows are tokens rel + 16t + n; lanes past the partition end
     // read zeros through an out-of-range offset.
     auto issue = [&](int it, u32x4 (*kk)[NC], u32x4 (*vv)[NC]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int rel = (it * NW + wave) * kChunk + 16 * t;  // wave-uniform
-            const int id = __builtin_amdgcn_readfirstlane(s_ids[((t0 + (rel < ntok ? rel : 0)) >> lbs) - j0]);
+            const int rel = (c0 + it * NW + wave) * kChunk + 16 * t;  // wave-uniform
+            const int id = __builtin_amdgcn_readfirstlane(s_ids[(rel < ntok ? rel : 0) >> lbs]);  // partitions start on a block
             const size_t slab = (size_t)id * block_bytes + (size_t)kvh * head_bytes;
-            const uint32_t off = (rel + n < ntok) ? (uint32_t)(((rel & (bs - 1)) + n) * D * 2) + seg : kOutOfRange;
+            const uint32_t off = (rel + n < ntok && rel + n >= rel_lo)
+                                     ? (uint32_t)(((rel & (bs - 1)) + n) * D * 2) + seg
+                                     : kOutOfRange;
             const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + slab, slab_bytes);
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + slab, slab_bytes);
 #pragma unroll
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     for (int s = 0; s < NS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int it, u32x4 (*kk)[NC], u32x4 (*vv)[NC]) {
-        const int rel0 = (it * NW + wave) * kChunk;
+        const int rel0 = (c0 + it * NW + wave) * kChunk;
         float sc[8];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = rel0 + 16 * t + 4 * g + i;
-                sc[4 * t + i] = (tok < ntok) ? st[i] * a.scale_log2 : -INFINITY;
+                sc[4 * t + i] = (tok < ntok && tok >= rel_lo) ? st[i] * a.scale_log2 : -INFINITY;
             }
         }
         float cm = sc[0];

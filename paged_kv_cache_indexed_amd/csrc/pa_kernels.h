@@ -31,6 +31,7 @@ struct DecodeArgs {
     int32_t max_context_len;
     int32_t partition_size;
     int32_t max_partitions;
+    int32_t window;    // > 0: attend to the last `window` tokens only; 0: the whole context
     float scale_log2;  // scale * log2(e): scores live in the base-2 exponent domain
 };
 

@@ -7,29 +7,43 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (CacheDesc, pa_copy_blocks, pa_decode, pa_decode_workspace_bytes,
+from ._lib import (CacheDesc, pa_copy_blocks, pa_decode, pa_decode_sliding_window,
+                   pa_decode_sliding_window_workspace_bytes, pa_decode_workspace_bytes,
                    pa_reshape_and_cache)
 
 
 def workspace_for(k_pool: torch.Tensor, batch: int, num_q_heads: int, max_context_len: int,
-                  partition_size: int = 0):
-    """A float32 workspace tensor of the size pa_decode needs, or None if it needs none."""
-    n = pa_decode_workspace_bytes(CacheDesc.of(k_pool), batch, num_q_heads, max_context_len,
-                                  partition_size)
+                  partition_size: int = 0, window: int = 0):
+    """A float32 workspace tensor of the size the decode needs, or None if it needs none."""
+    if window > 0:
+        n = pa_decode_sliding_window_workspace_bytes(CacheDesc.of(k_pool), batch, num_q_heads,
+                                                     max_context_len, window, partition_size)
+    else:
+        n = pa_decode_workspace_bytes(CacheDesc.of(k_pool), batch, num_q_heads, max_context_len,
+                                      partition_size)
     if n == 0:
         return None
     return torch.empty((n + 3) // 4, dtype=torch.float32, device=k_pool.device)
 
 
 def decode(q, k_pool, v_pool, block_table, context_lens, max_context_len: int, scale: float,
-           partition_size: int = 0, out=None, workspace=None, err_flag=None, stream=None):
-    """Paged decode attention; returns ``out`` [batch][num_q_heads][head_dim] in q's dtype."""
+           partition_size: int = 0, out=None, workspace=None, err_flag=None, stream=None,
+           window: int = 0):
+    """Paged decode attention; returns ``out`` [batch][num_q_heads][head_dim] in q's dtype.
+
+    ``window`` > 0 attends to the last ``window`` tokens of each sequence only."""
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = workspace_for(k_pool, q.shape[0], q.shape[1], max_context_len, partition_size)
-    pa_decode(CacheDesc.of(k_pool), out, q, k_pool, v_pool, block_table, context_lens,
-              max_context_len, scale, partition_size, workspace, err_flag, stream)
+        workspace = workspace_for(k_pool, q.shape[0], q.shape[1], max_context_len, partition_size,
+                                  window)
+    if window > 0:
+        pa_decode_sliding_window(CacheDesc.of(k_pool), out, q, k_pool, v_pool, block_table, context_lens,
+                                 max_context_len, scale, window, partition_size, workspace, err_flag,
+                                 stream)
+    else:
+        pa_decode(CacheDesc.of(k_pool), out, q, k_pool, v_pool, block_table, context_lens,
+                  max_context_len, scale, partition_size, workspace, err_flag, stream)
     return out
 
 

@@ -371,6 +371,33 @@ def pin_errors(o):
         raise AssertionError(f"{what} must raise")
 
 
+def pin_sliding_window(o):
+    """Window decode: brute force over the last W tokens; W >= L is the full decode bit for
+    bit; W = 1 returns the last value; blocks wholly before the window may be -1."""
+    lens, Hq, Hkv, d, bs = [1, 7, 13, 20], 4, 2, 5, 4
+    c = _make_case(71, lens, Hq, Hkv, d, bs)
+    scale = 0.4
+    full = _decode(o, c, scale)
+    for W in (1, 3, 4, 5, 12, 19, 20, 50):
+        got = o.paged_decode_window(c["q"], c["k_pool"], c["v_pool"], c["table"], c["lens"], scale, W)
+        kc = [k[max(0, L - W):] for k, L in zip(c["kc"], lens)]
+        vc = [v[max(0, L - W):] for v, L in zip(c["vc"], lens)]
+        ref = _brute_decode(c["q"], kc, vc, [min(L, W) for L in lens], scale, Hq, Hkv)
+        _close(got, ref, 1e-12, f"window {W}")
+        if W >= max(lens):
+            assert np.array_equal(got, full), "window >= L must equal the full decode"
+        # blocks that lie wholly before the window are released: -1 there is never read
+        t = c["table"].copy()
+        for b, L in enumerate(lens):
+            t[b, :max(0, L - W) // bs] = -1
+        got2 = o.paged_decode_window(c["q"], c["k_pool"], c["v_pool"], t, c["lens"], scale, W)
+        assert np.array_equal(got2, got), "released blocks before the window were read"
+    last = o.paged_decode_window(c["q"], c["k_pool"], c["v_pool"], c["table"], c["lens"], scale, 1)
+    for b, L in enumerate(lens):
+        for h in range(Hq):
+            assert np.array_equal(last[b, h], c["vc"][b][L - 1, h // (Hq // Hkv)].astype(np.float64))
+
+
 ALL_PINS = [pin_gather_roundtrip, pin_worked_example, pin_memory_formula, pin_bruteforce,
             pin_closed_forms, pin_invariants, pin_sdpa, pin_reshape_and_cache, pin_copy_blocks,
-            pin_errors]
+            pin_errors, pin_sliding_window]

@@ -70,6 +70,32 @@ def test_partition_policy(lib):
     assert _lib.pa_decode_partition_size(_desc(bs=8), 4, 32, 100, 8200) == -1
 
 
+def test_sliding_window_sizing(lib):
+    # partitions cover the window plus at most block_size - 1 tokens before it
+    c = _desc(bs=32)
+    span = 4096 + 31
+    p = _lib.pa_decode_partition_size(c, 32, 32, span, 0)
+    want = 32 * 32 * -(-span // p) * 130 * 4 if -(-span // p) > 1 else 0
+    assert _lib.pa_decode_sliding_window_workspace_bytes(c, 32, 32, 32769, 4096, 0) == want
+    # a window at least as long as every context sizes exactly like the full decode
+    for w in (32769, 40000, 2**31 - 1):
+        assert (_lib.pa_decode_sliding_window_workspace_bytes(c, 32, 32, 32769, w, 0)
+                == _lib.pa_decode_workspace_bytes(c, 32, 32, 32769, 0))
+    # explicit partition sizes
+    assert (_lib.pa_decode_sliding_window_workspace_bytes(c, 2, 4, 10000, 1000, 256)
+            == 2 * 4 * -(-(1000 + 31) // 256) * 130 * 4)
+    # never more than the full decode needs
+    for w in (1, 7, 33, 500, 1024, 5000):
+        for P in (0, 32, 128, 512):
+            assert (_lib.pa_decode_sliding_window_workspace_bytes(c, 8, 32, 9000, w, P)
+                    <= _lib.pa_decode_workspace_bytes(c, 8, 32, 9000, P))
+    assert _lib.pa_decode_sliding_window_workspace_bytes(c, 8, 32, 9000, 0, 0) == 0
+    d = c.c()
+    st = lib.pa_decode_sliding_window(ctypes.byref(d), None, None, None, None, None, 4, None, 0, 32, 10,
+                                      1.0, 0, 0, None, 0, None, None)
+    assert st == _lib.PA_ERR_INVALID_ARGUMENT  # window 0
+
+
 def test_unsupported_and_invalid_caches(lib):
     assert _lib.pa_decode_partition_size(_desc(bs=12), 4, 32, 100, 0) == -1
     assert _lib.pa_decode_partition_size(_desc(d=96), 4, 32, 100, 0) == -1

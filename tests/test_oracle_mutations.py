@@ -102,6 +102,16 @@ def m_heads_gqa_modulo(q, k_pool, v_pool, block_table, context_lens, scale, pair
     return out
 
 
+def m_window_off_by_one(q, k_pool, v_pool, block_table, context_lens, scale, window):
+    return pa.__dict__["_orig_paged_decode_window"](q, k_pool, v_pool, block_table, context_lens, scale,
+                                                    int(window) + 1)
+
+
+def m_window_start_floor_block(L, W):
+    lo = max(0, int(L) - int(W))
+    return lo - lo % 4
+
+
 def m_cache_divmod_swapped(k_pool, v_pool, key, value, slot_mapping):
     k_new, v_new = k_pool.copy(), v_pool.copy()
     nb, _, bs, _ = k_pool.shape
@@ -154,6 +164,8 @@ MUTANTS = {
     "gqa_identity": ("paged_decode", _decode_with_head_map(lambda h, Hq, Hkv: min(h, Hkv - 1))),
     "wrong_sequence_row": ("paged_decode", m_wrong_sequence_row),
     "heads_gqa_modulo": ("paged_decode_heads", m_heads_gqa_modulo),
+    "window_off_by_one": ("paged_decode_window", m_window_off_by_one),
+    "window_start_block_floor": ("window_start", m_window_start_floor_block),
     "cache_divmod_swapped": ("reshape_and_cache", m_cache_divmod_swapped),
     "cache_skips_value": ("reshape_and_cache", m_cache_skips_value),
     "copy_only_k": ("copy_blocks", m_copy_only_k),
@@ -166,7 +178,8 @@ MUTANTS = {
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
-    for orig in ("paged_decode", "reshape_and_cache", "copy_blocks", "kv_cache_bytes"):
+    for orig in ("paged_decode", "reshape_and_cache", "copy_blocks", "kv_cache_bytes",
+                 "paged_decode_window"):
         monkeypatch.setitem(pa.__dict__, "_orig_" + orig, getattr(pa, orig))
     monkeypatch.setattr(pa, attr, fn)
     failed = []
