@@ -3,6 +3,7 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
 may import this package. It is never on the product path, and it shares no code with the
 HIP library: it is written from the pages' description of what PagedAttention computes.
+``oracle.fp8_cache`` covers blocks stored as 8-bit floats with a scale per row.
 """
 
 from .paged_attention import (  # noqa: F401
@@ -20,3 +21,5 @@ from .paged_attention import (  # noqa: F401
     window_start,
     reshape_and_cache,
 )
+
+from . import fp8_cache  # noqa: F401,E402

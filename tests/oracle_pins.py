@@ -401,3 +401,178 @@ def pin_sliding_window(o):
 ALL_PINS = [pin_gather_roundtrip, pin_worked_example, pin_memory_formula, pin_bruteforce,
             pin_closed_forms, pin_invariants, pin_sdpa, pin_reshape_and_cache, pin_copy_blocks,
             pin_errors, pin_sliding_window]
+
+
+# ---- 8-bit float (OCP E4M3) blocks with a scale per row: pins take oracle.fp8_cache --------
+
+# Code -> value pairs fixed by the OCP 8-bit floating point specification (E4M3: bias 7,
+# subnormals below 2^-6, largest finite 448, S.1111.111 is NaN).
+_E4M3_SPEC = {0x00: 0.0, 0x01: 2.0 ** -9, 0x02: 2.0 ** -8, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+              0x0F: 1.875 * 2.0 ** -6, 0x30: 0.5, 0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x70: 128.0,
+              0x77: 240.0, 0x78: 256.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+
+
+def _torch_e4m3(codes):
+    """Independent decoder: torch's CPU float8_e4m3fn."""
+    import torch
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _torch_e4m3_encode(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_values(o8):
+    """The value table against the specification's printed codes and torch's decoder."""
+    for c, v in _E4M3_SPEC.items():
+        assert o8.e4m3_value(np.uint8(c)) == v, f"code {c:#x}"
+    assert np.isnan(o8.e4m3_value(np.uint8(0x7F))) and np.isnan(o8.e4m3_value(np.uint8(0xFF)))
+    assert np.signbit(o8.e4m3_value(np.uint8(0x80)))
+    all_codes = np.arange(256, dtype=np.uint8)
+    ours, ref = o8.e4m3_value(all_codes), _torch_e4m3(all_codes)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert fin.sum() == 254 and np.array_equal(ours[fin], ref[fin])
+    assert np.all(np.diff(ours[:0x7F]) > 0), "magnitudes must rise with the code"
+
+
+def pin_e4m3_encode(o8):
+    """Round trip of every finite code, ties to even at every midpoint, torch on random values."""
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    vals = _torch_e4m3(codes)
+    assert np.array_equal(o8.e4m3_encode(vals), codes)
+    mags = _torch_e4m3(np.arange(0x7F, dtype=np.uint8))
+    mid = (mags[:-1] + mags[1:]) / 2  # exact in float64
+    got = o8.e4m3_encode(mid)
+    lower = np.arange(0x7E)
+    want = np.where(lower % 2 == 0, lower, lower + 1)
+    assert np.array_equal(got, want), "midpoints must round to the even code"
+    eps = (mags[1:] - mags[:-1]) / 16
+    assert np.array_equal(o8.e4m3_encode(mid - eps), lower)
+    assert np.array_equal(o8.e4m3_encode(mid + eps), lower + 1)
+    assert np.array_equal(o8.e4m3_encode(-mid), want | 0x80)
+    x = (_rng(91).uniform(-448, 448, 20000)).astype(np.float32)
+    x[:100] *= np.float32(1e-3)
+    assert np.array_equal(o8.e4m3_encode(x), _torch_e4m3_encode(x))
+
+
+def pin_quantize_rows(o8):
+    """Row quantisation: the largest magnitude maps to +-448, the dequantised row stays within
+    E4M3's half-step of x, zero rows are all zero, and the codes are torch's for x / s."""
+    rng = _rng(92)
+    for mag in (1e-3, 1.0, 37.0, 3e4):
+        x = (rng.standard_normal((6, 3, 64)) * mag).astype(np.float32)
+        codes, s = o8.quantize_rows(x)
+        assert codes.dtype == np.uint8 and s.dtype == np.float32 and s.shape == (6, 3)
+        imax = np.argmax(np.abs(x), axis=-1)
+        top = np.take_along_axis(codes, imax[..., None], -1)[..., 0]
+        assert np.all((top & 0x7F) == 0x7E), "the row maximum must take the largest code"
+        deq = _torch_e4m3(codes) * s[..., None].astype(np.float64)
+        bound = np.abs(x) * 2.0 ** -4 + s[..., None] * 2.0 ** -10 * 1.001 + np.abs(x) * 1e-6
+        assert np.all(np.abs(deq - x) <= bound), "dequantised row outside E4M3's rounding bound"
+        quot = np.clip(x / np.where(s == 0, 1, s)[..., None], -448, 448).astype(np.float32)
+        assert np.array_equal(codes, _torch_e4m3_encode(quot))
+    z = np.zeros((2, 8), np.float32)
+    codes, s = o8.quantize_rows(z)
+    assert np.all(codes == 0) and np.all(s == 0)
+
+
+def _fp8_case(o8, seed, lens, Hq, Hkv, d, bs, spare=2):
+    """A tiny quantised cache: random finite codes of moderate size, a random scale per row,
+    unused slots holding NaN codes. Returns pools plus the per-sequence dequantised rows."""
+    rng = _rng(seed, 8)
+    B = len(lens)
+    nbs = [-(-int(L) // bs) for L in lens]
+    nb = sum(nbs) + spare
+    perm = rng.permutation(nb)
+    table = np.full((B, max(nbs) + 1), -1, np.int32)
+    kc = np.full((nb, Hkv, bs, d), 0x7F, np.uint8)
+    vc = np.full_like(kc, 0x7F)
+    ks = np.full((nb, Hkv, bs), np.nan, np.float32)
+    vs = np.full_like(ks, np.nan)
+    rows_k, rows_v, cur = [], [], 0
+    for b, L in enumerate(lens):
+        ids = perm[cur:cur + nbs[b]]
+        cur += nbs[b]
+        table[b, :nbs[b]] = ids
+        ck = rng.integers(0x20, 0x58, (L, Hkv, d)) | (rng.integers(0, 2, (L, Hkv, d)) << 7)
+        cv = rng.integers(0x20, 0x58, (L, Hkv, d)) | (rng.integers(0, 2, (L, Hkv, d)) << 7)
+        sk = rng.uniform(0.01, 0.2, (L, Hkv)).astype(np.float32)
+        sv = rng.uniform(0.01, 0.2, (L, Hkv)).astype(np.float32)
+        rk = np.zeros((L, Hkv, d))
+        rv = np.zeros((L, Hkv, d))
+        for t in range(L):
+            for h in range(Hkv):
+                kc[ids[t // bs], h, t % bs] = ck[t, h]
+                vc[ids[t // bs], h, t % bs] = cv[t, h]
+                ks[ids[t // bs], h, t % bs] = sk[t, h]
+                vs[ids[t // bs], h, t % bs] = sv[t, h]
+                rk[t, h] = _torch_e4m3(ck[t, h]) * float(sk[t, h])
+                rv[t, h] = _torch_e4m3(cv[t, h]) * float(sv[t, h])
+        rows_k.append(rk)
+        rows_v.append(rv)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    return dict(q=q, kc=kc, vc=vc, ks=ks, vs=vs, table=table, lens=np.array(lens, np.int32),
+                rows_k=rows_k, rows_v=rows_v)
+
+
+def pin_fp8_decode(o8):
+    """Decode over a quantised cache: brute force over rows dequantised with torch's table and
+    an explicit per-row loop; K scales act like a scaled query; V scales scale the output."""
+    lens, Hq, Hkv, d, bs = [1, 5, 9, 16], 4, 2, 8, 4
+    c = _fp8_case(o8, 93, lens, Hq, Hkv, d, bs)
+    scale = 0.3
+    got = o8.paged_decode_fp8(c["q"], c["kc"], c["vc"], c["ks"], c["vs"], c["table"], c["lens"], scale)
+    ref = _brute_decode(c["q"], c["rows_k"], c["rows_v"], lens, scale, Hq, Hkv)
+    _close(got, ref, 1e-12, "fp8 decode vs brute force")
+    k2 = o8.paged_decode_fp8(c["q"], c["kc"], c["vc"], c["ks"] * 2, c["vs"], c["table"], c["lens"], scale)
+    q2 = o8.paged_decode_fp8(c["q"] * 2, c["kc"], c["vc"], c["ks"], c["vs"], c["table"], c["lens"], scale)
+    assert np.array_equal(k2, q2), "doubling every K scale must equal doubling q"
+    v3 = o8.paged_decode_fp8(c["q"], c["kc"], c["vc"], c["ks"], c["vs"] * 4, c["table"], c["lens"], scale)
+    assert np.array_equal(v3, got * 4), "V scales must scale the output"
+    for W in (1, 3, 8):
+        gw = o8.paged_decode_fp8(c["q"], c["kc"], c["vc"], c["ks"], c["vs"], c["table"], c["lens"], scale,
+                                 window=W)
+        rw = _brute_decode(c["q"], [r[max(0, L - W):] for r, L in zip(c["rows_k"], lens)],
+                           [r[max(0, L - W):] for r, L in zip(c["rows_v"], lens)],
+                           [min(L, W) for L in lens], scale, Hq, Hkv)
+        _close(gw, rw, 1e-12, f"fp8 window {W}")
+
+
+def pin_fp8_append_and_copy(o8):
+    """Quantised append lands codes and scales in the slot's block and offset (per-element
+    loop), skips negative slots, and dequantises back within E4M3's bound; copy-on-write
+    moves codes and scales together."""
+    rng = _rng(94)
+    nb, Hkv, bs, d = 6, 2, 4, 16
+    kc = rng.integers(0, 256, (nb, Hkv, bs, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, (nb, Hkv, bs, d)).astype(np.uint8)
+    ks = rng.uniform(0.1, 1, (nb, Hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0.1, 1, (nb, Hkv, bs)).astype(np.float32)
+    key = rng.standard_normal((4, Hkv, d)).astype(np.float32)
+    value = (rng.standard_normal((4, Hkv, d)) * 5).astype(np.float32)
+    slots = np.array([5, -1, 22, 0], np.int32)
+    k2, v2, ks2, vs2 = o8.reshape_and_cache_fp8(kc, vc, ks, vs, key, value, slots)
+    touched = np.zeros((nb, Hkv, bs), bool)
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        blk, off = slot // bs, slot % bs
+        for h in range(Hkv):
+            touched[blk, h, off] = True
+            for src, codes, sc in ((key, k2, ks2), (value, v2, vs2)):
+                deq = _torch_e4m3(codes[blk, h, off]) * float(sc[blk, h, off])
+                bound = np.abs(src[i, h]) * 2.0 ** -4 + float(sc[blk, h, off]) * 2.0 ** -10 * 1.001 + 1e-7
+                assert np.all(np.abs(deq - src[i, h]) <= bound), (i, h)
+    assert np.array_equal(k2[~touched], kc[~touched]) and np.array_equal(v2[~touched], vc[~touched])
+    assert np.array_equal(ks2[~touched], ks[~touched]) and np.array_equal(vs2[~touched], vs[~touched])
+    pairs = np.array([[2, 4], [0, 5]], np.int32)
+    k3, v3, ks3, vs3 = o8.copy_blocks_fp8(kc, vc, ks, vs, pairs)
+    for src, dst in pairs:
+        assert np.array_equal(k3[dst], kc[src]) and np.array_equal(v3[dst], vc[src])
+        assert np.array_equal(ks3[dst], ks[src]) and np.array_equal(vs3[dst], vs[src])
+    assert np.array_equal(k3[[1, 3]], kc[[1, 3]]) and np.array_equal(ks3[[1, 3]], ks[[1, 3]])
+
+
+FP8_PINS = [pin_e4m3_values, pin_e4m3_encode, pin_quantize_rows, pin_fp8_decode, pin_fp8_append_and_copy]

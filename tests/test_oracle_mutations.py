@@ -189,3 +189,102 @@ def test_mutant_is_caught(name, monkeypatch):
         except Exception as e:  # noqa: BLE001 - any failure means the pin caught it
             failed.append((pin.__name__, type(e).__name__))
     assert failed, f"mutant {name} passed every pin"
+
+
+# ---- planted mistakes in the 8-bit float cache oracle ---------------------------------------
+
+import oracle.fp8_cache as o8  # noqa: E402
+
+_value = o8.e4m3_value
+_encode = o8.e4m3_encode
+_quantize = o8.quantize_rows
+_dequantize = o8.dequantize
+_append8 = o8.reshape_and_cache_fp8
+_copy8 = o8.copy_blocks_fp8
+
+
+def m8_bias_8(codes):
+    # the other common 8-bit float flavour: exponent bias 8
+    return _value(codes) / 2.0
+
+
+def m8_no_subnormals(codes):
+    c = np.asarray(codes, np.int64)
+    v = _value(codes)
+    return np.where(((c >> 3) & 0xF) == 0, 0.0 * v, v)
+
+
+def m8_ties_away(x):
+    x = np.asarray(x, np.float64)
+    mags = _value(np.arange(0x7F, dtype=np.uint8))
+    a = np.abs(x)
+    hi = np.minimum(np.searchsorted(mags, a), len(mags) - 1)
+    lo = np.maximum(hi - 1, 0)
+    code = np.where(mags[hi] - a <= a - mags[lo], hi, lo)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def m8_truncate(x):
+    x = np.asarray(x, np.float64)
+    mags = _value(np.arange(0x7F, dtype=np.uint8))
+    a = np.abs(x)
+    code = np.searchsorted(mags, a, side="right") - 1
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def m8_scale_127(x):
+    # an int8-style scale: s = max|x| / 127, so codes never reach the top of the range
+    x = np.asarray(x, np.float32)
+    s = (np.max(np.abs(x), axis=-1) / np.float32(127.0)).astype(np.float32)
+    quot = (x / np.where(s == 0, np.float32(1), s)[..., None]).astype(np.float32)
+    codes = np.where((s == 0)[..., None], np.uint8(0), o8.e4m3_encode(quot)).astype(np.uint8)
+    return codes, s
+
+
+def m8_dequant_no_scale(codes, scales):
+    return _value(codes)
+
+
+def m8_dequant_scale_shifted(codes, scales):
+    return _value(codes) * np.roll(np.asarray(scales, np.float64), 1, axis=-1)[..., None]
+
+
+def m8_append_scale_misplaced(kc, vc, ks, vs, key, value, slots):
+    k2, v2, ks2, vs2 = _append8(kc, vc, ks, vs, key, value, slots)
+    return k2, v2, np.roll(ks2, 1, axis=-1), vs2
+
+
+def m8_append_v_from_k(kc, vc, ks, vs, key, value, slots):
+    return _append8(kc, vc, ks, vs, key, key, slots)
+
+
+def m8_copy_without_scales(kc, vc, ks, vs, pairs):
+    k2, v2, _, _ = _copy8(kc, vc, ks, vs, pairs)
+    return k2, v2, ks.copy(), vs.copy()
+
+
+FP8_MUTANTS = {
+    "bias_8": ("e4m3_value", m8_bias_8),
+    "no_subnormals": ("e4m3_value", m8_no_subnormals),
+    "ties_away": ("e4m3_encode", m8_ties_away),
+    "truncate": ("e4m3_encode", m8_truncate),
+    "scale_127": ("quantize_rows", m8_scale_127),
+    "dequant_no_scale": ("dequantize", m8_dequant_no_scale),
+    "dequant_scale_shifted": ("dequantize", m8_dequant_scale_shifted),
+    "append_scale_misplaced": ("reshape_and_cache_fp8", m8_append_scale_misplaced),
+    "append_v_from_k": ("reshape_and_cache_fp8", m8_append_v_from_k),
+    "copy_without_scales": ("copy_blocks_fp8", m8_copy_without_scales),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(name, monkeypatch):
+    attr, fn = FP8_MUTANTS[name]
+    monkeypatch.setattr(o8, attr, fn)
+    failed = []
+    for pin in oracle_pins.FP8_PINS:
+        try:
+            pin(o8)
+        except Exception as e:  # noqa: BLE001 - any failure means the pin caught it
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"
