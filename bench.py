@@ -15,6 +15,9 @@ plus the decode kernel's roofline figure timed with HIP events and the CPU oracl
 
 With --window W the decode attends to the last W tokens of each sequence only
 (pa_decode_sliding_window) and the algorithmic bytes count min(context_len, W) tokens.
+With --kv fp8 the pools hold 8-bit floats (OCP E4M3) with a float32 scale per (token, kv
+head) row, filled by the library's own quantising append; the step uses the *_fp8 entry
+points and the algorithmic bytes are 2 x kv_heads x (head_dim + 4) per attended token.
 """
 
 from __future__ import annotations
@@ -142,6 +145,91 @@ def _cpu_baseline_beams(w, host, budget_s: float, window: int = 0) -> dict:
                       f"{w.num_kv_heads} heads, L={int(L[0])} ({per_seq / 1e6:.0f} MB of KV each) in {dt:.1f} s"}
 
 
+def _cpu_baseline_fp8(w, budget_s: float, window: int = 0) -> dict:
+    """The oracle's quantised step on host copies, one sequence at a time: its append of the
+    new row into the sequence's (oracle-quantised) blocks, then its decode. Quantising the
+    blocks that were already cached is setup and is not timed."""
+    import oracle
+    import oracle.fp8_cache as o8
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    per_tok = 2 * w.num_kv_heads * (w.head_dim + 4)
+    L = w.lens_after_append
+    bs = w.block_size
+    timed = 0.0
+    done = seqs = 0
+    for b in range(w.batch):
+        ids = w.block_table[b, :oracle.blocks_needed(int(L[b]), bs)]
+        kc, ks = o8.quantize_rows(np.nan_to_num(w.k_pool[ids]))
+        vc, vs = o8.quantize_rows(np.nan_to_num(w.v_pool[ids]))
+        slot = int(w.slot_mapping[b])
+        local = np.array([int(np.nonzero(ids == slot // bs)[0][0]) * bs + slot % bs], np.int32)
+        table = np.arange(len(ids), dtype=np.int32)[None]
+        t0 = time.perf_counter()
+        pools = o8.reshape_and_cache_fp8(kc, vc, ks, vs, w.new_key[b:b + 1], w.new_value[b:b + 1], local)
+        o8.paged_decode_fp8(w.q[b:b + 1], *pools, table, L[b:b + 1], w.scale, window=window)
+        timed += time.perf_counter() - t0
+        done += per_tok * (min(int(L[b]), window) if window > 0 else int(L[b]))
+        seqs += 1
+        if timed >= budget_s:
+            break
+    return {"value": round(done / timed / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle quantised append + float64 {'window-' + str(window) + ' ' if window > 0 else ''}"
+                      f"decode of sequences 0..{seqs - 1} (all heads, {done / 1e6:.1f} MB of codes and "
+                      f"scales) in {timed:.1f} s"}
+
+
+def _cpu_baseline_fp8_beams(w, host, budget_s: float, window: int = 0) -> dict:
+    """The oracle's quantised step for one beam of the 32K workload, on the heads in ``host``."""
+    import oracle.fp8_cache as o8
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    kc, ks = o8.quantize_rows(np.nan_to_num(host["k_pool"]))
+    vc, vs = o8.quantize_rows(np.nan_to_num(host["v_pool"]))
+    heads = host["k_pool"].shape[1]
+    L = np.full(1, w.context + 1, np.int32)
+    att = min(int(L[0]), window) if window > 0 else int(L[0])
+    per_seq = 2 * heads * (w.head_dim + 4) * att
+    t0 = time.perf_counter()
+    reps = 0
+    while reps == 0 or time.perf_counter() - t0 < budget_s:
+        p1 = o8.copy_blocks_fp8(kc, vc, ks, vs, host["copy_pairs"])
+        p2 = o8.reshape_and_cache_fp8(*p1, host["new_key"], host["new_value"], host["slot_mapping"])
+        o8.paged_decode_fp8(host["q"], *p2, host["table"], L, w.scale, window=window)
+        reps += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(reps * per_seq / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x (quantised copy-on-write + append + float64 decode) of beam 0, "
+                      f"{heads} of {w.num_kv_heads} heads, L={int(L[0])} in {dt:.1f} s"}
+
+
+def _fp8_pools(kp, vp):
+    """8-bit float copies of two float pools, quantised by the library's own append: every
+    slot of the pool is appended once (unwritten NaN slots as zeros, never read)."""
+    import torch
+
+    from paged_kv_cache_indexed_amd import ops
+
+    nb, hkv, bs, d = kp.shape
+    k8, v8, ks, vs = ops.empty_fp8_cache(nb, hkv, bs, d, kp.device)
+    slots = torch.arange(nb * bs, dtype=torch.int32, device=kp.device)
+
+    def rows(x):
+        return torch.nan_to_num(x).permute(0, 2, 1, 3).reshape(nb * bs, hkv, d).contiguous()
+
+    ops.reshape_and_cache_fp8(rows(kp), rows(vp), k8, v8, ks, vs, slots)
+    torch.cuda.synchronize()
+    return k8, v8, ks, vs
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +239,8 @@ def main() -> int:
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--median", type=float, default=None)
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--kv", choices=["native", "fp8"], default="native",
+                    help="pool elements: the workload's dtype, or 8-bit floats with a scale per row")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: attend to the last W tokens only (0: whole context)")
     ap.add_argument("--replica-bytes", type=float, default=1.5 * 2 ** 30,
@@ -179,14 +269,26 @@ def main() -> int:
         w = beam_workload(dev)
         t = dict(w.tensors)
         if not args.no_cpu_baseline:
-            host_sample = host_subset(w, [0], range(w.num_kv_heads))
+            host_sample = host_subset(w, [0], range(4 if args.kv == "fp8" else w.num_kv_heads))
     else:
         w = _workload(args.config, args.block_size, args.median)
         t = w.to_device(dev)
-    pool_bytes = 2 * t["k_pool"].numel() * t["k_pool"].element_size()
+    fp8 = args.kv == "fp8"
+    if fp8 and w.dtype == "f32":
+        print("--kv fp8 needs a workload with fp16 or bf16 queries", file=sys.stderr)
+        return 2
+    if fp8:
+        k8, v8, ks8, vs8 = _fp8_pools(t["k_pool"], t["v_pool"])
+        t["k_pool"], t["v_pool"] = k8, v8
+        pool_bytes = 2 * (k8.numel() + 4 * ks8.numel())
+    else:
+        pool_bytes = 2 * t["k_pool"].numel() * t["k_pool"].element_size()
     R = max(2, math.ceil(args.replica_bytes / pool_bytes))
     kps = [t["k_pool"]] + [t["k_pool"].clone() for _ in range(R - 1)]
     vps = [t["v_pool"]] + [t["v_pool"].clone() for _ in range(R - 1)]
+    if fp8:
+        kss = [ks8] + [ks8.clone() for _ in range(R - 1)]
+        vss = [vs8] + [vs8.clone() for _ in range(R - 1)]
     lens = t["lens_after"]
     max_len = int(w.lens_after_append.max())
     P = args.partition_size
@@ -196,18 +298,29 @@ def main() -> int:
     pairs = t["copy_pairs"]
     esize = t["k_pool"].element_size()
     attended = np.minimum(w.lens_after_append, W) if W > 0 else w.lens_after_append
-    kv_bytes = 2 * w.num_kv_heads * w.head_dim * esize * int(attended.sum())
+    row_bytes = w.head_dim + 4 if fp8 else w.head_dim * esize  # codes + scale, or elements
+    kv_bytes = 2 * w.num_kv_heads * row_bytes * int(attended.sum())
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
         r = i % R
-        if pairs.shape[0]:
-            ops.copy_blocks(kps[r], vps[r], pairs)
-        ops.reshape_and_cache(t["new_key"], t["new_value"], kps[r], vps[r], t["slot_mapping"])
+        if fp8:
+            if pairs.shape[0]:
+                ops.copy_blocks_fp8(kps[r], vps[r], kss[r], vss[r], pairs)
+            ops.reshape_and_cache_fp8(t["new_key"], t["new_value"], kps[r], vps[r], kss[r], vss[r],
+                                      t["slot_mapping"])
+        else:
+            if pairs.shape[0]:
+                ops.copy_blocks(kps[r], vps[r], pairs)
+            ops.reshape_and_cache(t["new_key"], t["new_value"], kps[r], vps[r], t["slot_mapping"])
         if ev is not None:
             ev[0].record(stream)
-        ops.decode(t["q"], kps[r], vps[r], t["block_table"], lens, max_len, w.scale,
-                   partition_size=P, out=out, workspace=ws, window=W)
+        if fp8:
+            ops.decode_fp8(t["q"], kps[r], vps[r], kss[r], vss[r], t["block_table"], lens, max_len, w.scale,
+                           window=W, partition_size=P, out=out, workspace=ws)
+        else:
+            ops.decode(t["q"], kps[r], vps[r], t["block_table"], lens, max_len, w.scale,
+                       partition_size=P, out=out, workspace=ws, window=W)
         if ev is not None:
             ev[1].record(stream)
 
@@ -239,15 +352,18 @@ def main() -> int:
     part = _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, w.num_q_heads,
                                          span, P)
     cfg = _describe(w)
+    if fp8:
+        cfg["workload"] = f"{w.name}-fp8"
+        cfg["kv_storage"] = "OCP E4M3 codes + float32 scale per (token, kv head) row"
     if W > 0:
-        cfg["workload"] = f"{w.name}-window{W}"
+        cfg["workload"] = f"{cfg['workload']}-window{W}"
         cfg["window"] = W
         cfg["attended_tokens_sum"] = int(attended.sum())
     cfg.update({"partition_size": part, "replicas": R, "tokens_per_step": w.batch,
                 "copy_pairs_per_step": int(pairs.shape[0]),
                 "step": ("copy-on-write + " if pairs.shape[0] else "") + "append 1 token/seq + decode"})
     if args.config == 5:
-        cfg["unique_kv_bytes"] = 2 * w.unique_blocks * w.block_size * w.num_kv_heads * w.head_dim * esize
+        cfg["unique_kv_bytes"] = 2 * w.unique_blocks * w.block_size * w.num_kv_heads * row_bytes
     result = {
         "metric": "paged-decode KV GB/s (% of HBM peak) and decode tokens/s at 1 MI355X",
         "value": round(value, 2),
@@ -259,7 +375,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": f"e4m3+{w.dtype}" if fp8 else w.dtype,
         "data": "synthetic (seeded N(0,1) contents, shuffled physical pool, NaN-filled padding)",
         "config": cfg,
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -273,8 +389,12 @@ def main() -> int:
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = (_cpu_baseline_beams(w, host_sample, args.cpu_budget, W) if host_sample
-                                  else _cpu_baseline(w, args.cpu_budget, W))
+        if fp8:
+            result["cpu_baseline"] = (_cpu_baseline_fp8_beams(w, host_sample, args.cpu_budget, W) if host_sample
+                                      else _cpu_baseline_fp8(w, args.cpu_budget, W))
+        else:
+            result["cpu_baseline"] = (_cpu_baseline_beams(w, host_sample, args.cpu_budget, W) if host_sample
+                                      else _cpu_baseline(w, args.cpu_budget, W))
     print(json.dumps(result), flush=True)
     return 0
 

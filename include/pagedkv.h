@@ -30,10 +30,12 @@
  *       context_lens       int32 [batch], number of valid tokens ([Valid-length essay] §4.1)
  *       slot_mapping       int32 [num_tokens], physical slot = block * block_size + offset
  *       pairs              int32 [num_pairs][2] = (src, dst) physical block ids
+ *       k_scale, v_scale   float32 [num_blocks][num_kv_heads][block_size] (8-bit pools only)
  *   - q, out, key, value, k_pool and v_pool must be 16-byte aligned
  *     ([KV Block course] §3.7 on aligned block starts).
- *   - Supported: dtype f32/f16/bf16; head_dim 64, 128, 256; block_size a power of two in
- *     [8, 512]; num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}.
+ *   - Supported: dtype f32/f16/bf16 (and 8-bit float pools, see PA_FP8_E4M3); head_dim
+ *     64, 128, 256; block_size a power of two in [8, 512]; num_q_heads / num_kv_heads in
+ *     {1, 2, 4, 8, 16}.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -55,7 +57,15 @@ typedef enum {
     PA_ERR_LAUNCH = 3            /* the HIP runtime refused a launch */
 } pa_status_t;
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
+/*
+ * Element types. PA_FP8_E4M3 is a pool element type only: 8-bit floats in the OCP E4M3
+ * format (sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite 448; S.1111.111
+ * is NaN) with one float32 scale per (block, kv head, offset) row, so a row is worth
+ * code * scale (the quantised blocks of [BlockManager essay] §3 and §6.3). Such pools are
+ * written, copied and read only by the *_fp8 entry points; q, out, key and value stay
+ * f16/bf16 (f32 too for key and value).
+ */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype_t;
 
 /* Device-side data error bits OR-ed into *err_flag. */
 #define PA_FLAG_BAD_BLOCK_ID   1  /* a table entry inside the valid range is outside [0, num_blocks) */
@@ -83,6 +93,7 @@ typedef struct {
  * padding token and is skipped, so padding KV never enters the cache ([Valid-length essay]
  * §2.3). A slot >= num_blocks * block_size is skipped and sets PA_FLAG_BAD_SLOT.
  * num_tokens == 0 launches nothing. Two tokens with the same slot race (caller error).
+ * An 8-bit pool returns PA_ERR_UNSUPPORTED (use pa_reshape_and_cache_fp8).
  */
 pa_status_t pa_reshape_and_cache(const pa_cache_desc_t* cache, const void* key, const void* value,
                                  void* k_pool, void* v_pool, const int32_t* slot_mapping,
@@ -96,7 +107,8 @@ pa_status_t pa_reshape_and_cache(const pa_cache_desc_t* cache, const void* key, 
  * writes into it ([BlockManager essay] §2, §4.2; [KV Block course] §3.4). Pairs run in
  * parallel: every dst must be distinct and no dst may be a src (a fresh block is always the
  * target of copy-on-write). A pair with an id outside [0, num_blocks) or src == dst is
- * skipped and sets PA_FLAG_BAD_COPY_PAIR. num_pairs == 0 launches nothing.
+ * skipped and sets PA_FLAG_BAD_COPY_PAIR. num_pairs == 0 launches nothing. An 8-bit pool
+ * returns PA_ERR_UNSUPPORTED (use pa_copy_blocks_fp8, which moves the scales too).
  */
 pa_status_t pa_copy_blocks(const pa_cache_desc_t* cache, void* k_pool, void* v_pool,
                            const int32_t* pairs, int32_t num_pairs, int32_t* err_flag,
@@ -140,7 +152,8 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, in
  * partition_size: 0 = default, else as pa_decode_partition_size. When a sequence spans
  * several partitions, each writes (max, sum, output) to `workspace` and a second kernel
  * combines them with a log-sum-exp weighting; workspace_bytes must be at least
- * pa_decode_workspace_bytes(...) (the workspace may be NULL when that is 0).
+ * pa_decode_workspace_bytes(...) (the workspace may be NULL when that is 0). An 8-bit pool
+ * returns PA_ERR_UNSUPPORTED (use pa_decode_fp8).
  */
 pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
@@ -180,6 +193,48 @@ pa_status_t pa_decode_sliding_window(const pa_cache_desc_t* cache, void* out, co
 size_t pa_decode_sliding_window_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch,
                                                 int32_t num_q_heads, int32_t max_context_len, int32_t window,
                                                 int32_t partition_size);
+
+/*
+ * pa_reshape_and_cache_fp8 - quantise new tokens' K and V into an 8-bit float pool.
+ *
+ * As pa_reshape_and_cache (same slots, padding and error rules), but each (token, kv head)
+ * row x of key/value (type src_dtype: PA_F32, PA_F16 or PA_BF16) is stored as codes with
+ * its own scale: a = max |x| over the row, s = a / 448, code = the E4M3 value nearest
+ * x / s clamped to [-448, 448], ties to the even mantissa; all arithmetic is float32 with
+ * correctly rounded division. A row of zeros stores s = 0 and codes 0. Rows must be finite.
+ * The cache dtype must be PA_FP8_E4M3; k_scale and v_scale must be 4-byte aligned.
+ */
+pa_status_t pa_reshape_and_cache_fp8(const pa_cache_desc_t* cache, int32_t src_dtype, const void* key,
+                                     const void* value, void* k_pool, void* v_pool, float* k_scale,
+                                     float* v_scale, const int32_t* slot_mapping, int32_t num_tokens,
+                                     int32_t* err_flag, pa_stream_t stream);
+
+/*
+ * pa_copy_blocks_fp8 - copy-on-write of 8-bit float blocks: as pa_copy_blocks, and every
+ * copied row keeps its scale (k_scale / v_scale rows move with the codes).
+ */
+pa_status_t pa_copy_blocks_fp8(const pa_cache_desc_t* cache, void* k_pool, void* v_pool, float* k_scale,
+                               float* v_scale, const int32_t* pairs, int32_t num_pairs, int32_t* err_flag,
+                               pa_stream_t stream);
+
+/*
+ * pa_decode_fp8 - decode over an 8-bit float cache.
+ *
+ * The result of pa_decode (window = 0) or pa_decode_sliding_window (window > 0) over the
+ * dequantised rows code * scale: K row t contributes scale * (q . codes_t) * k_scale_t to the
+ * score, V row t adds its softmax weight times v_scale_t times codes_t. Codes widen exactly;
+ * scores and accumulators are fp32. q_dtype (PA_F16 or PA_BF16) is the type of q and out.
+ * Launch shape, partitions, workspace (pa_decode_workspace_bytes, or
+ * pa_decode_sliding_window_workspace_bytes for a window) and error rules are those of the
+ * unquantised calls. The cache dtype must be PA_FP8_E4M3, num_q_heads / num_kv_heads at
+ * most 8, and block_size >= 16 when head_dim is 64 (else PA_ERR_UNSUPPORTED).
+ */
+pa_status_t pa_decode_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
+                          const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale, int32_t window,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                          pa_stream_t stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* pa_status_string(pa_status_t status);

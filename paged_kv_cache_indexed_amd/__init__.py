@@ -11,11 +11,14 @@ from ._lib import (  # noqa: F401
     CacheDesc,
     PagedKVError,
     pa_copy_blocks,
+    pa_copy_blocks_fp8,
     pa_decode,
+    pa_decode_fp8,
     pa_decode_partition_size,
     pa_decode_sliding_window,
     pa_decode_sliding_window_workspace_bytes,
     pa_decode_workspace_bytes,
     pa_reshape_and_cache,
+    pa_reshape_and_cache_fp8,
     pa_status_string,
 )

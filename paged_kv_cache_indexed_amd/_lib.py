@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_PKG, "libpagedkv.so")
 
 PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, 1, 2, 3
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_FLAG_BAD_BLOCK_ID = 1
 PA_FLAG_BAD_LENGTH = 2
 PA_FLAG_EMPTY_CONTEXT = 4
@@ -28,9 +28,12 @@ PA_FLAG_BAD_COPY_PAIR = 16
 
 EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_size",
             "pa_decode_workspace_bytes", "pa_decode", "pa_decode_sliding_window",
-            "pa_decode_sliding_window_workspace_bytes", "pa_status_string")
+            "pa_decode_sliding_window_workspace_bytes", "pa_reshape_and_cache_fp8",
+            "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_status_string")
 
-_DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+# 8-bit float pools are uint8 (or float8_e4m3fn) tensors of OCP E4M3 codes.
+_DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+               torch.uint8: PA_FP8_E4M3, torch.float8_e4m3fn: PA_FP8_E4M3}
 
 
 class pa_cache_desc_t(ctypes.Structure):
@@ -89,6 +92,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_sliding_window.restype = ctypes.c_int
     lib.pa_decode_sliding_window_workspace_bytes.argtypes = [D, I32, I32, I32, I32, I32]
     lib.pa_decode_sliding_window_workspace_bytes.restype = SZ
+    lib.pa_reshape_and_cache_fp8.argtypes = [D, I32, P, P, P, P, P, P, P, I32, P, P]
+    lib.pa_reshape_and_cache_fp8.restype = ctypes.c_int
+    lib.pa_copy_blocks_fp8.argtypes = [D, P, P, P, P, P, I32, P, P]
+    lib.pa_copy_blocks_fp8.restype = ctypes.c_int
+    lib.pa_decode_fp8.argtypes = [D, I32, P, P, P, P, P, P, P, I32, P, I32, I32, I32, F, I32, I32, P, SZ, P, P]
+    lib.pa_decode_fp8.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -181,3 +190,38 @@ def pa_decode_sliding_window(cache: CacheDesc, out, q, k_pool, v_pool, block_tab
         int(block_table.shape[1]), _ptr(context_lens), batch, num_q_heads, int(max_context_len),
         float(scale), int(window), int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag),
         _stream(stream)))
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    return _DTYPE_CODE[t.dtype]
+
+
+def pa_reshape_and_cache_fp8(cache: CacheDesc, key, value, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+                             err_flag=None, stream=None) -> None:
+    n = int(slot_mapping.numel())
+    desc = cache.c()
+    _check(load().pa_reshape_and_cache_fp8(ctypes.byref(desc), dtype_code(key), _ptr(key), _ptr(value),
+                                           _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                           _ptr(slot_mapping), n, _ptr(err_flag), _stream(stream)))
+
+
+def pa_copy_blocks_fp8(cache: CacheDesc, k_pool, v_pool, k_scale, v_scale, pairs, err_flag=None,
+                       stream=None) -> None:
+    n = int(pairs.shape[0]) if pairs is not None else 0
+    desc = cache.c()
+    _check(load().pa_copy_blocks_fp8(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                     _ptr(v_scale), _ptr(pairs) if n else None, n, _ptr(err_flag),
+                                     _stream(stream)))
+
+
+def pa_decode_fp8(cache: CacheDesc, out, q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                  max_context_len: int, scale: float, window: int = 0, partition_size: int = 0,
+                  workspace=None, err_flag=None, stream=None) -> None:
+    batch, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    desc = cache.c()
+    _check(load().pa_decode_fp8(
+        ctypes.byref(desc), dtype_code(q), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+        _ptr(v_scale), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), batch, num_q_heads,
+        int(max_context_len), float(scale), int(window), int(partition_size), _ptr(workspace), ws_bytes,
+        _ptr(err_flag), _stream(stream)))

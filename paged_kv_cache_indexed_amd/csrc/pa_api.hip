@@ -22,6 +22,7 @@ int dtype_bytes(int dtype) {
         case PA_F32: return 4;
         case PA_F16:
         case PA_BF16: return 2;
+        case PA_FP8_E4M3: return 1;
         default: return 0;
     }
 }
@@ -41,6 +42,9 @@ pa_status_t check_cache(const pa_cache_desc_t* c) {
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool is_fp8(const pa_cache_desc_t* c) { return c->dtype == PA_FP8_E4M3; }
 
 // Tokens a sequence's partitions cover: everything without a window; with one, the window
 // plus at most block_size - 1 tokens before it in the block where it starts.
@@ -69,6 +73,7 @@ pa_status_t pa_reshape_and_cache(const pa_cache_desc_t* cache, const void* key, 
                                  int32_t num_tokens, int32_t* err_flag, pa_stream_t stream) {
     pa_status_t st = check_cache(cache);
     if (st != PA_OK) return st;
+    if (is_fp8(cache)) return PA_ERR_UNSUPPORTED;
     if (num_tokens < 0) return PA_ERR_INVALID_ARGUMENT;
     if (num_tokens == 0) return PA_OK;
     if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PA_ERR_INVALID_ARGUMENT;
@@ -83,13 +88,52 @@ pa_status_t pa_copy_blocks(const pa_cache_desc_t* cache, void* k_pool, void* v_p
                            int32_t num_pairs, int32_t* err_flag, pa_stream_t stream) {
     pa_status_t st = check_cache(cache);
     if (st != PA_OK) return st;
+    if (is_fp8(cache)) return PA_ERR_UNSUPPORTED;
     if (num_pairs < 0) return PA_ERR_INVALID_ARGUMENT;
     if (num_pairs == 0) return PA_OK;
     if (!k_pool || !v_pool || !pairs) return PA_ERR_INVALID_ARGUMENT;
     if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARGUMENT;
     CacheArgs a{k_pool, v_pool, err_flag, cache->num_blocks, log2_exact(cache->block_size),
                 cache->num_kv_heads, cache->head_dim * dtype_bytes(cache->dtype) / 16};
-    return from_hip(launch_copy_blocks(a, pairs, num_pairs, (hipStream_t)stream));
+    return from_hip(launch_copy_blocks(a, pairs, num_pairs, nullptr, nullptr, (hipStream_t)stream));
+}
+
+pa_status_t pa_reshape_and_cache_fp8(const pa_cache_desc_t* cache, int32_t src_dtype, const void* key,
+                                     const void* value, void* k_pool, void* v_pool, float* k_scale,
+                                     float* v_scale, const int32_t* slot_mapping, int32_t num_tokens,
+                                     int32_t* err_flag, pa_stream_t stream) {
+    pa_status_t st = check_cache(cache);
+    if (st != PA_OK) return st;
+    if (!is_fp8(cache)) return PA_ERR_INVALID_ARGUMENT;
+    if (src_dtype != PA_F32 && src_dtype != PA_F16 && src_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (num_tokens < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !k_pool || !v_pool || !k_scale || !v_scale || !slot_mapping)
+        return PA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned4(k_scale) ||
+        !aligned4(v_scale))
+        return PA_ERR_INVALID_ARGUMENT;
+    CacheArgs a{k_pool, v_pool, err_flag, cache->num_blocks, log2_exact(cache->block_size),
+                cache->num_kv_heads, cache->head_dim / 16};
+    return from_hip(launch_reshape_and_cache_fp8(a, src_dtype, cache->head_dim, key, value, k_scale, v_scale,
+                                                 slot_mapping, num_tokens, (hipStream_t)stream));
+}
+
+pa_status_t pa_copy_blocks_fp8(const pa_cache_desc_t* cache, void* k_pool, void* v_pool, float* k_scale,
+                               float* v_scale, const int32_t* pairs, int32_t num_pairs, int32_t* err_flag,
+                               pa_stream_t stream) {
+    pa_status_t st = check_cache(cache);
+    if (st != PA_OK) return st;
+    if (!is_fp8(cache)) return PA_ERR_INVALID_ARGUMENT;
+    if (num_pairs < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_pool || !v_pool || !k_scale || !v_scale || !pairs) return PA_ERR_INVALID_ARGUMENT;
+    // scale rows are copied as 16-byte vectors: block_size >= 8 makes each head's run 32+ bytes
+    if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_scale) || !aligned16(v_scale))
+        return PA_ERR_INVALID_ARGUMENT;
+    CacheArgs a{k_pool, v_pool, err_flag, cache->num_blocks, log2_exact(cache->block_size),
+                cache->num_kv_heads, cache->head_dim / 16};
+    return from_hip(launch_copy_blocks(a, pairs, num_pairs, k_scale, v_scale, (hipStream_t)stream));
 }
 
 int32_t pa_decode_partition_size(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_heads,
@@ -154,8 +198,9 @@ size_t pa_decode_sliding_window_workspace_bytes(const pa_cache_desc_t* cache, in
 
 namespace {
 
-pa_status_t decode_impl(const pa_cache_desc_t* cache, void* out, const void* q, const void* k_pool,
-                        const void* v_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
+                        const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, int32_t max_blocks_per_seq,
                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                         int32_t max_context_len, float scale, int32_t partition_size, int32_t window,
                         void* workspace, size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream) {
@@ -165,6 +210,15 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, void* out, const void* q, 
     if (batch < 0 || batch > 65535) return PA_ERR_INVALID_ARGUMENT;
     if (batch == 0) return PA_OK;
     if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PA_ERR_INVALID_ARGUMENT;
+    // a VALU wave load covers 1 KiB of consecutive token rows, which must lie in one block
+    if ((int64_t)cache->head_dim * dtype_bytes(cache->dtype) * cache->block_size < 1024) return PA_ERR_UNSUPPORTED;
+    if (is_fp8(cache)) {
+        if (q_dtype != PA_F16 && q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+        if (num_q_heads / cache->num_kv_heads > 8) return PA_ERR_UNSUPPORTED;
+        if (!k_scale || !v_scale || !aligned4(k_scale) || !aligned4(v_scale)) return PA_ERR_INVALID_ARGUMENT;
+    } else if (q_dtype != cache->dtype) {
+        return PA_ERR_INVALID_ARGUMENT;
+    }
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
         return PA_ERR_INVALID_ARGUMENT;
     if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
@@ -188,6 +242,8 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, void* out, const void* q, 
     a.q = q;
     a.k_pool = k_pool;
     a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     a.block_table = block_table;
     a.context_lens = context_lens;
     a.ws_o = static_cast<float*>(workspace);
@@ -206,8 +262,9 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, void* out, const void* q, 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = decode_mfma_supported(cache->dtype, cache->head_dim, group, cache->block_size)
                        ? launch_decode_mfma(a, cache->dtype, cache->head_dim, group, batch, cache->num_kv_heads, s)
-                       : launch_decode_valu(a, cache->dtype, cache->head_dim, group, batch, cache->num_kv_heads, s);
-    if (e == hipSuccess && parts > 1) e = launch_reduce(a, cache->dtype, cache->head_dim, batch, s);
+                       : launch_decode_valu(a, cache->dtype, q_dtype, cache->head_dim, group, batch,
+                                            cache->num_kv_heads, s);
+    if (e == hipSuccess && parts > 1) e = launch_reduce(a, q_dtype, cache->head_dim, batch, s);
     return from_hip(e);
 }
 
@@ -220,9 +277,10 @@ pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, co
                       const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                       int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
                       size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream) {
-    return decode_impl(cache, out, q, k_pool, v_pool, block_table, max_blocks_per_seq, context_lens, batch,
-                       num_q_heads, max_context_len, scale, partition_size, 0, workspace, workspace_bytes,
-                       err_flag, stream);
+    if (cache && is_fp8(cache)) return PA_ERR_UNSUPPORTED;
+    return decode_impl(cache, cache ? cache->dtype : 0, out, q, k_pool, v_pool, nullptr, nullptr, block_table,
+                       max_blocks_per_seq, context_lens, batch, num_q_heads, max_context_len, scale, partition_size,
+                       0, workspace, workspace_bytes, err_flag, stream);
 }
 
 pa_status_t pa_decode_sliding_window(const pa_cache_desc_t* cache, void* out, const void* q,
@@ -232,9 +290,22 @@ pa_status_t pa_decode_sliding_window(const pa_cache_desc_t* cache, void* out, co
                                      int32_t window, int32_t partition_size, void* workspace,
                                      size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream) {
     if (window <= 0) return PA_ERR_INVALID_ARGUMENT;
-    return decode_impl(cache, out, q, k_pool, v_pool, block_table, max_blocks_per_seq, context_lens, batch,
-                       num_q_heads, max_context_len, scale, partition_size, window, workspace, workspace_bytes,
-                       err_flag, stream);
+    if (cache && is_fp8(cache)) return PA_ERR_UNSUPPORTED;
+    return decode_impl(cache, cache ? cache->dtype : 0, out, q, k_pool, v_pool, nullptr, nullptr, block_table,
+                       max_blocks_per_seq, context_lens, batch, num_q_heads, max_context_len, scale, partition_size,
+                       window, workspace, workspace_bytes, err_flag, stream);
+}
+
+pa_status_t pa_decode_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
+                          const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale, int32_t window,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                          pa_stream_t stream) {
+    if (!cache || !is_fp8(cache)) return PA_ERR_INVALID_ARGUMENT;
+    return decode_impl(cache, q_dtype, out, q, k_pool, v_pool, k_scale, v_scale, block_table, max_blocks_per_seq,
+                       context_lens, batch, num_q_heads, max_context_len, scale, partition_size, window, workspace,
+                       workspace_bytes, err_flag, stream);
 }
 
 }  // extern "C"

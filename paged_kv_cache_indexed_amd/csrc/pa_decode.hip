@@ -1,284 +1,10 @@
-// Paged-KV decode attention for gfx950: one workgroup per (context partition, kv head,
-// sequence), a log-sum-exp reduce kernel across partitions.
-//
-// Work decomposition (VALU path, used for every group size):
-//   * A workgroup is 4 wave64s. It owns the tokens [p*P, min(L, (p+1)*P)) of one kv head of
-//     one sequence and the G = Hq/Hkv query heads that read that kv head.
-//   * The partition's slice of the block table is staged in LDS once and checked, so the
-//     per-load address translation is an LDS broadcast read plus scalar arithmetic
-//     ([BlockManager essay] §2 on caching the mapping table on chip).
-//   * A K or V row of one token is head_dim * bytes long and is covered by LPR lanes with
-//     one 16-byte load each; a wave load covers RPL = 64 / LPR consecutive tokens of one
-//     block, 1 KiB of contiguous memory. Token groups of RPL rows are dealt round-robin to
-//     the 4 waves, so the waves of a workgroup stream adjacent KiB of the same block.
-//   * Each group of LPR lanes runs its own online softmax (running max and sum in fp32,
-//     base-2 exponent with the scale folded into q . k) over the tokens it loads, so the
-//     inner loop needs no cross-row traffic; rows are merged with lane shuffles and waves
-//     through LDS at the end.
-//   * Tokens at or past the valid length are never loaded ([Valid-length essay] §4.1-4.2):
-//     K/V are read with buffer loads whose resource spans one (block, kv head) slab, and a
-//     masked lane's offset is out of range, so the hardware returns zeros without a memory
-//     access; the lane's score is -inf and its weight exp2(-inf) = 0.
-//   * Two register buffers of UNROLL groups are kept loading: while one is consumed the
-//     other's loads are in flight, so each lane has 2 * UNROLL K+V loads outstanding.
-#include "pa_decode_common.h"
+// Paged-KV decode entry points for 16/32-bit pools (VALU kernels from pa_decode_valu.h) and
+// the log-sum-exp reduce kernel that combines context partitions.
+#include "pa_decode_valu.h"
 
 namespace pagedkv {
 
 namespace {
-
-constexpr int kWaves = kDecodeWaves;
-constexpr int kThreads = kDecodeThreads;
-
-template <typename T, int D>
-struct RowShape {
-    static constexpr int E = VecInfo<T>::kElems;  // elements per 16-byte vector
-    static constexpr int LPR = D / E;             // lanes per token row
-    static constexpr int RPL = 64 / LPR;          // token rows per wave load
-    static_assert(LPR >= 1 && LPR <= 64 && RPL * LPR == 64, "row shape");
-};
-
-// Streams this lane's share of a partition of kv head `kvh` and leaves the wave's merged
-// online-softmax state of the G query heads in every lane (m, l, and the E accumulators of
-// the lane's column). Row groups of RPL tokens are taken in the order
-// slot, slot + STRIDE, slot + 2 STRIDE, ...: STRIDE waves cooperate on one head, or one
-// wave (STRIDE = 1) owns it. All lanes must be active.
-template <typename T, int D, int G, int UNROLL, int STRIDE>
-__device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int* s_ids, const Partition& part,
-                                                 int kvh, int slot, const u32x4* qv, float* m, float* l,
-                                                 float (*acc)[RowShape<T, D>::E]) {
-    constexpr int E = RowShape<T, D>::E;
-    constexpr int LPR = RowShape<T, D>::LPR;
-    constexpr int RPL = RowShape<T, D>::RPL;
-    const int lane = threadIdx.x & 63;
-    const int row = lane / LPR;
-    const int col = lane % LPR;
-    const int lbs = a.log2_block_size;
-    const int bs = 1 << lbs;
-    const int ntok = part.ntok;
-    const int rel_lo = part.rel_lo;
-    const int g0 = rel_lo / RPL;  // first row group holding an attended token
-
-    const size_t head_bytes = (size_t)bs * D * T::kBytes;
-    const size_t block_bytes = head_bytes * a.num_kv_heads;
-    const char* kpool = static_cast<const char*>(a.k_pool);
-    const char* vpool = static_cast<const char*>(a.v_pool);
-    constexpr int kTokPerIter = UNROLL * STRIDE * RPL;
-    const int niters = (ntok - g0 * RPL + kTokPerIter - 1) / kTokPerIter;
-
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m[g] = -INFINITY;
-        l[g] = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
-    }
-
-    // Branch-free loads: every lane issues its loads; a lane whose token is at or past the
-    // partition end gets an out-of-range offset and reads zeros without a memory access.
-    // The buffer resource spans only this (block, kv head) slab.
-    const uint32_t slab_bytes = (uint32_t)head_bytes;
-    const uint32_t lane_bytes = (uint32_t)(((size_t)row * D + col * E) * T::kBytes);
-    auto issue = [&](int it, u32x4* kk, u32x4* vv) {
-        int idv[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int rel = (g0 + (it * UNROLL + u) * STRIDE + slot) * RPL;  // wave-uniform
-            idv[u] = s_ids[(rel < ntok ? rel : 0) >> lbs];  // partitions start on a block
-        }
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int rel = (g0 + (it * UNROLL + u) * STRIDE + slot) * RPL;
-            const int id = __builtin_amdgcn_readfirstlane(idv[u]);
-            const size_t slab = (size_t)id * block_bytes + (size_t)kvh * head_bytes;
-            const uint32_t off = (rel + row < ntok && rel + row >= rel_lo)
-                                     ? (uint32_t)((rel & (bs - 1)) * D * T::kBytes) + lane_bytes
-                                     : kOutOfRange;
-            kk[u] = buffer_load16(make_rsrc(kpool + slab, slab_bytes), off);
-            vv[u] = buffer_load16(make_rsrc(vpool + slab, slab_bytes), off);
-        }
-    };
-
-    auto compute = [&](int it, const u32x4* kk, const u32x4* vv) {
-        float s[G][UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int rel = (g0 + (it * UNROLL + u) * STRIDE + slot) * RPL + row;
-            const bool valid = rel < ntok && rel >= rel_lo;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float d = group_sum<LPR>(dot16(T{}, qv[g], kk[u]));
-                s[g][u] = valid ? d * a.scale_log2 : -INFINITY;
-            }
-        }
-        float vf[UNROLL][E];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) unpack(T{}, vv[u], vf[u]);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float cm = s[g][0];
-#pragma unroll
-            for (int u = 1; u < UNROLL; ++u) cm = fmaxf(cm, s[g][u]);
-            const float mn = fmaxf(m[g], cm);
-            const float ms = (mn == -INFINITY) ? 0.f : mn;
-            const float alpha = fast_exp2(m[g] - ms);
-            m[g] = mn;
-            l[g] *= alpha;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const float pr = fast_exp2(s[g][u] - ms);
-                l[g] += pr;
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pr, vf[u][e], acc[g][e]);
-            }
-        }
-    };
-
-    // Two register buffers, each refilled right after it is consumed, so two groups of
-    // loads are in flight at all times and every wait before a compute covers only the older
-    // group. Refills past the last group get out-of-range offsets: they return zeros and move
-    // no data. The scheduling barriers keep the compiler from sinking a refill below the next
-    // compute, which would drain the load queue.
-    u32x4 ka[UNROLL], va[UNROLL], kb[UNROLL], vb[UNROLL];
-    issue(0, ka, va);
-    issue(1, kb, vb);
-    int it = 0;
-    for (; it + 1 < niters; it += 2) {  // one latch: the wait state is the same on every entry
-        __builtin_amdgcn_sched_barrier(0);
-        compute(it, ka, va);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(it + 2, ka, va);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(it + 1, kb, vb);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(it + 3, kb, vb);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (it < niters) compute(it, ka, va);
-
-    // ---- merge the RPL row streams of this wave ----
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mo = shfl_xor(m[g], off);
-            const float lo = shfl_xor(l[g], off);
-            const float mn = fmaxf(m[g], mo);
-            const float ms = (mn == -INFINITY) ? 0.f : mn;
-            const float fa = fast_exp2(m[g] - ms);
-            const float fb = fast_exp2(mo - ms);
-            l[g] = l[g] * fa + lo * fb;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[g][e] = acc[g][e] * fa + shfl_xor(acc[g][e], off) * fb;
-            m[g] = mn;
-        }
-    }
-}
-
-template <typename T, int D, int G>
-__device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int h0, u32x4* qv) {
-    constexpr int E = RowShape<T, D>::E;
-    const int col = (threadIdx.x & 63) % RowShape<T, D>::LPR;
-    const char* qbase = static_cast<const char*>(a.q) + (((size_t)b * a.num_q_heads + h0) * D + col * E) * T::kBytes;
-#pragma unroll
-    for (int g = 0; g < G; ++g) qv[g] = load16(qbase + (size_t)g * D * T::kBytes);
-}
-
-// Split mode: the 4 waves of a workgroup share one kv head's partition (groups of RPL rows
-// dealt round-robin), and their states merge through LDS.
-template <typename T, int D, int G, int UNROLL>
-__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
-    constexpr int E = RowShape<T, D>::E;
-    constexpr int LPR = RowShape<T, D>::LPR;
-    __shared__ int s_ids[kMaxIdsPerPartition];
-    __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[kWaves][G];
-    __shared__ float s_acc[kWaves][G][D];
-
-    const int p = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int row = lane / LPR;
-    const int col = lane % LPR;
-
-    // q before the prologue, so its load overlaps the length and table round trip
-    u32x4 qv[G];
-    load_q<T, D, G>(a, b, kvh * G, qv);
-    Partition part;
-    if (!partition_prologue<T, D, G, kThreads>(a, p, kvh, b, s_ids, part)) return;
-
-    float m[G], l[G], acc[G][E];
-    stream_partition<T, D, G, UNROLL, kWaves>(a, s_ids, part, kvh, wave, qv, m, l, acc);
-    if (row == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < E; ++e) s_acc[wave][g][col * E + e] = acc[g][e];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            s_m[wave][g] = m[g];
-            s_l[wave][g] = l[g];
-        }
-    }
-    __syncthreads();
-    partition_epilogue<T, D, G>(a, p, kvh, b, part, s_m, s_l, s_acc);
-}
-
-// Head mode, for short partitions: a workgroup owns one (partition, sequence) and 4
-// consecutive kv heads that share the staged table slice; wave w streams kv head
-// 4 * blockIdx.y + w alone and writes its result without any cross-wave merge.
-template <typename T, int D, int G, int UNROLL>
-__global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs a) {
-    constexpr int E = RowShape<T, D>::E;
-    constexpr int LPR = RowShape<T, D>::LPR;
-    __shared__ int s_ids[kMaxIdsPerPartition];
-
-    const int p = blockIdx.x;
-    const int b = blockIdx.z;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int row = lane / LPR;
-    const int col = lane % LPR;
-    const int kvh0 = blockIdx.y * kWaves;
-    const int nkv = min(kWaves, a.num_kv_heads - kvh0);
-    const bool active = wave < nkv;
-    const int kvh = active ? kvh0 + wave : kvh0;
-    const int h0 = kvh * G;
-
-    u32x4 qv[G];
-    load_q<T, D, G>(a, b, h0, qv);
-    Partition part;
-    if (!partition_prologue_heads<T, D, kThreads>(a, p, kvh0 * G, nkv * G, b, s_ids, part)) return;
-    if (!active) return;  // no barrier follows
-
-    float m[G], l[G], acc[G][E];
-    stream_partition<T, D, G, UNROLL, 1>(a, s_ids, part, kvh, 0, qv, m, l, acc);
-    if (row == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const size_t hrow = (size_t)b * a.num_q_heads + h0 + g;
-            const float inv = 1.f / l[g];
-            if (part.nparts == 1) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) store_elem(T{}, a.out, hrow * D + col * E + e, acc[g][e] * inv);
-            } else {
-                const size_t rec = hrow * a.max_partitions + p;
-#pragma unroll
-                for (int e = 0; e < E; ++e) a.ws_o[rec * D + col * E + e] = acc[g][e] * inv;
-                if (col == 0) {
-                    a.ws_ml[rec * 2] = m[g];
-                    a.ws_ml[rec * 2 + 1] = l[g];
-                }
-            }
-        }
-    }
-}
 
 // Log-sum-exp combine of the per-partition records of one (sequence, query head):
 //   out = sum_p w_p o_p / sum_p w_p,  w_p = l_p * 2^(m_p - max_p m_p),
@@ -304,63 +30,6 @@ __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
         num = fmaf(w, a.ws_o[(rec0 + p) * D + e], num);
     }
     store_elem(T{}, a.out, ((size_t)b * a.num_q_heads + h) * D + e, num / den);
-}
-
-// Partitions of at most this many tokens run in head mode.
-#ifndef PA_HEAD_MODE_MAX_P
-#define PA_HEAD_MODE_MAX_P 128
-#endif
-
-template <typename T, int D, int G, int UNROLL>
-hipError_t launch_decode_tgdu(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
-    if (a.partition_size <= PA_HEAD_MODE_MAX_P) {
-        dim3 grid(a.max_partitions, (num_kv_heads + kWaves - 1) / kWaves, batch);
-        hipLaunchKernelGGL((decode_valu_heads_kernel<T, D, G, UNROLL>), grid, dim3(kThreads), 0, stream, a);
-    } else {
-        dim3 grid(a.max_partitions, num_kv_heads, batch);
-        hipLaunchKernelGGL((decode_valu_kernel<T, D, G, UNROLL>), grid, dim3(kThreads), 0, stream, a);
-    }
-    return hipGetLastError();
-}
-
-// Groups per iteration per wave: 4 for long partitions (and for head mode, where one wave
-// streams a whole partition); 2 for short split-mode partitions (<= 384 tokens), where a
-// 4-deep iteration would leave most lanes idle and the smaller register footprint lets 8
-// waves share a SIMD. Grouped-query heads multiply the registers per group.
-template <typename T, int D, int G>
-hipError_t launch_decode_tgd(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
-    if constexpr (G <= 2) {
-        if (a.partition_size > PA_HEAD_MODE_MAX_P && a.partition_size <= 384)
-            return launch_decode_tgdu<T, D, G, 2>(a, batch, num_kv_heads, stream);
-        return launch_decode_tgdu<T, D, G, 4>(a, batch, num_kv_heads, stream);
-    } else {
-        return launch_decode_tgdu<T, D, G, (G <= 4 ? 2 : 1)>(a, batch, num_kv_heads, stream);
-    }
-}
-
-template <typename T, int D>
-hipError_t launch_decode_td(const DecodeArgs& a, int group, int batch, int num_kv_heads, hipStream_t s) {
-    switch (group) {
-        case 1: return launch_decode_tgd<T, D, 1>(a, batch, num_kv_heads, s);
-        case 2: return launch_decode_tgd<T, D, 2>(a, batch, num_kv_heads, s);
-        case 4: return launch_decode_tgd<T, D, 4>(a, batch, num_kv_heads, s);
-        case 8: return launch_decode_tgd<T, D, 8>(a, batch, num_kv_heads, s);
-        case 16:
-            if constexpr (D <= 128) return launch_decode_tgd<T, D, 16>(a, batch, num_kv_heads, s);
-            return hipErrorInvalidValue;
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <typename T>
-hipError_t launch_decode_t(const DecodeArgs& a, int head_dim, int group, int batch, int num_kv_heads,
-                           hipStream_t s) {
-    switch (head_dim) {
-        case 64: return launch_decode_td<T, 64>(a, group, batch, num_kv_heads, s);
-        case 128: return launch_decode_td<T, 128>(a, group, batch, num_kv_heads, s);
-        case 256: return launch_decode_td<T, 256>(a, group, batch, num_kv_heads, s);
-        default: return hipErrorInvalidValue;
-    }
 }
 
 template <typename T, int D>
@@ -390,12 +59,14 @@ hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, int batch
     }
 }
 
-hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
+hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream) {
+    if (kv_dtype == PA_FP8_E4M3) return launch_decode_valu_fp8(a, dtype, head_dim, group, batch, num_kv_heads, stream);
+    if (kv_dtype != dtype) return hipErrorInvalidValue;
     switch (dtype) {
-        case PA_F32: return launch_decode_t<F32>(a, head_dim, group, batch, num_kv_heads, stream);
-        case PA_F16: return launch_decode_t<F16>(a, head_dim, group, batch, num_kv_heads, stream);
-        case PA_BF16: return launch_decode_t<BF16>(a, head_dim, group, batch, num_kv_heads, stream);
+        case PA_F32: return valu::launch_decode_t<F32, F32>(a, head_dim, group, batch, num_kv_heads, stream);
+        case PA_F16: return valu::launch_decode_t<F16, F16>(a, head_dim, group, batch, num_kv_heads, stream);
+        case PA_BF16: return valu::launch_decode_t<BF16, BF16>(a, head_dim, group, batch, num_kv_heads, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -12,6 +12,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Note: every reinterpretation below bit-casts the whole 16-byte vector and then takes
 // constant swizzles. Bit-casting single elements of a u32x4 (bit_cast<f16x2>(v[i]))
@@ -27,6 +28,12 @@ struct F16 {
 };
 struct BF16 {
     static constexpr int kBytes = 2;
+};
+
+// 8-bit floats in the OCP E4M3 format (bias 7, largest finite 448, S.1111.111 = NaN), one
+// float32 scale per (token, kv head) row kept beside the block: a row is worth code * scale.
+struct FP8 {
+    static constexpr int kBytes = 1;
 };
 
 template <typename T>
@@ -49,6 +56,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 template <int kPolicy = PA_KV_LOAD_POLICY>
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, kPolicy));
+}
+
+template <int kPolicy = PA_KV_LOAD_POLICY>
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)offset, 0, kPolicy));
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
@@ -76,6 +88,20 @@ __device__ __forceinline__ void unpack(BF16, u32x4 v, float* f) {
     }
 }
 
+// 16 E4M3 codes -> fp32, exact. gfx950's scaled conversions read the OCP formats; with a
+// scale of 1 they only widen.
+__device__ __forceinline__ void unpack(FP8, u32x4 v, float* f) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[w], 1.f, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[w], 1.f, true);
+        f[4 * w] = lo.x;
+        f[4 * w + 1] = lo.y;
+        f[4 * w + 2] = hi.x;
+        f[4 * w + 3] = hi.y;
+    }
+}
+
 // ---- partial dot product of one 16-byte vector of K with the matching slice of q ---------
 // q is kept in its storage form; products are exact in fp32 and accumulate in fp32.
 __device__ __forceinline__ float dot16(F32, u32x4 q, u32x4 k) {
@@ -100,6 +126,53 @@ __device__ __forceinline__ float dot16(BF16, u32x4 q, u32x4 k) {
     s = __builtin_amdgcn_fdot2_f32_bf16(a.s23, b.s23, s, false);
     s = __builtin_amdgcn_fdot2_f32_bf16(a.s45, b.s45, s, false);
     return __builtin_amdgcn_fdot2_f32_bf16(a.s67, b.s67, s, false);
+}
+
+// 16 E4M3 codes of K against the matching 16 elements of q (two 16-byte vectors of fp16 or
+// bf16). The codes widen exactly to q's type, products are exact in fp32 and accumulate in
+// fp32.
+__device__ __forceinline__ float dot16_fp8(F16, const u32x4* q, u32x4 k) {
+    const f16x8 a = __builtin_bit_cast(f16x8, q[0]);
+    const f16x8 b = __builtin_bit_cast(f16x8, q[1]);
+    float s = __builtin_amdgcn_fdot2(a.s01, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[0], 1.f, false), 0.f, false);
+    s = __builtin_amdgcn_fdot2(a.s23, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[0], 1.f, true), s, false);
+    s = __builtin_amdgcn_fdot2(a.s45, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[1], 1.f, false), s, false);
+    s = __builtin_amdgcn_fdot2(a.s67, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[1], 1.f, true), s, false);
+    s = __builtin_amdgcn_fdot2(b.s01, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[2], 1.f, false), s, false);
+    s = __builtin_amdgcn_fdot2(b.s23, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[2], 1.f, true), s, false);
+    s = __builtin_amdgcn_fdot2(b.s45, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[3], 1.f, false), s, false);
+    return __builtin_amdgcn_fdot2(b.s67, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k[3], 1.f, true), s, false);
+}
+__device__ __forceinline__ float dot16_fp8(BF16, const u32x4* q, u32x4 k) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, q[0]);
+    const bf16x8 b = __builtin_bit_cast(bf16x8, q[1]);
+    float s = __builtin_amdgcn_fdot2_f32_bf16(a.s01, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k[0], 1.f, false), 0.f,
+                                              false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(a.s23, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k[0], 1.f, true), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(a.s45, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k[1], 1.f, false), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(a.s67, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k[1], 1.f, true), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(b.s01, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k[2], 1.f, false), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(b.s23, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k[2], 1.f, true), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(b.s45, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k[3], 1.f, false), s, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(b.s67, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k[3], 1.f, true), s,
+                                           false);
+}
+
+// Nearest E4M3 code of x, ties to the even mantissa; |x| <= 448 and finite. Built from the
+// format's definition: below 2^-6 the code counts multiples of 2^-9; above, the value is
+// scaled by a power of two into [8, 16), rounded to an integer, and a carry to 16 moves to
+// the next exponent. Every scaling is exact, so the only rounding is the one rint makes.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = fabsf(x);
+    if (a < 0x1p-6f) return sign | (uint32_t)__builtin_rintf(a * 512.f);
+    int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+    int m = (int)__builtin_rintf(__builtin_ldexpf(a, 3 - e)) - 8;
+    if (m == 8) {
+        m = 0;
+        ++e;
+    }
+    return sign | (uint32_t)(((e + 7) << 3) | m);
 }
 
 // ---- fp32 -> storage (round to nearest even) ---------------------------------------------
@@ -140,6 +213,17 @@ __device__ __forceinline__ float group_sum(float x) {
     if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
     if constexpr (N >= 32) x += shfl_xor(x, 16);
     if constexpr (N >= 64) x += shfl_xor(x, 32);
+    return x;
+}
+
+// Maximum over aligned groups of N lanes (N <= 16); every lane of a group receives it.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group");
+    if constexpr (N >= 2) x = fmaxf(x, dpp<kDppQuadXor1>(x));
+    if constexpr (N >= 4) x = fmaxf(x, dpp<kDppQuadXor2>(x));
+    if constexpr (N >= 8) x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+    if constexpr (N >= 16) x = fmaxf(x, dpp<kDppRowMirror>(x));
     return x;
 }
 

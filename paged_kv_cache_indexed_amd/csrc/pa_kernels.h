@@ -18,6 +18,8 @@ struct DecodeArgs {
     const void* q;
     const void* k_pool;
     const void* v_pool;
+    const float* k_scale;  // 8-bit pools only: [num_blocks][num_kv_heads][block_size]
+    const float* v_scale;
     const int32_t* block_table;
     const int32_t* context_lens;
     float* ws_o;   // [batch][num_q_heads][max_partitions][head_dim]
@@ -45,9 +47,13 @@ struct CacheArgs {
     int32_t row_vecs;  // 16-byte vectors per [head_dim] row
 };
 
-// VALU decode (every dtype and group size).
-hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
+// VALU decode (every dtype and group size). kv_dtype is the pool's element type, dtype the
+// type of q and out (equal unless the pool holds 8-bit floats).
+hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream);
+// The same over 8-bit float pools (dtype = type of q and out: fp16 or bf16; group <= 8).
+hipError_t launch_decode_valu_fp8(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
+                                  int num_kv_heads, hipStream_t stream);
 // Matrix-core decode for grouped-query heads (fp16/bf16, group 4/8/16, block_size >= 16).
 bool decode_mfma_supported(int dtype, int head_dim, int group, int block_size);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
@@ -58,7 +64,13 @@ hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, int batch
 hipError_t launch_reshape_and_cache(const CacheArgs& a, const void* key, const void* value,
                                     const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
 
-hipError_t launch_copy_blocks(const CacheArgs& a, const int32_t* pairs, int32_t num_pairs,
-                              hipStream_t stream);
+// Copy-on-write. With 8-bit pools, k_scale/v_scale (non-null) are copied along with the codes.
+hipError_t launch_copy_blocks(const CacheArgs& a, const int32_t* pairs, int32_t num_pairs, float* k_scale,
+                              float* v_scale, hipStream_t stream);
+
+// Quantising append into 8-bit pools: src_dtype is the type of key/value rows.
+hipError_t launch_reshape_and_cache_fp8(const CacheArgs& a, int src_dtype, int head_dim, const void* key,
+                                        const void* value, float* k_scale, float* v_scale,
+                                        const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
 
 }  // namespace pagedkv

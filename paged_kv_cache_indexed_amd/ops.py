@@ -7,9 +7,9 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (CacheDesc, pa_copy_blocks, pa_decode, pa_decode_sliding_window,
-                   pa_decode_sliding_window_workspace_bytes, pa_decode_workspace_bytes,
-                   pa_reshape_and_cache)
+from ._lib import (CacheDesc, pa_copy_blocks, pa_copy_blocks_fp8, pa_decode, pa_decode_fp8,
+                   pa_decode_sliding_window, pa_decode_sliding_window_workspace_bytes,
+                   pa_decode_workspace_bytes, pa_reshape_and_cache, pa_reshape_and_cache_fp8)
 
 
 def workspace_for(k_pool: torch.Tensor, batch: int, num_q_heads: int, max_context_len: int,
@@ -54,3 +54,39 @@ def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, err_flag=None, s
 
 def copy_blocks(k_pool, v_pool, pairs, err_flag=None, stream=None):
     pa_copy_blocks(CacheDesc.of(k_pool), k_pool, v_pool, pairs, err_flag, stream)
+
+
+# ---- 8-bit float (OCP E4M3) pools: uint8 codes plus a float32 scale per (block, head, offset)
+
+def empty_fp8_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, device):
+    """Uninitialised (k_pool, v_pool, k_scale, v_scale) for an 8-bit float cache."""
+    shape = (num_blocks, num_kv_heads, block_size, head_dim)
+    return (torch.empty(shape, dtype=torch.uint8, device=device),
+            torch.empty(shape, dtype=torch.uint8, device=device),
+            torch.empty(shape[:3], dtype=torch.float32, device=device),
+            torch.empty(shape[:3], dtype=torch.float32, device=device))
+
+
+def decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, max_context_len: int,
+               scale: float, window: int = 0, partition_size: int = 0, out=None, workspace=None,
+               err_flag=None, stream=None):
+    """Decode over an 8-bit float cache; ``out`` has q's dtype (fp16 or bf16)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = workspace_for(k_pool, q.shape[0], q.shape[1], max_context_len, partition_size,
+                                  window)
+    pa_decode_fp8(CacheDesc.of(k_pool), out, q, k_pool, v_pool, k_scale, v_scale, block_table,
+                  context_lens, max_context_len, scale, window, partition_size, workspace, err_flag,
+                  stream)
+    return out
+
+
+def reshape_and_cache_fp8(key, value, k_pool, v_pool, k_scale, v_scale, slot_mapping, err_flag=None,
+                          stream=None):
+    pa_reshape_and_cache_fp8(CacheDesc.of(k_pool), key, value, k_pool, v_pool, k_scale, v_scale,
+                             slot_mapping, err_flag, stream)
+
+
+def copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, pairs, err_flag=None, stream=None):
+    pa_copy_blocks_fp8(CacheDesc.of(k_pool), k_pool, v_pool, k_scale, v_scale, pairs, err_flag, stream)

@@ -46,11 +46,22 @@ def max_err(a, b) -> float:
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
 
 
+# Half an ulp relative to |o| of the output type: the one rounding of the fp32 result.
+HALF_ULP = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
 def assert_close(got, ref, dtype: str, what: str) -> float:
+    """Elementwise |got - ref| <= TOL + |ref| * HALF_ULP: the max-abs tolerance bounds the fp32
+    result, and its final rounding to the output type adds at most half an ulp of |o|."""
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    err = max_err(got, ref)
-    print(f"[gpu-result] {what}: max abs err {err:.3e} (tol {TOL[dtype]:.0e})", flush=True)
-    assert err <= TOL[dtype], f"{what}: max abs error {err:.3e} > {TOL[dtype]}"
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    diff = np.abs(got - ref)
+    err = float(diff.max()) if diff.size else 0.0
+    excess = float(np.max(diff - np.abs(ref) * HALF_ULP[dtype])) if diff.size else 0.0
+    print(f"[gpu-result] {what}: max abs err {err:.3e}, beyond output rounding {excess:.3e} "
+          f"(tol {TOL[dtype]:.0e})", flush=True)
+    assert excess <= TOL[dtype], f"{what}: error beyond output rounding {excess:.3e} > {TOL[dtype]}"
     return err
 
 

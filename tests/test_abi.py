@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "pagedkv.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")

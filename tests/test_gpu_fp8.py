@@ -1,0 +1,245 @@
+"""GPU: 8-bit float (OCP E4M3) KV blocks with a scale per row, against the oracle.
+
+Quantised append and copy-on-write must match the oracle bit for bit (codes and scales);
+decode over such a cache must match the oracle's float64 decode of the same codes within the
+tolerance of q's dtype. Codes fed to the decode come from the oracle's quantiser applied to
+the seeded float contents; unwritten slots hold NaN codes and NaN scales, so a read of one
+would show.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.fp8_cache as o8
+from paged_kv_cache_indexed_amd import ops
+from tests.gpu_util import assert_close, note, require_gpu
+from workloads import build_paged, config_workload
+
+pytestmark = pytest.mark.gpu
+
+_TORCH = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _quantise_pool(pool):
+    """Oracle codes and scales of a float pool; rows that are NaN (unwritten) stay poisoned."""
+    dead = np.isnan(pool).any(axis=-1)
+    codes, s = o8.quantize_rows(np.nan_to_num(pool, nan=0.0))
+    codes[dead] = o8.E4M3_NAN_CODE
+    s = s.copy()
+    s[dead] = np.nan
+    return codes, s
+
+
+def _dev_fp8(codes, scales, dev):
+    return (torch.from_numpy(np.ascontiguousarray(codes)).to(dev),
+            torch.from_numpy(np.ascontiguousarray(scales, np.float32)).to(dev))
+
+
+def _fp8_case(w, dev, q_dtype):
+    kc, ks = _quantise_pool(w.k_pool)
+    vc, vs = _quantise_pool(w.v_pool)
+    t = dict(q=torch.from_numpy(w.q).to(_TORCH[q_dtype]).to(dev),
+             block_table=torch.from_numpy(w.block_table).to(dev),
+             context_lens=torch.from_numpy(w.context_lens).to(dev))
+    t["kc"], t["ks"] = _dev_fp8(kc, ks, dev)
+    t["vc"], t["vs"] = _dev_fp8(vc, vs, dev)
+    # the oracle reads q as the GPU does: rounded to q's dtype
+    qh = t["q"].float().cpu().numpy()
+    return t, dict(q=qh, kc=kc, vc=vc, ks=ks, vs=vs)
+
+
+def _gpu_decode(w, t, window=0, P=0):
+    err = torch.zeros(1, dtype=torch.int32, device=t["q"].device)
+    out = ops.decode_fp8(t["q"], t["kc"], t["vc"], t["ks"], t["vs"], t["block_table"], t["context_lens"],
+                         int(w.context_lens.max()), w.scale, window=window, partition_size=P, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, f"error flag {int(err.item())}"
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("src", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_append_bit_exact(src, d):
+    dev = require_gpu()
+    rng = np.random.default_rng([500, d])
+    nb, hkv, bs, T = 12, 3, 8, 37
+    kc = rng.integers(0, 256, (nb, hkv, bs, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, (nb, hkv, bs, d)).astype(np.uint8)
+    ks = rng.uniform(0, 1, (nb, hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0, 1, (nb, hkv, bs)).astype(np.float32)
+    key = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    value = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    key[1] *= 1e4
+    value[2] *= 1e-3
+    key[3] = 0.0  # zero rows: scale 0, codes 0
+    value[4, 0] = 0.0
+    key[5, :, 0] = 448.0  # the row's scale is exactly 1, so the next values are exact ties
+    key[5, :, 1:6] = np.array([1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -11], np.float32)
+    key = torch.from_numpy(key).to(_TORCH[src]).float().numpy()
+    value = torch.from_numpy(value).to(_TORCH[src]).float().numpy()
+    slots = rng.permutation(nb * bs)[:T].astype(np.int32)
+    slots[[7, 20]] = -1
+    ref = o8.reshape_and_cache_fp8(kc, vc, ks, vs, key, value, slots)
+    dk = torch.from_numpy(kc).to(dev)
+    dv = torch.from_numpy(vc).to(dev)
+    dks = torch.from_numpy(ks).to(dev)
+    dvs = torch.from_numpy(vs).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    note(f"fp8 append src={src} d={d}")
+    ops.reshape_and_cache_fp8(torch.from_numpy(key).to(_TORCH[src]).to(dev),
+                              torch.from_numpy(value).to(_TORCH[src]).to(dev), dk, dv, dks, dvs,
+                              torch.from_numpy(slots).to(dev), err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for got, want, what in ((dk, ref[0], "k codes"), (dv, ref[1], "v codes"), (dks, ref[2], "k scales"),
+                            (dvs, ref[3], "v scales")):
+        g = got.cpu().numpy()
+        if g.dtype == np.float32:
+            assert np.array_equal(g.view(np.uint32), want.view(np.uint32)), what
+        else:
+            assert np.array_equal(g, want), f"{what}: {np.count_nonzero(g != want)} codes differ"
+
+
+def test_fp8_append_bad_slot_flag():
+    dev = require_gpu()
+    nb, hkv, bs, d = 4, 2, 8, 128
+    k, v, ks, vs = ops.empty_fp8_cache(nb, hkv, bs, d, dev)
+    for x in (k, v):
+        x.fill_(7)
+    ks.fill_(0.5)
+    vs.fill_(0.5)
+    key = torch.randn(3, hkv, d, dtype=torch.float16, device=dev)
+    slots = torch.tensor([0, nb * bs, 9], dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    note("fp8 append bad slot")
+    ops.reshape_and_cache_fp8(key, key, k, v, ks, vs, slots, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 8
+    ref = o8.reshape_and_cache_fp8(np.full((nb, hkv, bs, d), 7, np.uint8), np.full((nb, hkv, bs, d), 7, np.uint8),
+                                   np.full((nb, hkv, bs), 0.5, np.float32), np.full((nb, hkv, bs), 0.5, np.float32),
+                                   key.float().cpu().numpy()[[0, 2]], key.float().cpu().numpy()[[0, 2]],
+                                   np.array([0, 9], np.int32))
+    assert np.array_equal(k.cpu().numpy(), ref[0]) and np.array_equal(ks.cpu().numpy(), ref[2])
+
+
+def test_fp8_copy_blocks_bit_exact():
+    dev = require_gpu()
+    rng = np.random.default_rng(501)
+    nb, hkv, bs, d = 10, 4, 16, 128
+    kc = rng.integers(0, 256, (nb, hkv, bs, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, (nb, hkv, bs, d)).astype(np.uint8)
+    ks = rng.uniform(0, 1, (nb, hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0, 1, (nb, hkv, bs)).astype(np.float32)
+    pairs = np.array([[0, 5], [3, 7], [9, 1]], np.int32)
+    ref = o8.copy_blocks_fp8(kc, vc, ks, vs, pairs)
+    dk, dv = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    dks, dvs = torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev)
+    note("fp8 copy blocks")
+    ops.copy_blocks_fp8(dk, dv, dks, dvs, torch.from_numpy(pairs).to(dev))
+    torch.cuda.synchronize()
+    for got, want in zip((dk, dv, dks, dvs), ref):
+        assert np.array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("q_dtype,group,bs,d", [("f16", 1, 16, 128), ("bf16", 1, 8, 128), ("f16", 2, 32, 64),
+                                                ("bf16", 4, 16, 128), ("f16", 8, 16, 128),
+                                                ("f16", 1, 16, 256), ("bf16", 2, 64, 256)])
+def test_fp8_decode_matches_oracle(q_dtype, group, bs, d):
+    dev = require_gpu()
+    lens = np.array([1, 5, 16, 17, 100, 333, 530], np.int32)
+    w = build_paged(f"fp8-{q_dtype}", 510 + group, bs, lens, bs, 2, 2 * group, d, "f32")
+    t, h = _fp8_case(w, dev, q_dtype)
+    ref = o8.paged_decode_fp8(h["q"], h["kc"], h["vc"], h["ks"], h["vs"], w.block_table, w.context_lens, w.scale)
+    for P in (0, 2 * bs, 128, 512):
+        note(f"fp8 decode q={q_dtype} G={group} bs={bs} d={d} P={P}")
+        assert_close(_gpu_decode(w, t, 0, P), ref, q_dtype, f"fp8 decode {q_dtype} G={group} d={d} P={P}")
+
+
+def test_fp8_single_token_returns_dequantised_value():
+    dev = require_gpu()
+    w = build_paged("fp8-one", 520, 0, np.array([1, 1, 1], np.int32), 16, 4, 4, 128, "f32")
+    t, h = _fp8_case(w, dev, "f16")
+    note("fp8 single token")
+    got = _gpu_decode(w, t)
+    vals = o8.e4m3_value(h["vc"]).astype(np.float32)  # exact: 4 significant bits
+    for b in range(3):
+        blk = w.block_table[b, 0]
+        prod = vals[blk, :, 0, :] * h["vs"][blk, :, 0][:, None]  # float32 product, as the kernel
+        want = torch.from_numpy(prod).half().double().numpy()
+        assert np.array_equal(got[b], want), "a one-token context must return its value row"
+
+
+@pytest.mark.parametrize("window,P", [(1, 0), (7, 32), (100, 0), (300, 64)])
+def test_fp8_window(window, P):
+    dev = require_gpu()
+    lens = np.array([3, 64, 200, 530], np.int32)
+    w = build_paged("fp8-win", 530, 1, lens, 16, 2, 8, 128, "f32")
+    t, h = _fp8_case(w, dev, "bf16")
+    ref = o8.paged_decode_fp8(h["q"], h["kc"], h["vc"], h["ks"], h["vs"], w.block_table, w.context_lens, w.scale,
+                              window=window)
+    note(f"fp8 window {window} P={P}")
+    assert_close(_gpu_decode(w, t, window, P), ref, "bf16", f"fp8 window {window}")
+
+
+def test_fp8_step_append_then_decode():
+    """The whole quantised step: quantising append of one token per sequence, then decode at
+    L + 1, against the oracle's own append and decode."""
+    dev = require_gpu()
+    w = config_workload(2, seed=3, batch=16, heads=8)
+    t, h = _fp8_case(w, dev, "f16")
+    key = torch.from_numpy(w.new_key).half().to(dev)
+    value = torch.from_numpy(w.new_value).half().to(dev)
+    ref_pools = o8.reshape_and_cache_fp8(h["kc"], h["vc"], h["ks"], h["vs"], key.float().cpu().numpy(),
+                                         value.float().cpu().numpy(), w.slot_mapping)
+    lens1 = w.lens_after_append
+    ref = o8.paged_decode_fp8(h["q"], *ref_pools, w.block_table, lens1, w.scale)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    note("fp8 step")
+    ops.reshape_and_cache_fp8(key, value, t["kc"], t["vc"], t["ks"], t["vs"],
+                              torch.from_numpy(w.slot_mapping).to(dev), err_flag=err)
+    out = ops.decode_fp8(t["q"], t["kc"], t["vc"], t["ks"], t["vs"], t["block_table"],
+                         torch.from_numpy(lens1).to(dev), int(lens1.max()), w.scale, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert_close(out.float().cpu().numpy().astype(np.float64), ref, "f16", "fp8 step")
+
+
+def test_fp8_bad_block_id_poisons_only_its_sequence():
+    dev = require_gpu()
+    lens = np.array([40, 70], np.int32)
+    w = build_paged("fp8-bad", 540, 0, lens, 16, 2, 2, 128, "f32")
+    t, h = _fp8_case(w, dev, "f16")
+    ref = o8.paged_decode_fp8(h["q"], h["kc"], h["vc"], h["ks"], h["vs"], w.block_table, w.context_lens, w.scale)
+    bad = t["block_table"].clone()
+    bad[0, 1] = 1 << 30
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    note("fp8 bad block id")
+    out = ops.decode_fp8(t["q"], t["kc"], t["vc"], t["ks"], t["vs"], bad, t["context_lens"], 70, w.scale,
+                         err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 1
+    o = out.float().cpu().numpy()
+    assert np.all(np.isnan(o[0]))
+    assert_close(o[1:].astype(np.float64), ref[1:], "f16", "fp8 other sequence")
+
+
+def test_fp8_rejects_mismatched_calls():
+    dev = require_gpu()
+    k, v, ks, vs = ops.empty_fp8_cache(4, 2, 16, 128, dev)
+    q = torch.zeros(1, 2, 128, dtype=torch.float16, device=dev)
+    table = torch.zeros(1, 4, dtype=torch.int32, device=dev)
+    lens = torch.ones(1, dtype=torch.int32, device=dev)
+    with pytest.raises(Exception):
+        ops.decode(q, k, v, table, lens, 1, 1.0)  # an 8-bit pool needs its scales
+    with pytest.raises(Exception):
+        ops.decode_fp8(q.float(), k, v, ks, vs, table, lens, 1, 1.0)  # q must be fp16/bf16
+    with pytest.raises(Exception):
+        ops.copy_blocks(k, v, torch.tensor([[0, 1]], dtype=torch.int32, device=dev))
+    k8, v8, ks8, vs8 = ops.empty_fp8_cache(4, 2, 8, 64, dev)
+    with pytest.raises(Exception):  # 8-token blocks of 64-byte rows: a wave load spans 2 blocks
+        ops.decode_fp8(torch.zeros(1, 2, 64, dtype=torch.float16, device=dev), k8, v8, ks8, vs8, table, lens, 1, 1.0)
+    q16 = torch.zeros(1, 32, 128, dtype=torch.float16, device=dev)
+    with pytest.raises(Exception):
+        ops.decode_fp8(q16, k, v, ks, vs, table, lens, 1, 1.0)  # 16 query heads per kv head
