@@ -214,7 +214,10 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out
     if ((int64_t)cache->head_dim * dtype_bytes(cache->dtype) * cache->block_size < 1024) return PA_ERR_UNSUPPORTED;
     if (is_fp8(cache)) {
         if (q_dtype != PA_F16 && q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
-        if (num_q_heads / cache->num_kv_heads > 8) return PA_ERR_UNSUPPORTED;
+        // the VALU kernel takes at most 8 query heads per kv head over 8-bit pools
+        const int g8 = num_q_heads / cache->num_kv_heads;
+        if (g8 > 8 && !decode_mfma_supported(cache->dtype, cache->head_dim, g8, cache->block_size))
+            return PA_ERR_UNSUPPORTED;
         if (!k_scale || !v_scale || !aligned4(k_scale) || !aligned4(v_scale)) return PA_ERR_INVALID_ARGUMENT;
     } else if (q_dtype != cache->dtype) {
         return PA_ERR_INVALID_ARGUMENT;
@@ -261,7 +264,8 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out
     a.scale_log2 = scale * 1.4426950408889634f;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = decode_mfma_supported(cache->dtype, cache->head_dim, group, cache->block_size)
-                       ? launch_decode_mfma(a, cache->dtype, cache->head_dim, group, batch, cache->num_kv_heads, s)
+                       ? launch_decode_mfma(a, cache->dtype, q_dtype, cache->head_dim, group, batch,
+                                            cache->num_kv_heads, s)
                        : launch_decode_valu(a, cache->dtype, q_dtype, cache->head_dim, group, batch,
                                             cache->num_kv_heads, s);
     if (e == hipSuccess && parts > 1) e = launch_reduce(a, q_dtype, cache->head_dim, batch, s);

@@ -25,6 +25,16 @@
 //   * Everything else (length checks, block ids staged and checked in LDS, branch-free
 //     masked buffer loads that never touch padding, base-2 online softmax in fp32, wave and
 //     partition merge) is shared with the VALU path.
+//
+// 8-bit float pools (OCP E4M3 codes, a float32 scale per (token, kv head) row): a lane's
+// 16-byte load holds 16 codes, dims 64c' + 16g .. +15 of token row n (still 64 contiguous
+// bytes of 16 rows per instruction). They widen exactly to q's 16-bit type as the A operands
+// of k-blocks 2c' (dims +0..7) and 2c' + 1 (dims +8..15); Q's B operand follows the same
+// assignment. Lane (n, g) holds the scores of tokens 4g .. 4g+3 of each tile, which are also
+// its P entries, so one aligned 16-byte load per tile brings the four K scales (they multiply
+// the scores) and one the four V scales (they multiply P before the split into hi and lo).
+#include <type_traits>
+
 #include "pa_decode_common.h"
 
 // Cache policy of this kernel's K/V loads. Four loads of a lane cover one 64-byte piece of
@@ -91,13 +101,30 @@ struct Mma<F16> {
     __device__ static uint32_t pack_exact(float x, float y) { return pack_round(x, y); }
 };
 
-template <typename T, int D, int G, int NW, bool kDoubleBuffer>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
-    static_assert(T::kBytes == 2, "matrix-core path is for 16-bit storage");
+// Eight E4M3 codes (two dwords) -> the same values in T (exact), packed as an A/B operand.
+__device__ __forceinline__ u32x4 widen8(F16, uint32_t w0, uint32_t w1) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, true))};
+}
+__device__ __forceinline__ u32x4 widen8(BF16, uint32_t w0, uint32_t w1) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
+}
+
+// T: type of q, out and the MFMA operands (fp16 / bf16); KV: the pool's storage (T or FP8).
+template <typename T, typename KV, int D, int G, int NW, bool kDoubleBuffer>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
+    static_assert(T::kBytes == 2, "matrix-core operands are 16-bit");
     static_assert(G >= 1 && G <= 16, "at most 16 query heads per kv head");
-    constexpr int NC = D / 32;  // 16-byte chunks of a token row per lane group (D/4 dims)
-    constexpr int NS = D / 16;  // 16-dim output slices
-    constexpr int kChunk = 32;  // tokens per wave iteration (two 16-token tiles)
+    constexpr bool kFp8 = std::is_same_v<KV, FP8>;
+    constexpr int NC = D / 32;             // 32-dim k-blocks of the score contraction
+    constexpr int NL = D * KV::kBytes / 64;  // 16-byte loads per lane per tile row (64 B of each row)
+    constexpr int NS = D / 16;             // 16-dim output slices
+    constexpr int kChunk = 32;             // tokens per wave iteration (two 16-token tiles)
     using M = Mma<T>;
 
     __shared__ int s_ids[kMaxIdsPerPartition];
@@ -116,13 +143,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int bs = 1 << lbs;
 
     // Q as the B operand of S^T = K Q^T: column n is head h0 + n (zero past G); k-block c
-    // of lane group g holds dims 32c + 8g .. +7, the same dims the K loads below give.
+    // of lane group g holds the dims the K operand gives it: 32c + 8g .. +7 for 16-bit pools,
+    // 64(c/2) + 16g + 8(c%2) .. +7 for 8-bit pools.
     u32x4 qb[NC];
     {
         const char* qrow = static_cast<const char*>(a.q) +
-                           (((size_t)b * a.num_q_heads + kvh * G + (n < G ? n : 0)) * D + 8 * g) * 2;
+                           ((size_t)b * a.num_q_heads + kvh * G + (n < G ? n : 0)) * D * 2;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) qb[c] = (n < G) ? load16(qrow + 64 * c) : u32x4{0, 0, 0, 0};
+        for (int c = 0; c < NC; ++c) {
+            const int d0 = kFp8 ? 64 * (c >> 1) + 16 * g + 8 * (c & 1) : 32 * c + 8 * g;
+            qb[c] = (n < G) ? load16(qrow + 2 * d0) : u32x4{0, 0, 0, 0};
+        }
     }
     Partition part;
     if (!partition_prologue<T, D, G, NW * 64>(a, p, kvh, b, s_ids, part)) return;
@@ -135,7 +166,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     ident.x = ((4 * g + 0 == n) ? M::kOne : 0u) | (((4 * g + 1 == n) ? M::kOne : 0u) << 16);
     ident.y = ((4 * g + 2 == n) ? M::kOne : 0u) | (((4 * g + 3 == n) ? M::kOne : 0u) << 16);
 
-    const size_t head_bytes = (size_t)bs * D * 2;
+    const size_t head_bytes = (size_t)bs * D * KV::kBytes;
     const size_t block_bytes = head_bytes * a.num_kv_heads;
     const char* kpool = static_cast<const char*>(a.k_pool);
     const char* vpool = static_cast<const char*>(a.v_pool);
@@ -144,23 +175,31 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int niters = (ntok - c0 * kChunk + kChunk * NW - 1) / (kChunk * NW);
 
     // Loads of one chunk: tile t rows are tokens rel + 16t + n; lanes past the partition end
-    // read zeros through an out-of-range offset.
-    auto issue = [&](int it, u32x4 (*kk)[NC], u32x4 (*vv)[NC]) {
+    // read zeros through an out-of-range offset. With 8-bit pools, ks/vs[t] are the scales
+    // of tokens rel + 16t + 4g .. +3 (the rows of this lane's scores), loaded whole when the
+    // tile starts inside the partition and cleared per token before use.
+    auto issue = [&](int it, u32x4 (*kk)[NL], u32x4 (*vv)[NL], u32x4* ks, u32x4* vs) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int rel = (c0 + it * NW + wave) * kChunk + 16 * t;  // wave-uniform
             const int id = __builtin_amdgcn_readfirstlane(s_ids[(rel < ntok ? rel : 0) >> lbs]);  // partitions start on a block
             const size_t slab = (size_t)id * block_bytes + (size_t)kvh * head_bytes;
             const uint32_t off = (rel + n < ntok && rel + n >= rel_lo)
-                                     ? (uint32_t)(((rel & (bs - 1)) + n) * D * 2) + seg
+                                     ? (uint32_t)(((rel & (bs - 1)) + n) * D * KV::kBytes) + seg
                                      : kOutOfRange;
             const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + slab, slab_bytes);
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + slab, slab_bytes);
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
+            for (int c = 0; c < NL; ++c) {
                 const uint32_t o = off == kOutOfRange ? kOutOfRange : off + 64 * c;
                 kk[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rk, o);
                 vv[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rv, o);
+            }
+            if constexpr (kFp8) {
+                const size_t srow = ((size_t)id * a.num_kv_heads + kvh) << lbs;  // this slab's scales
+                const uint32_t so = rel < ntok ? (uint32_t)(((rel & (bs - 1)) + 4 * g) * 4) : kOutOfRange;
+                ks[t] = buffer_load16<PA_MFMA_LOAD_POLICY>(make_rsrc(a.k_scale + srow, (uint32_t)bs * 4), so);
+                vs[t] = buffer_load16<PA_MFMA_LOAD_POLICY>(make_rsrc(a.v_scale + srow, (uint32_t)bs * 4), so);
             }
         }
     };
@@ -171,18 +210,33 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int it, u32x4 (*kk)[NC], u32x4 (*vv)[NC]) {
+    auto compute = [&](int it, u32x4 (*kk)[NL], u32x4 (*vv)[NL], const u32x4* ks, const u32x4* vs) {
         const int rel0 = (c0 + it * NW + wave) * kChunk;
         float sc[8];
+        float vscale[8];  // V scale of each P entry (8-bit pools)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             f32x4 st = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (kFp8) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) st = M::k32(kk[t][c], qb[c], st);
+                for (int c = 0; c < NL; ++c) {
+                    st = M::k32(widen8(T{}, kk[t][c][0], kk[t][c][1]), qb[2 * c], st);
+                    st = M::k32(widen8(T{}, kk[t][c][2], kk[t][c][3]), qb[2 * c + 1], st);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NC; ++c) st = M::k32(kk[t][c], qb[c], st);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = rel0 + 16 * t + 4 * g + i;
-                sc[4 * t + i] = (tok < ntok && tok >= rel_lo) ? st[i] * a.scale_log2 : -INFINITY;
+                const bool live = tok < ntok && tok >= rel_lo;
+                float d = st[i];
+                if constexpr (kFp8) {
+                    d *= __uint_as_float(ks[t][i]);
+                    vscale[4 * t + i] = live ? __uint_as_float(vs[t][i]) : 0.f;
+                }
+                sc[4 * t + i] = live ? d * a.scale_log2 : -INFINITY;
             }
         }
         float cm = sc[0];
@@ -209,7 +263,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int s = 0; s < NS; ++s) acc[s][i] *= ai;
         }
-        // P as the A operand, split into rounded high and low parts
+        // P as the A operand (times the V scales for 8-bit pools), split into rounded high and
+        // low parts
+        if constexpr (kFp8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pr[j] *= vscale[j];
+        }
         u32x4 phi, plo;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -217,13 +276,27 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             phi[w] = h;
             plo[w] = M::pack_round(pr[2 * w] - M::lo(h), pr[2 * w + 1] - M::hi(h));
         }
+        // V rows as 16-bit words: vw[t][c] holds the 8 dims of token row n that k-block c of
+        // lane group g covers
+        u32x4 vw[2][NC];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if constexpr (kFp8) {
+                    vw[t][c] = (c & 1) ? widen8(T{}, vv[t][c >> 1][2], vv[t][c >> 1][3])
+                                       : widen8(T{}, vv[t][c >> 1][0], vv[t][c >> 1][1]);
+                } else {
+                    vw[t][c] = vv[t][c];
+                }
+            }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const int c = s >> 1;
             f32x4 vt[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const u32x2 half = (s & 1) ? u32x2{vv[t][c][2], vv[t][c][3]} : u32x2{vv[t][c][0], vv[t][c][1]};
+                const u32x2 half = (s & 1) ? u32x2{vw[t][c][2], vw[t][c][3]} : u32x2{vw[t][c][0], vw[t][c][1]};
                 vt[t] = M::k16(half, ident, f32x4{0.f, 0.f, 0.f, 0.f});
             }
             const u32x4 vb = {M::pack_exact(vt[0][0], vt[0][1]), M::pack_exact(vt[0][2], vt[0][3]),
@@ -233,28 +306,28 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         }
     };
 
-    u32x4 ka[2][NC], va[2][NC];
+    u32x4 ka[2][NL], va[2][NL], ksa[2], vsa[2];
     if constexpr (kDoubleBuffer) {
-        u32x4 kb[2][NC], vb[2][NC];
-        issue(0, ka, va);
-        issue(1, kb, vb);
+        u32x4 kb[2][NL], vb[2][NL], ksb[2], vsb[2];
+        issue(0, ka, va, ksa, vsa);
+        issue(1, kb, vb, ksb, vsb);
         int it = 0;
         for (; it + 1 < niters; it += 2) {
             __builtin_amdgcn_sched_barrier(0);
-            compute(it, ka, va);
+            compute(it, ka, va, ksa, vsa);
             __builtin_amdgcn_sched_barrier(0);
-            issue(it + 2, ka, va);
+            issue(it + 2, ka, va, ksa, vsa);
             __builtin_amdgcn_sched_barrier(0);
-            compute(it + 1, kb, vb);
+            compute(it + 1, kb, vb, ksb, vsb);
             __builtin_amdgcn_sched_barrier(0);
-            issue(it + 3, kb, vb);
+            issue(it + 3, kb, vb, ksb, vsb);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (it < niters) compute(it, ka, va);
+        if (it < niters) compute(it, ka, va, ksa, vsa);
     } else {
         for (int it = 0; it < niters; ++it) {
-            issue(it, ka, va);
-            compute(it, ka, va);
+            issue(it, ka, va, ksa, vsa);
+            compute(it, ka, va, ksa, vsa);
         }
     }
 
@@ -267,7 +340,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const int dim = 32 * (s >> 1) + 8 * (n >> 2) + 4 * (s & 1) + (n & 3);  // column n of slice s
+        const int c = s >> 1;  // column n of slice s
+        const int dim = (kFp8 ? 64 * (c >> 1) + 16 * (n >> 2) + 8 * (c & 1) : 32 * c + 8 * (n >> 2)) + 4 * (s & 1) +
+                        (n & 3);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (4 * g + i < G) s_acc[wave][4 * g + i][dim] = acc[s][i];
@@ -280,47 +355,57 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #define PA_MFMA_WAVES 4
 #endif
 
-template <typename T, int D, int G>
+template <typename T, typename KV, int D, int G>
 hipError_t launch_tdg(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     constexpr int NW = PA_MFMA_WAVES;
     dim3 grid(a.max_partitions, num_kv_heads, batch);
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, NW, (D <= 128)>), grid, dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, KV, D, G, NW, (D <= 128)>), grid, dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, typename KV, int D>
 hipError_t launch_td(const DecodeArgs& a, int group, int batch, int num_kv_heads, hipStream_t s) {
     switch (group) {
-        case 4: return launch_tdg<T, D, 4>(a, batch, num_kv_heads, s);
-        case 8: return launch_tdg<T, D, 8>(a, batch, num_kv_heads, s);
-        case 16: return launch_tdg<T, D, 16>(a, batch, num_kv_heads, s);
+        case 4: return launch_tdg<T, KV, D, 4>(a, batch, num_kv_heads, s);
+        case 8: return launch_tdg<T, KV, D, 8>(a, batch, num_kv_heads, s);
+        case 16:
+            if constexpr (D <= 128) return launch_tdg<T, KV, D, 16>(a, batch, num_kv_heads, s);
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T>
+template <typename T, typename KV>
 hipError_t launch_t(const DecodeArgs& a, int head_dim, int group, int batch, int num_kv_heads, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_td<T, 64>(a, group, batch, num_kv_heads, s);
-        case 128: return launch_td<T, 128>(a, group, batch, num_kv_heads, s);
-        case 256: return launch_td<T, 256>(a, group, batch, num_kv_heads, s);
+        case 64: return launch_td<T, KV, 64>(a, group, batch, num_kv_heads, s);
+        case 128: return launch_td<T, KV, 128>(a, group, batch, num_kv_heads, s);
+        case 256: return launch_td<T, KV, 256>(a, group, batch, num_kv_heads, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-bool decode_mfma_supported(int dtype, int head_dim, int group, int block_size) {
-    return (dtype == PA_F16 || dtype == PA_BF16) && (group == 4 || group == 8 || group == 16) &&
-           block_size >= 16 && (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
-           !(group == 16 && head_dim == 256);
+bool decode_mfma_supported(int kv_dtype, int head_dim, int group, int block_size) {
+    return (kv_dtype == PA_F16 || kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) &&
+           (group == 4 || group == 8 || group == 16) && block_size >= 16 &&
+           (head_dim == 64 || head_dim == 128 || head_dim == 256) && !(group == 16 && head_dim == 256);
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
+hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream) {
+    if (kv_dtype == PA_FP8_E4M3) {
+        switch (dtype) {
+            case PA_F16: return launch_t<F16, FP8>(a, head_dim, group, batch, num_kv_heads, stream);
+            case PA_BF16: return launch_t<BF16, FP8>(a, head_dim, group, batch, num_kv_heads, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (kv_dtype != dtype) return hipErrorInvalidValue;
     switch (dtype) {
-        case PA_F16: return launch_t<F16>(a, head_dim, group, batch, num_kv_heads, stream);
-        case PA_BF16: return launch_t<BF16>(a, head_dim, group, batch, num_kv_heads, stream);
+        case PA_F16: return launch_t<F16, F16>(a, head_dim, group, batch, num_kv_heads, stream);
+        case PA_BF16: return launch_t<BF16, BF16>(a, head_dim, group, batch, num_kv_heads, stream);
         default: return hipErrorInvalidValue;
     }
 }

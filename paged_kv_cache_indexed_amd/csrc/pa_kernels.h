@@ -54,9 +54,10 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int dtype, int 
 // The same over 8-bit float pools (dtype = type of q and out: fp16 or bf16; group <= 8).
 hipError_t launch_decode_valu_fp8(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
                                   int num_kv_heads, hipStream_t stream);
-// Matrix-core decode for grouped-query heads (fp16/bf16, group 4/8/16, block_size >= 16).
-bool decode_mfma_supported(int dtype, int head_dim, int group, int block_size);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
+// Matrix-core decode for grouped-query heads (fp16/bf16 or 8-bit pools, group 4/8/16,
+// block_size >= 16); dtype is the type of q and out.
+bool decode_mfma_supported(int kv_dtype, int head_dim, int group, int block_size);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream);
 // Log-sum-exp combine of partition records (only when some sequence has > 1 partition).
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, int batch, hipStream_t stream);

@@ -143,16 +143,20 @@ def test_fp8_copy_blocks_bit_exact():
         assert np.array_equal(got.cpu().numpy(), want)
 
 
+# VALU kernel: groups 1-2, and 4-8 with 8-token blocks; matrix cores: groups 4-16 with blocks
+# of 16 tokens or more.
 @pytest.mark.parametrize("q_dtype,group,bs,d", [("f16", 1, 16, 128), ("bf16", 1, 8, 128), ("f16", 2, 32, 64),
-                                                ("bf16", 4, 16, 128), ("f16", 8, 16, 128),
-                                                ("f16", 1, 16, 256), ("bf16", 2, 64, 256)])
+                                                ("f16", 1, 16, 256), ("bf16", 2, 64, 256), ("f16", 4, 8, 128),
+                                                ("bf16", 8, 8, 128), ("bf16", 4, 16, 128), ("f16", 8, 16, 128),
+                                                ("bf16", 16, 16, 128), ("f16", 16, 32, 64), ("bf16", 8, 32, 256),
+                                                ("f16", 4, 256, 128)])
 def test_fp8_decode_matches_oracle(q_dtype, group, bs, d):
     dev = require_gpu()
     lens = np.array([1, 5, 16, 17, 100, 333, 530], np.int32)
     w = build_paged(f"fp8-{q_dtype}", 510 + group, bs, lens, bs, 2, 2 * group, d, "f32")
     t, h = _fp8_case(w, dev, q_dtype)
     ref = o8.paged_decode_fp8(h["q"], h["kc"], h["vc"], h["ks"], h["vs"], w.block_table, w.context_lens, w.scale)
-    for P in (0, 2 * bs, 128, 512):
+    for P in [P for P in (0, 2 * bs, 128, 512) if P % bs == 0]:
         note(f"fp8 decode q={q_dtype} G={group} bs={bs} d={d} P={P}")
         assert_close(_gpu_decode(w, t, 0, P), ref, q_dtype, f"fp8 decode {q_dtype} G={group} d={d} P={P}")
 
@@ -240,6 +244,19 @@ def test_fp8_rejects_mismatched_calls():
     k8, v8, ks8, vs8 = ops.empty_fp8_cache(4, 2, 8, 64, dev)
     with pytest.raises(Exception):  # 8-token blocks of 64-byte rows: a wave load spans 2 blocks
         ops.decode_fp8(torch.zeros(1, 2, 64, dtype=torch.float16, device=dev), k8, v8, ks8, vs8, table, lens, 1, 1.0)
+    k9, v9, ks9, vs9 = ops.empty_fp8_cache(4, 2, 8, 128, dev)
     q16 = torch.zeros(1, 32, 128, dtype=torch.float16, device=dev)
-    with pytest.raises(Exception):
-        ops.decode_fp8(q16, k, v, ks, vs, table, lens, 1, 1.0)  # 16 query heads per kv head
+    with pytest.raises(Exception):  # 16 query heads per kv head need the matrix cores: blocks >= 16
+        ops.decode_fp8(q16, k9, v9, ks9, vs9, table, lens, 1, 1.0)
+
+
+def test_fp8_gqa_workload_full_size():
+    """The grouped-query workload's sequences (2048 tokens, 64 query / 8 kv heads; 16 of its
+    32 sequences) over an 8-bit cache on the matrix cores, every output against the oracle."""
+    dev = require_gpu()
+    w = config_workload(4, seed=5, batch=16)
+    t, h = _fp8_case(w, dev, "bf16")
+    ref = o8.paged_decode_fp8(h["q"], h["kc"], h["vc"], h["ks"], h["vs"], w.block_table, w.context_lens, w.scale)
+    for P in (0, 512):
+        note(f"fp8 GQA workload P={P}")
+        assert_close(_gpu_decode(w, t, 0, P), ref, "bf16", f"fp8 GQA workload P={P}")
