@@ -74,13 +74,25 @@ typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype_t
 #define PA_FLAG_BAD_SLOT       8  /* slot >= num_blocks * block_size */
 #define PA_FLAG_BAD_COPY_PAIR 16  /* src or dst outside [0, num_blocks), or src == dst */
 
-/* Shape of one physical pool pair (K and V have the same shape). */
+/*
+ * Shape of one physical pool pair (K and V have the same shape).
+ *
+ * block_stride is the distance in bytes from block i to block i + 1 in k_pool and in
+ * v_pool; 0 means dense (num_kv_heads * block_size * head_dim * element bytes). A larger
+ * stride lets one allocation hold every layer's K and V, [num_blocks][2][num_layers]
+ * [num_kv_heads][block_size][head_dim] ([BlockManager essay] §5.1): the pools of layer l
+ * are then k_pool = base + (0 * num_layers + l) * dense bytes, v_pool = base + (1 *
+ * num_layers + l) * dense bytes, and block_stride = 2 * num_layers * dense bytes. Inside a
+ * block, heads, tokens and dims stay dense. block_stride must be 0 or a multiple of 16 that
+ * is at least the dense size. Scale pools of 8-bit caches are always dense.
+ */
 typedef struct {
     int32_t num_blocks;
     int32_t block_size;
     int32_t num_kv_heads;
     int32_t head_dim;
     int32_t dtype; /* pa_dtype_t */
+    int64_t block_stride;
 } pa_cache_desc_t;
 
 /*

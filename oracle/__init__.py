@@ -11,14 +11,17 @@ from .paged_attention import (  # noqa: F401
     allocated_kv_bytes,
     attention_one_query,
     blocks_needed,
+    compact_blocks,
     copy_blocks,
     gather_range,
     gather_sequence,
     kv_cache_bytes,
+    layer_pools,
     paged_decode,
     paged_decode_heads,
     paged_decode_window,
     window_start,
+    reblock,
     reshape_and_cache,
 )
 

@@ -213,3 +213,49 @@ def copy_blocks(k_pool, v_pool, pairs):
         k_new[dst] = k_new[src]
         v_new[dst] = v_new[src]
     return k_new, v_new
+
+
+def layer_pools(cache: np.ndarray, layer: int):
+    """K and V pools of one layer of a multi-layer cache [num_blocks][2][num_layers][heads]
+    [block_size][head_dim], whose dim 1 selects K or V ([BlockManager essay] §5.1). The views
+    share the cache's memory; consecutive blocks are 2 * num_layers slabs apart."""
+    return cache[:, 0, int(layer)], cache[:, 1, int(layer)]
+
+
+def reblock(pool, block_table, context_lens, new_block_size: int, new_table, new_num_blocks: int):
+    """Migrate a paged cache to another block size ([CANN paging article] §4.1: a new block
+    size invalidates the tables, so the block contents move to a new layout).
+
+    Every sequence's valid rows, read through its old table, are written in order into the
+    blocks its new table lists, block_size ``new_block_size`` each. Returns the new pool;
+    slots that hold no valid token are NaN. Bad ids or lengths raise.
+    """
+    nb_old, H, bs, d = pool.shape
+    out = np.full((int(new_num_blocks), H, int(new_block_size), d), np.nan, pool.dtype)
+    nbs = int(new_block_size)
+    for b, L in enumerate(np.asarray(context_lens).tolist()):
+        need = blocks_needed(L, nbs)
+        if need > np.shape(new_table)[1]:
+            raise OracleInputError(f"sequence {b}: {need} new blocks > new table width")
+        for h in range(H):
+            rows = gather_sequence(pool, block_table[b], L, h)
+            for j in range(need):
+                pid = int(new_table[b][j])
+                if not 0 <= pid < new_num_blocks:
+                    raise OracleInputError(f"new block id {pid} outside [0, {new_num_blocks})")
+                chunk = rows[j * nbs:(j + 1) * nbs]
+                out[pid, h, :len(chunk)] = chunk
+    return out
+
+
+def compact_blocks(k_pool, v_pool, block_table, pairs):
+    """Defragmentation step ([CANN paging article] §5.1): live blocks move to their new ids
+    (copy-on-write's block copy, pair by pair) and every table entry naming a moved block is
+    rewritten to its new id. Returns (k_pool, v_pool, block_table)."""
+    k_new, v_new = copy_blocks(k_pool, v_pool, pairs)
+    moved = {int(s): int(d) for s, d in np.asarray(pairs).reshape(-1, 2).tolist()}
+    table = np.array(block_table, copy=True)
+    for idx, pid in np.ndenumerate(table):
+        if int(pid) in moved:
+            table[idx] = moved[int(pid)]
+    return k_new, v_new, table

@@ -39,7 +39,7 @@ _DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_
 class pa_cache_desc_t(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("block_stride", ctypes.c_int64)]
 
 
 @dataclass(frozen=True)
@@ -49,16 +49,23 @@ class CacheDesc:
     num_kv_heads: int
     head_dim: int
     dtype: int
+    block_stride: int = 0  # bytes between consecutive blocks; 0 = dense
 
     @staticmethod
     def of(k_pool: torch.Tensor) -> "CacheDesc":
-        """Describe a [num_blocks][kv_heads][block_size][head_dim] pool tensor."""
+        """Describe a [num_blocks][kv_heads][block_size][head_dim] pool tensor. Blocks must be
+        dense inside; the distance between blocks (dim 0's stride) may be larger, as for one
+        layer's K or V in a [blocks][2][layers][heads][block_size][head_dim] allocation."""
         nb, hkv, bs, d = k_pool.shape
-        return CacheDesc(int(nb), int(bs), int(hkv), int(d), _DTYPE_CODE[k_pool.dtype])
+        _check_pool_layout(k_pool)
+        dense = hkv * bs * d
+        stride = int(k_pool.stride(0))
+        return CacheDesc(int(nb), int(bs), int(hkv), int(d), _DTYPE_CODE[k_pool.dtype],
+                         0 if stride == dense else stride * k_pool.element_size())
 
     def c(self) -> pa_cache_desc_t:
         return pa_cache_desc_t(self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim,
-                               self.dtype)
+                               self.dtype, self.block_stride)
 
 
 class PagedKVError(RuntimeError):
@@ -114,6 +121,22 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _check_pool_layout(t) -> None:
+    nb, hkv, bs, d = t.shape
+    if t.stride(3) != 1 or t.stride(2) != d or t.stride(1) != bs * d or (nb > 1 and t.stride(0) < hkv * bs * d):
+        raise PagedKVError("pool blocks must be dense [kv_heads][block_size][head_dim] slabs")
+
+
+def _pool_ptr(t, like=None):
+    """Pointer of a pool tensor whose blocks may be strided (dim 0) but are dense inside."""
+    if not t.is_cuda:
+        raise PagedKVError("tensor must live on the GPU")
+    _check_pool_layout(t)
+    if like is not None and t.stride() != like.stride():
+        raise PagedKVError("k_pool and v_pool must have the same layout")
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -132,15 +155,15 @@ def pa_reshape_and_cache(cache: CacheDesc, key, value, k_pool, v_pool, slot_mapp
                          err_flag=None, stream=None) -> None:
     n = int(slot_mapping.numel())
     desc = cache.c()
-    _check(load().pa_reshape_and_cache(ctypes.byref(desc), _ptr(key), _ptr(value), _ptr(k_pool),
-                                       _ptr(v_pool), _ptr(slot_mapping), n, _ptr(err_flag),
+    _check(load().pa_reshape_and_cache(ctypes.byref(desc), _ptr(key), _ptr(value), _pool_ptr(k_pool),
+                                       _pool_ptr(v_pool, k_pool), _ptr(slot_mapping), n, _ptr(err_flag),
                                        _stream(stream)))
 
 
 def pa_copy_blocks(cache: CacheDesc, k_pool, v_pool, pairs, err_flag=None, stream=None) -> None:
     n = int(pairs.shape[0]) if pairs is not None else 0
     desc = cache.c()
-    _check(load().pa_copy_blocks(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
+    _check(load().pa_copy_blocks(ctypes.byref(desc), _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool),
                                  _ptr(pairs) if n else None, n, _ptr(err_flag), _stream(stream)))
 
 
@@ -172,7 +195,7 @@ def pa_decode(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_len
     batch, num_q_heads = int(q.shape[0]), int(q.shape[1])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     desc = cache.c()
-    _check(load().pa_decode(ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+    _check(load().pa_decode(ctypes.byref(desc), _ptr(out), _ptr(q), _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool),
                             _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens),
                             batch, num_q_heads, int(max_context_len), float(scale),
                             int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag),
@@ -186,7 +209,7 @@ def pa_decode_sliding_window(cache: CacheDesc, out, q, k_pool, v_pool, block_tab
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     desc = cache.c()
     _check(load().pa_decode_sliding_window(
-        ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+        ctypes.byref(desc), _ptr(out), _ptr(q), _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool), _ptr(block_table),
         int(block_table.shape[1]), _ptr(context_lens), batch, num_q_heads, int(max_context_len),
         float(scale), int(window), int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag),
         _stream(stream)))
@@ -201,7 +224,7 @@ def pa_reshape_and_cache_fp8(cache: CacheDesc, key, value, k_pool, v_pool, k_sca
     n = int(slot_mapping.numel())
     desc = cache.c()
     _check(load().pa_reshape_and_cache_fp8(ctypes.byref(desc), dtype_code(key), _ptr(key), _ptr(value),
-                                           _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                           _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool), _ptr(k_scale), _ptr(v_scale),
                                            _ptr(slot_mapping), n, _ptr(err_flag), _stream(stream)))
 
 
@@ -209,7 +232,7 @@ def pa_copy_blocks_fp8(cache: CacheDesc, k_pool, v_pool, k_scale, v_scale, pairs
                        stream=None) -> None:
     n = int(pairs.shape[0]) if pairs is not None else 0
     desc = cache.c()
-    _check(load().pa_copy_blocks_fp8(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+    _check(load().pa_copy_blocks_fp8(ctypes.byref(desc), _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool), _ptr(k_scale),
                                      _ptr(v_scale), _ptr(pairs) if n else None, n, _ptr(err_flag),
                                      _stream(stream)))
 
@@ -221,7 +244,7 @@ def pa_decode_fp8(cache: CacheDesc, out, q, k_pool, v_pool, k_scale, v_scale, bl
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     desc = cache.c()
     _check(load().pa_decode_fp8(
-        ctypes.byref(desc), dtype_code(q), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+        ctypes.byref(desc), dtype_code(q), _ptr(out), _ptr(q), _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool), _ptr(k_scale),
         _ptr(v_scale), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), batch, num_q_heads,
         int(max_context_len), float(scale), int(window), int(partition_size), _ptr(workspace), ws_bytes,
         _ptr(err_flag), _stream(stream)))

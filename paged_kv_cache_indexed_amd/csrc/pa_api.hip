@@ -27,6 +27,10 @@ int dtype_bytes(int dtype) {
     }
 }
 
+int64_t dense_block_bytes(const pa_cache_desc_t* c) {
+    return (int64_t)c->num_kv_heads * c->block_size * c->head_dim * dtype_bytes(c->dtype);
+}
+
 pa_status_t check_cache(const pa_cache_desc_t* c) {
     if (!c) return PA_ERR_INVALID_ARGUMENT;
     if (dtype_bytes(c->dtype) == 0) return PA_ERR_UNSUPPORTED;
@@ -36,8 +40,13 @@ pa_status_t check_cache(const pa_cache_desc_t* c) {
     if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->num_kv_heads > 65535) return PA_ERR_INVALID_ARGUMENT;
     // one pool must be addressable with the kernels' 64-bit byte offsets and 32-bit slots
     if ((int64_t)c->num_blocks * c->block_size > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
+    if (c->block_stride != 0 && (c->block_stride % 16 != 0 || c->block_stride < dense_block_bytes(c)))
+        return PA_ERR_INVALID_ARGUMENT;
     return PA_OK;
 }
+
+// Bytes from one physical block to the next (the dense size unless a stride is given).
+int64_t block_stride(const pa_cache_desc_t* c) { return c->block_stride ? c->block_stride : dense_block_bytes(c); }
 
 pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
@@ -80,7 +89,7 @@ pa_status_t pa_reshape_and_cache(const pa_cache_desc_t* cache, const void* key, 
     if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool))
         return PA_ERR_INVALID_ARGUMENT;
     CacheArgs a{k_pool, v_pool, err_flag, cache->num_blocks, log2_exact(cache->block_size),
-                cache->num_kv_heads, cache->head_dim * dtype_bytes(cache->dtype) / 16};
+                cache->num_kv_heads, cache->head_dim * dtype_bytes(cache->dtype) / 16, block_stride(cache)};
     return from_hip(launch_reshape_and_cache(a, key, value, slot_mapping, num_tokens, (hipStream_t)stream));
 }
 
@@ -94,7 +103,7 @@ pa_status_t pa_copy_blocks(const pa_cache_desc_t* cache, void* k_pool, void* v_p
     if (!k_pool || !v_pool || !pairs) return PA_ERR_INVALID_ARGUMENT;
     if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARGUMENT;
     CacheArgs a{k_pool, v_pool, err_flag, cache->num_blocks, log2_exact(cache->block_size),
-                cache->num_kv_heads, cache->head_dim * dtype_bytes(cache->dtype) / 16};
+                cache->num_kv_heads, cache->head_dim * dtype_bytes(cache->dtype) / 16, block_stride(cache)};
     return from_hip(launch_copy_blocks(a, pairs, num_pairs, nullptr, nullptr, (hipStream_t)stream));
 }
 
@@ -114,7 +123,7 @@ pa_status_t pa_reshape_and_cache_fp8(const pa_cache_desc_t* cache, int32_t src_d
         !aligned4(v_scale))
         return PA_ERR_INVALID_ARGUMENT;
     CacheArgs a{k_pool, v_pool, err_flag, cache->num_blocks, log2_exact(cache->block_size),
-                cache->num_kv_heads, cache->head_dim / 16};
+                cache->num_kv_heads, cache->head_dim / 16, block_stride(cache)};
     return from_hip(launch_reshape_and_cache_fp8(a, src_dtype, cache->head_dim, key, value, k_scale, v_scale,
                                                  slot_mapping, num_tokens, (hipStream_t)stream));
 }
@@ -132,7 +141,7 @@ pa_status_t pa_copy_blocks_fp8(const pa_cache_desc_t* cache, void* k_pool, void*
     if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_scale) || !aligned16(v_scale))
         return PA_ERR_INVALID_ARGUMENT;
     CacheArgs a{k_pool, v_pool, err_flag, cache->num_blocks, log2_exact(cache->block_size),
-                cache->num_kv_heads, cache->head_dim / 16};
+                cache->num_kv_heads, cache->head_dim / 16, block_stride(cache)};
     return from_hip(launch_copy_blocks(a, pairs, num_pairs, k_scale, v_scale, (hipStream_t)stream));
 }
 
@@ -262,6 +271,7 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out
     a.max_partitions = (int32_t)parts;
     a.window = window;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.block_stride = block_stride(cache);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = decode_mfma_supported(cache->dtype, cache->head_dim, group, cache->block_size)
                        ? launch_decode_mfma(a, cache->dtype, q_dtype, cache->head_dim, group, batch,

@@ -32,9 +32,10 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(CacheArgs a
         return;
     }
     const int off = slot & ((1 << a.log2_block_size) - 1);
-    const size_t dst = ((((size_t)blk * a.num_kv_heads + h) << a.log2_block_size) + off) * a.row_vecs + v;
-    store16(static_cast<char*>(a.k_pool) + dst * 16, load16(key + i * 16));
-    store16(static_cast<char*>(a.v_pool) + dst * 16, load16(value + i * 16));
+    const size_t dst = (size_t)blk * a.block_stride +
+                       (((((size_t)h) << a.log2_block_size) + off) * a.row_vecs + v) * 16;
+    store16(static_cast<char*>(a.k_pool) + dst, load16(key + i * 16));
+    store16(static_cast<char*>(a.v_pool) + dst, load16(value + i * 16));
 }
 
 // Quantising append into 8-bit float pools. LPR = head_dim / 16 lanes own one (token, kv
@@ -85,7 +86,8 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(CacheAr
             }
         }
         char* pool = static_cast<char*>(which == 0 ? a.k_pool : a.v_pool);
-        store16(pool + srow * D + (size_t)col * 16, codes);
+        const size_t row_in_block = ((size_t)h << a.log2_block_size) + off;
+        store16(pool + (size_t)blk * a.block_stride + row_in_block * D + (size_t)col * 16, codes);
         if (col == 0) (which == 0 ? k_scale : v_scale)[srow] = sc;
     }
 }
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(CacheArgs a, cons
     const char* vp = static_cast<const char*>(a.v_pool);
     u32x4 kbuf[kCopyVecsPerThread], vbuf[kCopyVecsPerThread];
     auto addr = [&](size_t idx, int blk) -> size_t {  // byte offset of vector idx
-        return idx < block_vecs0 ? ((size_t)blk * block_vecs0 + idx) * 16
+        return idx < block_vecs0 ? (size_t)blk * a.block_stride + idx * 16
                                  : ((size_t)blk * block_vecs1 + (idx - block_vecs0)) * 16;
     };
     const size_t total = block_vecs0 + block_vecs1;

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     ident.y = ((4 * g + 2 == n) ? M::kOne : 0u) | (((4 * g + 3 == n) ? M::kOne : 0u) << 16);
 
     const size_t head_bytes = (size_t)bs * D * KV::kBytes;
-    const size_t block_bytes = head_bytes * a.num_kv_heads;
+    const size_t block_bytes = (size_t)a.block_stride;
     const char* kpool = static_cast<const char*>(a.k_pool);
     const char* vpool = static_cast<const char*>(a.v_pool);
     const uint32_t slab_bytes = (uint32_t)head_bytes;

@@ -82,7 +82,7 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
     const int g0 = rel_lo / RPL;  // first row group holding an attended token
 
     const size_t head_bytes = (size_t)bs * D * KV::kBytes;
-    const size_t block_bytes = head_bytes * a.num_kv_heads;
+    const size_t block_bytes = (size_t)a.block_stride;
     const char* kpool = static_cast<const char*>(a.k_pool);
     const char* vpool = static_cast<const char*>(a.v_pool);
     constexpr int kTokPerIter = UNROLL * STRIDE * RPL;

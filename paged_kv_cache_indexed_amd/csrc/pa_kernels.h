@@ -35,6 +35,7 @@ struct DecodeArgs {
     int32_t max_partitions;
     int32_t window;    // > 0: attend to the last `window` tokens only; 0: the whole context
     float scale_log2;  // scale * log2(e): scores live in the base-2 exponent domain
+    int64_t block_stride;  // bytes from one physical block to the next in k_pool / v_pool
 };
 
 struct CacheArgs {
@@ -44,7 +45,8 @@ struct CacheArgs {
     int32_t num_blocks;
     int32_t log2_block_size;
     int32_t num_kv_heads;
-    int32_t row_vecs;  // 16-byte vectors per [head_dim] row
+    int32_t row_vecs;      // 16-byte vectors per [head_dim] row
+    int64_t block_stride;  // bytes from one physical block to the next in k_pool / v_pool
 };
 
 // VALU decode (every dtype and group size). kv_dtype is the pool's element type, dtype the

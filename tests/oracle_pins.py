@@ -398,9 +398,101 @@ def pin_sliding_window(o):
             assert np.array_equal(last[b, h], c["vc"][b][L - 1, h // (Hq // Hkv)].astype(np.float64))
 
 
+def pin_multilayer_pools(o):
+    """One allocation [blocks][2][layers][heads][bs][d] (K/V in dim 1): each layer's pools,
+    taken as views, decode to the brute force over that layer's contiguous contents."""
+    lens, Hq, Hkv, d, bs, nl = [3, 9, 14], 4, 2, 4, 4, 3
+    rng = _rng(81)
+    nbs = [-(-L // bs) for L in lens]
+    nb = sum(nbs) + 2
+    perm = rng.permutation(nb)
+    table = np.full((len(lens), max(nbs)), -1, np.int32)
+    cur = 0
+    for b, n in enumerate(nbs):
+        table[b, :n] = perm[cur:cur + n]
+        cur += n
+    cache = np.full((nb, 2, nl, Hkv, bs, d), np.nan, np.float64)
+    contents = {}
+    for layer in range(nl):
+        for kv in range(2):
+            for b, L in enumerate(lens):
+                x = rng.standard_normal((L, Hkv, d))
+                contents[(layer, kv, b)] = x
+                for t in range(L):
+                    for h in range(Hkv):
+                        for e in range(d):
+                            cache[table[b, t // bs], kv, layer, h, t % bs, e] = x[t, h, e]
+    q = rng.standard_normal((len(lens), Hq, d))
+    for layer in range(nl):
+        k, v = o.layer_pools(cache, layer)
+        assert k.shape == (nb, Hkv, bs, d) and np.shares_memory(k, cache)
+        assert k.strides[0] == 2 * nl * Hkv * bs * d * 8, "blocks are 2 x layers slabs apart"
+        got = o.paged_decode(q, k, v, table, np.array(lens), 0.5)
+        ref = _brute_decode(q, [contents[(layer, 0, b)] for b in range(len(lens))],
+                            [contents[(layer, 1, b)] for b in range(len(lens))], lens, 0.5, Hq, Hkv)
+        _close(got, ref, 1e-12, f"layer {layer}")
+
+
+def pin_reblock(o):
+    """Re-blocking moves every valid row, in order, into the new tables' blocks of the new
+    size: each sequence gathers back to its contiguous contents bit for bit, nothing else is
+    written, and the decode is bitwise unchanged."""
+    lens, Hq, Hkv, d, bs = [1, 4, 7, 13], 2, 2, 3, 4
+    c = _make_case(82, lens, Hq, Hkv, d, bs)
+    base = o.paged_decode(c["q"], c["k_pool"], c["v_pool"], c["table"], c["lens"], 0.7)
+    for nbs in (1, 2, 8, 16):
+        need = [-(-L // nbs) for L in lens]
+        nnb = sum(need) + 3
+        perm = _rng(83, nbs).permutation(nnb)
+        ntab = np.full((len(lens), max(need) + 1), -1, np.int32)
+        cur = 0
+        for b, n in enumerate(need):
+            ntab[b, :n] = perm[cur:cur + n]
+            cur += n
+        nk = o.reblock(c["k_pool"], c["table"], c["lens"], nbs, ntab, nnb)
+        nv = o.reblock(c["v_pool"], c["table"], c["lens"], nbs, ntab, nnb)
+        assert nk.shape == (nnb, Hkv, nbs, d)
+        for b, L in enumerate(lens):
+            for h in range(Hkv):
+                assert np.array_equal(o.gather_sequence(nk, ntab[b], L, h), c["kc"][b][:, h].astype(np.float64))
+                assert np.array_equal(o.gather_sequence(nv, ntab[b], L, h), c["vc"][b][:, h].astype(np.float64))
+        assert np.count_nonzero(~np.isnan(nk[..., 0])) == sum(lens) * Hkv, "only valid rows are written"
+        got = o.paged_decode(c["q"], nk, nv, ntab, c["lens"], 0.7)
+        assert np.array_equal(got, base), f"decode changed by re-blocking to {nbs}"
+    bad = np.full((len(lens), 1), 0, np.int32)
+    try:
+        o.reblock(c["k_pool"], c["table"], c["lens"], 4, bad, 10)
+    except o.OracleInputError:
+        pass
+    else:
+        raise AssertionError("a new table too narrow for the lengths must raise")
+
+
+def pin_compact_blocks(o):
+    """Compaction: live blocks move to the lowest ids, tables are rewritten, and the decode
+    and every gathered sequence are bitwise unchanged."""
+    lens, Hq, Hkv, d, bs = [5, 9, 2, 12], 4, 2, 4, 4
+    c = _make_case(84, lens, Hq, Hkv, d, bs, spare=7)
+    live = sorted({int(x) for x in c["table"].ravel() if x >= 0})
+    n_live = len(live)
+    free_low = [i for i in range(n_live) if i not in live]
+    high = [i for i in live if i >= n_live]
+    pairs = np.array(list(zip(high, free_low)), np.int32).reshape(-1, 2)
+    assert len(pairs) > 0
+    base = o.paged_decode(c["q"], c["k_pool"], c["v_pool"], c["table"], c["lens"], 0.4)
+    k2, v2, t2 = o.compact_blocks(c["k_pool"], c["v_pool"], c["table"], pairs)
+    assert {int(x) for x in t2.ravel() if x >= 0} == set(range(n_live)), "live blocks must end up in [0, n_live)"
+    assert np.array_equal(t2 < 0, c["table"] < 0)
+    got = o.paged_decode(c["q"], k2, v2, t2, c["lens"], 0.4)
+    assert np.array_equal(got, base), "compaction changed the decode"
+    for b, L in enumerate(lens):
+        for h in range(Hkv):
+            assert np.array_equal(o.gather_sequence(k2, t2[b], L, h), c["kc"][b][:, h].astype(np.float64))
+
+
 ALL_PINS = [pin_gather_roundtrip, pin_worked_example, pin_memory_formula, pin_bruteforce,
             pin_closed_forms, pin_invariants, pin_sdpa, pin_reshape_and_cache, pin_copy_blocks,
-            pin_errors, pin_sliding_window]
+            pin_errors, pin_sliding_window, pin_multilayer_pools, pin_reblock, pin_compact_blocks]
 
 
 # ---- 8-bit float (OCP E4M3) blocks with a scale per row: pins take oracle.fp8_cache --------

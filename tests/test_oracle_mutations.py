@@ -150,6 +150,36 @@ def m_blocks_floor(L, bs):
     return int(L) // int(bs)
 
 
+def m_layer_pools_kv_swapped(cache, layer):
+    return cache[:, 1, int(layer)], cache[:, 0, int(layer)]
+
+
+def m_layer_pools_layer_zero(cache, layer):
+    return cache[:, 0, 0], cache[:, 1, 0]
+
+
+def m_reblock_identity_table(pool, table, lens, nbs, new_table, nnb):
+    ident = np.tile(np.arange(np.shape(new_table)[1], dtype=np.int32), (len(lens), 1))
+    return pa.__dict__["_orig_reblock"](pool, table, lens, nbs, ident, nnb)
+
+
+def m_reblock_shifted(pool, table, lens, nbs, new_table, nnb):
+    out = pa.__dict__["_orig_reblock"](pool, table, lens, nbs, new_table, nnb)
+    return np.roll(out, 1, axis=2)
+
+
+def m_compact_no_relabel(k_pool, v_pool, table, pairs):
+    k2, v2, _ = pa.__dict__["_orig_compact_blocks"](k_pool, v_pool, table, pairs)
+    return k2, v2, np.array(table, copy=True)
+
+
+def m_compact_copy_reversed(k_pool, v_pool, table, pairs):
+    p = np.asarray(pairs).reshape(-1, 2)[:, ::-1]
+    k2, v2 = pa.__dict__["_orig_copy_blocks"](k_pool, v_pool, p)
+    _, _, t2 = pa.__dict__["_orig_compact_blocks"](k_pool, v_pool, table, pairs)
+    return k2, v2, t2
+
+
 MUTANTS = {
     "drop_scale": ("attention_one_query", m_drop_scale),
     "softmin": ("attention_one_query", m_softmin),
@@ -172,6 +202,12 @@ MUTANTS = {
     "copy_reversed": ("copy_blocks", m_copy_reversed),
     "bytes_no_factor2": ("kv_cache_bytes", m_bytes_no_factor2),
     "blocks_floor": ("blocks_needed", m_blocks_floor),
+    "layer_pools_kv_swapped": ("layer_pools", m_layer_pools_kv_swapped),
+    "layer_pools_layer_zero": ("layer_pools", m_layer_pools_layer_zero),
+    "reblock_identity_table": ("reblock", m_reblock_identity_table),
+    "reblock_shifted": ("reblock", m_reblock_shifted),
+    "compact_no_relabel": ("compact_blocks", m_compact_no_relabel),
+    "compact_copy_reversed": ("compact_blocks", m_compact_copy_reversed),
 }
 
 
@@ -179,7 +215,7 @@ MUTANTS = {
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
     for orig in ("paged_decode", "reshape_and_cache", "copy_blocks", "kv_cache_bytes",
-                 "paged_decode_window"):
+                 "paged_decode_window", "reblock", "compact_blocks"):
         monkeypatch.setitem(pa.__dict__, "_orig_" + orig, getattr(pa, orig))
     monkeypatch.setattr(pa, attr, fn)
     failed = []
