@@ -230,6 +230,62 @@ def _fp8_pools(kp, vp):
     return k8, v8, ks, vs
 
 
+def _bench_reblock(args, w, t, kps, vps, R, dev) -> int:
+    """Time pa_reblock of the workload's cache (context_lens tokens per sequence) into a new
+    layout of block size args.reblock; bytes = the valid K+V rows read plus written."""
+    import torch
+
+    from paged_kv_cache_indexed_amd import ops
+
+    if args.kv == "fp8":
+        print("--reblock times 16/32-bit pools only", file=sys.stderr)
+        return 2
+    nbs = int(args.reblock)
+    lens_np = w.context_lens
+    need = -(-lens_np // nbs)
+    nnb = int(need.sum())
+    perm = np.random.default_rng([7, nbs]).permutation(nnb).astype(np.int32)
+    ntab = np.full((w.batch, int(need.max())), -1, np.int32)
+    cur = 0
+    for b, n in enumerate(need.tolist()):
+        ntab[b, :n] = perm[cur:cur + n]
+        cur += n
+    shape = (nnb,) + tuple(t["k_pool"].shape[1:2]) + (nbs,) + tuple(t["k_pool"].shape[3:])
+    dk = torch.empty(shape, dtype=kps[0].dtype, device=dev)
+    dv = torch.empty_like(dk)
+    ntab_d = torch.from_numpy(ntab).to(dev)
+    lens = t["context_lens"]
+    max_len = int(lens_np.max())
+    moved = 2 * 2 * w.num_kv_heads * w.head_dim * kps[0].element_size() * int(lens_np.sum())
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        ops.reblock(kps[i % R], vps[i % R], t["block_table"], dk, dv, ntab_d, lens, max_len)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        ops.reblock(kps[i % R], vps[i % R], t["block_table"], dk, dv, ntab_d, lens, max_len)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    achieved = moved / (ms.mean() * 1e-3) / 1e9
+    cfg = _describe(w)
+    cfg.update({"workload": f"{w.name}-reblock{w.block_size}to{nbs}", "new_block_size": nbs, "replicas": R,
+                "step": "pa_reblock of every valid K/V row to the new layout"})
+    print(json.dumps({
+        "metric": "re-blocking GB/s (valid K+V rows read + written) at 1 MI355X",
+        "value": round(moved / (wall / args.steps) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": cfg,
+        "kernel_ms": {"mean": round(float(ms.mean()), 5), "p50": round(float(np.percentile(ms, 50)), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +297,10 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--kv", choices=["native", "fp8"], default="native",
                     help="pool elements: the workload's dtype, or 8-bit floats with a scale per row")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="run the step on one layer's strided view of a [blocks][2][layers][heads][bs][d] cache")
+    ap.add_argument("--reblock", type=int, default=0,
+                    help="instead of the step, time pa_reblock of the cache to this block size")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: attend to the last W tokens only (0: whole context)")
     ap.add_argument("--replica-bytes", type=float, default=1.5 * 2 ** 30,
@@ -283,9 +343,21 @@ def main() -> int:
         pool_bytes = 2 * (k8.numel() + 4 * ks8.numel())
     else:
         pool_bytes = 2 * t["k_pool"].numel() * t["k_pool"].element_size()
-    R = max(2, math.ceil(args.replica_bytes / pool_bytes))
-    kps = [t["k_pool"]] + [t["k_pool"].clone() for _ in range(R - 1)]
-    vps = [t["v_pool"]] + [t["v_pool"].clone() for _ in range(R - 1)]
+    NL = max(1, args.layers)
+    R = max(2, math.ceil(args.replica_bytes / (pool_bytes * NL)))
+    if NL > 1:
+        # one allocation per replica holding NL layers' K and V; the step reads the last layer
+        def layered(kp, vp):
+            cache = torch.zeros((kp.shape[0], 2, NL) + tuple(kp.shape[1:]), dtype=kp.dtype, device=dev)
+            cache[:, 0, NL - 1].copy_(kp)
+            cache[:, 1, NL - 1].copy_(vp)
+            return cache
+        caches = [layered(t["k_pool"], t["v_pool"]) for _ in range(R)]
+        kps = [c[:, 0, NL - 1] for c in caches]
+        vps = [c[:, 1, NL - 1] for c in caches]
+    else:
+        kps = [t["k_pool"]] + [t["k_pool"].clone() for _ in range(R - 1)]
+        vps = [t["v_pool"]] + [t["v_pool"].clone() for _ in range(R - 1)]
     if fp8:
         kss = [ks8] + [ks8.clone() for _ in range(R - 1)]
         vss = [vs8] + [vs8.clone() for _ in range(R - 1)]
@@ -332,6 +404,8 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.reblock:
+        return _bench_reblock(args, w, t, kps, vps, R, dev)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -352,8 +426,11 @@ def main() -> int:
     part = _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, w.num_q_heads,
                                          span, P)
     cfg = _describe(w)
+    if NL > 1:
+        cfg["workload"] = f"{w.name}-layer{NL - 1}of{NL}"
+        cfg["block_stride_bytes"] = int(kps[0].stride(0) * kps[0].element_size())
     if fp8:
-        cfg["workload"] = f"{w.name}-fp8"
+        cfg["workload"] = f"{cfg['workload']}-fp8"
         cfg["kv_storage"] = "OCP E4M3 codes + float32 scale per (token, kv head) row"
     if W > 0:
         cfg["workload"] = f"{cfg['workload']}-window{W}"

@@ -248,6 +248,30 @@ pa_status_t pa_decode_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* o
                           int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* err_flag,
                           pa_stream_t stream);
 
+/*
+ * pa_reblock - migrate a paged cache to another block size.
+ *
+ * A new block size invalidates every block table, so the contents move to the new layout
+ * ([CANN paging article] §4.1). For every sequence b and token t < context_lens[b], the K
+ * and V rows of every kv head are copied bit for bit from block src_table[b][t /
+ * src->block_size], offset t % src->block_size, of (src_k, src_v) to block dst_table[b][t /
+ * dst->block_size], offset t % dst->block_size, of (dst_k, dst_v). With 8-bit pools the row
+ * scales move too (all four scale pointers non-NULL; else they must be NULL). Other slots of
+ * the destination are not written.
+ *
+ * Both descriptors must agree on num_kv_heads, head_dim and dtype; block sizes, pool sizes
+ * and strides may differ. The two caches must not overlap, and no two tokens may share a
+ * destination slot (caller error: they race). A sequence with context_len <= 0 moves
+ * nothing; context_len > max_context_len or past either table's width skips the sequence
+ * and sets PA_FLAG_BAD_LENGTH; an id outside its pool skips that token and sets
+ * PA_FLAG_BAD_BLOCK_ID.
+ */
+pa_status_t pa_reblock(const pa_cache_desc_t* src, const void* src_k, const void* src_v, const float* src_k_scale,
+                       const float* src_v_scale, const int32_t* src_table, int32_t src_max_blocks_per_seq,
+                       const pa_cache_desc_t* dst, void* dst_k, void* dst_v, float* dst_k_scale, float* dst_v_scale,
+                       const int32_t* dst_table, int32_t dst_max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t batch, int32_t max_context_len, int32_t* err_flag, pa_stream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* pa_status_string(pa_status_t status);
 

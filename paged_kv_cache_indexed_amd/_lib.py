@@ -29,7 +29,7 @@ PA_FLAG_BAD_COPY_PAIR = 16
 EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_size",
             "pa_decode_workspace_bytes", "pa_decode", "pa_decode_sliding_window",
             "pa_decode_sliding_window_workspace_bytes", "pa_reshape_and_cache_fp8",
-            "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_status_string")
+            "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_reblock", "pa_status_string")
 
 # 8-bit float pools are uint8 (or float8_e4m3fn) tensors of OCP E4M3 codes.
 _DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
@@ -105,6 +105,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_copy_blocks_fp8.restype = ctypes.c_int
     lib.pa_decode_fp8.argtypes = [D, I32, P, P, P, P, P, P, P, I32, P, I32, I32, I32, F, I32, I32, P, SZ, P, P]
     lib.pa_decode_fp8.restype = ctypes.c_int
+    lib.pa_reblock.argtypes = [D, P, P, P, P, P, I32, D, P, P, P, P, P, I32, P, I32, I32, P, P]
+    lib.pa_reblock.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -248,3 +250,14 @@ def pa_decode_fp8(cache: CacheDesc, out, q, k_pool, v_pool, k_scale, v_scale, bl
         _ptr(v_scale), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), batch, num_q_heads,
         int(max_context_len), float(scale), int(window), int(partition_size), _ptr(workspace), ws_bytes,
         _ptr(err_flag), _stream(stream)))
+
+
+def pa_reblock(src: CacheDesc, src_k, src_v, src_table, dst: CacheDesc, dst_k, dst_v, dst_table, context_lens,
+               max_context_len: int, src_k_scale=None, src_v_scale=None, dst_k_scale=None, dst_v_scale=None,
+               err_flag=None, stream=None) -> None:
+    sd, dd = src.c(), dst.c()
+    _check(load().pa_reblock(
+        ctypes.byref(sd), _pool_ptr(src_k), _pool_ptr(src_v, src_k), _ptr(src_k_scale), _ptr(src_v_scale),
+        _ptr(src_table), int(src_table.shape[1]), ctypes.byref(dd), _pool_ptr(dst_k), _pool_ptr(dst_v, dst_k),
+        _ptr(dst_k_scale), _ptr(dst_v_scale), _ptr(dst_table), int(dst_table.shape[1]), _ptr(context_lens),
+        int(context_lens.numel()), int(max_context_len), _ptr(err_flag), _stream(stream)))

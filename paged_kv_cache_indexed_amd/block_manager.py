@@ -20,7 +20,10 @@ Rules from the pages:
     the pool only at zero ([KV Block course] §3.4); every exit path releases them, including
     cancellation, through a context manager ([BlockManager essay] §4.2);
   * a sequence about to write into a block it shares gets a private copy first (copy-on-
-    write); the sequence that forks keeps the original.
+    write); the sequence that forks keeps the original;
+  * defragmentation moves the live blocks into one contiguous range of ids and rewrites the
+    tables ([CANN paging article] §5.1); changing the block size needs a new layout and a
+    migration of the contents ([CANN paging article] §4.1).
 """
 
 from __future__ import annotations
@@ -160,6 +163,55 @@ class BlockManager:
             slots.append(s.blocks[j] * bs + off)
         s.length += n
         return np.array(slots, np.int32), pairs
+
+    # -------------------------------------------------------------- maintenance
+    def num_live(self) -> int:
+        return int(np.count_nonzero(self.ref_count))
+
+    def is_compact(self) -> bool:
+        """Every live block has an id below the number of live blocks."""
+        return bool(np.all(self.ref_count[self.num_live():] == 0))
+
+    def compact(self) -> np.ndarray:
+        """Defragment: move every live block with an id >= the number of live blocks into a
+        free id below it ([CANN paging article] §5.1: compact the active blocks into one
+        region, then update the mapping), and rewrite the tables and reference counts.
+
+        Returns int32 pairs (src, dst) for pa_copy_blocks. Every dst is free and every src is
+        live, so the pairs may run in parallel; the device copy must complete before the new
+        tables (block_table) are used, and the moved sources are free afterwards. Afterwards
+        the free list hands out the lowest ids first.
+        """
+        n_live = self.num_live()
+        movers = [int(i) for i in np.nonzero(self.ref_count[n_live:])[0] + n_live]
+        holes = [int(i) for i in np.nonzero(self.ref_count[:n_live] == 0)[0]]
+        assert len(movers) == len(holes)
+        mapping = dict(zip(movers, holes))
+        for s in self._seqs.values():
+            s.blocks = [mapping.get(b, b) for b in s.blocks]
+        for src, dst in mapping.items():
+            self.ref_count[dst] = self.ref_count[src]
+            self.ref_count[src] = 0
+        self._free = list(range(self.num_blocks - 1, n_live - 1, -1))
+        return np.array(list(mapping.items()), np.int32).reshape(-1, 2)
+
+    def reblocked(self, block_size: int, num_blocks: int | None = None,
+                  max_blocks_per_seq: int | None = None) -> "BlockManager":
+        """A manager for a new pool of another block size that holds the same sequences with
+        the same lengths ([CANN paging article] §4.1). Each sequence gets private blocks in
+        the new pool (blocks of two sizes do not line up, so sharing is not carried over).
+        Pass both managers' block_table() for the same sequence order to pa_reblock.
+        """
+        bs = int(block_size)
+        need = {sid: -(-s.length // bs) for sid, s in self._seqs.items()}
+        nb = int(num_blocks) if num_blocks is not None else max(1, sum(need.values()))
+        mbs = int(max_blocks_per_seq) if max_blocks_per_seq is not None else max([1, *need.values()])
+        new = BlockManager(nb, bs, mbs)
+        for sid, s in self._seqs.items():
+            new.add_sequence(sid)
+            if s.length:
+                new.append_slots(sid, s.length)
+        return new
 
     # -------------------------------------------------------------- device inputs
     def block_table(self, seq_ids) -> np.ndarray:

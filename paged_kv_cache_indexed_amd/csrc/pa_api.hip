@@ -145,6 +145,40 @@ pa_status_t pa_copy_blocks_fp8(const pa_cache_desc_t* cache, void* k_pool, void*
     return from_hip(launch_copy_blocks(a, pairs, num_pairs, k_scale, v_scale, (hipStream_t)stream));
 }
 
+pa_status_t pa_reblock(const pa_cache_desc_t* src, const void* src_k, const void* src_v, const float* src_k_scale,
+                       const float* src_v_scale, const int32_t* src_table, int32_t src_max_blocks_per_seq,
+                       const pa_cache_desc_t* dst, void* dst_k, void* dst_v, float* dst_k_scale, float* dst_v_scale,
+                       const int32_t* dst_table, int32_t dst_max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t batch, int32_t max_context_len, int32_t* err_flag, pa_stream_t stream) {
+    pa_status_t st = check_cache(src);
+    if (st != PA_OK) return st;
+    if ((st = check_cache(dst)) != PA_OK) return st;
+    if (src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim || src->dtype != dst->dtype)
+        return PA_ERR_INVALID_ARGUMENT;
+    if (batch < 0 || batch > 65535 || max_context_len < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (batch == 0 || max_context_len == 0) return PA_OK;
+    if (!src_k || !src_v || !src_table || !dst_k || !dst_v || !dst_table || !context_lens)
+        return PA_ERR_INVALID_ARGUMENT;
+    if (src_max_blocks_per_seq <= 0 || dst_max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v)) return PA_ERR_INVALID_ARGUMENT;
+    const bool scaled = is_fp8(src);
+    const bool any_scale = src_k_scale || src_v_scale || dst_k_scale || dst_v_scale;
+    if (scaled) {
+        if (!src_k_scale || !src_v_scale || !dst_k_scale || !dst_v_scale) return PA_ERR_INVALID_ARGUMENT;
+        if (!aligned4(src_k_scale) || !aligned4(src_v_scale) || !aligned4(dst_k_scale) || !aligned4(dst_v_scale))
+            return PA_ERR_INVALID_ARGUMENT;
+    } else if (any_scale) {
+        return PA_ERR_INVALID_ARGUMENT;
+    }
+    ReblockArgs a{static_cast<const char*>(src_k), static_cast<const char*>(src_v), src_k_scale, src_v_scale,
+                  src_table, static_cast<char*>(dst_k), static_cast<char*>(dst_v), dst_k_scale, dst_v_scale,
+                  dst_table, context_lens, err_flag, block_stride(src), block_stride(dst), src->num_blocks,
+                  dst->num_blocks, log2_exact(src->block_size), log2_exact(dst->block_size), src_max_blocks_per_seq,
+                  dst_max_blocks_per_seq, src->num_kv_heads, src->head_dim * dtype_bytes(src->dtype) / 16,
+                  max_context_len};
+    return from_hip(launch_reblock(a, batch, (hipStream_t)stream));
+}
+
 int32_t pa_decode_partition_size(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_heads,
                                  int32_t max_context_len, int32_t requested) {
     if (check_cache(cache) != PA_OK || batch < 0 || max_context_len <= 0 || num_q_heads <= 0) return -1;

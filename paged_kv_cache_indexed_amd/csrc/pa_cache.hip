@@ -136,6 +136,49 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(CacheArgs a, cons
     }
 }
 
+// Re-blocking. Grid (row chunks, sequences): thread i of sequence b moves 16-byte vector
+// i % row_vecs of kv head (i / row_vecs) % heads of token i / (heads * row_vecs), for K and
+// V, looking the token's block up in both tables; with 8-bit pools the thread holding a
+// row's first vector also moves its two scales.
+__global__ __launch_bounds__(kThreads) void reblock_kernel(ReblockArgs a) {
+    const int b = blockIdx.y;
+    const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    const int L = a.context_lens[b];
+    if (L <= 0) return;
+    if (L > a.max_context_len || ((L - 1) >> a.src_log2_bs) >= a.src_mbs || ((L - 1) >> a.dst_log2_bs) >= a.dst_mbs) {
+        if (i == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_LENGTH);
+        return;
+    }
+    const size_t per_token = (size_t)a.num_kv_heads * a.row_vecs;
+    const int t = (int)(i / per_token);
+    if (t >= L) return;
+    const int rem = (int)(i - (size_t)t * per_token);
+    const int h = rem / a.row_vecs;
+    const int v = rem - h * a.row_vecs;
+    const int sid = a.src_table[(size_t)b * a.src_mbs + (t >> a.src_log2_bs)];
+    const int did = a.dst_table[(size_t)b * a.dst_mbs + (t >> a.dst_log2_bs)];
+    if ((unsigned)sid >= (unsigned)a.src_num_blocks || (unsigned)did >= (unsigned)a.dst_num_blocks) {
+        if (v == 0 && h == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_BLOCK_ID);
+        return;
+    }
+    const int soff = t & ((1 << a.src_log2_bs) - 1);
+    const int doff = t & ((1 << a.dst_log2_bs) - 1);
+    const size_t srow = ((size_t)h << a.src_log2_bs) + soff;  // row inside the block
+    const size_t drow = ((size_t)h << a.dst_log2_bs) + doff;
+    const size_t so = (size_t)sid * a.src_stride + (srow * a.row_vecs + v) * 16;
+    const size_t dof = (size_t)did * a.dst_stride + (drow * a.row_vecs + v) * 16;
+    const u32x4 kv = load16(a.src_k + so);
+    const u32x4 vv = load16(a.src_v + so);
+    store16(a.dst_k + dof, kv);
+    store16(a.dst_v + dof, vv);
+    if (a.src_ks && v == 0) {
+        const size_t ss = ((size_t)sid * a.num_kv_heads << a.src_log2_bs) + srow;
+        const size_t ds = ((size_t)did * a.num_kv_heads << a.dst_log2_bs) + drow;
+        a.dst_ks[ds] = a.src_ks[ss];
+        a.dst_vs[ds] = a.src_vs[ss];
+    }
+}
+
 template <typename S>
 hipError_t launch_fp8_append_s(const CacheArgs& a, int head_dim, const void* key, const void* value, float* k_scale,
                                float* v_scale, const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream,
@@ -173,6 +216,14 @@ hipError_t launch_copy_blocks(const CacheArgs& a, const int32_t* pairs, int32_t 
     if (chunks > 65535) return hipErrorInvalidValue;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, (unsigned)chunks), dim3(kThreads), 0, stream, a, pairs,
                        reinterpret_cast<char*>(k_scale), reinterpret_cast<char*>(v_scale), block_vecs1);
+    return hipGetLastError();
+}
+
+hipError_t launch_reblock(const ReblockArgs& a, int batch, hipStream_t stream) {
+    const size_t threads = (size_t)a.max_context_len * a.num_kv_heads * a.row_vecs;
+    const size_t blocks = (threads + kThreads - 1) / kThreads;
+    if (blocks > 0x7fffffff || batch > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(reblock_kernel, dim3((unsigned)blocks, (unsigned)batch), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

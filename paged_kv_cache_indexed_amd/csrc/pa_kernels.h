@@ -71,6 +71,35 @@ hipError_t launch_reshape_and_cache(const CacheArgs& a, const void* key, const v
 hipError_t launch_copy_blocks(const CacheArgs& a, const int32_t* pairs, int32_t num_pairs, float* k_scale,
                               float* v_scale, hipStream_t stream);
 
+// Re-blocking: every valid (token, kv head) row moves from the source layout to the
+// destination layout (block size, stride and pool may differ; heads, dims and dtype agree).
+struct ReblockArgs {
+    const char* src_k;
+    const char* src_v;
+    const float* src_ks;  // 8-bit pools only
+    const float* src_vs;
+    const int32_t* src_table;
+    char* dst_k;
+    char* dst_v;
+    float* dst_ks;
+    float* dst_vs;
+    const int32_t* dst_table;
+    const int32_t* context_lens;
+    int32_t* err_flag;
+    int64_t src_stride;  // bytes between blocks
+    int64_t dst_stride;
+    int32_t src_num_blocks;
+    int32_t dst_num_blocks;
+    int32_t src_log2_bs;
+    int32_t dst_log2_bs;
+    int32_t src_mbs;  // table widths
+    int32_t dst_mbs;
+    int32_t num_kv_heads;
+    int32_t row_vecs;  // 16-byte vectors per row
+    int32_t max_context_len;
+};
+hipError_t launch_reblock(const ReblockArgs& a, int batch, hipStream_t stream);
+
 // Quantising append into 8-bit pools: src_dtype is the type of key/value rows.
 hipError_t launch_reshape_and_cache_fp8(const CacheArgs& a, int src_dtype, int head_dim, const void* key,
                                         const void* value, float* k_scale, float* v_scale,

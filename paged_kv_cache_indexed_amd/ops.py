@@ -9,7 +9,7 @@ import torch
 
 from ._lib import (CacheDesc, pa_copy_blocks, pa_copy_blocks_fp8, pa_decode, pa_decode_fp8,
                    pa_decode_sliding_window, pa_decode_sliding_window_workspace_bytes,
-                   pa_decode_workspace_bytes, pa_reshape_and_cache, pa_reshape_and_cache_fp8)
+                   pa_decode_workspace_bytes, pa_reblock, pa_reshape_and_cache, pa_reshape_and_cache_fp8)
 
 
 def workspace_for(k_pool: torch.Tensor, batch: int, num_q_heads: int, max_context_len: int,
@@ -90,3 +90,12 @@ def reshape_and_cache_fp8(key, value, k_pool, v_pool, k_scale, v_scale, slot_map
 
 def copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, pairs, err_flag=None, stream=None):
     pa_copy_blocks_fp8(CacheDesc.of(k_pool), k_pool, v_pool, k_scale, v_scale, pairs, err_flag, stream)
+
+
+def reblock(src_k, src_v, src_table, dst_k, dst_v, dst_table, context_lens, max_context_len: int,
+            scales=None, err_flag=None, stream=None):
+    """Copy every valid row from one paged layout to another (another block size); ``scales``
+    = (src_k_scale, src_v_scale, dst_k_scale, dst_v_scale) for 8-bit pools."""
+    sk = scales if scales is not None else (None, None, None, None)
+    pa_reblock(CacheDesc.of(src_k), src_k, src_v, src_table, CacheDesc.of(dst_k), dst_k, dst_v, dst_table,
+               context_lens, max_context_len, *sk, err_flag=err_flag, stream=stream)

@@ -190,3 +190,57 @@ def test_manager_slots_drive_the_oracle_cache():
         for h in range(H):
             got = oracle.gather_sequence(kp, t[r], bm.length(sid), h)
             assert np.array_equal(got, contents[sid][:, h].astype(np.float64))
+
+
+def _fragmented(seed=0, nb=64, bs=4):
+    rng = np.random.default_rng(seed)
+    bm = BlockManager(nb, bs, 16, shuffle_seed=seed)
+    for sid in range(10):
+        bm.add_sequence(sid)
+        bm.append_slots(sid, int(rng.integers(1, 20)))
+    bm.fork(2, 100)  # shared blocks move as one
+    bm.append_slots(100, 3)
+    for sid in (1, 4, 7):
+        bm.free_sequence(sid)
+    return bm
+
+
+def test_compact_moves_live_blocks_to_the_front_and_keeps_contents():
+    import oracle
+
+    bm = _fragmented()
+    seqs = sorted(bm._seqs)
+    before = bm.block_table(seqs)
+    lens = bm.context_lens(seqs)
+    assert not bm.is_compact()
+    rng = np.random.default_rng(1)
+    pool_k = rng.standard_normal((bm.num_blocks, 2, bm.block_size, 3))
+    pool_v = rng.standard_normal((bm.num_blocks, 2, bm.block_size, 3))
+    live_before = set(np.nonzero(bm.ref_count)[0].tolist())
+    pairs = bm.compact()
+    bm.check_invariants()
+    assert bm.is_compact()
+    assert {int(s) for s in pairs[:, 0]} <= live_before
+    assert not ({int(d) for d in pairs[:, 1]} & live_before), "a destination must be free"
+    after = bm.block_table(seqs)
+    k2, v2, t2 = oracle.compact_blocks(pool_k, pool_v, before, pairs)
+    assert np.array_equal(t2, after), "the planner's tables must equal the relabelled tables"
+    for r, L in enumerate(lens):
+        for h in range(2):
+            assert np.array_equal(oracle.gather_sequence(k2, after[r], L, h),
+                                  oracle.gather_sequence(pool_k, before[r], L, h))
+    assert bm.allocate_block() == bm.num_live() - 1  # the lowest free id comes next
+    assert len(bm.compact()) == 0 or bm.is_compact()
+
+
+def test_reblocked_manager_holds_the_same_sequences():
+    bm = _fragmented(3)
+    seqs = sorted(bm._seqs)
+    for bs in (1, 2, 8, 32):
+        nb2 = bm.reblocked(bs)
+        nb2.check_invariants()
+        assert np.array_equal(nb2.context_lens(seqs), bm.context_lens(seqs))
+        t = nb2.block_table(seqs)
+        for r, L in enumerate(bm.context_lens(seqs)):
+            n = -(-int(L) // bs)
+            assert np.all(t[r, :n] >= 0) and np.all(t[r, n:] == -1)
