@@ -17,6 +17,7 @@ from .paged_attention import (  # noqa: F401
     gather_sequence,
     kv_cache_bytes,
     layer_pools,
+    paged_attention_multi,
     paged_decode,
     paged_decode_heads,
     paged_decode_window,

@@ -259,3 +259,39 @@ def compact_blocks(k_pool, v_pool, block_table, pairs):
         if int(pid) in moved:
             table[idx] = moved[int(pid)]
     return k_new, v_new, table
+
+
+def paged_attention_multi(q, k_pool, v_pool, block_table, context_lens, query_start, scale) -> np.ndarray:
+    """Several new query tokens per sequence over a paged cache, causally masked: float64
+    [num_q_tokens][Hq][d].
+
+    Sequence b owns query rows query_start[b] .. query_start[b+1]-1 (n_b tokens). Its cache
+    already holds those tokens, appended after the history, so its length L_b includes them
+    ([Valid-length essay] §2.2: each round's tokens are appended after the previous rounds').
+    Query i sits at position p = L_b - n_b + i and attends to tokens 0 .. p only: the causal
+    mask inside the valid range ([Valid-length essay] §4.2, key j visible to query i iff
+    j <= i). n_b = 1 is the single-query decode.
+    """
+    T, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    if Hq % Hkv:
+        raise OracleInputError(f"num_q_heads {Hq} not a multiple of num_kv_heads {Hkv}")
+    group = Hq // Hkv
+    qs = np.asarray(query_start, np.int64)
+    if qs[0] != 0 or qs[-1] != T or np.any(np.diff(qs) < 0):
+        raise OracleInputError("query_start must rise from 0 to the number of query rows")
+    out = np.full((T, Hq, d), np.nan, np.float64)
+    for b, L in enumerate(np.asarray(context_lens).tolist()):
+        n = int(qs[b + 1] - qs[b])
+        if n > L:
+            raise OracleInputError(f"sequence {b}: {n} new tokens > context length {L}")
+        if n == 0:
+            continue
+        for g in range(Hkv):
+            K = gather_sequence(k_pool, block_table[b], L, g)
+            V = gather_sequence(v_pool, block_table[b], L, g)
+            for i in range(n):
+                p = L - n + i
+                for h in range(g * group, (g + 1) * group):
+                    out[qs[b] + i, h] = attention_one_query(q[qs[b] + i, h], K[:p + 1], V[:p + 1], scale)
+    return out

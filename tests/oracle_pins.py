@@ -490,9 +490,55 @@ def pin_compact_blocks(o):
             assert np.array_equal(o.gather_sequence(k2, t2[b], L, h), c["kc"][b][:, h].astype(np.float64))
 
 
+def pin_multi_token(o):
+    """Several queries per sequence: one query equals the decode; a whole sequence of queries
+    equals torch's causal scaled_dot_product_attention (float64, CPU); brute force on tiny
+    cases; and a query's output does not depend on tokens after its position."""
+    import torch
+
+    lens, Hq, Hkv, d, bs = [1, 6, 11, 16], 4, 2, 8, 4
+    c = _make_case(85, lens, Hq, Hkv, d, bs)
+    scale = 0.45
+    rng = _rng(86)
+    # n = 1: the single-query decode, bit for bit
+    qs1 = np.arange(len(lens) + 1)
+    got = o.paged_attention_multi(c["q"], c["k_pool"], c["v_pool"], c["table"], c["lens"], qs1, scale)
+    assert np.array_equal(got, o.paged_decode(c["q"], c["k_pool"], c["v_pool"], c["table"], c["lens"], scale))
+    # mixed query counts against brute force over the causal prefix
+    ns = [1, 3, 0, 16]
+    qs = np.concatenate([[0], np.cumsum(ns)])
+    q = rng.standard_normal((int(qs[-1]), Hq, d))
+    got = o.paged_attention_multi(q, c["k_pool"], c["v_pool"], c["table"], c["lens"], qs, scale)
+    for b, (L, n) in enumerate(zip(lens, ns)):
+        for i in range(n):
+            p = L - n + i
+            ref = _brute_decode(q[qs[b] + i][None], [c["kc"][b][:p + 1]], [c["vc"][b][:p + 1]], [p + 1], scale,
+                                Hq, Hkv)[0]
+            _close(got[qs[b] + i], ref, 1e-12, f"seq {b} query {i}")
+    # n = L: causal attention over the whole sequence, torch's SDPA in float64
+    b = 3
+    L = lens[b]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[qs[b]:qs[b + 1]].transpose(1, 0, 2).astype(np.float64)),
+        torch.from_numpy(np.repeat(c["kc"][b].transpose(1, 0, 2), Hq // Hkv, axis=0).astype(np.float64)),
+        torch.from_numpy(np.repeat(c["vc"][b].transpose(1, 0, 2), Hq // Hkv, axis=0).astype(np.float64)),
+        is_causal=True, scale=scale).numpy().transpose(1, 0, 2)
+    _close(got[qs[b]:qs[b + 1]], ref, 1e-12, "causal SDPA")
+    # tokens after a query's position never matter: poison them
+    kp = c["k_pool"].copy()
+    vp = c["v_pool"].copy()
+    t_last = L - 1
+    kp[c["table"][b, t_last // bs], :, t_last % bs] = 1e6
+    vp[c["table"][b, t_last // bs], :, t_last % bs] = np.nan
+    got2 = o.paged_attention_multi(q, kp, vp, c["table"], c["lens"], qs, scale)
+    assert np.array_equal(got2[qs[b]:qs[b + 1] - 1], got[qs[b]:qs[b + 1] - 1]), "a later token leaked"
+    assert np.all(np.isnan(got2[qs[b + 1] - 1])), "the last query must see the last token"
+
+
 ALL_PINS = [pin_gather_roundtrip, pin_worked_example, pin_memory_formula, pin_bruteforce,
             pin_closed_forms, pin_invariants, pin_sdpa, pin_reshape_and_cache, pin_copy_blocks,
-            pin_errors, pin_sliding_window, pin_multilayer_pools, pin_reblock, pin_compact_blocks]
+            pin_errors, pin_sliding_window, pin_multilayer_pools, pin_reblock, pin_compact_blocks,
+            pin_multi_token]
 
 
 # ---- 8-bit float (OCP E4M3) blocks with a scale per row: pins take oracle.fp8_cache --------

@@ -180,6 +180,26 @@ def m_compact_copy_reversed(k_pool, v_pool, table, pairs):
     return k2, v2, t2
 
 
+def _multi_with_position(shift):
+    def paged_attention_multi(q, k_pool, v_pool, block_table, context_lens, query_start, scale):
+        T, Hq, d = q.shape
+        Hkv = k_pool.shape[1]
+        G = Hq // Hkv
+        qs = np.asarray(query_start)
+        out = np.full((T, Hq, d), np.nan)
+        for b, L in enumerate(context_lens):
+            n = int(qs[b + 1] - qs[b])
+            for g in range(Hkv):
+                K = _gather(k_pool, block_table[b], L, g)
+                V = _gather(v_pool, block_table[b], L, g)
+                for i in range(n):
+                    p = min(max(int(L) - n + i + shift(i, n, int(L)), 0), int(L) - 1)
+                    for h in range(g * G, (g + 1) * G):
+                        out[qs[b] + i, h] = _attn(q[qs[b] + i, h], K[:p + 1], V[:p + 1], scale)
+        return out
+    return paged_attention_multi
+
+
 MUTANTS = {
     "drop_scale": ("attention_one_query", m_drop_scale),
     "softmin": ("attention_one_query", m_softmin),
@@ -208,6 +228,9 @@ MUTANTS = {
     "reblock_shifted": ("reblock", m_reblock_shifted),
     "compact_no_relabel": ("compact_blocks", m_compact_no_relabel),
     "compact_copy_reversed": ("compact_blocks", m_compact_copy_reversed),
+    "multi_no_causal_mask": ("paged_attention_multi", _multi_with_position(lambda i, n, L: n - 1 - i)),
+    "multi_mask_one_short": ("paged_attention_multi", _multi_with_position(lambda i, n, L: -1)),
+    "multi_forgets_history": ("paged_attention_multi", _multi_with_position(lambda i, n, L: n - L)),
 }
 
 
