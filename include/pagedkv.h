@@ -272,6 +272,41 @@ pa_status_t pa_reblock(const pa_cache_desc_t* src, const void* src_k, const void
                        const int32_t* dst_table, int32_t dst_max_blocks_per_seq, const int32_t* context_lens,
                        int32_t batch, int32_t max_context_len, int32_t* err_flag, pa_stream_t stream);
 
+/*
+ * pa_multi_token_attention - several new query tokens per sequence over the paged cache.
+ *
+ * Sequence b owns query rows query_start[b] .. query_start[b+1]-1 of q and out
+ * ([num_q_tokens][num_q_heads][head_dim]): its n_b new tokens (a prefill chunk, a round of
+ * a multi-round conversation, or speculative tokens), whose K and V were already appended
+ * (pa_reshape_and_cache*) so that context_lens[b] includes them ([Valid-length essay] §2.2).
+ * Query i sits at position p = context_lens[b] - n_b + i and attends to tokens 0 .. p only,
+ * the causal mask inside the valid range ([Valid-length essay] §4.2):
+ *   out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . K_b[t]) V_b[t].
+ * n_b = 1 is pa_decode. query_start is int32 [batch + 1], non-decreasing from 0, with
+ * query_start[batch] <= num_q_tokens; rows outside every sequence are not written.
+ *
+ * Runs on the matrix cores: dtype f16/bf16 (q_dtype equal to it) or PA_FP8_E4M3 (q f16/bf16,
+ * k_scale/v_scale as in pa_decode_fp8); block_size >= 16; num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8, 16} (16 only with head_dim <= 128); else PA_ERR_UNSUPPORTED. max_query_len
+ * bounds every n_b and sizes the launch (batch * ceil(max_query_len * group / 16) <= 65535).
+ * A sequence with n_b > context_len, a bad length or n_b > max_query_len sets
+ * PA_FLAG_BAD_LENGTH (its rows NaN where the launch covers them); a bad block id sets
+ * PA_FLAG_BAD_BLOCK_ID and poisons that sequence's rows. Partitions and workspace work as
+ * for pa_decode; the workspace must hold pa_multi_token_workspace_bytes(...).
+ */
+pa_status_t pa_multi_token_attention(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
+                                     const void* k_pool, const void* v_pool, const float* k_scale,
+                                     const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, const int32_t* query_start, int32_t batch,
+                                     int32_t num_q_tokens, int32_t num_q_heads, int32_t max_context_len,
+                                     int32_t max_query_len, float scale, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream);
+
+/* Workspace bytes pa_multi_token_attention needs (0: none, or an invalid argument). */
+size_t pa_multi_token_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_tokens,
+                                      int32_t num_q_heads, int32_t max_context_len, int32_t max_query_len,
+                                      int32_t partition_size);
+
 /* Human-readable text for a status code (static storage). */
 const char* pa_status_string(pa_status_t status);
 

@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     pa_decode_sliding_window,
     pa_decode_sliding_window_workspace_bytes,
     pa_decode_workspace_bytes,
+    pa_multi_token_attention,
+    pa_multi_token_workspace_bytes,
     pa_reblock,
     pa_reshape_and_cache,
     pa_reshape_and_cache_fp8,

@@ -29,7 +29,8 @@ PA_FLAG_BAD_COPY_PAIR = 16
 EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_size",
             "pa_decode_workspace_bytes", "pa_decode", "pa_decode_sliding_window",
             "pa_decode_sliding_window_workspace_bytes", "pa_reshape_and_cache_fp8",
-            "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_reblock", "pa_status_string")
+            "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_reblock", "pa_multi_token_attention",
+            "pa_multi_token_workspace_bytes", "pa_status_string")
 
 # 8-bit float pools are uint8 (or float8_e4m3fn) tensors of OCP E4M3 codes.
 _DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
@@ -107,6 +108,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_fp8.restype = ctypes.c_int
     lib.pa_reblock.argtypes = [D, P, P, P, P, P, I32, D, P, P, P, P, P, I32, P, I32, I32, P, P]
     lib.pa_reblock.restype = ctypes.c_int
+    lib.pa_multi_token_attention.argtypes = [D, I32, P, P, P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32, F,
+                                             I32, P, SZ, P, P]
+    lib.pa_multi_token_attention.restype = ctypes.c_int
+    lib.pa_multi_token_workspace_bytes.argtypes = [D, I32, I32, I32, I32, I32, I32]
+    lib.pa_multi_token_workspace_bytes.restype = SZ
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -261,3 +267,24 @@ def pa_reblock(src: CacheDesc, src_k, src_v, src_table, dst: CacheDesc, dst_k, d
         _ptr(src_table), int(src_table.shape[1]), ctypes.byref(dd), _pool_ptr(dst_k), _pool_ptr(dst_v, dst_k),
         _ptr(dst_k_scale), _ptr(dst_v_scale), _ptr(dst_table), int(dst_table.shape[1]), _ptr(context_lens),
         int(context_lens.numel()), int(max_context_len), _ptr(err_flag), _stream(stream)))
+
+
+def pa_multi_token_workspace_bytes(cache: CacheDesc, batch: int, num_q_tokens: int, num_q_heads: int,
+                                   max_context_len: int, max_query_len: int, partition_size: int = 0) -> int:
+    desc = cache.c()
+    return int(load().pa_multi_token_workspace_bytes(ctypes.byref(desc), batch, num_q_tokens, num_q_heads,
+                                                      max_context_len, max_query_len, partition_size))
+
+
+def pa_multi_token_attention(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_lens, query_start,
+                             max_context_len: int, max_query_len: int, scale: float, k_scale=None, v_scale=None,
+                             partition_size: int = 0, workspace=None, err_flag=None, stream=None) -> None:
+    num_q_tokens, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    desc = cache.c()
+    _check(load().pa_multi_token_attention(
+        ctypes.byref(desc), dtype_code(q), _ptr(out), _ptr(q), _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens),
+        _ptr(query_start), int(context_lens.numel()), num_q_tokens, num_q_heads, int(max_context_len),
+        int(max_query_len), float(scale), int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag),
+        _stream(stream)))

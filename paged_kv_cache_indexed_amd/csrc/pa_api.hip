@@ -241,6 +241,112 @@ size_t pa_decode_sliding_window_workspace_bytes(const pa_cache_desc_t* cache, in
 
 namespace {
 
+int32_t multi_partition_size(const pa_cache_desc_t* c, int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                             int32_t max_query_len, int32_t requested) {
+    if (check_cache(c) != PA_OK || batch < 0 || max_context_len <= 0 || num_q_heads <= 0 || max_query_len <= 0)
+        return -1;
+    const int bs = c->block_size;
+    const int64_t max_p = (int64_t)kMaxIdsPerPartition * bs;
+    if (requested > 0) return (requested % bs != 0 || requested > max_p) ? -1 : requested;
+    // As the grouped decode: one partition when the (sequence, kv head, column tile) grid
+    // already holds 256 workgroups, else split towards 256; at most 4096 tokens each.
+    const int group = num_q_heads % c->num_kv_heads == 0 ? num_q_heads / c->num_kv_heads : 1;
+    const int64_t tiles = (int64_t)batch * c->num_kv_heads * ceil_div((int64_t)max_query_len * group, 16);
+    int64_t parts = tiles >= 256 ? 1 : ceil_div(256, tiles > 0 ? tiles : 1);
+    if (parts < ceil_div(max_context_len, 4096)) parts = ceil_div(max_context_len, 4096);
+    int64_t P = ceil_div(ceil_div(max_context_len, parts), bs) * bs;
+    if (P > max_p) P = max_p;
+    return (int32_t)P;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_multi_token_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_tokens,
+                                      int32_t num_q_heads, int32_t max_context_len, int32_t max_query_len,
+                                      int32_t partition_size) {
+    const int32_t P = multi_partition_size(cache, batch, num_q_heads, max_context_len, max_query_len, partition_size);
+    if (P <= 0 || num_q_tokens <= 0) return 0;
+    const int64_t parts = ceil_div(max_context_len, P);
+    if (parts <= 1) return 0;
+    return (size_t)num_q_tokens * num_q_heads * parts * (cache->head_dim + 2) * sizeof(float);
+}
+
+pa_status_t pa_multi_token_attention(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
+                                     const void* k_pool, const void* v_pool, const float* k_scale,
+                                     const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, const int32_t* query_start, int32_t batch,
+                                     int32_t num_q_tokens, int32_t num_q_heads, int32_t max_context_len,
+                                     int32_t max_query_len, float scale, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream) {
+    pa_status_t st = check_cache(cache);
+    if (st != PA_OK) return st;
+    if (batch < 0 || batch > 65535 || num_q_tokens < 0) return PA_ERR_INVALID_ARGUMENT;
+    if (batch == 0 || num_q_tokens == 0) return PA_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens || !query_start)
+        return PA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARGUMENT;
+    if (is_fp8(cache)) {
+        if (q_dtype != PA_F16 && q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+        if (!k_scale || !v_scale || !aligned4(k_scale) || !aligned4(v_scale)) return PA_ERR_INVALID_ARGUMENT;
+    } else if (q_dtype != cache->dtype) {
+        return PA_ERR_INVALID_ARGUMENT;
+    }
+    if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+    const int group = num_q_heads / cache->num_kv_heads;
+    if (!multi_token_supported(cache->dtype, cache->head_dim, group, cache->block_size)) return PA_ERR_UNSUPPORTED;
+    if (max_blocks_per_seq <= 0 || max_context_len <= 0 || max_query_len <= 0 || max_query_len > max_context_len)
+        return PA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * cache->block_size) return PA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+    const int64_t col_tiles = ceil_div((int64_t)max_query_len * group, 16);
+    if (col_tiles * batch > 65535) return PA_ERR_UNSUPPORTED;
+    const int32_t P =
+        multi_partition_size(cache, batch, num_q_heads, max_context_len, max_query_len, partition_size);
+    if (P <= 0) return PA_ERR_INVALID_ARGUMENT;
+    const int64_t parts = ceil_div(max_context_len, P);
+    const size_t need = pa_multi_token_workspace_bytes(cache, batch, num_q_tokens, num_q_heads, max_context_len,
+                                                       max_query_len, partition_size);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_INVALID_ARGUMENT;
+
+    DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = need > 0 ? a.ws_o + (size_t)num_q_tokens * num_q_heads * parts * cache->head_dim : nullptr;
+    a.err_flag = err_flag;
+    a.num_blocks = cache->num_blocks;
+    a.log2_block_size = log2_exact(cache->block_size);
+    a.num_kv_heads = cache->num_kv_heads;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.partition_size = P;
+    a.max_partitions = (int32_t)parts;
+    a.window = 0;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.block_stride = block_stride(cache);
+    a.query_start = query_start;
+    a.col_tiles = (int32_t)col_tiles;
+    a.batch = batch;
+    a.num_q_tokens = num_q_tokens;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_multi_token(a, cache->dtype, q_dtype, cache->head_dim, group, batch, cache->num_kv_heads, s);
+    if (e == hipSuccess && parts > 1) e = launch_reduce_multi(a, q_dtype, cache->head_dim, s);
+    return from_hip(e);
+}
+
+}  // extern "C"
+
+namespace {
+
 pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
                         const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
                         const int32_t* block_table, int32_t max_blocks_per_seq,

@@ -16,6 +16,7 @@ struct Partition {
     int rel_lo;  // first attended token, relative to t0 (< block_size; 0 unless a window starts inside)
     int ntok;    // end of the attended tokens, relative to t0
     int j0;      // logical block of t0: s_ids[i] is the id of block j0 + i
+    int len;     // the sequence's context length
 };
 
 // First attended position of a sequence of length L: a sliding window keeps the last
@@ -37,9 +38,9 @@ __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
 
 // Checks the sequence length, stages the partition's block ids in s_ids and validates
 // them. Returns false when the workgroup has nothing more to do: the partition is past the
-// end of the sequence, or the sequence is invalid (its outputs, or this partition's record,
-// are set to NaN and the error bit is raised). Never reads a table entry or a pool byte
-// that the checks have not cleared.
+// end of the sequence, or the sequence is invalid (the sink sets its outputs, or this
+// partition's records, to NaN, and the error bit is raised). Never reads a table entry or a
+// pool byte that the checks have not cleared.
 //
 // Without a window the table slice of partition p starts at logical block p * P / block_size
 // whatever the length is, so it is loaded in the same round trip as the length (entries past
@@ -47,10 +48,11 @@ __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
 // the ids and the OR of their range checks. With a window the slice starts at the block of
 // the window start, so the length is read first.
 //
-// The workgroup covers query heads [h0, h0 + nq): its NaN outputs cover exactly those.
-template <typename T, int D, int NT>
-__device__ bool partition_prologue_heads(const DecodeArgs& a, int p, int h0, int nq, int b, int* s_ids,
-                                         Partition& part) {
+// A valid length is at least min_len (1 for a decode; the number of new queries otherwise).
+// Sink provides nan_outputs() and nan_records(p) for the outputs this workgroup owns.
+template <typename T, int D, int NT, typename Sink>
+__device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int min_len, const Sink& sink,
+                                        int* s_ids, Partition& part) {
     constexpr int kPerThread = (kMaxIdsPerPartition + NT - 1) / NT;
     const int tid = threadIdx.x;
     const int lbs = a.log2_block_size;
@@ -72,15 +74,17 @@ __device__ bool partition_prologue_heads(const DecodeArgs& a, int p, int h0, int
     if (a.window <= 0) L = a.context_lens[b];
     int flag = 0;
     if (L <= 0) flag = PA_FLAG_EMPTY_CONTEXT;
-    else if (L > a.max_context_len || ((L - 1) >> lbs) >= a.max_blocks_per_seq) flag = PA_FLAG_BAD_LENGTH;
+    else if (L > a.max_context_len || ((L - 1) >> lbs) >= a.max_blocks_per_seq || L < min_len)
+        flag = PA_FLAG_BAD_LENGTH;
     if (flag) {
         if (p == 0) {
             if (tid == 0 && a.err_flag) atomicOr(a.err_flag, flag);
-            store_nan<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, nq * D);
+            sink.nan_outputs();
         }
         return false;
     }
     part.nparts = (L - base + P - 1) / P;
+    part.len = L;
     if (p >= part.nparts) return false;
     part.t0 = base + p * P;
     part.rel_lo = max(window_start(a, L) - part.t0, 0);
@@ -105,19 +109,33 @@ __device__ bool partition_prologue_heads(const DecodeArgs& a, int p, int h0, int
     }
     if (__syncthreads_or(bad)) {
         if (tid == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_BLOCK_ID);
-        if (part.nparts == 1) {
-            store_nan<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, nq * D);
-        } else {
-            for (int i = tid; i < nq * (D + 2); i += NT) {
-                const int g = i / (D + 2), e = i % (D + 2);
-                const size_t rec = ((size_t)b * a.num_q_heads + h0 + g) * a.max_partitions + p;
-                if (e < D) a.ws_o[rec * D + e] = __builtin_nanf("");
-                else a.ws_ml[rec * 2 + (e - D)] = (e == D) ? -INFINITY : __builtin_nanf("");
-            }
-        }
+        if (part.nparts == 1) sink.nan_outputs();
+        else sink.nan_records(p);
         return false;
     }
     return true;
+}
+
+// NaN sink of a decode workgroup: query heads [h0, h0 + nq) of sequence b.
+template <typename T, int D>
+struct DecodeNanSink {
+    const DecodeArgs& a;
+    int b, h0, nq;
+    __device__ void nan_outputs() const { store_nan<T>(a.out, ((size_t)b * a.num_q_heads + h0) * D, nq * D); }
+    __device__ void nan_records(int p) const {
+        for (int i = threadIdx.x; i < nq * (D + 2); i += blockDim.x) {
+            const int g = i / (D + 2), e = i % (D + 2);
+            const size_t rec = ((size_t)b * a.num_q_heads + h0 + g) * a.max_partitions + p;
+            if (e < D) a.ws_o[rec * D + e] = __builtin_nanf("");
+            else a.ws_ml[rec * 2 + (e - D)] = (e == D) ? -INFINITY : __builtin_nanf("");
+        }
+    }
+};
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ bool partition_prologue_heads(const DecodeArgs& a, int p, int h0, int nq, int b,
+                                                         int* s_ids, Partition& part) {
+    return partition_prologue_sink<T, D, NT>(a, p, b, 1, DecodeNanSink<T, D>{a, b, h0, nq}, s_ids, part);
 }
 
 template <typename T, int D, int G, int NT>

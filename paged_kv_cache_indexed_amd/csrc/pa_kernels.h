@@ -36,6 +36,12 @@ struct DecodeArgs {
     int32_t window;    // > 0: attend to the last `window` tokens only; 0: the whole context
     float scale_log2;  // scale * log2(e): scores live in the base-2 exponent domain
     int64_t block_stride;  // bytes from one physical block to the next in k_pool / v_pool
+    // multi-token attention only: query rows query_start[b] .. query_start[b+1]-1 belong to
+    // sequence b; each workgroup covers one of col_tiles tiles of 16 (query, head) columns
+    const int32_t* query_start;
+    int32_t col_tiles;
+    int32_t batch;
+    int32_t num_q_tokens;  // rows of q and out
 };
 
 struct CacheArgs {
@@ -61,6 +67,12 @@ hipError_t launch_decode_valu_fp8(const DecodeArgs& a, int dtype, int head_dim, 
 bool decode_mfma_supported(int kv_dtype, int head_dim, int group, int block_size);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream);
+// Multi-token attention on the matrix cores (16-bit or 8-bit pools, any group, block_size
+// >= 16) and its log-sum-exp combine per query row.
+bool multi_token_supported(int kv_dtype, int head_dim, int group, int block_size);
+hipError_t launch_multi_token(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
+                              int num_kv_heads, hipStream_t stream);
+hipError_t launch_reduce_multi(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 // Log-sum-exp combine of partition records (only when some sequence has > 1 partition).
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, int batch, hipStream_t stream);
 

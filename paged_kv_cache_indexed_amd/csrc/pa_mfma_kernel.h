@@ -1,0 +1,454 @@
+#pragma once
+// Paged attention on the gfx950 matrix cores (fp16 / bf16 operands): the kernel template shared
+// by the grouped-query decode (pa_decode_mfma.hip) and multi-token attention (pa_multi_token.hip).
+//
+// When G = Hq / Hkv query heads share one kv head, scores and the value sum are small dense
+// contractions: S = Q K^T over head_dim and O = P V over tokens. One workgroup still owns
+// one (context partition, kv head, sequence); each of its 4 waves walks 32-token chunks
+// (two 16-token tiles) of the partition with its own online softmax.
+//
+// Per chunk and wave (16 x 16 MFMA tiles; lane l has n = l % 16 and lane group g = l / 16):
+//   * Scores, transposed: S^T[token][head] = K[token][:] . Q[head][:] with
+//     v_mfma_f32_16x16x32. The K tile is the A operand straight from memory: for k-block c,
+//     lane l loads dims 32c + 8g .. +7 of token row n (one load instruction covers 64
+//     contiguous bytes of 16 rows). Q (B operand, heads as columns, zero beyond G) uses the
+//     same dim-to-k-slot assignment, so the contraction is exact whatever order the
+//     hardware sums k in. Lane l receives S^T for head n at tokens
+//     4g..4g+3 of each tile.
+//   * Those 8 values per lane are exactly an A operand of the P V product with tokens on the
+//     contraction axis (k-slot (g, j) <-> token 16 * (j / 4) + 4g + j % 4), so P never moves
+//     between lanes. P is split into a rounded high part and the rounded remainder; two
+//     MFMAs (hi and lo) keep ~16 mantissa bits in the weights.
+//   * V has tokens on rows and dims contiguous, but the B operand needs tokens along k. Each
+//     16-token x 16-dim slice is transposed by one v_mfma_f32_16x16x16 against an identity
+//     B operand (exact: products with 1 and sums with 0); its fp32 output (4 tokens of one
+//     dim per lane) packs back to 16-bit without rounding and is the B operand of
+//     v_mfma_f32_16x16x32 for O += P V.
+//   * Everything else (length checks, block ids staged and checked in LDS, branch-free
+//     masked buffer loads that never touch padding, base-2 online softmax in fp32, wave and
+//     partition merge) is shared with the VALU path.
+//
+// 8-bit float pools (OCP E4M3 codes, a float32 scale per (token, kv head) row): a lane's
+// 16-byte load holds 16 codes, dims 64c' + 16g .. +15 of token row n (still 64 contiguous
+// bytes of 16 rows per instruction). They widen exactly to q's 16-bit type as the A operands
+// of k-blocks 2c' (dims +0..7) and 2c' + 1 (dims +8..15); Q's B operand follows the same
+// assignment. Lane (n, g) holds the scores of tokens 4g .. 4g+3 of each tile, which are also
+// its P entries, so one aligned 16-byte load per tile brings the four K scales (they multiply
+// the scores) and one the four V scales (they multiply P before the split into hi and lo).
+#include <type_traits>
+
+#include "pa_decode_common.h"
+
+// Cache policy of this kernel's K/V loads. Four loads of a lane cover one 64-byte piece of
+// each of 16 rows, so lines are revisited by the next load: keep them cacheable.
+#ifndef PA_MFMA_LOAD_POLICY
+#define PA_MFMA_LOAD_POLICY 0
+#endif
+
+namespace pagedkv {
+namespace mfma {
+
+typedef __bf16 mf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 mf_f16x8 __attribute__((ext_vector_type(8)));
+typedef short mf_s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 mf_f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<BF16> {
+    static constexpr uint32_t kOne = 0x3F80u;
+    __device__ static f32x4 k32(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mf_bf16x8, a),
+                                                      __builtin_bit_cast(mf_bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ static f32x4 k16(u32x2 a, u32x2 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mf_s16x4, a),
+                                                        __builtin_bit_cast(mf_s16x4, b), c, 0, 0, 0);
+    }
+    // Round two fp32 values to bf16 (nearest even) and pack them (x in the low half).
+    __device__ static uint32_t pack_round(float x, float y) {
+        const bf16x2 h = {(__bf16)x, (__bf16)y};
+        return __builtin_bit_cast(uint32_t, h);
+    }
+    __device__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    __device__ static float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+    // Pack two fp32 values that are exactly representable in bf16 (no rounding needed).
+    __device__ static uint32_t pack_exact(float x, float y) {
+        return (__float_as_uint(x) >> 16) | (__float_as_uint(y) & 0xffff0000u);
+    }
+};
+
+template <>
+struct Mma<F16> {
+    static constexpr uint32_t kOne = 0x3C00u;
+    __device__ static f32x4 k32(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mf_f16x8, a),
+                                                     __builtin_bit_cast(mf_f16x8, b), c, 0, 0, 0);
+    }
+    __device__ static f32x4 k16(u32x2 a, u32x2 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(mf_f16x4, a),
+                                                    __builtin_bit_cast(mf_f16x4, b), c, 0, 0, 0);
+    }
+    __device__ static uint32_t pack_round(float x, float y) {
+        const f16x2 h = {(_Float16)x, (_Float16)y};
+        return __builtin_bit_cast(uint32_t, h);
+    }
+    __device__ static float lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).x; }
+    __device__ static float hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).y; }
+    __device__ static uint32_t pack_exact(float x, float y) { return pack_round(x, y); }
+};
+
+// Eight E4M3 codes (two dwords) -> the same values in T (exact), packed as an A/B operand.
+__device__ __forceinline__ u32x4 widen8(F16, uint32_t w0, uint32_t w1) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, true))};
+}
+__device__ __forceinline__ u32x4 widen8(BF16, uint32_t w0, uint32_t w1) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
+}
+
+// T: type of q, out and the MFMA operands (fp16 / bf16); KV: the pool's storage (T or FP8).
+// NaN sink of a multi-token workgroup: the (query, head) columns of column tile ct.
+template <typename T, int D, int G>
+struct MultiNanSink {
+    const DecodeArgs& a;
+    int q0, nq, kvh, ct;
+    __device__ size_t row(int c) const {  // output row of tile column c
+        const int col = 16 * ct + c;
+        return (size_t)(q0 + col / G) * a.num_q_heads + kvh * G + col % G;
+    }
+    __device__ bool valid(int c) const { return (16 * ct + c) / G < nq; }
+    __device__ void nan_outputs() const {
+        for (int i = threadIdx.x; i < 16 * D; i += blockDim.x)
+            if (valid(i / D)) store_elem(T{}, a.out, row(i / D) * D + i % D, __builtin_nanf(""));
+    }
+    __device__ void nan_records(int p) const {
+        for (int i = threadIdx.x; i < 16 * (D + 2); i += blockDim.x) {
+            const int c = i / (D + 2), e = i % (D + 2);
+            if (!valid(c)) continue;
+            const size_t rec = row(c) * a.max_partitions + p;
+            if (e < D) a.ws_o[rec * D + e] = __builtin_nanf("");
+            else a.ws_ml[rec * 2 + (e - D)] = (e == D) ? -INFINITY : __builtin_nanf("");
+        }
+    }
+};
+
+// kMulti = false: one query per sequence, column n of the B operand is head kvh * G + n.
+// kMulti = true: several queries per sequence (query_start), columns are (query, head)
+// pairs taken query-major, 16 per workgroup (column tile blockIdx.z % col_tiles); query i of
+// a sequence with n new tokens sits at position L - n + i and its column sees tokens up to
+// that position only (causal mask inside the valid range).
+template <typename T, typename KV, int D, int G, int NW, bool kDoubleBuffer, bool kMulti = false>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
+    static_assert(T::kBytes == 2, "matrix-core operands are 16-bit");
+    static_assert(G >= 1 && G <= 16, "at most 16 query heads per kv head");
+    constexpr int NCOL = kMulti ? 16 : G;  // columns whose results this workgroup keeps
+    constexpr bool kFp8 = std::is_same_v<KV, FP8>;
+    constexpr int NC = D / 32;             // 32-dim k-blocks of the score contraction
+    constexpr int NL = D * KV::kBytes / 64;  // 16-byte loads per lane per tile row (64 B of each row)
+    constexpr int NS = D / 16;             // 16-dim output slices
+    constexpr int kChunk = 32;             // tokens per wave iteration (two 16-token tiles)
+    using M = Mma<T>;
+
+    __shared__ int s_ids[kMaxIdsPerPartition];
+    __shared__ float s_m[NW][NCOL];
+    __shared__ float s_l[NW][NCOL];
+    __shared__ float s_acc[NW][NCOL][D];
+
+    const int p = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int b = kMulti ? (int)blockIdx.z / a.col_tiles : (int)blockIdx.z;
+    const int ct = kMulti ? (int)blockIdx.z - b * a.col_tiles : 0;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int lbs = a.log2_block_size;
+    const int bs = 1 << lbs;
+
+    // This lane's column: a head of the group (decode) or a (query, head) pair.
+    int q0 = 0, nq = 1;
+    if constexpr (kMulti) {
+        q0 = a.query_start[b];
+        nq = a.query_start[b + 1] - q0;
+        // query rows outside q, or more queries than the launch has column tiles for: flagged,
+        // and those rows are not written
+        if (q0 < 0 || nq < 0 || q0 + nq > a.num_q_tokens || nq * G > 16 * a.col_tiles) {
+            if (p == 0 && kvh == 0 && ct == 0 && threadIdx.x == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_LENGTH);
+            return;
+        }
+        if (16 * ct >= nq * G) return;  // no query of this sequence in this tile (uniform)
+    }
+    const int col = 16 * ct + n;
+    const int qi = kMulti ? col / G : 0;       // query of the column
+    const int qh = kMulti ? col - qi * G : n;  // head of the column inside the group
+    const bool col_valid = kMulti ? qi < nq : n < G;
+
+    // Q as the B operand of S^T = K Q^T (zero in invalid columns); k-block c of lane group g
+    // holds the dims the K operand gives it: 32c + 8g .. +7 for 16-bit pools, 64(c/2) + 16g +
+    // 8(c%2) .. +7 for 8-bit pools.
+    u32x4 qb[NC];
+    {
+        const size_t qrow_idx = kMulti ? (size_t)(q0 + (col_valid ? qi : 0)) * a.num_q_heads + kvh * G + qh
+                                       : (size_t)b * a.num_q_heads + kvh * G + (col_valid ? n : 0);
+        const char* qrow = static_cast<const char*>(a.q) + qrow_idx * D * 2;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int d0 = kFp8 ? 64 * (c >> 1) + 16 * g + 8 * (c & 1) : 32 * c + 8 * g;
+            qb[c] = col_valid ? load16(qrow + 2 * d0) : u32x4{0, 0, 0, 0};
+        }
+    }
+    Partition part;
+    if constexpr (kMulti) {
+        if (!partition_prologue_sink<T, D, NW * 64>(a, p, b, max(nq, 1), MultiNanSink<T, D, G>{a, q0, nq, kvh, ct},
+                                                    s_ids, part))
+            return;
+    } else {
+        if (!partition_prologue<T, D, G, NW * 64>(a, p, kvh, b, s_ids, part)) return;
+    }
+    int ntok = part.ntok;
+    int lim_col = ntok;  // tokens (relative to the partition) this lane's column may see
+    if constexpr (kMulti) {
+        const int first_pos = part.len - nq;  // position of query 0
+        const int last_q = min(16 * ct + 15, nq * G - 1) / G;
+        const int tile_end = first_pos + last_q + 1 - part.t0;  // tokens the tile's last query sees
+        if (tile_end <= 0) return;  // the whole partition is after this tile's queries (uniform)
+        ntok = min(ntok, tile_end);
+        lim_col = col_valid ? min(ntok, first_pos + qi + 1 - part.t0) : 0;
+    }
+    const int rel_lo = part.rel_lo;
+    const int c0 = rel_lo / kChunk;  // first chunk holding an attended token
+
+    // Identity B operand of the 16x16x16 transpose: k-slot (g, i) is 1 in column 4g + i.
+    u32x2 ident;
+    ident.x = ((4 * g + 0 == n) ? M::kOne : 0u) | (((4 * g + 1 == n) ? M::kOne : 0u) << 16);
+    ident.y = ((4 * g + 2 == n) ? M::kOne : 0u) | (((4 * g + 3 == n) ? M::kOne : 0u) << 16);
+
+    const size_t head_bytes = (size_t)bs * D * KV::kBytes;
+    const size_t block_bytes = (size_t)a.block_stride;
+    const char* kpool = static_cast<const char*>(a.k_pool);
+    const char* vpool = static_cast<const char*>(a.v_pool);
+    const uint32_t slab_bytes = (uint32_t)head_bytes;
+    const uint32_t seg = 16u * g;  // lane group g reads bytes 64c + 16g .. +15 of a row
+    const int niters = (ntok - c0 * kChunk + kChunk * NW - 1) / (kChunk * NW);
+
+    // Loads of one chunk: tile t rows are tokens rel + 16t + n; lanes past the partition end
+    // read zeros through an out-of-range offset. With 8-bit pools, ks/vs[t] are the scales
+    // of tokens rel + 16t + 4g .. +3 (the rows of this lane's scores), loaded whole when the
+    // tile starts inside the partition and cleared per token before use.
+    auto issue = [&](int it, u32x4 (*kk)[NL], u32x4 (*vv)[NL], u32x4* ks, u32x4* vs) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int rel = (c0 + it * NW + wave) * kChunk + 16 * t;  // wave-uniform
+            const int id = __builtin_amdgcn_readfirstlane(s_ids[(rel < ntok ? rel : 0) >> lbs]);  // partitions start on a block
+            const size_t slab = (size_t)id * block_bytes + (size_t)kvh * head_bytes;
+            const uint32_t off = (rel + n < ntok && rel + n >= rel_lo)
+                                     ? (uint32_t)(((rel & (bs - 1)) + n) * D * KV::kBytes) + seg
+                                     : kOutOfRange;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + slab, slab_bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + slab, slab_bytes);
+#pragma unroll
+            for (int c = 0; c < NL; ++c) {
+                const uint32_t o = off == kOutOfRange ? kOutOfRange : off + 64 * c;
+                kk[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rk, o);
+                vv[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rv, o);
+            }
+            if constexpr (kFp8) {
+                const size_t srow = ((size_t)id * a.num_kv_heads + kvh) << lbs;  // this slab's scales
+                const uint32_t so = rel < ntok ? (uint32_t)(((rel & (bs - 1)) + 4 * g) * 4) : kOutOfRange;
+                ks[t] = buffer_load16<PA_MFMA_LOAD_POLICY>(make_rsrc(a.k_scale + srow, (uint32_t)bs * 4), so);
+                vs[t] = buffer_load16<PA_MFMA_LOAD_POLICY>(make_rsrc(a.v_scale + srow, (uint32_t)bs * 4), so);
+            }
+        }
+    };
+
+    float m = -INFINITY;  // running base-2 max of head n (same in all four lane groups)
+    float l = 0.f;        // this lane's part of head n's running sum
+    f32x4 acc[NS];        // acc[s][i] = O[head 4g + i][dim of column n in slice s]
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int it, u32x4 (*kk)[NL], u32x4 (*vv)[NL], const u32x4* ks, const u32x4* vs) {
+        const int rel0 = (c0 + it * NW + wave) * kChunk;
+        float sc[8];
+        float vscale[8];  // V scale of each P entry (8-bit pools)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x4 st = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (kFp8) {
+#pragma unroll
+                for (int c = 0; c < NL; ++c) {
+                    st = M::k32(widen8(T{}, kk[t][c][0], kk[t][c][1]), qb[2 * c], st);
+                    st = M::k32(widen8(T{}, kk[t][c][2], kk[t][c][3]), qb[2 * c + 1], st);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NC; ++c) st = M::k32(kk[t][c], qb[c], st);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = rel0 + 16 * t + 4 * g + i;
+                const bool live = tok < lim_col && tok >= rel_lo;
+                float d = st[i];
+                if constexpr (kFp8) {
+                    d *= __uint_as_float(ks[t][i]);
+                    vscale[4 * t + i] = live ? __uint_as_float(vs[t][i]) : 0.f;
+                }
+                sc[4 * t + i] = live ? d * a.scale_log2 : -INFINITY;
+            }
+        }
+        float cm = sc[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
+        cm = fmaxf(cm, shfl_xor(cm, 16));
+        cm = fmaxf(cm, shfl_xor(cm, 32));
+        const float mn = fmaxf(m, cm);
+        const float ms = (mn == -INFINITY) ? 0.f : mn;
+        const float alpha = fast_exp2(m - ms);
+        m = mn;
+        float pr[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pr[j] = fast_exp2(sc[j] - ms);
+            psum += pr[j];
+        }
+        l = l * alpha + psum;
+        // rows 4g + i of acc belong to heads 4g + i: fetch their factors from lanes 4g + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ai = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, __float_as_int(alpha)));
+#pragma unroll
+            for (int s = 0; s < NS; ++s) acc[s][i] *= ai;
+        }
+        // P as the A operand (times the V scales for 8-bit pools), split into rounded high and
+        // low parts
+        if constexpr (kFp8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pr[j] *= vscale[j];
+        }
+        u32x4 phi, plo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t h = M::pack_round(pr[2 * w], pr[2 * w + 1]);
+            phi[w] = h;
+            plo[w] = M::pack_round(pr[2 * w] - M::lo(h), pr[2 * w + 1] - M::hi(h));
+        }
+        // V rows as 16-bit words: vw[t][c] holds the 8 dims of token row n that k-block c of
+        // lane group g covers
+        u32x4 vw[2][NC];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if constexpr (kFp8) {
+                    vw[t][c] = (c & 1) ? widen8(T{}, vv[t][c >> 1][2], vv[t][c >> 1][3])
+                                       : widen8(T{}, vv[t][c >> 1][0], vv[t][c >> 1][1]);
+                } else {
+                    vw[t][c] = vv[t][c];
+                }
+            }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int c = s >> 1;
+            f32x4 vt[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const u32x2 half = (s & 1) ? u32x2{vw[t][c][2], vw[t][c][3]} : u32x2{vw[t][c][0], vw[t][c][1]};
+                vt[t] = M::k16(half, ident, f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+            const u32x4 vb = {M::pack_exact(vt[0][0], vt[0][1]), M::pack_exact(vt[0][2], vt[0][3]),
+                              M::pack_exact(vt[1][0], vt[1][1]), M::pack_exact(vt[1][2], vt[1][3])};
+            acc[s] = M::k32(phi, vb, acc[s]);
+            acc[s] = M::k32(plo, vb, acc[s]);
+        }
+    };
+
+    u32x4 ka[2][NL], va[2][NL], ksa[2], vsa[2];
+    if constexpr (kDoubleBuffer) {
+        u32x4 kb[2][NL], vb[2][NL], ksb[2], vsb[2];
+        issue(0, ka, va, ksa, vsa);
+        issue(1, kb, vb, ksb, vsb);
+        int it = 0;
+        for (; it + 1 < niters; it += 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            compute(it, ka, va, ksa, vsa);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(it + 2, ka, va, ksa, vsa);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(it + 1, kb, vb, ksb, vsb);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(it + 3, kb, vb, ksb, vsb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (it < niters) compute(it, ka, va, ksa, vsa);
+    } else {
+        for (int it = 0; it < niters; ++it) {
+            issue(it, ka, va, ksa, vsa);
+            compute(it, ka, va, ksa, vsa);
+        }
+    }
+
+    // column n's sum over the four lane groups
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (g == 0 && n < NCOL) {
+        s_m[wave][n] = m;
+        s_l[wave][n] = l;
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int c = s >> 1;  // column n of slice s
+        const int dim = (kFp8 ? 64 * (c >> 1) + 16 * (n >> 2) + 8 * (c & 1) : 32 * c + 8 * (n >> 2)) + 4 * (s & 1) +
+                        (n & 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * g + i < NCOL) s_acc[wave][4 * g + i][dim] = acc[s][i];
+    }
+    __syncthreads();
+    if constexpr (kMulti) {
+        // merge the waves per column; one output row (single partition) or record per column
+        const MultiNanSink<T, D, G> rows{a, q0, nq, kvh, ct};
+        for (int i = threadIdx.x; i < 16 * D; i += NW * 64) {
+            const int c = i / D;
+            const int e = i % D;
+            if (!rows.valid(c)) continue;
+            float M = s_m[0][c];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][c]);
+            const float Ms = (M == -INFINITY) ? 0.f : M;
+            float num = 0.f, den = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float f = __builtin_amdgcn_exp2f(s_m[w][c] - Ms);
+                num = fmaf(s_acc[w][c][e], f, num);
+                den = fmaf(s_l[w][c], f, den);
+            }
+            const size_t r = rows.row(c);
+            if (part.nparts == 1) {
+                store_elem(T{}, a.out, r * D + e, num / den);
+            } else {
+                const size_t rec = r * a.max_partitions + p;
+                a.ws_o[rec * D + e] = num / den;
+                if (e == 0) {
+                    a.ws_ml[rec * 2] = M;
+                    a.ws_ml[rec * 2 + 1] = den;
+                }
+            }
+        }
+    } else {
+        partition_epilogue<T, D, G, NW>(a, p, kvh, b, part, s_m, s_l, s_acc);
+    }
+}
+
+}  // namespace mfma
+}  // namespace pagedkv

@@ -9,7 +9,8 @@ import torch
 
 from ._lib import (CacheDesc, pa_copy_blocks, pa_copy_blocks_fp8, pa_decode, pa_decode_fp8,
                    pa_decode_sliding_window, pa_decode_sliding_window_workspace_bytes,
-                   pa_decode_workspace_bytes, pa_reblock, pa_reshape_and_cache, pa_reshape_and_cache_fp8)
+                   pa_decode_workspace_bytes, pa_multi_token_attention, pa_multi_token_workspace_bytes,
+                   pa_reblock, pa_reshape_and_cache, pa_reshape_and_cache_fp8)
 
 
 def workspace_for(k_pool: torch.Tensor, batch: int, num_q_heads: int, max_context_len: int,
@@ -99,3 +100,20 @@ def reblock(src_k, src_v, src_table, dst_k, dst_v, dst_table, context_lens, max_
     sk = scales if scales is not None else (None, None, None, None)
     pa_reblock(CacheDesc.of(src_k), src_k, src_v, src_table, CacheDesc.of(dst_k), dst_k, dst_v, dst_table,
                context_lens, max_context_len, *sk, err_flag=err_flag, stream=stream)
+
+
+def multi_token_attention(q, k_pool, v_pool, block_table, context_lens, query_start, max_context_len: int,
+                          max_query_len: int, scale: float, k_scale=None, v_scale=None, partition_size: int = 0,
+                          out=None, workspace=None, err_flag=None, stream=None):
+    """Causal attention of several new query rows per sequence (rows query_start[b] ..
+    query_start[b+1]-1, already appended to the cache) over the paged cache."""
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        n = pa_multi_token_workspace_bytes(CacheDesc.of(k_pool), int(context_lens.numel()), int(q.shape[0]),
+                                           int(q.shape[1]), max_context_len, max_query_len, partition_size)
+        workspace = torch.empty((n + 3) // 4, dtype=torch.float32, device=q.device) if n else None
+    pa_multi_token_attention(CacheDesc.of(k_pool), out, q, k_pool, v_pool, block_table, context_lens, query_start,
+                             max_context_len, max_query_len, scale, k_scale, v_scale, partition_size, workspace,
+                             err_flag, stream)
+    return out
