@@ -38,12 +38,27 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hbm_traffic.txt")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources and the ABI header; recorded next to every counter figure."""
+# Sources each decode kernel is built from: a recorded counter figure stays valid while the
+# sources of the kernel that produced it are unchanged.
+_COMMON_SOURCES = ("pa_device.h", "pa_kernels.h", "pa_decode_common.h", "pa_api.hip")
+_PATH_SOURCES = {"valu": ("pa_decode_valu.h", "pa_decode.hip", "pa_decode_fp8.hip"),
+                 "mfma": ("pa_mfma_kernel.h", "pa_decode_mfma.hip")}
+
+
+def decode_path(dtype: str, head_dim: int, group: int, block_size: int) -> str:
+    """Which decode kernel the library launches (its dispatch rule, restated for the record):
+    the matrix cores for 4, 8 or 16 query heads per kv head over fp16/bf16/8-bit pools with
+    blocks of 16+ tokens (16 heads only up to head_dim 128), else the VALU kernel."""
+    ok = dtype in ("f16", "bf16", "fp8") and group in (4, 8, 16) and block_size >= 16
+    return "mfma" if ok and not (group == 16 and head_dim > 128) else "valu"
+
+
+def kernel_source_hash(path: str = "valu") -> str:
+    """Hash of the sources of one decode kernel path and the ABI header."""
     import hashlib
 
     csrc = os.path.join(ROOT, "paged_kv_cache_indexed_amd", "csrc")
-    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    files = [os.path.join(csrc, f) for f in _COMMON_SOURCES + _PATH_SOURCES[path]]
     files.append(os.path.join(ROOT, "include", "pagedkv.h"))
     h = hashlib.sha256()
     for f in files:
@@ -53,12 +68,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, path: str):
     """HBM bytes per decode launch measured with rocprofv3 for this workload, if the table in
-    profiles/ was taken from the current kernel sources; else None."""
+    profiles/ was taken from the current sources of its kernel; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    cur = kernel_source_hash()
+    cur = kernel_source_hash(path)
     with open(TRAFFIC_FILE) as f:
         for line in f:
             cells = [c.strip() for c in line.strip().strip("|").split("|")]
@@ -230,6 +245,118 @@ def _fp8_pools(kp, vp):
     return k8, v8, ks, vs
 
 
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix-core peak, published
+
+
+def _bench_multi(args, dev) -> int:
+    """Multi-token step: N new tokens per sequence appended after the workload's context, then
+    pa_multi_token_attention of those N causal queries over the grown context."""
+    import torch
+
+    from paged_kv_cache_indexed_amd import _lib, ops
+    from workloads import build_paged
+
+    N = int(args.queries)
+    base = _workload(args.config, args.block_size, args.median)
+    if base.dtype not in ("f16", "bf16"):
+        print("--queries needs a workload with fp16 or bf16 pools", file=sys.stderr)
+        return 2
+    lens = (base.context_lens + N).astype(np.int32)
+    w = build_paged(f"{base.name}-q{N}", base.meta["cfg"], 0, lens, base.block_size, base.num_kv_heads,
+                    base.num_q_heads, base.head_dim, base.dtype, scale=base.scale, std=base.meta["std"],
+                    append=False)
+    t = w.to_device(dev)
+    B, Hq, d = w.batch, w.num_q_heads, w.head_dim
+    qs = np.arange(B + 1, dtype=np.int32) * N
+    gen = torch.Generator(device=dev).manual_seed(11)
+    q = torch.randn((B * N, Hq, d), generator=gen, device=dev).to(t["k_pool"].dtype)
+    kc, vc, starts = w.meta["contents_k"], w.meta["contents_v"], w.meta["starts"]
+    rows = np.concatenate([np.arange(L - N, L) + starts[b] for b, L in enumerate(lens)])
+    keys = torch.from_numpy(kc[rows]).to(t["k_pool"].dtype).to(dev)
+    vals = torch.from_numpy(vc[rows]).to(t["k_pool"].dtype).to(dev)
+    tok = np.concatenate([np.arange(L - N, L) for L in lens])
+    seq = np.repeat(np.arange(B), N)
+    slots = torch.from_numpy((w.block_table[seq, tok // w.block_size] * w.block_size + tok % w.block_size)
+                             .astype(np.int32)).to(dev)
+    pool_bytes = 2 * t["k_pool"].numel() * t["k_pool"].element_size()
+    R = max(2, math.ceil(args.replica_bytes / pool_bytes))
+    kps = [t["k_pool"]] + [t["k_pool"].clone() for _ in range(R - 1)]
+    vps = [t["v_pool"]] + [t["v_pool"].clone() for _ in range(R - 1)]
+    qs_d = torch.from_numpy(qs).to(dev)
+    max_len = int(lens.max())
+    desc = _lib.CacheDesc.of(t["k_pool"])
+    wsn = _lib.pa_multi_token_workspace_bytes(desc, B, B * N, Hq, max_len, N, args.partition_size)
+    ws = torch.empty((wsn + 3) // 4, dtype=torch.float32, device=dev) if wsn else None
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        r = i % R
+        ops.reshape_and_cache(keys, vals, kps[r], vps[r], slots)
+        if ev is not None:
+            ev[0].record(stream)
+        ops.multi_token_attention(q, kps[r], vps[r], t["block_table"], t["context_lens"], qs_d, max_len, N, w.scale,
+                                  partition_size=args.partition_size, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    kv_bytes = 2 * w.num_kv_heads * d * t["k_pool"].element_size() * int(lens.sum())
+    visible = sum(int((L - N + np.arange(N) + 1).sum()) for L in lens)  # (query, key) pairs per head
+    flops = 4.0 * Hq * d * visible
+    sec = ms.mean() * 1e-3
+    gbs, tfl = kv_bytes / sec / 1e9, flops / sec / 1e12
+    peak_t = MFMA_PEAK_TFLOPS[w.dtype]
+    mfma_bound = flops / kv_bytes > peak_t * 1e12 / (HBM_PEAK_GBS * 1e9)
+    cfg = _describe(w)
+    cfg.update({"workload": w.name, "queries_per_seq": N, "replicas": R,
+                "step": f"append {N} tokens/seq + causal attention of those {N} queries"})
+    result = {
+        "metric": "multi-token paged attention: query tokens/s at 1 MI355X",
+        "value": round(B * N / (wall / args.steps), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": cfg,
+        "attention_kernel_ms": {"mean": round(float(ms.mean()), 5), "p50": round(float(np.percentile(ms, 50)), 5)},
+        "kv_gbs": round(gbs, 1), "tflops": round(tfl, 2),
+        "roofline": ({"bound": "mfma", "achieved": round(tfl, 2), "peak": peak_t, "unit": "TFLOP/s",
+                      "frac": round(tfl / peak_t, 4), "traffic": None} if mfma_bound else
+                     {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}),
+        "kernel_source_hash": kernel_source_hash("mfma"),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        t1 = time.perf_counter()
+        done = nseq = 0
+        while nseq < B and (nseq == 0 or time.perf_counter() - t1 < args.cpu_budget):
+            sl = slice(nseq, nseq + 1)
+            oracle.paged_attention_multi(q[nseq * N:(nseq + 1) * N].float().cpu().numpy(), w.k_pool, w.v_pool,
+                                         w.block_table[sl], lens[sl], np.array([0, N]), w.scale)
+            done += N
+            nseq += 1
+        dt = time.perf_counter() - t1
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        except Exception:  # noqa: BLE001
+            threads = 1
+        result["cpu_baseline"] = {"value": round(done / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                  "sample": f"float64 multi-token attention of sequences 0..{nseq - 1} "
+                                            f"({done} query tokens, all heads) in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def _bench_reblock(args, w, t, kps, vps, R, dev) -> int:
     """Time pa_reblock of the workload's cache (context_lens tokens per sequence) into a new
     layout of block size args.reblock; bytes = the valid K+V rows read plus written."""
@@ -297,6 +424,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--kv", choices=["native", "fp8"], default="native",
                     help="pool elements: the workload's dtype, or 8-bit floats with a scale per row")
+    ap.add_argument("--queries", type=int, default=0,
+                    help="multi-token step: append this many tokens per sequence, then their causal attention")
     ap.add_argument("--layers", type=int, default=1,
                     help="run the step on one layer's strided view of a [blocks][2][layers][heads][bs][d] cache")
     ap.add_argument("--reblock", type=int, default=0,
@@ -322,6 +451,8 @@ def main() -> int:
 
     _lib.load()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda", 0)
+    if args.queries > 0:
+        return _bench_multi(args, dev)
     host_sample = None
     if args.config == 5:
         from workloads.longctx import beam_workload, host_subset
@@ -422,6 +553,7 @@ def main() -> int:
     dec_avg = float(dec_ms.mean())
     achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
+    path = decode_path("fp8" if fp8 else w.dtype, w.head_dim, w.num_q_heads // w.num_kv_heads, w.block_size)
     span = min(max_len, W + w.block_size - 1) if W > 0 else max_len
     part = _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, w.num_q_heads,
                                          span, P)
@@ -462,8 +594,9 @@ def main() -> int:
                              "p90": round(float(np.percentile(dec_ms, 90)), 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(cfg["workload"])},
-        "kernel_source_hash": kernel_source_hash(),
+                     "traffic": recorded_traffic(cfg["workload"], path)},
+        "kernel_source_hash": kernel_source_hash(path),
+        "decode_kernel": path,
     }
     if not args.no_cpu_baseline:
         if fp8:
