@@ -1,15 +1,20 @@
 """Paged-KV decode benchmark on one MI355X.
 
 One step = the whole hot path over one batch: copy-on-write of shared blocks (when the
-workload has any), append of one new token per sequence through its slot (pa_reshape_and_
-cache), then decode over the grown context (pa_decode). Inputs are seeded synthetic tensors
+workload has any), append of one new token per sequence through its slot, then decode over
+the grown context. Append and decode are one launch (pa_decode_append) for 16/32-bit pools
+without a window, else pa_reshape_and_cache[_fp8] then the decode. Inputs are seeded synthetic tensors
 already resident in HBM. Pools are replicated R times and step i uses replica i % R, so the
 bytes touched between two reads of a replica exceed the 256 MB Infinity Cache and the
 per-XCD L2 (a cold-cache measurement).
 
 Prints one JSON line: effective KV GB/s of the whole step (algorithmic K+V bytes of the
 decode, 2 x kv_heads x head_dim x dtype_bytes x sum(context_len), over the step time),
-plus the decode kernel's roofline figure timed with HIP events and the CPU oracle's rate.
+plus the decode kernel's roofline figure and the CPU oracle's rate. The K timed steps run
+back to back with nothing else on the stream. The decode kernel's average launch duration
+comes from a second pass: K back-to-back launches of it (same inputs, same replica
+rotation) between one pair of HIP events on its stream. An event pair around every launch
+would add 2-5 us to each measured launch, and one inside every step about 7 us to the step.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2] [--window W]
 
@@ -248,6 +253,36 @@ def _fp8_pools(kp, vp):
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix-core peak, published
 
 
+def _timed(step, first: int, steps: int):
+    """The timed region: `steps` steps with nothing else on the stream, bracketed by device
+    synchronisation; returns the wall time in seconds."""
+    import torch
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(first + i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def _event_pass(launch, first: int, steps: int) -> float:
+    """Average duration in ms of the measured kernel: `steps` back-to-back launches of it (same
+    inputs and replica rotation as the steps) between one pair of HIP events on its stream.
+    An event pair around every single launch would add 2-5 us to each measured duration."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        launch(first + i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def _bench_multi(args, dev) -> int:
     """Multi-token step: N new tokens per sequence appended after the workload's context, then
     pa_multi_token_attention of those N causal queries over the grown context."""
@@ -290,30 +325,25 @@ def _bench_multi(args, dev) -> int:
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
-        r = i % R
-        ops.reshape_and_cache(keys, vals, kps[r], vps[r], slots)
-        if ev is not None:
-            ev[0].record(stream)
-        ops.multi_token_attention(q, kps[r], vps[r], t["block_table"], t["context_lens"], qs_d, max_len, N, w.scale,
-                                  partition_size=args.partition_size, out=out, workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
+    # one launch for append + decode unless the pools are 8-bit, a window is set or asked not to
+    fused = not (fp8 or W > 0 or args.unfused)
+
+    def attend(i):
+        ops.multi_token_attention(q, kps[i % R], vps[i % R], t["block_table"], t["context_lens"], qs_d, max_len, N,
+                                  w.scale, partition_size=args.partition_size, out=out, workspace=ws)
+
+    def step(i):
+        ops.reshape_and_cache(keys, vals, kps[i % R], vps[i % R], slots)
+        attend(i)
 
     for i in range(args.warmup):
         step(i)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    wall = _timed(step, args.warmup, args.steps)
+    ms = _event_pass(attend, args.warmup + args.steps, args.steps)
     kv_bytes = 2 * w.num_kv_heads * d * t["k_pool"].element_size() * int(lens.sum())
     visible = sum(int((L - N + np.arange(N) + 1).sum()) for L in lens)  # (query, key) pairs per head
     flops = 4.0 * Hq * d * visible
-    sec = ms.mean() * 1e-3
+    sec = ms * 1e-3
     gbs, tfl = kv_bytes / sec / 1e9, flops / sec / 1e12
     peak_t = MFMA_PEAK_TFLOPS[w.dtype]
     mfma_bound = flops / kv_bytes > peak_t * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -325,7 +355,7 @@ def _bench_multi(args, dev) -> int:
         "value": round(B * N / (wall / args.steps), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": cfg,
-        "attention_kernel_ms": {"mean": round(float(ms.mean()), 5), "p50": round(float(np.percentile(ms, 50)), 5)},
+        "attention_kernel_ms": round(ms, 5),
         "kv_gbs": round(gbs, 1), "tflops": round(tfl, 2),
         "roofline": ({"bound": "mfma", "achieved": round(tfl, 2), "peak": peak_t, "unit": "TFLOP/s",
                       "frac": round(tfl / peak_t, 4), "traffic": None} if mfma_bound else
@@ -385,19 +415,14 @@ def _bench_reblock(args, w, t, kps, vps, R, dev) -> int:
     max_len = int(lens_np.max())
     moved = 2 * 2 * w.num_kv_heads * w.head_dim * kps[0].element_size() * int(lens_np.sum())
     stream = torch.cuda.current_stream()
+    def step(i):
+        ops.reblock(kps[i % R], vps[i % R], t["block_table"], dk, dv, ntab_d, lens, max_len)
+
     for i in range(args.warmup):
-        ops.reblock(kps[i % R], vps[i % R], t["block_table"], dk, dv, ntab_d, lens, max_len)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        evs[i][0].record(stream)
-        ops.reblock(kps[i % R], vps[i % R], t["block_table"], dk, dv, ntab_d, lens, max_len)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = np.array([a.elapsed_time(b) for a, b in evs])
-    achieved = moved / (ms.mean() * 1e-3) / 1e9
+        step(i)
+    wall = _timed(step, args.warmup, args.steps)
+    ms = _event_pass(step, args.warmup + args.steps, args.steps)
+    achieved = moved / (ms * 1e-3) / 1e9
     cfg = _describe(w)
     cfg.update({"workload": f"{w.name}-reblock{w.block_size}to{nbs}", "new_block_size": nbs, "replicas": R,
                 "step": "pa_reblock of every valid K/V row to the new layout"})
@@ -406,7 +431,7 @@ def _bench_reblock(args, w, t, kps, vps, R, dev) -> int:
         "value": round(moved / (wall / args.steps) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": cfg,
-        "kernel_ms": {"mean": round(float(ms.mean()), 5), "p50": round(float(np.percentile(ms, 50)), 5)},
+        "kernel_ms": round(ms, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
     }), flush=True)
@@ -424,6 +449,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--kv", choices=["native", "fp8"], default="native",
                     help="pool elements: the workload's dtype, or 8-bit floats with a scale per row")
+    ap.add_argument("--unfused", action="store_true",
+                    help="append with pa_reshape_and_cache and decode with pa_decode (two launches)")
     ap.add_argument("--queries", type=int, default=0,
                     help="multi-token step: append this many tokens per sequence, then their causal attention")
     ap.add_argument("--layers", type=int, default=1,
@@ -505,7 +532,22 @@ def main() -> int:
     kv_bytes = 2 * w.num_kv_heads * row_bytes * int(attended.sum())
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    # one launch for append + decode unless the pools are 8-bit, a window is set or asked not to
+    fused = not (fp8 or W > 0 or args.unfused)
+
+    def decode(i):  # the measured kernel: the decode launch of step i
+        r = i % R
+        if fused:
+            ops.decode_append(t["q"], kps[r], vps[r], t["block_table"], lens, max_len, w.scale, t["new_key"],
+                              t["new_value"], t["slot_mapping"], partition_size=P, out=out, workspace=ws)
+        elif fp8:
+            ops.decode_fp8(t["q"], kps[r], vps[r], kss[r], vss[r], t["block_table"], lens, max_len, w.scale,
+                           window=W, partition_size=P, out=out, workspace=ws)
+        else:
+            ops.decode(t["q"], kps[r], vps[r], t["block_table"], lens, max_len, w.scale,
+                       partition_size=P, out=out, workspace=ws, window=W)
+
+    def step(i):
         r = i % R
         if fp8:
             if pairs.shape[0]:
@@ -515,17 +557,9 @@ def main() -> int:
         else:
             if pairs.shape[0]:
                 ops.copy_blocks(kps[r], vps[r], pairs)
-            ops.reshape_and_cache(t["new_key"], t["new_value"], kps[r], vps[r], t["slot_mapping"])
-        if ev is not None:
-            ev[0].record(stream)
-        if fp8:
-            ops.decode_fp8(t["q"], kps[r], vps[r], kss[r], vss[r], t["block_table"], lens, max_len, w.scale,
-                           window=W, partition_size=P, out=out, workspace=ws)
-        else:
-            ops.decode(t["q"], kps[r], vps[r], t["block_table"], lens, max_len, w.scale,
-                       partition_size=P, out=out, workspace=ws, window=W)
-        if ev is not None:
-            ev[1].record(stream)
+            if not fused:
+                ops.reshape_and_cache(t["new_key"], t["new_value"], kps[r], vps[r], t["slot_mapping"])
+        decode(i)
 
     if args.calib_copy_mb > 0:
         nbytes = args.calib_copy_mb << 20
@@ -539,18 +573,9 @@ def main() -> int:
         return _bench_reblock(args, w, t, kps, vps, R, dev)
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    wall = _timed(step, args.warmup, args.steps)
+    dec_avg = _event_pass(decode, args.warmup + args.steps, args.steps)
     ms_step = wall * 1e3 / args.steps
-    dec_avg = float(dec_ms.mean())
     achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     path = decode_path("fp8" if fp8 else w.dtype, w.head_dim, w.num_q_heads // w.num_kv_heads, w.block_size)
@@ -570,7 +595,8 @@ def main() -> int:
         cfg["attended_tokens_sum"] = int(attended.sum())
     cfg.update({"partition_size": part, "replicas": R, "tokens_per_step": w.batch,
                 "copy_pairs_per_step": int(pairs.shape[0]),
-                "step": ("copy-on-write + " if pairs.shape[0] else "") + "append 1 token/seq + decode"})
+                "step": ("copy-on-write + " if pairs.shape[0] else "") + "append 1 token/seq + decode"
+                        + (" (one launch: pa_decode_append)" if fused else "")})
     if args.config == 5:
         cfg["unique_kv_bytes"] = 2 * w.unique_blocks * w.block_size * w.num_kv_heads * row_bytes
     result = {
@@ -589,9 +615,7 @@ def main() -> int:
         "config": cfg,
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
-        "decode_kernel_ms": {"mean": round(dec_avg, 5), "p10": round(float(np.percentile(dec_ms, 10)), 5),
-                             "p50": round(float(np.percentile(dec_ms, 50)), 5),
-                             "p90": round(float(np.percentile(dec_ms, 90)), 5)},
+        "decode_kernel_ms": round(dec_avg, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(cfg["workload"], path)},

@@ -127,6 +127,31 @@ pa_status_t pa_copy_blocks(const pa_cache_desc_t* cache, void* k_pool, void* v_p
                            pa_stream_t stream);
 
 /*
+ * pa_decode_append - pa_reshape_and_cache of one new token per sequence followed by
+ * pa_decode, in one launch.
+ *
+ * key/value: [batch][num_kv_heads][head_dim] (the new token of each sequence, 16-byte
+ * aligned); slot_mapping: int32 [batch]. context_lens are the lengths after the append, so
+ * the new token is at position context_lens[b] - 1. For a sequence with slot_mapping[b] >= 0
+ * the decode workgroup that owns that position writes the token's K and V rows to the slot
+ * ([BlockManager essay] §4.4; [Valid-length essay] §4.1: the write lands at the valid
+ * length) and then reads them like every other row, so pool and output equal those of the
+ * two separate calls, bit for bit. slot_mapping[b] < 0 appends nothing for that sequence.
+ * A slot that is not the slot of position context_lens[b] - 1 through block_table is not
+ * written and sets PA_FLAG_BAD_SLOT; the append also does not happen for a sequence whose
+ * length or block ids are invalid (its outputs are NaN, as in pa_decode). The appended
+ * block must not be shared with another sequence (copy it first, pa_copy_blocks). 8-bit
+ * pools return PA_ERR_UNSUPPORTED (use pa_reshape_and_cache_fp8 and pa_decode_fp8).
+ * Everything else is as pa_decode.
+ */
+pa_status_t pa_decode_append(const pa_cache_desc_t* cache, void* out, const void* q, void* k_pool, void* v_pool,
+                             const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale,
+                             const void* key, const void* value, const int32_t* slot_mapping,
+                             int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                             pa_stream_t stream);
+
+/*
  * pa_decode_partition_size - the context-partition length pa_decode will use.
  *
  * `requested` > 0 must be a multiple of block_size covering at most 1024 blocks (else

@@ -352,7 +352,9 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out
                         const int32_t* block_table, int32_t max_blocks_per_seq,
                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                         int32_t max_context_len, float scale, int32_t partition_size, int32_t window,
-                        void* workspace, size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream) {
+                        void* workspace, size_t workspace_bytes, int32_t* err_flag, pa_stream_t stream,
+                        const void* new_key = nullptr, const void* new_value = nullptr,
+                        const int32_t* slot_mapping = nullptr) {
     if (window < 0) return PA_ERR_INVALID_ARGUMENT;
     pa_status_t st = check_cache(cache);
     if (st != PA_OK) return st;
@@ -412,6 +414,10 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out
     a.window = window;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.block_stride = block_stride(cache);
+    a.batch = batch;
+    a.new_key = new_key;
+    a.new_value = new_value;
+    a.slot_mapping = slot_mapping;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = decode_mfma_supported(cache->dtype, cache->head_dim, group, cache->block_size)
                        ? launch_decode_mfma(a, cache->dtype, q_dtype, cache->head_dim, group, batch,
@@ -448,6 +454,20 @@ pa_status_t pa_decode_sliding_window(const pa_cache_desc_t* cache, void* out, co
     return decode_impl(cache, cache ? cache->dtype : 0, out, q, k_pool, v_pool, nullptr, nullptr, block_table,
                        max_blocks_per_seq, context_lens, batch, num_q_heads, max_context_len, scale, partition_size,
                        window, workspace, workspace_bytes, err_flag, stream);
+}
+
+pa_status_t pa_decode_append(const pa_cache_desc_t* cache, void* out, const void* q, void* k_pool, void* v_pool,
+                             const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale,
+                             const void* key, const void* value, const int32_t* slot_mapping,
+                             int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                             pa_stream_t stream) {
+    if (cache && is_fp8(cache)) return PA_ERR_UNSUPPORTED;
+    if (batch > 0 && (!key || !value || !slot_mapping || !aligned16(key) || !aligned16(value)))
+        return PA_ERR_INVALID_ARGUMENT;
+    return decode_impl(cache, cache ? cache->dtype : 0, out, q, k_pool, v_pool, nullptr, nullptr, block_table,
+                       max_blocks_per_seq, context_lens, batch, num_q_heads, max_context_len, scale, partition_size,
+                       0, workspace, workspace_bytes, err_flag, stream, key, value, slot_mapping);
 }
 
 pa_status_t pa_decode_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,

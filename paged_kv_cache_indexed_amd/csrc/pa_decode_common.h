@@ -17,6 +17,8 @@ struct Partition {
     int ntok;    // end of the attended tokens, relative to t0
     int j0;      // logical block of t0: s_ids[i] is the id of block j0 + i
     int len;     // the sequence's context length
+    int npos;    // fused append: the new token's position relative to t0 (its rows are in s_new, and
+                 // the workgroup ends with store_new_rows), or -1
 };
 
 // First attended position of a sequence of length L: a sliding window keeps the last
@@ -36,6 +38,70 @@ __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
     for (int i = threadIdx.x; i < count; i += blockDim.x) store_elem(T{}, out, base + i, __builtin_nanf(""));
 }
 
+// Fused append, step 1: the new token's K and V rows of kv heads [kv0, kv0 + nkv) in
+// registers (vector i of [nkv][K row, V row] held by thread i % NT in slot i / NT), read in
+// the prologue's first round trip where possible; the owner parks them in s_new before the
+// barrier.
+template <typename T, int D, int NT>
+struct NewRows {
+    static constexpr int kRowVecs = D * T::kBytes / 16;
+    static constexpr int kPerThread = (2 * 4 * kRowVecs + NT - 1) / NT;  // up to 4 kv heads
+    u32x4 v[kPerThread];
+
+    __device__ void load(const DecodeArgs& a, int b, int kv0, int nkv) {
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int i = threadIdx.x + k * NT;
+            if (i < 2 * nkv * kRowVecs) {
+                const int kv = i / (2 * kRowVecs);
+                const int which = (i / kRowVecs) & 1;
+                const char* src = static_cast<const char*>(which ? a.new_value : a.new_key) +
+                                  (((size_t)b * a.num_kv_heads + kv0 + kv) * D) * T::kBytes + 16 * (i % kRowVecs);
+                v[k] = load16(src);
+            }
+        }
+    }
+    __device__ void park(int nkv, char* s_new) const {
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int i = threadIdx.x + k * NT;
+            if (i < 2 * nkv * kRowVecs) store16(s_new + (size_t)i * 16, v[k]);
+        }
+    }
+};
+
+// Fused append, step 2 (after the barrier, block ids checked): true if slot_mapping[b] is
+// the slot of position L - 1 through the table; the stream then takes the new token's rows
+// from s_new, so nothing in this launch reads the slot. Otherwise PA_FLAG_BAD_SLOT is raised
+// and the rows are never written.
+__device__ __forceinline__ bool check_new_slot(const DecodeArgs& a, int L, int jp, int slot, const int* s_ids) {
+    const int lbs = a.log2_block_size;
+    const int pos = L - 1;
+    if (slot == (s_ids[(pos >> lbs) - jp] << lbs) + (pos & ((1 << lbs) - 1))) return true;
+    if (threadIdx.x == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_SLOT);
+    return false;
+}
+
+// Fused append, step 3 (the owner's last act, after its outputs): the staged rows go to the
+// slot ([BlockManager essay] §4.4; [Valid-length essay] §4.1). Issued at the end so that the
+// stores do not compete with the workgroup's own stream; nothing waits for them.
+template <typename T, int D>
+__device__ void store_new_rows(const DecodeArgs& a, int b, int kv0, int nkv, const char* s_new) {
+    constexpr int kRowVecs = D * T::kBytes / 16;
+    const int lbs = a.log2_block_size;
+    const int slot = a.slot_mapping[b];
+    const int blk = slot >> lbs;
+    const int off = slot & ((1 << lbs) - 1);
+    for (int i = threadIdx.x; i < 2 * nkv * kRowVecs; i += blockDim.x) {
+        const int kv = i / (2 * kRowVecs);
+        const int which = (i / kRowVecs) & 1;
+        const int v = i % kRowVecs;
+        char* dst = static_cast<char*>(const_cast<void*>(which ? a.v_pool : a.k_pool)) + (size_t)blk * a.block_stride +
+                    (((((size_t)kv0 + kv) << lbs) + off) * D) * T::kBytes + 16 * v;
+        store16(dst, load16(s_new + (size_t)i * 16));
+    }
+}
+
 // Checks the sequence length, stages the partition's block ids in s_ids and validates
 // them. Returns false when the workgroup has nothing more to do: the partition is past the
 // end of the sequence, or the sequence is invalid (the sink sets its outputs, or this
@@ -50,9 +116,16 @@ __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
 //
 // A valid length is at least min_len (1 for a decode; the number of new queries otherwise).
 // Sink provides nan_outputs() and nan_records(p) for the outputs this workgroup owns.
+//
+// Fused append (a.slot_mapping set; the workgroup covers kv heads [kv0, kv0 + nkv) and
+// gives s_new): the workgroup whose partition holds the last position L - 1 stages the new
+// token's rows in s_new, checks the slot once its ids are checked, and reports the token's
+// position in part.npos: the stream takes its rows from s_new and the workgroup writes them
+// to the slot when it is done (store_new_rows).
 template <typename T, int D, int NT, typename Sink>
 __device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int min_len, const Sink& sink,
-                                        int* s_ids, Partition& part) {
+                                        int* s_ids, Partition& part, int kv0 = 0, int nkv = 0,
+                                        char* s_new = nullptr) {
     constexpr int kPerThread = (kMaxIdsPerPartition + NT - 1) / NT;
     const int tid = threadIdx.x;
     const int lbs = a.log2_block_size;
@@ -72,6 +145,13 @@ __device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int m
         idv[k] = (i < lim) ? trow[jp + i] : 0;
     }
     if (a.window <= 0) L = a.context_lens[b];
+    const bool appending = a.slot_mapping != nullptr && nkv > 0 && s_new != nullptr;
+    const int slot = appending ? a.slot_mapping[b] : -1;
+    // speculative only in partition 0 (the owner for every one-partition sequence): workgroups
+    // of later partitions are mostly past the end of short sequences, and a wave cannot retire
+    // before its loads return
+    NewRows<T, D, NT> rows;
+    if (appending && p == 0) rows.load(a, b, kv0, nkv);
     int flag = 0;
     if (L <= 0) flag = PA_FLAG_EMPTY_CONTEXT;
     else if (L > a.max_context_len || ((L - 1) >> lbs) >= a.max_blocks_per_seq || L < min_len)
@@ -91,6 +171,12 @@ __device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int m
     const int t1 = min(L, part.t0 + P);
     part.ntok = t1 - part.t0;
     part.j0 = jp;
+    part.npos = -1;
+    const bool owner = slot >= 0 && t1 == L;  // holds the new token
+    if (owner) {
+        if (p != 0) rows.load(a, b, kv0, nkv);
+        rows.park(nkv, s_new);
+    }
     // only the blocks overlapping [t0, t1) are staged and checked: blocks before a window
     // may already be released (-1)
     const int nids = ((t1 - 1) >> lbs) - jp + 1;
@@ -113,6 +199,7 @@ __device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int m
         else sink.nan_records(p);
         return false;
     }
+    if (owner && check_new_slot(a, L, jp, slot, s_ids)) part.npos = L - 1 - part.t0;
     return true;
 }
 
@@ -134,14 +221,16 @@ struct DecodeNanSink {
 
 template <typename T, int D, int NT>
 __device__ __forceinline__ bool partition_prologue_heads(const DecodeArgs& a, int p, int h0, int nq, int b,
-                                                         int* s_ids, Partition& part) {
-    return partition_prologue_sink<T, D, NT>(a, p, b, 1, DecodeNanSink<T, D>{a, b, h0, nq}, s_ids, part);
+                                                         int* s_ids, Partition& part, char* s_new = nullptr) {
+    const int group = a.num_q_heads / a.num_kv_heads;
+    return partition_prologue_sink<T, D, NT>(a, p, b, 1, DecodeNanSink<T, D>{a, b, h0, nq}, s_ids, part, h0 / group,
+                                             nq / group, s_new);
 }
 
 template <typename T, int D, int G, int NT>
 __device__ __forceinline__ bool partition_prologue(const DecodeArgs& a, int p, int kvh, int b, int* s_ids,
-                                                   Partition& part) {
-    return partition_prologue_heads<T, D, NT>(a, p, kvh * G, G, b, s_ids, part);
+                                                   Partition& part, char* s_new = nullptr) {
+    return partition_prologue_heads<T, D, NT>(a, p, kvh * G, G, b, s_ids, part, s_new);
 }
 
 // Merges the per-wave states (s_m, s_l: base-2 running max and sum; s_acc: unnormalised

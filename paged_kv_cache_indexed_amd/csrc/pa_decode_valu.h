@@ -64,10 +64,13 @@ __device__ __forceinline__ float dot_frag(const QFrag<T, KV>& q, u32x4 k) {
 // With 8-bit pools each token row also has a float32 scale (k_scale / v_scale, one per
 // (block, kv head, offset)): the K scale multiplies the row's score, the V scale its softmax
 // weight in the weighted sum (not in the running sum, which normalises the weights).
+//
+// Fused append: the row at position part.npos (if >= 0) is taken from s_new (K row, then V
+// row, of this wave's kv head) instead of the pool.
 template <typename T, typename KV, int D, int G, int UNROLL, int STRIDE>
 __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int* s_ids, const Partition& part,
                                                  int kvh, int slot, const QFrag<T, KV>* qv, float* m, float* l,
-                                                 float (*acc)[RowShape<KV, D>::E]) {
+                                                 float (*acc)[RowShape<KV, D>::E], const char* s_new = nullptr) {
     constexpr bool kScaled = std::is_same_v<KV, FP8>;
     constexpr int E = RowShape<KV, D>::E;
     constexpr int LPR = RowShape<KV, D>::LPR;
@@ -80,6 +83,7 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
     const int ntok = part.ntok;
     const int rel_lo = part.rel_lo;
     const int g0 = rel_lo / RPL;  // first row group holding an attended token
+    const int npos = part.npos;   // fused append: this row comes from s_new, after the loop
 
     const size_t head_bytes = (size_t)bs * D * KV::kBytes;
     const size_t block_bytes = (size_t)a.block_stride;
@@ -113,7 +117,7 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
             const int rel = (g0 + (it * UNROLL + u) * STRIDE + slot) * RPL;
             const int id = __builtin_amdgcn_readfirstlane(idv[u]);
             const size_t slab = (size_t)id * block_bytes + (size_t)kvh * head_bytes;
-            const bool live = rel + row < ntok && rel + row >= rel_lo;
+            const bool live = rel + row < ntok && rel + row >= rel_lo && rel + row != npos;
             const uint32_t off = live ? (uint32_t)((rel & (bs - 1)) * D * KV::kBytes) + lane_bytes : kOutOfRange;
             kk[u] = buffer_load16(make_rsrc(kpool + slab, slab_bytes), off);
             vv[u] = buffer_load16(make_rsrc(vpool + slab, slab_bytes), off);
@@ -131,7 +135,7 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int rel = (g0 + (it * UNROLL + u) * STRIDE + slot) * RPL + row;
-            const bool valid = rel < ntok && rel >= rel_lo;
+            const bool valid = rel < ntok && rel >= rel_lo && rel != npos;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float d = group_sum<LPR>(dot_frag(qv[g], kk[u]));
@@ -189,6 +193,29 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
     __builtin_amdgcn_sched_barrier(0);
     if (it < niters) compute(it, ka, va, ksa, vsa);
 
+    // Fused append: the new token (masked in the loop above) joins the row-0 stream of the
+    // first wave that owns this head, its K and V rows read from s_new.
+    if constexpr (!kScaled) {
+        if (npos >= 0 && slot == 0) {
+            const u32x4 kx = *reinterpret_cast<const u32x4*>(s_new + 16 * col);
+            float vx[E];
+            unpack(KV{}, *reinterpret_cast<const u32x4*>(s_new + D * KV::kBytes + 16 * col), vx);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float d = group_sum<LPR>(dot_frag(qv[g], kx));
+                const float sc = (row == 0) ? d * a.scale_log2 : -INFINITY;
+                const float mn = fmaxf(m[g], sc);
+                const float ms = (mn == -INFINITY) ? 0.f : mn;
+                const float alpha = fast_exp2(m[g] - ms);
+                const float pr = fast_exp2(sc - ms);
+                m[g] = mn;
+                l[g] = l[g] * alpha + pr;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pr, vx[e], acc[g][e] * alpha);
+            }
+        }
+    }
+
     // ---- merge the RPL row streams of this wave ----
 #pragma unroll
     for (int off = LPR; off < 64; off <<= 1) {
@@ -221,18 +248,16 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int h0, QFrag
 
 // Split mode: the 4 waves of a workgroup share one kv head's partition (groups of RPL rows
 // dealt round-robin), and their states merge through LDS.
+// One (partition, kv head, sequence) item of split mode: the 4 waves share the partition,
+// merge through LDS and write the item's output or partition record. All threads call it;
+// it returns with every thread past the item (the LDS buffers may be reused after the next
+// barrier).
 template <typename T, typename KV, int D, int G, int UNROLL>
-__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
+__device__ __forceinline__ void split_item(const DecodeArgs& a, int p, int kvh, int b, int* s_ids,
+                                           float (*s_m)[G], float (*s_l)[G], float (*s_acc)[G][D],
+                                           char* s_new) {
     constexpr int E = RowShape<KV, D>::E;
     constexpr int LPR = RowShape<KV, D>::LPR;
-    __shared__ int s_ids[kMaxIdsPerPartition];
-    __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[kWaves][G];
-    __shared__ float s_acc[kWaves][G][D];
-
-    const int p = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int row = lane / LPR;
@@ -242,10 +267,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     QFrag<T, KV> qv[G];
     load_q<T, KV, D, G>(a, b, kvh * G, qv);
     Partition part;
-    if (!partition_prologue<T, D, G, kThreads>(a, p, kvh, b, s_ids, part)) return;
+    if (!partition_prologue<T, D, G, kThreads>(a, p, kvh, b, s_ids, part, s_new)) return;
 
     float m[G], l[G], acc[G][E];
-    stream_partition<T, KV, D, G, UNROLL, kWaves>(a, s_ids, part, kvh, wave, qv, m, l, acc);
+    stream_partition<T, KV, D, G, UNROLL, kWaves>(a, s_ids, part, kvh, wave, qv, m, l, acc, s_new);
     if (row == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -261,6 +286,21 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     }
     __syncthreads();
     partition_epilogue<T, D, G>(a, p, kvh, b, part, s_m, s_l, s_acc);
+    if (part.npos >= 0) store_new_rows<KV, D>(a, b, kvh, 1, s_new);
+}
+
+// Split mode: the 4 waves of a workgroup share one kv head's partition (groups of RPL rows
+// dealt round-robin), and their states merge through LDS. One workgroup per grid cell.
+template <typename T, typename KV, int D, int G, int UNROLL>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
+    __shared__ int s_ids[kMaxIdsPerPartition];
+    __shared__ float s_m[kWaves][G];
+    __shared__ float s_l[kWaves][G];
+    __shared__ float s_acc[kWaves][G][D];
+    // the new token's K and V rows (fused append; 16/32-bit pools only)
+    __shared__ __align__(16) char s_new[std::is_same_v<KV, FP8> ? 16 : 2 * D * KV::kBytes];
+    split_item<T, KV, D, G, UNROLL>(a, blockIdx.x, blockIdx.y, blockIdx.z, s_ids, s_m, s_l, s_acc,
+                                    std::is_same_v<KV, FP8> ? nullptr : s_new);
 }
 
 // Head mode, for short partitions: a workgroup owns one (partition, sequence) and 4
@@ -284,14 +324,20 @@ __global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs 
     const int kvh = active ? kvh0 + wave : kvh0;
     const int h0 = kvh * G;
 
+    // the new token's K and V rows of the workgroup's kv heads (fused append; 16/32-bit pools)
+    constexpr int kRowBytes = D * KV::kBytes;
+    __shared__ __align__(16) char s_new[std::is_same_v<KV, FP8> ? 16 : kWaves * 2 * kRowBytes];
     QFrag<T, KV> qv[G];
     load_q<T, KV, D, G>(a, b, h0, qv);
     Partition part;
-    if (!partition_prologue_heads<T, D, kThreads>(a, p, kvh0 * G, nkv * G, b, s_ids, part)) return;
+    if (!partition_prologue_heads<T, D, kThreads>(a, p, kvh0 * G, nkv * G, b, s_ids, part,
+                                                  std::is_same_v<KV, FP8> ? nullptr : s_new))
+        return;
     if (!active) return;  // no barrier follows
 
     float m[G], l[G], acc[G][E];
-    stream_partition<T, KV, D, G, UNROLL, 1>(a, s_ids, part, kvh, 0, qv, m, l, acc);
+    stream_partition<T, KV, D, G, UNROLL, 1>(a, s_ids, part, kvh, 0, qv, m, l, acc,
+                                             s_new + (std::is_same_v<KV, FP8> ? 0 : wave * 2 * kRowBytes));
     if (row == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -308,6 +354,23 @@ __global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs 
                     a.ws_ml[rec * 2] = m[g];
                     a.ws_ml[rec * 2 + 1] = l[g];
                 }
+            }
+        }
+    }
+    // each wave stores its own kv head's new rows (nothing to do when not appending)
+    if constexpr (!std::is_same_v<KV, FP8>) {
+        if (part.npos >= 0) {
+            constexpr int kVecs = 2 * kRowBytes / 16;
+            const int lbs = a.log2_block_size;
+            const int slot = a.slot_mapping[b];
+            char* base[2] = {static_cast<char*>(const_cast<void*>(a.k_pool)),
+                             static_cast<char*>(const_cast<void*>(a.v_pool))};
+            for (int i = lane; i < kVecs; i += 64) {
+                const int which = i / (kRowBytes / 16);
+                const int v = i % (kRowBytes / 16);
+                char* dst = base[which] + (size_t)(slot >> lbs) * a.block_stride +
+                            ((((size_t)kvh << lbs) + (slot & ((1 << lbs) - 1))) * kRowBytes) + 16 * v;
+                store16(dst, load16(s_new + (size_t)(wave * 2 * kRowBytes) + 16 * i));
             }
         }
     }

@@ -38,6 +38,11 @@ struct DecodeArgs {
     int64_t block_stride;  // bytes from one physical block to the next in k_pool / v_pool
     // multi-token attention only: query rows query_start[b] .. query_start[b+1]-1 belong to
     // sequence b; each workgroup covers one of col_tiles tiles of 16 (query, head) columns
+    // fused append (pa_decode_append): the new token of sequence b, rows new_key/new_value
+    // [batch][num_kv_heads][head_dim], goes to slot_mapping[b] before the decode reads it
+    const void* new_key;
+    const void* new_value;
+    const int32_t* slot_mapping;
     const int32_t* query_start;
     int32_t col_tiles;
     int32_t batch;

@@ -163,6 +163,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __shared__ float s_m[NW][NCOL];
     __shared__ float s_l[NW][NCOL];
     __shared__ float s_acc[NW][NCOL][D];
+    // the new token's K and V rows (fused append of the decode over 16-bit pools)
+    constexpr bool kAppendable = !kFp8 && !kMulti;
+    __shared__ __align__(16) char s_new[kAppendable ? 2 * D * 2 : 16];
 
     const int p = blockIdx.x;
     const int kvh = blockIdx.y;
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                                                     s_ids, part))
             return;
     } else {
-        if (!partition_prologue<T, D, G, NW * 64>(a, p, kvh, b, s_ids, part)) return;
+        if (!partition_prologue<T, D, G, NW * 64>(a, p, kvh, b, s_ids, part, kAppendable ? s_new : nullptr)) return;
     }
     int ntok = part.ntok;
     int lim_col = ntok;  // tokens (relative to the partition) this lane's column may see
@@ -277,8 +280,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int s = 0; s < NS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    const int npos = part.npos;
     auto compute = [&](int it, u32x4 (*kk)[NL], u32x4 (*vv)[NL], const u32x4* ks, const u32x4* vs) {
         const int rel0 = (c0 + it * NW + wave) * kChunk;
+        if constexpr (kAppendable) {
+            if (npos >= 0) {  // fused append: the new token's rows come from s_new (wave-uniform test)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int d = npos - (rel0 + 16 * t);
+                    if (d >= 0 && d < 16 && n == d) {
+#pragma unroll
+                        for (int c = 0; c < NL; ++c) {
+                            kk[t][c] = *reinterpret_cast<const u32x4*>(s_new + 64 * c + seg);
+                            vv[t][c] = *reinterpret_cast<const u32x4*>(s_new + D * 2 + 64 * c + seg);
+                        }
+                    }
+                }
+            }
+        }
         float sc[8];
         float vscale[8];  // V scale of each P entry (8-bit pools)
 #pragma unroll
@@ -447,6 +466,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
     } else {
         partition_epilogue<T, D, G, NW>(a, p, kvh, b, part, s_m, s_l, s_acc);
+        if constexpr (kAppendable) {
+            if (part.npos >= 0) store_new_rows<T, D>(a, b, kvh, 1, s_new);
+        }
     }
 }
 

@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (CacheDesc, pa_copy_blocks, pa_copy_blocks_fp8, pa_decode, pa_decode_fp8,
+from ._lib import (CacheDesc, pa_copy_blocks, pa_copy_blocks_fp8, pa_decode, pa_decode_append, pa_decode_fp8,
                    pa_decode_sliding_window, pa_decode_sliding_window_workspace_bytes,
                    pa_decode_workspace_bytes, pa_multi_token_attention, pa_multi_token_workspace_bytes,
                    pa_reblock, pa_reshape_and_cache, pa_reshape_and_cache_fp8)
@@ -45,6 +45,19 @@ def decode(q, k_pool, v_pool, block_table, context_lens, max_context_len: int, s
     else:
         pa_decode(CacheDesc.of(k_pool), out, q, k_pool, v_pool, block_table, context_lens,
                   max_context_len, scale, partition_size, workspace, err_flag, stream)
+    return out
+
+
+def decode_append(q, k_pool, v_pool, block_table, context_lens, max_context_len: int, scale: float, key, value,
+                  slot_mapping, partition_size: int = 0, out=None, workspace=None, err_flag=None, stream=None):
+    """reshape_and_cache of one token per sequence, then decode over the grown contexts
+    (context_lens include the new token), in one launch."""
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = workspace_for(k_pool, q.shape[0], q.shape[1], max_context_len, partition_size)
+    pa_decode_append(CacheDesc.of(k_pool), out, q, k_pool, v_pool, block_table, context_lens, max_context_len,
+                     scale, key, value, slot_mapping, partition_size, workspace, err_flag, stream)
     return out
 
 

@@ -1,0 +1,94 @@
+"""GPU: the fused append + decode (pa_decode_append) against the two separate calls (pools
+bit for bit; outputs bit for bit on the matrix cores, within tolerance on the VALU kernels,
+where the new token is summed in another order) and against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_indexed_amd import ops
+from tests.gpu_util import assert_close, note, require_gpu
+from workloads import build_paged, config_workload
+
+pytestmark = pytest.mark.gpu
+
+_INT = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16}
+
+
+def _both(w, dev, P=0, slots=None):
+    """Fused and separate runs from identical device inputs; returns (fused, separate,
+    err_fused, pools_fused, pools_separate)."""
+    t1, t2 = w.to_device(dev), w.to_device(dev)
+    sl = t1["slot_mapping"] if slots is None else torch.as_tensor(slots, dtype=torch.int32, device=dev)
+    L = int(w.lens_after_append.max())
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    fused = ops.decode_append(t1["q"], t1["k_pool"], t1["v_pool"], t1["block_table"], t1["lens_after"], L, w.scale,
+                              t1["new_key"], t1["new_value"], sl, partition_size=P, err_flag=err)
+    ops.reshape_and_cache(t2["new_key"], t2["new_value"], t2["k_pool"], t2["v_pool"], sl)
+    sep = ops.decode(t2["q"], t2["k_pool"], t2["v_pool"], t2["block_table"], t2["lens_after"], L, w.scale,
+                     partition_size=P)
+    torch.cuda.synchronize()
+    return fused, sep, int(err.item()), (t1["k_pool"], t1["v_pool"]), (t2["k_pool"], t2["v_pool"])
+
+
+def _bits(x):
+    return x.view(_INT[x.dtype])
+
+
+@pytest.mark.parametrize("cfg,kw,P", [(1, {}, 0), (1, {}, 32), (2, dict(batch=16, heads=8), 0),
+                                      (2, dict(batch=16, heads=8), 64), (2, dict(batch=16, heads=8), 256),
+                                      (3, dict(batch=64, heads=4), 0), (4, dict(batch=8), 0), (4, dict(batch=8), 512),
+                                      (3, dict(batch=64, heads=4, block_size=8), 0)])
+def test_fused_equals_separate_calls_bitwise(cfg, kw, P):
+    dev = require_gpu()
+    w = config_workload(cfg, seed=11, **kw)
+    note(f"decode_append cfg={cfg} {kw} P={P}")
+    fused, sep, err, pf, ps = _both(w, dev, P)
+    assert err == 0
+    for a, b in zip(pf, ps):
+        assert torch.equal(_bits(a), _bits(b)), "fused append wrote a different pool"
+    if cfg == 4:  # matrix cores: the new row takes its usual place in the stream, bit for bit
+        assert torch.equal(_bits(fused), _bits(sep)), "fused output differs from the separate calls"
+    else:  # VALU: the new token joins one row stream after the loop (another summation order)
+        assert_close(fused.float().cpu().numpy(), sep.float().cpu().numpy().astype(np.float64), w.dtype,
+                     f"fused vs separate cfg {cfg} P={P}")
+    ka, va = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.new_key, w.new_value, w.slot_mapping)
+    ref = oracle.paged_decode(w.q, ka, va, w.block_table, w.lens_after_append, w.scale)
+    assert_close(fused.float().cpu().numpy(), ref, w.dtype, f"decode_append cfg {cfg} P={P}")
+
+
+def test_fused_skips_negative_slots_and_flags_wrong_ones():
+    dev = require_gpu()
+    w = config_workload(2, seed=12, batch=8, heads=4)
+    slots = w.slot_mapping.copy()
+    slots[1] = -1                       # no append: the decode reads the old (NaN) slot
+    slots[2] = slots[3]                 # not this sequence's last position: flagged, not written
+    note("decode_append slots")
+    fused, sep, err, pf, ps = _both(w, dev, 0, slots)
+    assert err & 8
+    o = fused.float().cpu().numpy()
+    assert np.all(np.isnan(o[1])) and np.all(np.isnan(o[2]))  # their last rows were never written
+    keep = [0] + list(range(3, 8))
+    ka, va = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.new_key[keep], w.new_value[keep], w.slot_mapping[keep])
+    ref = oracle.paged_decode(w.q, ka, va, w.block_table, w.lens_after_append, w.scale)
+    assert_close(o[keep], ref[keep], "f16", "decode_append next to skipped and bad slots")
+
+
+def test_fused_on_a_multilayer_view():
+    dev = require_gpu()
+    w = config_workload(2, seed=13, batch=8, heads=4)
+    t = w.to_device(dev)
+    nb, hkv, bs, d = t["k_pool"].shape
+    cache = torch.zeros((nb, 2, 3, hkv, bs, d), dtype=torch.float16, device=dev)
+    cache[:, 0, 1].copy_(t["k_pool"])
+    cache[:, 1, 1].copy_(t["v_pool"])
+    L = int(w.lens_after_append.max())
+    note("decode_append on a strided layer view")
+    out = ops.decode_append(t["q"], cache[:, 0, 1], cache[:, 1, 1], t["block_table"], t["lens_after"], L, w.scale,
+                            t["new_key"], t["new_value"], t["slot_mapping"])
+    torch.cuda.synchronize()
+    ka, va = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.new_key, w.new_value, w.slot_mapping)
+    ref = oracle.paged_decode(w.q, ka, va, w.block_table, w.lens_after_append, w.scale)
+    assert_close(out.float().cpu().numpy(), ref, "f16", "decode_append multilayer")
+    assert torch.all(cache[:, :, 0] == 0) and torch.all(cache[:, :, 2] == 0), "other layers were written"
