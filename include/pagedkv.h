@@ -128,18 +128,22 @@ pa_status_t pa_copy_blocks(const pa_cache_desc_t* cache, void* k_pool, void* v_p
 
 /*
  * pa_decode_append - pa_reshape_and_cache of one new token per sequence followed by
- * pa_decode, in one launch.
+ * pa_decode, fused: the decode takes the new rows straight from key/value.
  *
  * key/value: [batch][num_kv_heads][head_dim] (the new token of each sequence, 16-byte
  * aligned); slot_mapping: int32 [batch]. context_lens are the lengths after the append, so
  * the new token is at position context_lens[b] - 1. For a sequence with slot_mapping[b] >= 0
- * the decode workgroup that owns that position writes the token's K and V rows to the slot
- * ([BlockManager essay] §4.4; [Valid-length essay] §4.1: the write lands at the valid
- * length) and then reads them like every other row, so pool and output equal those of the
- * two separate calls, bit for bit. slot_mapping[b] < 0 appends nothing for that sequence.
- * A slot that is not the slot of position context_lens[b] - 1 through block_table is not
- * written and sets PA_FLAG_BAD_SLOT; the append also does not happen for a sequence whose
- * length or block ids are invalid (its outputs are NaN, as in pa_decode). The appended
+ * the decode reads the token's K and V rows from key/value, never from the pool, and the
+ * rows are written to the slot ([BlockManager essay] §4.4; [Valid-length essay] §4.1: the
+ * write lands at the valid length) by the decode workgroup that owns that position, as its
+ * last act, or, when the launch has a reduce pass (some sequence spans several partitions),
+ * by the reduce kernel after the decode. Afterwards the pool equals that of the two separate
+ * calls bit for bit, and the output equals pa_decode's up to the order of the fp32 sums
+ * (bit for bit on the matrix-core path). slot_mapping[b] < 0 appends nothing for that
+ * sequence. A slot that is not the slot of position context_lens[b] - 1 through block_table
+ * is not written and sets PA_FLAG_BAD_SLOT. A sequence with an invalid length or block id
+ * gets NaN outputs, as in pa_decode; its row is written only if its length is valid and
+ * every block id of the partition holding the new position is valid. The appended
  * block must not be shared with another sequence (copy it first, pa_copy_blocks). 8-bit
  * pools return PA_ERR_UNSUPPORTED (use pa_reshape_and_cache_fp8 and pa_decode_fp8).
  * Everything else is as pa_decode.
@@ -165,7 +169,8 @@ int32_t pa_decode_partition_size(const pa_cache_desc_t* cache, int32_t batch, in
  * pa_decode_workspace_bytes - bytes of device workspace pa_decode needs (0 if none).
  *
  * The workspace holds one (max, sum, normalised output) record per sequence, query head
- * and context partition when some sequence spans more than one partition.
+ * and context partition, and one int32 per sequence (pa_decode_append), when some sequence
+ * spans more than one partition.
  */
 size_t pa_decode_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, int32_t num_q_heads,
                                  int32_t max_context_len, int32_t partition_size);
@@ -189,8 +194,10 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, in
  * partition_size: 0 = default, else as pa_decode_partition_size. When a sequence spans
  * several partitions, each writes (max, sum, output) to `workspace` and a second kernel
  * combines them with a log-sum-exp weighting; workspace_bytes must be at least
- * pa_decode_workspace_bytes(...) (the workspace may be NULL when that is 0). An 8-bit pool
- * returns PA_ERR_UNSUPPORTED (use pa_decode_fp8).
+ * pa_decode_workspace_bytes(...) (the workspace may be NULL when that is 0). A launch
+ * holds at most 65535 partitions per sequence (max_context_len / partition size, rounded
+ * up); more returns PA_ERR_UNSUPPORTED. An 8-bit pool returns PA_ERR_UNSUPPORTED (use
+ * pa_decode_fp8).
  */
 pa_status_t pa_decode(const pa_cache_desc_t* cache, void* out, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table, int32_t max_blocks_per_seq,

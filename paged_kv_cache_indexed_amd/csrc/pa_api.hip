@@ -226,7 +226,8 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, in
     if (P <= 0 || num_q_heads <= 0) return 0;
     const int64_t parts = ceil_div(max_context_len, P);
     if (parts <= 1) return 0;
-    return (size_t)batch * num_q_heads * parts * (cache->head_dim + 2) * sizeof(float);
+    // partition records, then one slot per sequence for a fused append (pa_decode_append)
+    return (size_t)batch * num_q_heads * parts * (cache->head_dim + 2) * sizeof(float) + (size_t)batch * sizeof(int32_t);
 }
 
 size_t pa_decode_sliding_window_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch,
@@ -306,6 +307,7 @@ pa_status_t pa_multi_token_attention(const pa_cache_desc_t* cache, int32_t q_dty
         multi_partition_size(cache, batch, num_q_heads, max_context_len, max_query_len, partition_size);
     if (P <= 0) return PA_ERR_INVALID_ARGUMENT;
     const int64_t parts = ceil_div(max_context_len, P);
+    if (parts > kMaxPartitionSlots) return PA_ERR_UNSUPPORTED;
     const size_t need = pa_multi_token_workspace_bytes(cache, batch, num_q_tokens, num_q_heads, max_context_len,
                                                        max_query_len, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_INVALID_ARGUMENT;
@@ -387,7 +389,7 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out
     const int32_t P = pa_decode_partition_size(cache, batch, num_q_heads, span, partition_size);
     if (P <= 0) return PA_ERR_INVALID_ARGUMENT;
     const int64_t parts = ceil_div(span, P);
-    if (parts > INT32_MAX) return PA_ERR_INVALID_ARGUMENT;
+    if (parts > kMaxPartitionSlots) return PA_ERR_UNSUPPORTED;
     const size_t need = pa_decode_workspace_bytes(cache, batch, num_q_heads, span, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_INVALID_ARGUMENT;
 
@@ -418,6 +420,9 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out
     a.new_key = new_key;
     a.new_value = new_value;
     a.slot_mapping = slot_mapping;
+    // with a reduce pass, the new rows are written by it, after the decode has read the pool
+    a.ws_slot = (slot_mapping && parts > 1) ? reinterpret_cast<int32_t*>(a.ws_ml + (size_t)batch * num_q_heads * parts * 2)
+                                            : nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = decode_mfma_supported(cache->dtype, cache->head_dim, group, cache->block_size)
                        ? launch_decode_mfma(a, cache->dtype, q_dtype, cache->head_dim, group, batch,

@@ -10,11 +10,34 @@ namespace {
 //   out = sum_p w_p o_p / sum_p w_p,  w_p = l_p * 2^(m_p - max_p m_p),
 // where o_p is the partition's normalised output and (m_p, l_p) its base-2 running max and
 // sum. A NaN sum (bad block in that partition) makes the whole output NaN.
+//
+// Fused append: the work-group of the first query head of each kv head also writes that kv
+// head's new K and V rows to the slot the decode checked (a.ws_slot). Written here, in a
+// short burst after the decode, they cost far less than as scattered stores among the
+// decode's reads.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
     const int h = blockIdx.x;
     const int b = blockIdx.y;
     const int e = threadIdx.x;
+    if (a.ws_slot) {
+        const int group = a.num_q_heads / a.num_kv_heads;
+        const int slot = a.ws_slot[b];
+        if (h % group == 0 && slot >= 0) {
+            constexpr int kRowVecs = D * T::kBytes / 16;
+            const int kvh = h / group;
+            const int lbs = a.log2_block_size;
+            for (int i = e; i < 2 * kRowVecs; i += D) {
+                const int which = i / kRowVecs;
+                const int v = i % kRowVecs;
+                const size_t row = ((size_t)b * a.num_kv_heads + kvh) * D * T::kBytes + 16 * v;
+                char* dst = static_cast<char*>(const_cast<void*>(which ? a.v_pool : a.k_pool)) +
+                            (size_t)(slot >> lbs) * a.block_stride +
+                            ((((size_t)kvh << lbs) + (slot & ((1 << lbs) - 1))) * D) * T::kBytes + 16 * v;
+                store16(dst, load16(static_cast<const char*>(which ? a.new_value : a.new_key) + row));
+            }
+        }
+    }
     const int L = a.context_lens[b];
     if (L <= 0 || L > a.max_context_len || (L - 1) >> a.log2_block_size >= a.max_blocks_per_seq) return;
     const int nparts = (L - partition_base(a, L) + a.partition_size - 1) / a.partition_size;

@@ -10,6 +10,16 @@ namespace pagedkv {
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeThreads = kDecodeWaves * 64;
 
+// Grid of the decode kernels: x = kv head (or group of kv heads), y = sequence (times the
+// column tiles of a multi-token launch), z = partition. Work-groups are dealt to the 8 XCDs
+// round-robin in linear order, x fastest, so every XCD gets an equal share of every
+// partition index. (With the partition fastest, a partition count that is a multiple of 4
+// sends every first partition, the only live one of a short sequence, to 2 of the 8 XCDs:
+// twice the time on long-tailed lengths. Taking the last partitions first, so that the
+// longest sequences start early, measured slower than this order: the dead work-groups of
+// the late partitions then all queue ahead of the live ones.)
+__device__ __forceinline__ int grid_partition() { return (int)blockIdx.z; }
+
 struct Partition {
     int nparts;  // partitions of this sequence
     int t0;      // first position of this partition (a block multiple)
@@ -19,6 +29,7 @@ struct Partition {
     int len;     // the sequence's context length
     int npos;    // fused append: the new token's position relative to t0 (its rows are in s_new, and
                  // the workgroup ends with store_new_rows), or -1
+    int slot;    // fused append: the new token's slot (when npos >= 0)
 };
 
 // First attended position of a sequence of length L: a sliding window keeps the last
@@ -41,11 +52,11 @@ __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
 // Fused append, step 1: the new token's K and V rows of kv heads [kv0, kv0 + nkv) in
 // registers (vector i of [nkv][K row, V row] held by thread i % NT in slot i / NT), read in
 // the prologue's first round trip where possible; the owner parks them in s_new before the
-// barrier.
-template <typename T, int D, int NT>
+// barrier. NKV bounds nkv.
+template <typename T, int D, int NT, int NKV>
 struct NewRows {
     static constexpr int kRowVecs = D * T::kBytes / 16;
-    static constexpr int kPerThread = (2 * 4 * kRowVecs + NT - 1) / NT;  // up to 4 kv heads
+    static constexpr int kPerThread = (2 * NKV * kRowVecs + NT - 1) / NT;
     u32x4 v[kPerThread];
 
     __device__ void load(const DecodeArgs& a, int b, int kv0, int nkv) {
@@ -82,14 +93,16 @@ __device__ __forceinline__ bool check_new_slot(const DecodeArgs& a, int L, int j
     return false;
 }
 
-// Fused append, step 3 (the owner's last act, after its outputs): the staged rows go to the
-// slot ([BlockManager essay] §4.4; [Valid-length essay] §4.1). Issued at the end so that the
-// stores do not compete with the workgroup's own stream; nothing waits for them.
+// Fused append, step 3 (the owner's last act, after its outputs, when the launch has no
+// reduce pass): the staged rows go to the slot ([BlockManager essay] §4.4; [Valid-length
+// essay] §4.1). Issued at the end so that the stores do not compete with the workgroup's own
+// stream; nothing waits for them.
+// The slot comes from the prologue's registers: reading slot_mapping again here would add a
+// memory round trip to the end of every owner workgroup.
 template <typename T, int D>
-__device__ void store_new_rows(const DecodeArgs& a, int b, int kv0, int nkv, const char* s_new) {
+__device__ void store_new_rows(const DecodeArgs& a, int slot, int kv0, int nkv, const char* s_new) {
     constexpr int kRowVecs = D * T::kBytes / 16;
     const int lbs = a.log2_block_size;
-    const int slot = a.slot_mapping[b];
     const int blk = slot >> lbs;
     const int off = slot & ((1 << lbs) - 1);
     for (int i = threadIdx.x; i < 2 * nkv * kRowVecs; i += blockDim.x) {
@@ -121,8 +134,8 @@ __device__ void store_new_rows(const DecodeArgs& a, int b, int kv0, int nkv, con
 // gives s_new): the workgroup whose partition holds the last position L - 1 stages the new
 // token's rows in s_new, checks the slot once its ids are checked, and reports the token's
 // position in part.npos: the stream takes its rows from s_new and the workgroup writes them
-// to the slot when it is done (store_new_rows).
-template <typename T, int D, int NT, typename Sink>
+// to the slot when it is done (store_new_rows). NKV bounds nkv.
+template <typename T, int D, int NT, typename Sink, int NKV = 1>
 __device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int min_len, const Sink& sink,
                                         int* s_ids, Partition& part, int kv0 = 0, int nkv = 0,
                                         char* s_new = nullptr) {
@@ -147,10 +160,13 @@ __device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int m
     if (a.window <= 0) L = a.context_lens[b];
     const bool appending = a.slot_mapping != nullptr && nkv > 0 && s_new != nullptr;
     const int slot = appending ? a.slot_mapping[b] : -1;
+    // the workgroup of the first kv heads that holds the last position (or partition 0, when
+    // the length is bad) records the slot for a reduce pass that writes the rows
+    const bool record = appending && a.ws_slot != nullptr && kv0 == 0 && tid == 0;
     // speculative only in partition 0 (the owner for every one-partition sequence): workgroups
     // of later partitions are mostly past the end of short sequences, and a wave cannot retire
     // before its loads return
-    NewRows<T, D, NT> rows;
+    NewRows<T, D, NT, NKV> rows;
     if (appending && p == 0) rows.load(a, b, kv0, nkv);
     int flag = 0;
     if (L <= 0) flag = PA_FLAG_EMPTY_CONTEXT;
@@ -159,6 +175,7 @@ __device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int m
     if (flag) {
         if (p == 0) {
             if (tid == 0 && a.err_flag) atomicOr(a.err_flag, flag);
+            if (record) a.ws_slot[b] = -1;
             sink.nan_outputs();
         }
         return false;
@@ -172,7 +189,9 @@ __device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int m
     part.ntok = t1 - part.t0;
     part.j0 = jp;
     part.npos = -1;
-    const bool owner = slot >= 0 && t1 == L;  // holds the new token
+    part.slot = slot;
+    const bool last = t1 == L;
+    const bool owner = slot >= 0 && last;  // holds the new token
     if (owner) {
         if (p != 0) rows.load(a, b, kv0, nkv);
         rows.park(nkv, s_new);
@@ -195,11 +214,13 @@ __device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int m
     }
     if (__syncthreads_or(bad)) {
         if (tid == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_BLOCK_ID);
+        if (last && record) a.ws_slot[b] = -1;
         if (part.nparts == 1) sink.nan_outputs();
         else sink.nan_records(p);
         return false;
     }
     if (owner && check_new_slot(a, L, jp, slot, s_ids)) part.npos = L - 1 - part.t0;
+    if (last && record) a.ws_slot[b] = part.npos >= 0 ? slot : -1;
     return true;
 }
 
@@ -219,18 +240,18 @@ struct DecodeNanSink {
     }
 };
 
-template <typename T, int D, int NT>
+template <typename T, int D, int NT, int NKV>
 __device__ __forceinline__ bool partition_prologue_heads(const DecodeArgs& a, int p, int h0, int nq, int b,
                                                          int* s_ids, Partition& part, char* s_new = nullptr) {
     const int group = a.num_q_heads / a.num_kv_heads;
-    return partition_prologue_sink<T, D, NT>(a, p, b, 1, DecodeNanSink<T, D>{a, b, h0, nq}, s_ids, part, h0 / group,
+    return partition_prologue_sink<T, D, NT, DecodeNanSink<T, D>, NKV>(a, p, b, 1, DecodeNanSink<T, D>{a, b, h0, nq}, s_ids, part, h0 / group,
                                              nq / group, s_new);
 }
 
 template <typename T, int D, int G, int NT>
 __device__ __forceinline__ bool partition_prologue(const DecodeArgs& a, int p, int kvh, int b, int* s_ids,
                                                    Partition& part, char* s_new = nullptr) {
-    return partition_prologue_heads<T, D, NT>(a, p, kvh * G, G, b, s_ids, part, s_new);
+    return partition_prologue_heads<T, D, NT, 1>(a, p, kvh * G, G, b, s_ids, part, s_new);
 }
 
 // Merges the per-wave states (s_m, s_l: base-2 running max and sum; s_acc: unnormalised

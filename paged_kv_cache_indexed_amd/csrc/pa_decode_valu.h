@@ -246,13 +246,10 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int h0, QFrag
         for (int j = 0; j < QFrag<T, KV>::kVecs; ++j) qv[g].v[j] = load16(qbase + (size_t)g * D * T::kBytes + 16 * j);
 }
 
-// Split mode: the 4 waves of a workgroup share one kv head's partition (groups of RPL rows
-// dealt round-robin), and their states merge through LDS.
-// One (partition, kv head, sequence) item of split mode: the 4 waves share the partition,
-// merge through LDS and write the item's output or partition record. All threads call it;
-// it returns with every thread past the item (the LDS buffers may be reused after the next
-// barrier).
-template <typename T, typename KV, int D, int G, int UNROLL>
+// One (partition, kv head, sequence) item of split mode: the NW waves of the workgroup share
+// the partition (groups of RPL rows dealt round-robin), merge their states through LDS and
+// write the item's output or partition record. All threads call it.
+template <typename T, typename KV, int D, int G, int UNROLL, int NW>
 __device__ __forceinline__ void split_item(const DecodeArgs& a, int p, int kvh, int b, int* s_ids,
                                            float (*s_m)[G], float (*s_l)[G], float (*s_acc)[G][D],
                                            char* s_new) {
@@ -267,10 +264,10 @@ __device__ __forceinline__ void split_item(const DecodeArgs& a, int p, int kvh, 
     QFrag<T, KV> qv[G];
     load_q<T, KV, D, G>(a, b, kvh * G, qv);
     Partition part;
-    if (!partition_prologue<T, D, G, kThreads>(a, p, kvh, b, s_ids, part, s_new)) return;
+    if (!partition_prologue<T, D, G, NW * 64>(a, p, kvh, b, s_ids, part, s_new)) return;
 
     float m[G], l[G], acc[G][E];
-    stream_partition<T, KV, D, G, UNROLL, kWaves>(a, s_ids, part, kvh, wave, qv, m, l, acc, s_new);
+    stream_partition<T, KV, D, G, UNROLL, NW>(a, s_ids, part, kvh, wave, qv, m, l, acc, s_new);
     if (row == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -285,21 +282,21 @@ __device__ __forceinline__ void split_item(const DecodeArgs& a, int p, int kvh, 
         }
     }
     __syncthreads();
-    partition_epilogue<T, D, G>(a, p, kvh, b, part, s_m, s_l, s_acc);
-    if (part.npos >= 0) store_new_rows<KV, D>(a, b, kvh, 1, s_new);
+    partition_epilogue<T, D, G, NW>(a, p, kvh, b, part, s_m, s_l, s_acc);
+    if (part.npos >= 0 && !a.ws_slot) store_new_rows<KV, D>(a, part.slot, kvh, 1, s_new);
 }
 
-// Split mode: the 4 waves of a workgroup share one kv head's partition (groups of RPL rows
-// dealt round-robin), and their states merge through LDS. One workgroup per grid cell.
-template <typename T, typename KV, int D, int G, int UNROLL>
-__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
+// Split mode: the NW waves of a workgroup share one kv head's partition. One workgroup per
+// grid cell.
+template <typename T, typename KV, int D, int G, int UNROLL, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
     __shared__ int s_ids[kMaxIdsPerPartition];
-    __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[kWaves][G];
-    __shared__ float s_acc[kWaves][G][D];
+    __shared__ float s_m[NW][G];
+    __shared__ float s_l[NW][G];
+    __shared__ float s_acc[NW][G][D];
     // the new token's K and V rows (fused append; 16/32-bit pools only)
     __shared__ __align__(16) char s_new[std::is_same_v<KV, FP8> ? 16 : 2 * D * KV::kBytes];
-    split_item<T, KV, D, G, UNROLL>(a, blockIdx.x, blockIdx.y, blockIdx.z, s_ids, s_m, s_l, s_acc,
+    split_item<T, KV, D, G, UNROLL, NW>(a, grid_partition(), blockIdx.x, blockIdx.y, s_ids, s_m, s_l, s_acc,
                                     std::is_same_v<KV, FP8> ? nullptr : s_new);
 }
 
@@ -312,13 +309,13 @@ __global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs 
     constexpr int LPR = RowShape<KV, D>::LPR;
     __shared__ int s_ids[kMaxIdsPerPartition];
 
-    const int p = blockIdx.x;
-    const int b = blockIdx.z;
+    const int p = grid_partition();
+    const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int row = lane / LPR;
     const int col = lane % LPR;
-    const int kvh0 = blockIdx.y * kWaves;
+    const int kvh0 = blockIdx.x * kWaves;
     const int nkv = min(kWaves, a.num_kv_heads - kvh0);
     const bool active = wave < nkv;
     const int kvh = active ? kvh0 + wave : kvh0;
@@ -330,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs 
     QFrag<T, KV> qv[G];
     load_q<T, KV, D, G>(a, b, h0, qv);
     Partition part;
-    if (!partition_prologue_heads<T, D, kThreads>(a, p, kvh0 * G, nkv * G, b, s_ids, part,
+    if (!partition_prologue_heads<T, D, kThreads, kWaves>(a, p, kvh0 * G, nkv * G, b, s_ids, part,
                                                   std::is_same_v<KV, FP8> ? nullptr : s_new))
         return;
     if (!active) return;  // no barrier follows
@@ -359,10 +356,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs 
     }
     // each wave stores its own kv head's new rows (nothing to do when not appending)
     if constexpr (!std::is_same_v<KV, FP8>) {
-        if (part.npos >= 0) {
+        if (part.npos >= 0 && !a.ws_slot) {
             constexpr int kVecs = 2 * kRowBytes / 16;
             const int lbs = a.log2_block_size;
-            const int slot = a.slot_mapping[b];
+            const int slot = part.slot;
             char* base[2] = {static_cast<char*>(const_cast<void*>(a.k_pool)),
                              static_cast<char*>(const_cast<void*>(a.v_pool))};
             for (int i = lane; i < kVecs; i += 64) {
@@ -380,15 +377,20 @@ __global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs 
 #ifndef PA_HEAD_MODE_MAX_P
 #define PA_HEAD_MODE_MAX_P 128
 #endif
+// Waves per split-mode workgroup.
+#ifndef PA_SPLIT_WAVES
+#define PA_SPLIT_WAVES 4
+#endif
 
 template <typename T, typename KV, int D, int G, int UNROLL>
 hipError_t launch_decode_tgdu(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     if (a.partition_size <= PA_HEAD_MODE_MAX_P) {
-        dim3 grid(a.max_partitions, (num_kv_heads + kWaves - 1) / kWaves, batch);
+        dim3 grid((num_kv_heads + kWaves - 1) / kWaves, batch, a.max_partitions);
         hipLaunchKernelGGL((decode_valu_heads_kernel<T, KV, D, G, UNROLL>), grid, dim3(kThreads), 0, stream, a);
     } else {
-        dim3 grid(a.max_partitions, num_kv_heads, batch);
-        hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, G, UNROLL>), grid, dim3(kThreads), 0, stream, a);
+        constexpr int NW = PA_SPLIT_WAVES;
+        dim3 grid(num_kv_heads, batch, a.max_partitions);
+        hipLaunchKernelGGL((decode_valu_kernel<T, KV, D, G, UNROLL, NW>), grid, dim3(NW * 64), 0, stream, a);
     }
     return hipGetLastError();
 }

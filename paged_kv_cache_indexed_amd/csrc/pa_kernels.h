@@ -12,6 +12,8 @@ namespace pagedkv {
 
 // Largest number of block-table entries one decode partition stages in LDS.
 constexpr int kMaxIdsPerPartition = 1024;
+// Partition slots of one decode launch (the grid's z extent).
+constexpr int kMaxPartitionSlots = 65535;
 
 struct DecodeArgs {
     void* out;
@@ -43,6 +45,9 @@ struct DecodeArgs {
     const void* new_key;
     const void* new_value;
     const int32_t* slot_mapping;
+    // fused append with a reduce pass: the decode records sequence b's checked slot here (-1:
+    // none) and the reduce kernel writes the rows, after every read of the pool
+    int32_t* ws_slot;
     const int32_t* query_start;
     int32_t col_tiles;
     int32_t batch;

@@ -144,7 +144,7 @@ struct MultiNanSink {
 
 // kMulti = false: one query per sequence, column n of the B operand is head kvh * G + n.
 // kMulti = true: several queries per sequence (query_start), columns are (query, head)
-// pairs taken query-major, 16 per workgroup (column tile blockIdx.z % col_tiles); query i of
+// pairs taken query-major, 16 per workgroup (column tile blockIdx.y % col_tiles); query i of
 // a sequence with n new tokens sits at position L - n + i and its column sees tokens up to
 // that position only (causal mask inside the valid range).
 template <typename T, typename KV, int D, int G, int NW, bool kDoubleBuffer, bool kMulti = false>
@@ -167,10 +167,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     constexpr bool kAppendable = !kFp8 && !kMulti;
     __shared__ __align__(16) char s_new[kAppendable ? 2 * D * 2 : 16];
 
-    const int p = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = kMulti ? (int)blockIdx.z / a.col_tiles : (int)blockIdx.z;
-    const int ct = kMulti ? (int)blockIdx.z - b * a.col_tiles : 0;
+    const int p = grid_partition();
+    const int kvh = blockIdx.x;
+    const int b = kMulti ? (int)blockIdx.y / a.col_tiles : (int)blockIdx.y;
+    const int ct = kMulti ? (int)blockIdx.y - b * a.col_tiles : 0;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     } else {
         partition_epilogue<T, D, G, NW>(a, p, kvh, b, part, s_m, s_l, s_acc);
         if constexpr (kAppendable) {
-            if (part.npos >= 0) store_new_rows<T, D>(a, b, kvh, 1, s_new);
+            if (part.npos >= 0 && !a.ws_slot) store_new_rows<T, D>(a, part.slot, kvh, 1, s_new);
         }
     }
 }

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(D) void reduce_multi_kernel(DecodeArgs a) {
 template <typename T, typename KV, int D, int G>
 hipError_t launch_tdg(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     constexpr int NW = PA_MFMA_WAVES;
-    dim3 grid(a.max_partitions, num_kv_heads, batch * a.col_tiles);
+    dim3 grid(num_kv_heads, batch * a.col_tiles, a.max_partitions);
     hipLaunchKernelGGL((mfma::decode_mfma_kernel<T, KV, D, G, NW, (D <= 128), true>), grid, dim3(NW * 64), 0, stream,
                        a);
     return hipGetLastError();

@@ -53,7 +53,8 @@ def test_partition_policy(lib):
     assert _lib.pa_decode_workspace_bytes(c, 64, 32, 521, 0) == 0
     # long contexts: 512-token partitions
     assert _lib.pa_decode_partition_size(_desc(bs=32), 32, 32, 32769, 0) == 512
-    assert _lib.pa_decode_workspace_bytes(_desc(bs=32), 32, 32, 32769, 0) == 32 * 32 * 65 * 130 * 4
+    # partition records (head_dim + 2 floats) and one int32 slot per sequence
+    assert _lib.pa_decode_workspace_bytes(_desc(bs=32), 32, 32, 32769, 0) == 32 * 32 * 65 * 130 * 4 + 32 * 4
     # VALU path with few workgroups: partitions shrink toward ~2048 workgroups
     p = _lib.pa_decode_partition_size(_desc(hkv=8, dtype=_lib.PA_F32), 32, 64, 2049, 0)
     assert p % 16 == 0 and 32 * 8 * -(-2049 // p) >= 2048 - 256
@@ -75,7 +76,7 @@ def test_sliding_window_sizing(lib):
     c = _desc(bs=32)
     span = 4096 + 31
     p = _lib.pa_decode_partition_size(c, 32, 32, span, 0)
-    want = 32 * 32 * -(-span // p) * 130 * 4 if -(-span // p) > 1 else 0
+    want = 32 * 32 * -(-span // p) * 130 * 4 + 32 * 4 if -(-span // p) > 1 else 0
     assert _lib.pa_decode_sliding_window_workspace_bytes(c, 32, 32, 32769, 4096, 0) == want
     # a window at least as long as every context sizes exactly like the full decode
     for w in (32769, 40000, 2**31 - 1):
@@ -83,7 +84,7 @@ def test_sliding_window_sizing(lib):
                 == _lib.pa_decode_workspace_bytes(c, 32, 32, 32769, 0))
     # explicit partition sizes
     assert (_lib.pa_decode_sliding_window_workspace_bytes(c, 2, 4, 10000, 1000, 256)
-            == 2 * 4 * -(-(1000 + 31) // 256) * 130 * 4)
+            == 2 * 4 * -(-(1000 + 31) // 256) * 130 * 4 + 2 * 4)
     # never more than the full decode needs
     for w in (1, 7, 33, 500, 1024, 5000):
         for P in (0, 32, 128, 512):

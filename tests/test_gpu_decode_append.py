@@ -58,14 +58,16 @@ def test_fused_equals_separate_calls_bitwise(cfg, kw, P):
     assert_close(fused.float().cpu().numpy(), ref, w.dtype, f"decode_append cfg {cfg} P={P}")
 
 
-def test_fused_skips_negative_slots_and_flags_wrong_ones():
+@pytest.mark.parametrize("P", [0, 64])
+def test_fused_skips_negative_slots_and_flags_wrong_ones(P):
+    """P = 64 splits every context, so the rows are written by the reduce pass."""
     dev = require_gpu()
     w = config_workload(2, seed=12, batch=8, heads=4)
     slots = w.slot_mapping.copy()
     slots[1] = -1                       # no append: the decode reads the old (NaN) slot
     slots[2] = slots[3]                 # not this sequence's last position: flagged, not written
-    note("decode_append slots")
-    fused, sep, err, pf, ps = _both(w, dev, 0, slots)
+    note(f"decode_append slots P={P}")
+    fused, sep, err, pf, ps = _both(w, dev, P, slots)
     assert err & 8
     o = fused.float().cpu().numpy()
     assert np.all(np.isnan(o[1])) and np.all(np.isnan(o[2]))  # their last rows were never written
@@ -73,6 +75,50 @@ def test_fused_skips_negative_slots_and_flags_wrong_ones():
     ka, va = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.new_key[keep], w.new_value[keep], w.slot_mapping[keep])
     ref = oracle.paged_decode(w.q, ka, va, w.block_table, w.lens_after_append, w.scale)
     assert_close(o[keep], ref[keep], "f16", "decode_append next to skipped and bad slots")
+    for got, want in zip(pf, (ka, va)):  # only the kept sequences' slots were written
+        g = got.float().cpu().numpy()
+        assert np.array_equal(np.isnan(g), np.isnan(want)) and np.array_equal(np.nan_to_num(g), np.nan_to_num(want))
+
+
+@pytest.mark.parametrize("P", [0, 64])
+def test_fused_poisoned_sequences(P):
+    """Bad block ids and an empty context next to valid sequences: NaN outputs for the
+    poisoned ones, exact outputs and appends for the others, and no row written through a
+    bad id or for a bad length."""
+    dev = require_gpu()
+    w = config_workload(2, seed=14, batch=8, heads=4)
+    bs = w.block_size
+    L = w.lens_after_append.copy()
+    table = w.block_table.copy()
+    table[3, (L[3] - 1) // bs] = w.k_pool.shape[0] + 5  # the new token's block
+    table[4, 0] = -7                                     # the first block only
+    lens = L.copy()
+    lens[5] = 0
+    t = w.to_device(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    note(f"decode_append poisoned sequences P={P}")
+    out = ops.decode_append(t["q"], t["k_pool"], t["v_pool"], torch.from_numpy(table).to(dev),
+                            torch.from_numpy(lens).to(dev), int(L.max()), w.scale, t["new_key"], t["new_value"],
+                            t["slot_mapping"], partition_size=P, err_flag=err)
+    torch.cuda.synchronize()
+    e = int(err.item())
+    assert e & 1 and e & 4 and not e & 8
+    o = out.float().cpu().numpy()
+    assert all(np.all(np.isnan(o[b])) for b in (3, 4, 5))
+    keep = [0, 1, 2, 6, 7]
+    ka, va = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.new_key[keep], w.new_value[keep], w.slot_mapping[keep])
+    ref = oracle.paged_decode(w.q, ka, va, w.block_table, L, w.scale)
+    assert_close(o[keep], ref[keep], "f16", f"valid sequences next to poisoned ones, P={P}")
+    # sequence 4's last partition is valid when P splits its context: its row may land there
+    s4 = int(w.slot_mapping[4])
+    blk, off = s4 // bs, s4 % bs
+    for got, want, new in zip((t["k_pool"], t["v_pool"]), (ka, va), (w.new_key, w.new_value)):
+        g = got.float().cpu().numpy()
+        row = g[blk, :, off].copy()
+        assert np.array_equal(np.nan_to_num(row), np.nan_to_num(want[blk, :, off])) or \
+            np.array_equal(row, new[4].astype(np.float16).astype(np.float32))
+        g[blk, :, off] = want[blk, :, off]
+        assert np.array_equal(np.isnan(g), np.isnan(want)) and np.array_equal(np.nan_to_num(g), np.nan_to_num(want))
 
 
 def test_fused_on_a_multilayer_view():
