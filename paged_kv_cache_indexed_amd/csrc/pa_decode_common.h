@@ -44,6 +44,22 @@ __device__ __forceinline__ int partition_base(const DecodeArgs& a, int L) {
     return (window_start(a, L) >> a.log2_block_size) << a.log2_block_size;
 }
 
+// A work-group whose partition lies past the end of its sequence (or of a sequence with an
+// invalid length, which partition 0 reports) has nothing to do. Partitions after the first
+// check this before issuing any other load: a wave cannot retire while its loads are in
+// flight, so a dead work-group that had issued its q and table loads would hold its slot
+// for a whole memory round trip, and a launch sized for a loose max_context_len has many of
+// them. Live later partitions pay one short extra round trip for the length.
+#ifndef PA_EARLY_DEAD_CHECK
+#define PA_EARLY_DEAD_CHECK 1
+#endif
+__device__ __forceinline__ bool partition_is_dead(const DecodeArgs& a, int p, int b) {
+    if (!PA_EARLY_DEAD_CHECK || p == 0) return false;
+    const int L = a.context_lens[b];
+    if (L <= 0 || L > a.max_context_len) return true;
+    return partition_base(a, L) + p * a.partition_size >= L;
+}
+
 template <typename T>
 __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
     for (int i = threadIdx.x; i < count; i += blockDim.x) store_elem(T{}, out, base + i, __builtin_nanf(""));

@@ -260,6 +260,7 @@ __device__ __forceinline__ void split_item(const DecodeArgs& a, int p, int kvh, 
     const int row = lane / LPR;
     const int col = lane % LPR;
 
+    if (partition_is_dead(a, p, b)) return;
     // q before the prologue, so its load overlaps the length and table round trip
     QFrag<T, KV> qv[G];
     load_q<T, KV, D, G>(a, b, kvh * G, qv);
@@ -324,6 +325,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs 
     // the new token's K and V rows of the workgroup's kv heads (fused append; 16/32-bit pools)
     constexpr int kRowBytes = D * KV::kBytes;
     __shared__ __align__(16) char s_new[std::is_same_v<KV, FP8> ? 16 : kWaves * 2 * kRowBytes];
+    if (partition_is_dead(a, p, b)) return;
     QFrag<T, KV> qv[G];
     load_q<T, KV, D, G>(a, b, h0, qv);
     Partition part;

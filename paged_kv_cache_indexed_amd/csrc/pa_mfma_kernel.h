@@ -196,6 +196,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int qh = kMulti ? col - qi * G : n;  // head of the column inside the group
     const bool col_valid = kMulti ? qi < nq : n < G;
 
+    if constexpr (!kMulti) {
+        if (partition_is_dead(a, p, b)) return;
+    }
     // Q as the B operand of S^T = K Q^T (zero in invalid columns); k-block c of lane group g
     // holds the dims the K operand gives it: 32c + 8g .. +7 for 16-bit pools, 64(c/2) + 16g +
     // 8(c%2) .. +7 for 8-bit pools.
