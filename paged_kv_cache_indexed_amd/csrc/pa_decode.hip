@@ -1,63 +1,74 @@
 // Paged-KV decode entry points for 16/32-bit pools (VALU kernels from pa_decode_valu.h) and
 // the log-sum-exp reduce kernel that combines context partitions.
+#include <algorithm>
+
 #include "pa_decode_valu.h"
 
 namespace pagedkv {
 
 namespace {
 
-// Log-sum-exp combine of the per-partition records of one (sequence, query head):
-//   out = sum_p w_p o_p / sum_p w_p,  w_p = l_p * 2^(m_p - max_p m_p),
-// where o_p is the partition's normalised output and (m_p, l_p) its base-2 running max and
-// sum. A NaN sum (bad block in that partition) makes the whole output NaN.
+// Log-sum-exp combine (lse_combine) of the per-partition records. One work-group covers
+// query heads [h0, h0 + hpw) of one sequence, hpw = ceil(num_q_heads / gridDim.x): the
+// launch sizes gridDim.x so that the grid has about 1024 work-groups, since most of them
+// only read a length and leave (sequences with one partition were finished by the decode).
 //
-// Fused append: the work-group of the first query head of each kv head also writes that kv
-// head's new K and V rows to the slot the decode checked (a.ws_slot). Written here, in a
-// short burst after the decode, they cost far less than as scattered stores among the
-// decode's reads.
+// Fused append: the work-group also writes the new K and V rows of the kv heads whose first
+// query head it covers to the slot the decode checked (a.ws_slot). Written here, in a short
+// burst after the decode, they cost far less than as scattered stores among the decode's
+// reads.
+constexpr int kReduceThreads = 256;
+constexpr int kReduceGroups = 1024;
+
 template <typename T, int D>
-__global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
-    const int h = blockIdx.x;
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     const int b = blockIdx.y;
-    const int e = threadIdx.x;
+    const int hpw = (a.num_q_heads + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int h0 = blockIdx.x * hpw;
+    const int h1 = min(h0 + hpw, a.num_q_heads);
     if (a.ws_slot) {
+        constexpr int kRowVecs = D * T::kBytes / 16;
         const int group = a.num_q_heads / a.num_kv_heads;
+        const int kv0 = (h0 + group - 1) / group;
+        const int nvec = ((h1 + group - 1) / group - kv0) * 2 * kRowVecs;
+        const int lbs = a.log2_block_size;
+        // vector i: kv head kv0 + i / (2 kRowVecs), K row then V row
+        auto src = [&](int i) {
+            return static_cast<const char*>(((i / kRowVecs) & 1) ? a.new_value : a.new_key) +
+                   ((size_t)b * a.num_kv_heads + kv0 + i / (2 * kRowVecs)) * D * T::kBytes + 16 * (i % kRowVecs);
+        };
+        // the first pass of rows is read in the same round trip as the slot
+        const int tid = threadIdx.x;
+        const u32x4 first = tid < nvec ? load16(src(tid)) : u32x4{0, 0, 0, 0};
         const int slot = a.ws_slot[b];
-        if (h % group == 0 && slot >= 0) {
-            constexpr int kRowVecs = D * T::kBytes / 16;
-            const int kvh = h / group;
-            const int lbs = a.log2_block_size;
-            for (int i = e; i < 2 * kRowVecs; i += D) {
-                const int which = i / kRowVecs;
-                const int v = i % kRowVecs;
-                const size_t row = ((size_t)b * a.num_kv_heads + kvh) * D * T::kBytes + 16 * v;
-                char* dst = static_cast<char*>(const_cast<void*>(which ? a.v_pool : a.k_pool)) +
-                            (size_t)(slot >> lbs) * a.block_stride +
-                            ((((size_t)kvh << lbs) + (slot & ((1 << lbs) - 1))) * D) * T::kBytes + 16 * v;
-                store16(dst, load16(static_cast<const char*>(which ? a.new_value : a.new_key) + row));
-            }
+        if (slot >= 0) {
+            auto dst = [&](int i) {
+                return static_cast<char*>(const_cast<void*>(((i / kRowVecs) & 1) ? a.v_pool : a.k_pool)) +
+                       (size_t)(slot >> lbs) * a.block_stride +
+                       (((((size_t)kv0 + i / (2 * kRowVecs)) << lbs) + (slot & ((1 << lbs) - 1))) * D) * T::kBytes +
+                       16 * (i % kRowVecs);
+            };
+            if (tid < nvec) store16(dst(tid), first);
+            for (int i = tid + kReduceThreads; i < nvec; i += kReduceThreads) store16(dst(i), load16(src(i)));
         }
     }
     const int L = a.context_lens[b];
     if (L <= 0 || L > a.max_context_len || (L - 1) >> a.log2_block_size >= a.max_blocks_per_seq) return;
     const int nparts = (L - partition_base(a, L) + a.partition_size - 1) / a.partition_size;
     if (nparts <= 1) return;
-    const size_t rec0 = ((size_t)b * a.num_q_heads + h) * a.max_partitions;
-    const float* ml = a.ws_ml + rec0 * 2;
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-    float num = 0.f, den = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-        const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
-        den += w;
-        num = fmaf(w, a.ws_o[(rec0 + p) * D + e], num);
+    for (int i = threadIdx.x; i < (h1 - h0) * D; i += kReduceThreads) {
+        const int h = h0 + i / D;
+        const int e = i % D;
+        const size_t row = (size_t)b * a.num_q_heads + h;
+        const size_t rec0 = row * a.max_partitions;
+        store_elem(T{}, a.out, row * D + e, lse_combine<D>(a.ws_ml + rec0 * 2, a.ws_o + rec0 * D, nparts, e));
     }
-    store_elem(T{}, a.out, ((size_t)b * a.num_q_heads + h) * D + e, num / den);
 }
 
 template <typename T, int D>
 hipError_t launch_reduce_td(const DecodeArgs& a, int batch, hipStream_t stream) {
-    hipLaunchKernelGGL((reduce_kernel<T, D>), dim3(a.num_q_heads, batch), dim3(D), 0, stream, a);
+    const int groups = std::min(a.num_q_heads, std::max(1, (kReduceGroups + batch - 1) / batch));
+    hipLaunchKernelGGL((reduce_kernel<T, D>), dim3(groups, batch), dim3(kReduceThreads), 0, stream, a);
     return hipGetLastError();
 }
 

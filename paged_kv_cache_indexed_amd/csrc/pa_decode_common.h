@@ -270,6 +270,46 @@ __device__ __forceinline__ bool partition_prologue(const DecodeArgs& a, int p, i
     return partition_prologue_heads<T, D, NT, 1>(a, p, kvh * G, G, b, s_ids, part, s_new);
 }
 
+// Log-sum-exp combine of the `nparts` partition records of one output row, for element e:
+//   sum_p w_p o_p / sum_p w_p,  w_p = l_p * 2^(m_p - max_p m_p),
+// where o_p is the partition's normalised output and (m_p, l_p) its base-2 running max and
+// sum (ml holds (m_p, l_p) pairs, o the o_p rows with stride D). Records are read in chunks
+// of 8 whose loads are all issued before any is used, so a chunk costs one memory round
+// trip; the running max and sums are rescaled between chunks. A NaN sum (bad block in that
+// partition) makes the result NaN.
+template <int D>
+__device__ __forceinline__ float lse_combine(const float* ml, const float* o, int nparts, int e) {
+    constexpr int kChunk = 8;
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int p0 = 0; p0 < nparts; p0 += kChunk) {
+        float mv[kChunk], lv[kChunk], ov[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const bool ok = p0 + i < nparts;
+            mv[i] = ok ? ml[2 * (p0 + i)] : -INFINITY;
+            lv[i] = ok ? ml[2 * (p0 + i) + 1] : 0.f;
+            ov[i] = ok ? o[(size_t)(p0 + i) * D + e] : 0.f;
+        }
+        float Mn = M;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) Mn = fmaxf(Mn, mv[i]);
+        const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
+        const float r = fast_exp2(M - Ms);
+        num *= r;
+        den *= r;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            if (p0 + i < nparts) {
+                const float w = lv[i] * fast_exp2(mv[i] - Ms);
+                den += w;
+                num = fmaf(w, ov[i], num);
+            }
+        }
+        M = Mn;
+    }
+    return num / den;
+}
+
 // Merges the per-wave states (s_m, s_l: base-2 running max and sum; s_acc: unnormalised
 // weighted sums) of G heads and writes either the final output (single partition) or the
 // partition's record (normalised output, max, sum) for the log-sum-exp reduce.

@@ -32,16 +32,8 @@ __global__ __launch_bounds__(D) void reduce_multi_kernel(DecodeArgs a) {
     if ((L + P - 1) / P <= 1) return;
     const int nparts = (L - nq + (tok - q0)) / P + 1;
     const size_t rec0 = ((size_t)tok * a.num_q_heads + h) * a.max_partitions;
-    const float* ml = a.ws_ml + rec0 * 2;
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-    float num = 0.f, den = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-        const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
-        den += w;
-        num = fmaf(w, a.ws_o[(rec0 + p) * D + e], num);
-    }
-    store_elem(T{}, a.out, ((size_t)tok * a.num_q_heads + h) * D + e, num / den);
+    const float o = lse_combine<D>(a.ws_ml + rec0 * 2, a.ws_o + rec0 * D, nparts, e);
+    store_elem(T{}, a.out, ((size_t)tok * a.num_q_heads + h) * D + e, o);
 }
 
 #ifndef PA_MFMA_WAVES

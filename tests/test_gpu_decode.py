@@ -220,6 +220,39 @@ def test_bad_inputs_set_flags_and_nan_only_that_sequence(P):
     assert torch.all(buf[:64] == 7.0) and torch.all(buf[-64:] == 7.0), "canary overwritten"
 
 
+@pytest.mark.parametrize("dtype,group,P", [("f16", 1, 64), ("f16", 1, 256), ("bf16", 8, 64), ("f32", 2, 32)])
+def test_loose_max_context_len(dtype, group, P):
+    """max_context_len far above every length: most partitions are past the end of their
+    sequence and retire early; the outputs (and a fused append) are unchanged. f16 G=1 P=64
+    runs the head-mode kernel, P=256 the split kernel, bf16 G=8 the matrix cores."""
+    dev = require_gpu()
+    lens = np.array([1, 17, 64, 65, 300, 5, 129, 40], np.int32)
+    w = build_paged(f"loose-{dtype}", 310 + group, 0, lens, 16, 2, 2 * group, 128, dtype, max_blocks_per_seq=256)
+    ref = oracle_decode(w)
+    t = w.to_device(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for max_len in (300, 4096):
+        note(f"loose max_context_len={max_len} {dtype} G={group} P={P}")
+        out = ops.decode(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["context_lens"], max_len, w.scale,
+                         partition_size=P, err_flag=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert_close(out.float().cpu().numpy(), ref, dtype, f"max_context_len={max_len} P={P}")
+    if dtype == "f32":
+        return
+    note(f"loose max_context_len fused append {dtype} G={group} P={P}")
+    out = ops.decode_append(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["lens_after"], 4096, w.scale,
+                            t["new_key"], t["new_value"], t["slot_mapping"], partition_size=P, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ka, va = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.new_key, w.new_value, w.slot_mapping)
+    assert_close(out.float().cpu().numpy(), oracle.paged_decode(w.q, ka, va, w.block_table, w.lens_after_append,
+                                                                w.scale), dtype, f"fused, loose bound, P={P}")
+    for got, want in zip((t["k_pool"], t["v_pool"]), (ka, va)):
+        g = got.float().cpu().numpy()
+        assert np.array_equal(np.isnan(g), np.isnan(want)) and np.array_equal(np.nan_to_num(g), np.nan_to_num(want))
+
+
 def test_max_sizes_and_single_long_partition():
     dev = require_gpu()
     bs = 8
