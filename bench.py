@@ -11,10 +11,11 @@ per-XCD L2 (a cold-cache measurement).
 Prints one JSON line: effective KV GB/s of the whole step (algorithmic K+V bytes of the
 decode, 2 x kv_heads x head_dim x dtype_bytes x sum(context_len), over the step time),
 plus the decode kernel's roofline figure and the CPU oracle's rate. The K timed steps run
-back to back with nothing else on the stream. The decode kernel's average launch duration
-comes from a second pass: K back-to-back launches of it (same inputs, same replica
-rotation) between one pair of HIP events on its stream. An event pair around every launch
-would add 2-5 us to each measured launch, and one inside every step about 7 us to the step.
+back to back with nothing else on the stream (--graph replays one captured HIP graph per
+replica instead). The decode kernel's average launch duration comes from a second pass: K
+back-to-back launches of it alone (same inputs, same replica rotation) between one pair of
+HIP events on its stream. An event pair around every launch would add 2-5 us to each measured launch, and one
+inside every step about 7 us to the step.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2] [--window W]
 
@@ -266,6 +267,22 @@ def _timed(step, first: int, steps: int):
     return time.perf_counter() - t0
 
 
+def _capture(fn, R: int) -> list:
+    """fn(r) for r < R, each captured into its own HIP graph (the launches record their kernels
+    on the capture stream; none of them allocates or clears memory)."""
+    import torch
+
+    graphs = []
+    torch.cuda.synchronize()
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
 def _event_pass(launch, first: int, steps: int) -> float:
     """Average duration in ms of the measured kernel: `steps` back-to-back launches of it (same
     inputs and replica rotation as the steps) between one pair of HIP events on its stream.
@@ -449,6 +466,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--kv", choices=["native", "fp8"], default="native",
                     help="pool elements: the workload's dtype, or 8-bit floats with a scale per row")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one captured HIP graph per replica instead of launching from Python")
     ap.add_argument("--unfused", action="store_true",
                     help="append with pa_reshape_and_cache and decode with pa_decode (two launches)")
     ap.add_argument("--queries", type=int, default=0,
@@ -573,8 +592,17 @@ def main() -> int:
         return _bench_reblock(args, w, t, kps, vps, R, dev)
     for i in range(args.warmup):
         step(i)
-    wall = _timed(step, args.warmup, args.steps)
-    dec_avg = _event_pass(decode, args.warmup + args.steps, args.steps)
+    run_step, run_decode = step, decode
+    if args.graph:
+        # One HIP graph per replica for the step and for the decode launch alone. Measured
+        # 3-12% slower than launching from Python on every workload here (the Python and
+        # ctypes time of a launch hides behind the kernel before it), so not the default.
+        step_g, dec_g = _capture(step, R), _capture(decode, R)
+        run_step, run_decode = (lambda i: step_g[i % R].replay()), (lambda i: dec_g[i % R].replay())
+        for i in range(2 * R):
+            run_step(i)
+    wall = _timed(run_step, args.warmup, args.steps)
+    dec_avg = _event_pass(run_decode, args.warmup + args.steps, args.steps)
     ms_step = wall * 1e3 / args.steps
     # Blocks shared by several sequences (beams of one prompt) hold one copy of their bytes:
     # the roofline counts each physical block once, the least the launch has to move.
@@ -599,6 +627,7 @@ def main() -> int:
         cfg["window"] = W
         cfg["attended_tokens_sum"] = int(attended.sum())
     cfg.update({"partition_size": part, "replicas": R, "tokens_per_step": w.batch,
+                "launch": "hip graph per replica" if args.graph else "eager",
                 "copy_pairs_per_step": int(pairs.shape[0]),
                 "step": ("copy-on-write + " if pairs.shape[0] else "") + "append 1 token/seq + decode"
                         + (" (append fused into the decode: pa_decode_append)" if fused else "")})
