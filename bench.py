@@ -340,11 +340,6 @@ def _bench_multi(args, dev) -> int:
     wsn = _lib.pa_multi_token_workspace_bytes(desc, B, B * N, Hq, max_len, N, args.partition_size)
     ws = torch.empty((wsn + 3) // 4, dtype=torch.float32, device=dev) if wsn else None
     out = torch.empty_like(q)
-    stream = torch.cuda.current_stream()
-
-    # one launch for append + decode unless the pools are 8-bit, a window is set or asked not to
-    fused = not (fp8 or W > 0 or args.unfused)
-
     def attend(i):
         ops.multi_token_attention(q, kps[i % R], vps[i % R], t["block_table"], t["context_lens"], qs_d, max_len, N,
                                   w.scale, partition_size=args.partition_size, out=out, workspace=ws)

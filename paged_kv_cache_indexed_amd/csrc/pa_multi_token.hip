@@ -36,6 +36,269 @@ __global__ __launch_bounds__(D) void reduce_multi_kernel(DecodeArgs a) {
     store_elem(T{}, a.out, ((size_t)tok * a.num_q_heads + h) * D + e, o);
 }
 
+// ---- Long query chunks: 64 (query, head) rows per work-group ---------------------------------
+//
+// When a sequence brings more than 16 (query, head) rows per kv head (chunked prefill, long
+// speculative runs), the kernel above re-reads every K/V tile for each 16-column tile and
+// transposes V once per tile and wave. This one gives a work-group 64 rows (16 per wave) of
+// one kv head and streams the partition's K/V once for all of them:
+//   * 32-token tiles are loaded by the whole work-group with whole-row loads (1 KiB
+//     contiguous per wave instruction) into LDS, double-buffered, one barrier per tile. K is
+//     stored row-major (16-byte unit u of token r at u ^ (r & 7), so the operand reads below
+//     hit distinct banks); V is stored transposed, [dim][token], 72-byte rows.
+//   * Each wave computes S^T = K Q^T for its 16 rows (K tile rows from LDS as the A operand,
+//     Q^T in registers as B), runs the same base-2 online softmax as the decode (P stays in
+//     the lanes that computed it, split into rounded high and low parts), and accumulates
+//     O = P V with V^T rows from LDS as the B operand: lane (n, g) reads tokens 4g..4g+3 and
+//     16+4g..16+4g+3 of dim n of the slice, the tokens its k-slots stand for.
+//   * Rows belong to one wave from start to end, so there is no cross-wave merge: each wave
+//     writes its rows' outputs, or their partition records for the log-sum-exp reduce.
+// 16-bit pools, head_dim 64 or 128; the group size is a run-time value.
+namespace prefill {
+
+using mfma::f32x4;
+using mfma::u32x2;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 16 * kWaves;  // (query, head) rows per work-group
+constexpr int kTile = 32;           // tokens per K/V tile
+constexpr int kVtStride = kTile + 4;  // V^T row in 16-bit elements (72 bytes: conflict-free 8-byte reads)
+
+// NaN sink: the rows of row tile rt of sequence b (query-major (query, head) rows).
+template <typename T, int D>
+struct RowTileNanSink {
+    const DecodeArgs& a;
+    int q0, nq, kvh, rt, G;
+    __device__ bool valid(int r) const { return kRows * rt + r < nq * G; }
+    __device__ size_t row(int r) const {
+        const int x = kRows * rt + r;
+        return (size_t)(q0 + x / G) * a.num_q_heads + kvh * G + x % G;
+    }
+    __device__ void nan_outputs() const {
+        for (int i = threadIdx.x; i < kRows * D; i += kThreads)
+            if (valid(i / D)) store_elem(T{}, a.out, row(i / D) * D + i % D, __builtin_nanf(""));
+    }
+    __device__ void nan_records(int p) const {
+        for (int i = threadIdx.x; i < kRows * (D + 2); i += kThreads) {
+            const int r = i / (D + 2), e = i % (D + 2);
+            if (!valid(r)) continue;
+            const size_t rec = row(r) * a.max_partitions + p;
+            if (e < D) a.ws_o[rec * D + e] = __builtin_nanf("");
+            else a.ws_ml[rec * 2 + (e - D)] = (e == D) ? -INFINITY : __builtin_nanf("");
+        }
+    }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
+    static_assert(T::kBytes == 2 && (D == 64 || D == 128), "16-bit rows of 64 or 128 elements");
+    using M = mfma::Mma<T>;
+    constexpr int U = D / 8;                   // 16-byte units per row
+    constexpr int NC = D / 32;                 // k-blocks of the score contraction
+    constexpr int NS = D / 16;                 // 16-dim output slices
+    constexpr int kLoads = kTile * U / kThreads;  // 16-byte units per thread per tile, for K and for V
+    static_assert(kLoads >= 1 && kLoads * kThreads == kTile * U, "tile split");
+    __shared__ int s_ids[kMaxIdsPerPartition];
+    __shared__ u32x4 s_k[2][kTile * U];
+    __shared__ __align__(16) uint16_t s_vt[2][D * kVtStride];
+
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int row_tiles = (a.col_tiles + 3) / 4;
+    const int p = grid_partition();
+    const int kvh = blockIdx.x;
+    const int b = (int)blockIdx.y / row_tiles;
+    const int rt = (int)blockIdx.y - b * row_tiles;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int lbs = a.log2_block_size;
+    const int bs = 1 << lbs;
+
+    const int q0 = a.query_start[b];
+    const int nq = a.query_start[b + 1] - q0;
+    if (q0 < 0 || nq < 0 || q0 + nq > a.num_q_tokens || nq * G > 16 * a.col_tiles) {
+        if (p == 0 && kvh == 0 && rt == 0 && tid == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_LENGTH);
+        return;
+    }
+    if (kRows * rt >= nq * G) return;  // no row of this sequence in this tile (uniform)
+    const int r_tile = 16 * wave + n;   // this lane's row inside the tile (column n of S^T)
+    const int x = kRows * rt + r_tile;  // row index in the sequence
+    const bool row_valid = x < nq * G;
+    const int qi = x / G;
+
+    // Q^T as the B operand: k-block c of lane group g holds dims 32c + 8g .. +7 of the row
+    u32x4 qb[NC];
+    {
+        const char* qrow = static_cast<const char*>(a.q) +
+                           ((size_t)(q0 + (row_valid ? qi : 0)) * a.num_q_heads + kvh * G + (row_valid ? x % G : 0)) * D * 2;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qb[c] = row_valid ? load16(qrow + 2 * (32 * c + 8 * g)) : u32x4{0, 0, 0, 0};
+    }
+    Partition part;
+    if (!partition_prologue_sink<T, D, kThreads>(a, p, b, max(nq, 1), RowTileNanSink<T, D>{a, q0, nq, kvh, rt, G},
+                                                 s_ids, part))
+        return;
+    const int first_pos = part.len - nq;  // position of query 0
+    const int last_q = min(kRows * rt + kRows - 1, nq * G - 1) / G;
+    const int tile_end = first_pos + last_q + 1 - part.t0;  // tokens the tile's last query sees
+    if (tile_end <= 0) return;  // the whole partition is after this tile's queries (uniform)
+    const int ntok = min(part.ntok, tile_end);
+    const int rel_lo = part.rel_lo;
+    const int lim = row_valid ? min(ntok, first_pos + qi + 1 - part.t0) : 0;  // this row sees [rel_lo, lim)
+    const int k0 = rel_lo / kTile;
+    const int ntiles = (ntok + kTile - 1) / kTile - k0;
+
+    const size_t head_bytes = (size_t)bs * D * 2;
+    const char* kpool = static_cast<const char*>(a.k_pool);
+    const char* vpool = static_cast<const char*>(a.v_pool);
+
+    // Tile k: thread tid's load i covers 16-byte unit 256 i + tid of the tile, i.e. unit
+    // (256 i + tid) % U of token (256 i + tid) / U. A wave instruction covers 64 / U whole
+    // rows, consecutive tokens of one block, so the block id is wave-uniform.
+    auto issue = [&](int k, u32x4* kr, u32x4* vr) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int unit = kThreads * i + tid;
+            const int rel = (k0 + k) * kTile + unit / U;
+            const int rel_w = (k0 + k) * kTile + (kThreads * i + 64 * wave) / U;  // the wave's first token
+            const int id = __builtin_amdgcn_readfirstlane(s_ids[(rel_w < ntok ? rel_w : 0) >> lbs]);
+            const size_t slab = (size_t)id * a.block_stride + (size_t)kvh * head_bytes;
+            const uint32_t off = (rel < ntok && rel >= rel_lo) ? (uint32_t)((((rel & (bs - 1)) * U) + unit % U) * 16)
+                                                                : kOutOfRange;
+            kr[i] = buffer_load16<0>(make_rsrc(kpool + slab, (uint32_t)head_bytes), off);
+            vr[i] = buffer_load16<0>(make_rsrc(vpool + slab, (uint32_t)head_bytes), off);
+        }
+    };
+    auto park = [&](int buf, const u32x4* kr, const u32x4* vr) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int unit = kThreads * i + tid;
+            const int t = unit / U;
+            const int u = unit % U;
+            s_k[buf][t * U + (u ^ (t & 7))] = kr[i];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                s_vt[buf][(8 * u + e) * kVtStride + t] = (uint16_t)(vr[i][e >> 1] >> (16 * (e & 1)));
+        }
+    };
+
+    float m = -INFINITY;  // running base-2 max of row n (same in the four lane groups)
+    float l = 0.f;        // this lane's part of row n's running sum
+    f32x4 acc[NS];        // acc[s][i] = O[row 4g + i][dim 16s + n]
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int k, int buf) {
+        const int rel0 = (k0 + k) * kTile;
+        float sc[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x4 st = {0.f, 0.f, 0.f, 0.f};
+            const int r = 16 * t + n;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) st = M::k32(s_k[buf][r * U + ((4 * c + g) ^ (r & 7))], qb[c], st);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = rel0 + 16 * t + 4 * g + i;
+                sc[4 * t + i] = (tok < lim && tok >= rel_lo) ? st[i] * a.scale_log2 : -INFINITY;
+            }
+        }
+        float cm = sc[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
+        cm = fmaxf(cm, shfl_xor(cm, 16));
+        cm = fmaxf(cm, shfl_xor(cm, 32));
+        const float mn = fmaxf(m, cm);
+        const float ms = (mn == -INFINITY) ? 0.f : mn;
+        const float alpha = fast_exp2(m - ms);
+        m = mn;
+        float pr[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pr[j] = fast_exp2(sc[j] - ms);
+            psum += pr[j];
+        }
+        l = l * alpha + psum;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ai = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, __float_as_int(alpha)));
+#pragma unroll
+            for (int s = 0; s < NS; ++s) acc[s][i] *= ai;
+        }
+        u32x4 phi, plo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t h = M::pack_round(pr[2 * w], pr[2 * w + 1]);
+            phi[w] = h;
+            plo[w] = M::pack_round(pr[2 * w] - M::lo(h), pr[2 * w + 1] - M::hi(h));
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint16_t* vt = &s_vt[buf][(16 * s + n) * kVtStride];
+            const u32x2 lo4 = *reinterpret_cast<const u32x2*>(vt + 4 * g);
+            const u32x2 hi4 = *reinterpret_cast<const u32x2*>(vt + 16 + 4 * g);
+            const u32x4 vb = {lo4.x, lo4.y, hi4.x, hi4.y};
+            acc[s] = M::k32(phi, vb, acc[s]);
+            acc[s] = M::k32(plo, vb, acc[s]);
+        }
+    };
+
+    if (ntiles > 0) {
+        u32x4 kr[kLoads], vr[kLoads];
+        issue(0, kr, vr);
+        park(0, kr, vr);
+        __syncthreads();
+        if (ntiles > 1) issue(1, kr, vr);
+        for (int k = 0; k < ntiles; ++k) {
+            compute(k, k & 1);
+            if (k + 1 < ntiles) park((k + 1) & 1, kr, vr);
+            __syncthreads();
+            if (k + 2 < ntiles) issue(k + 2, kr, vr);
+        }
+    }
+
+    // row n's totals, then each lane's four rows 4g + i from their lanes
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    const int xr0 = kRows * rt + 16 * wave;  // row index of this wave's row 0
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * g + i;
+        const float li = __int_as_float(__builtin_amdgcn_ds_bpermute(rr << 2, __float_as_int(l)));
+        const int xi = xr0 + rr;
+        if (xi >= nq * G) continue;
+        const size_t orow = (size_t)(q0 + xi / G) * a.num_q_heads + kvh * G + xi % G;
+        const float inv = 1.f / li;
+        if (part.nparts == 1) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) store_elem(T{}, a.out, orow * D + 16 * s + n, acc[s][i] * inv);
+        } else {
+            const size_t rec = orow * a.max_partitions + p;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) a.ws_o[rec * D + 16 * s + n] = acc[s][i] * inv;
+        }
+    }
+    if (part.nparts > 1 && g == 0 && row_valid) {
+        const size_t rec = ((size_t)(q0 + qi) * a.num_q_heads + kvh * G + x % G) * a.max_partitions + p;
+        a.ws_ml[rec * 2] = m;
+        a.ws_ml[rec * 2 + 1] = l;
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_prefill_td(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
+    const int row_tiles = (a.col_tiles + 3) / 4;
+    dim3 grid(num_kv_heads, batch * row_tiles, a.max_partitions);
+    hipLaunchKernelGGL((prefill_kernel<T, D>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace prefill
+
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
 #endif
@@ -99,6 +362,16 @@ bool multi_token_supported(int kv_dtype, int head_dim, int group, int block_size
 
 hipError_t launch_multi_token(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream) {
+    // 64 or more (query, head) rows per kv head over 16-bit pools: the 64-row kernel (with
+    // fewer rows its tiles run mostly empty: 2 column tiles measured 30% slower there)
+    if (a.col_tiles >= 4 && kv_dtype == dtype && (head_dim == 64 || head_dim == 128)) {
+        if (dtype == PA_F16)
+            return head_dim == 64 ? prefill::launch_prefill_td<F16, 64>(a, batch, num_kv_heads, stream)
+                                  : prefill::launch_prefill_td<F16, 128>(a, batch, num_kv_heads, stream);
+        if (dtype == PA_BF16)
+            return head_dim == 64 ? prefill::launch_prefill_td<BF16, 64>(a, batch, num_kv_heads, stream)
+                                  : prefill::launch_prefill_td<BF16, 128>(a, batch, num_kv_heads, stream);
+    }
     if (kv_dtype == PA_FP8_E4M3) {
         switch (dtype) {
             case PA_F16: return launch_t<F16, FP8>(a, head_dim, group, batch, num_kv_heads, stream);
