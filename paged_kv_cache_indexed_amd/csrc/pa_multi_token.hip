@@ -45,7 +45,10 @@ __global__ __launch_bounds__(D) void reduce_multi_kernel(DecodeArgs a) {
 //   * 32-token tiles are loaded by the whole work-group with whole-row loads (1 KiB
 //     contiguous per wave instruction) into LDS, double-buffered, one barrier per tile. K is
 //     stored row-major (16-byte unit u of token r at u ^ (r & 7), so the operand reads below
-//     hit distinct banks); V is stored transposed, [dim][token], 72-byte rows.
+//     hit distinct banks); V is stored transposed, [dim][token], in 80-byte rows whose 8-byte
+//     chunks of 4 tokens are permuted by the dim (chunk c of dim d at c ^ ((d / 8) % 8)):
+//     the transposing 16-bit writes then spread over the banks, and the 8-byte operand reads
+//     stay conflict-free.
 //   * Each wave computes S^T = K Q^T for its 16 rows (K tile rows from LDS as the A operand,
 //     Q^T in registers as B), runs the same base-2 online softmax as the decode (P stays in
 //     the lanes that computed it, split into rounded high and low parts), and accumulates
@@ -63,7 +66,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 16 * kWaves;  // (query, head) rows per work-group
 constexpr int kTile = 32;           // tokens per K/V tile
-constexpr int kVtStride = kTile + 4;  // V^T row in 16-bit elements (72 bytes: conflict-free 8-byte reads)
+constexpr int kVtStride = kTile + 8;  // V^T row in 16-bit elements (80 bytes)
+
+// Position (16-bit elements) of token t of dim d in a V^T tile.
+__device__ __forceinline__ int vt_pos(int d, int t) {
+    return d * kVtStride + 4 * ((t >> 2) ^ ((d >> 3) & 7)) + (t & 3);
+}
 
 // NaN sink: the rows of row tile rt of sequence b (query-major (query, head) rows).
 template <typename T, int D>
@@ -155,18 +163,30 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
     const char* kpool = static_cast<const char*>(a.k_pool);
     const char* vpool = static_cast<const char*>(a.v_pool);
 
-    // Tile k: thread tid's load i covers 16-byte unit 256 i + tid of the tile, i.e. unit
-    // (256 i + tid) % U of token (256 i + tid) / U. A wave instruction covers 64 / U whole
-    // rows, consecutive tokens of one block, so the block id is wave-uniform.
+    // Load i of thread tid covers 16-byte unit u of tile token t: with two loads per thread
+    // (head_dim 128) tokens 2 (tid / U) and 2 (tid / U) + 1 at the same unit, so that the
+    // transposed V writes pair two tokens per 32-bit word; with one, unit tid. The tokens of a
+    // wave instruction lie in one aligned group of 8, so in one block: the id is wave-uniform.
+    auto slot_of = [&](int i, int& t, int& u) {
+        if constexpr (kLoads == 2) {
+            t = 2 * (tid / U) + i;
+            u = tid % U;
+        } else {
+            t = (kThreads * i + tid) / U;
+            u = (kThreads * i + tid) % U;
+        }
+    };
     auto issue = [&](int k, u32x4* kr, u32x4* vr) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            const int unit = kThreads * i + tid;
-            const int rel = (k0 + k) * kTile + unit / U;
-            const int rel_w = (k0 + k) * kTile + (kThreads * i + 64 * wave) / U;  // the wave's first token
+            int t, u;
+            slot_of(i, t, u);
+            const int rel = (k0 + k) * kTile + t;
+            const int tw = kLoads == 2 ? 2 * (64 * wave / U) + i : (kThreads * i + 64 * wave) / U;
+            const int rel_w = (k0 + k) * kTile + tw;  // the wave's first token
             const int id = __builtin_amdgcn_readfirstlane(s_ids[(rel_w < ntok ? rel_w : 0) >> lbs]);
             const size_t slab = (size_t)id * a.block_stride + (size_t)kvh * head_bytes;
-            const uint32_t off = (rel < ntok && rel >= rel_lo) ? (uint32_t)((((rel & (bs - 1)) * U) + unit % U) * 16)
+            const uint32_t off = (rel < ntok && rel >= rel_lo) ? (uint32_t)((((rel & (bs - 1)) * U) + u) * 16)
                                                                 : kOutOfRange;
             kr[i] = buffer_load16<0>(make_rsrc(kpool + slab, (uint32_t)head_bytes), off);
             vr[i] = buffer_load16<0>(make_rsrc(vpool + slab, (uint32_t)head_bytes), off);
@@ -175,13 +195,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
     auto park = [&](int buf, const u32x4* kr, const u32x4* vr) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            const int unit = kThreads * i + tid;
-            const int t = unit / U;
-            const int u = unit % U;
+            int t, u;
+            slot_of(i, t, u);
             s_k[buf][t * U + (u ^ (t & 7))] = kr[i];
+        }
+        int t, u;
+        slot_of(0, t, u);
+        if constexpr (kLoads == 2) {
+            // dims 8u .. 8u + 7 of tokens t (even) and t + 1: one 32-bit word per dim
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t lo = (vr[0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                const uint32_t hi = (vr[1][e >> 1] >> (16 * (e & 1))) << 16;
+                *reinterpret_cast<uint32_t*>(&s_vt[buf][vt_pos(8 * u + e, t)]) = hi | lo;
+            }
+        } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                s_vt[buf][(8 * u + e) * kVtStride + t] = (uint16_t)(vr[i][e >> 1] >> (16 * (e & 1)));
+                s_vt[buf][vt_pos(8 * u + e, t)] = (uint16_t)(vr[0][e >> 1] >> (16 * (e & 1)));
         }
     };
 
@@ -238,9 +269,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const uint16_t* vt = &s_vt[buf][(16 * s + n) * kVtStride];
-            const u32x2 lo4 = *reinterpret_cast<const u32x2*>(vt + 4 * g);
-            const u32x2 hi4 = *reinterpret_cast<const u32x2*>(vt + 16 + 4 * g);
+            const u32x2 lo4 = *reinterpret_cast<const u32x2*>(&s_vt[buf][vt_pos(16 * s + n, 4 * g)]);
+            const u32x2 hi4 = *reinterpret_cast<const u32x2*>(&s_vt[buf][vt_pos(16 * s + n, 16 + 4 * g)]);
             const u32x4 vb = {lo4.x, lo4.y, hi4.x, hi4.y};
             acc[s] = M::k32(phi, vb, acc[s]);
             acc[s] = M::k32(plo, vb, acc[s]);
