@@ -158,6 +158,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
     const int lim = row_valid ? min(ntok, first_pos + qi + 1 - part.t0) : 0;  // this row sees [rel_lo, lim)
     const int k0 = rel_lo / kTile;
     const int ntiles = (ntok + kTile - 1) / kTile - k0;
+    // Tokens every row of this wave sees: rows are query-major, so the wave's first row has the
+    // smallest limit when all 16 rows are valid (a partial wave takes the masked path).
+    const int xw = kRows * rt + 16 * wave;
+    const int lim_wave = xw + 15 < nq * G ? min(ntok, first_pos + xw / G + 1 - part.t0) : 0;
 
     const size_t head_bytes = (size_t)bs * D * 2;
     const char* kpool = static_cast<const char*>(a.k_pool);
@@ -224,6 +228,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
 
     auto compute = [&](int k, int buf) {
         const int rel0 = (k0 + k) * kTile;
+        const bool full = rel0 >= rel_lo && rel0 + kTile <= lim_wave;
         float sc[8];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -231,10 +236,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
             const int r = 16 * t + n;
 #pragma unroll
             for (int c = 0; c < NC; ++c) st = M::k32(s_k[buf][r * U + ((4 * c + g) ^ (r & 7))], qb[c], st);
+            if (full) {  // every row of the wave sees the whole tile (wave-uniform)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = rel0 + 16 * t + 4 * g + i;
-                sc[4 * t + i] = (tok < lim && tok >= rel_lo) ? st[i] * a.scale_log2 : -INFINITY;
+                for (int i = 0; i < 4; ++i) sc[4 * t + i] = st[i] * a.scale_log2;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = rel0 + 16 * t + 4 * g + i;
+                    sc[4 * t + i] = (tok < lim && tok >= rel_lo) ? st[i] * a.scale_log2 : -INFINITY;
+                }
             }
         }
         float cm = sc[0];
@@ -242,10 +252,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
         for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
         cm = fmaxf(cm, shfl_xor(cm, 16));
         cm = fmaxf(cm, shfl_xor(cm, 32));
-        const float mn = fmaxf(m, cm);
-        const float ms = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = fast_exp2(m - ms);
-        m = mn;
+        // The reference max m moves only when a row's tile max exceeds it by more than 2^8
+        // (weights then stay below 256, far inside fp32 and the split into high and low
+        // parts), so most tiles skip rescaling the accumulators; m and l stay a consistent
+        // pair for the normalisation and the partition records whichever reference is used.
+        const bool grow = cm > m + 8.f;
+        if (__any(grow)) {
+            const float mn = grow ? cm : m;
+            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
+            m = mn;
+            l *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai =
+                    __int_as_float(__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, __float_as_int(alpha)));
+#pragma unroll
+                for (int s = 0; s < NS; ++s) acc[s][i] *= ai;
+            }
+        }
+        const float ms = (m == -INFINITY) ? 0.f : m;
         float pr[8];
         float psum = 0.f;
 #pragma unroll
@@ -253,13 +278,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
             pr[j] = fast_exp2(sc[j] - ms);
             psum += pr[j];
         }
-        l = l * alpha + psum;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float ai = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, __float_as_int(alpha)));
-#pragma unroll
-            for (int s = 0; s < NS; ++s) acc[s][i] *= ai;
-        }
+        l += psum;
         u32x4 phi, plo;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
