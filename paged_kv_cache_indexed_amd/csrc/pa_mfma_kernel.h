@@ -233,6 +233,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     const int rel_lo = part.rel_lo;
     const int c0 = rel_lo / kChunk;  // first chunk holding an attended token
+    // tokens every column of the wave sees: ntok for the decode; for several queries the
+    // tile's first query's limit when all 16 columns are valid (else the masked path)
+    int lim_wave = ntok;
+    if constexpr (kMulti) {
+        const int first_pos = part.len - nq;
+        lim_wave = 16 * ct + 15 < nq * G ? min(ntok, first_pos + (16 * ct) / G + 1 - part.t0) : 0;
+    }
 
     // Identity B operand of the 16x16x16 transpose: k-slot (g, i) is 1 in column 4g + i.
     u32x2 ident;
@@ -316,16 +323,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
                 for (int c = 0; c < NC; ++c) st = M::k32(kk[t][c], qb[c], st);
             }
+            if (rel0 >= rel_lo && rel0 + kChunk <= lim_wave) {  // the whole chunk is visible (wave-uniform)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = rel0 + 16 * t + 4 * g + i;
-                const bool live = tok < lim_col && tok >= rel_lo;
-                float d = st[i];
-                if constexpr (kFp8) {
-                    d *= __uint_as_float(ks[t][i]);
-                    vscale[4 * t + i] = live ? __uint_as_float(vs[t][i]) : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    float d = st[i];
+                    if constexpr (kFp8) {
+                        d *= __uint_as_float(ks[t][i]);
+                        vscale[4 * t + i] = __uint_as_float(vs[t][i]);
+                    }
+                    sc[4 * t + i] = d * a.scale_log2;
                 }
-                sc[4 * t + i] = live ? d * a.scale_log2 : -INFINITY;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = rel0 + 16 * t + 4 * g + i;
+                    const bool live = tok < lim_col && tok >= rel_lo;
+                    float d = st[i];
+                    if constexpr (kFp8) {
+                        d *= __uint_as_float(ks[t][i]);
+                        vscale[4 * t + i] = live ? __uint_as_float(vs[t][i]) : 0.f;
+                    }
+                    sc[4 * t + i] = live ? d * a.scale_log2 : -INFINITY;
+                }
             }
         }
         float cm = sc[0];
@@ -333,10 +352,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
         cm = fmaxf(cm, shfl_xor(cm, 16));
         cm = fmaxf(cm, shfl_xor(cm, 32));
-        const float mn = fmaxf(m, cm);
-        const float ms = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = fast_exp2(m - ms);
-        m = mn;
+        // The reference max m moves only when a column's chunk max exceeds it by more than 2^8
+        // (weights then stay below 256, far inside fp32 and the split of P into high and low
+        // parts), so most chunks skip rescaling the accumulators; m and l stay a consistent
+        // pair for the normalisation and the partition records whichever reference is used.
+        const bool grow = cm > m + 8.f;
+        if (__any(grow)) {
+            const float mn = grow ? cm : m;
+            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
+            m = mn;
+            l *= alpha;
+            // rows 4g + i of acc belong to columns 4g + i: fetch their factors from those lanes
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai =
+                    __int_as_float(__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, __float_as_int(alpha)));
+#pragma unroll
+                for (int s = 0; s < NS; ++s) acc[s][i] *= ai;
+            }
+        }
+        const float ms = (m == -INFINITY) ? 0.f : m;
         float pr[8];
         float psum = 0.f;
 #pragma unroll
@@ -344,14 +379,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             pr[j] = fast_exp2(sc[j] - ms);
             psum += pr[j];
         }
-        l = l * alpha + psum;
-        // rows 4g + i of acc belong to heads 4g + i: fetch their factors from lanes 4g + i
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float ai = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, __float_as_int(alpha)));
-#pragma unroll
-            for (int s = 0; s < NS; ++s) acc[s][i] *= ai;
-        }
+        l += psum;
         // P as the A operand (times the V scales for 8-bit pools), split into rounded high and
         // low parts
         if constexpr (kFp8) {
