@@ -2,7 +2,7 @@
 
 One step = the whole hot path over one batch: copy-on-write of shared blocks (when the
 workload has any), append of one new token per sequence through its slot, then decode over
-the grown context. Append and decode are one launch (pa_decode_append) for 16/32-bit pools
+the grown context. Append and decode are fused (pa_decode_append, pa_decode_append_fp8)
 without a window, else pa_reshape_and_cache[_fp8] then the decode. Inputs are seeded synthetic tensors
 already resident in HBM. Pools are replicated R times and step i uses replica i % R, so the
 bytes touched between two reads of a replica exceed the 256 MB Infinity Cache and the
@@ -546,12 +546,16 @@ def main() -> int:
     kv_bytes = 2 * w.num_kv_heads * row_bytes * int(attended.sum())
     stream = torch.cuda.current_stream()
 
-    # one launch for append + decode unless the pools are 8-bit, a window is set or asked not to
-    fused = not (fp8 or W > 0 or args.unfused)
+    # append and decode fused unless a window is set or asked not to
+    fused = not (W > 0 or args.unfused)
 
     def decode(i):  # the measured kernel: the decode launch of step i
         r = i % R
-        if fused:
+        if fused and fp8:
+            ops.decode_append_fp8(t["q"], kps[r], vps[r], kss[r], vss[r], t["block_table"], lens, max_len, w.scale,
+                                  t["new_key"], t["new_value"], t["slot_mapping"], partition_size=P, out=out,
+                                  workspace=ws)
+        elif fused:
             ops.decode_append(t["q"], kps[r], vps[r], t["block_table"], lens, max_len, w.scale, t["new_key"],
                               t["new_value"], t["slot_mapping"], partition_size=P, out=out, workspace=ws)
         elif fp8:
@@ -566,8 +570,9 @@ def main() -> int:
         if fp8:
             if pairs.shape[0]:
                 ops.copy_blocks_fp8(kps[r], vps[r], kss[r], vss[r], pairs)
-            ops.reshape_and_cache_fp8(t["new_key"], t["new_value"], kps[r], vps[r], kss[r], vss[r],
-                                      t["slot_mapping"])
+            if not fused:
+                ops.reshape_and_cache_fp8(t["new_key"], t["new_value"], kps[r], vps[r], kss[r], vss[r],
+                                          t["slot_mapping"])
         else:
             if pairs.shape[0]:
                 ops.copy_blocks(kps[r], vps[r], pairs)

@@ -145,7 +145,7 @@ pa_status_t pa_copy_blocks(const pa_cache_desc_t* cache, void* k_pool, void* v_p
  * gets NaN outputs, as in pa_decode; its row is written only if its length is valid and
  * every block id of the partition holding the new position is valid. The appended
  * block must not be shared with another sequence (copy it first, pa_copy_blocks). 8-bit
- * pools return PA_ERR_UNSUPPORTED (use pa_reshape_and_cache_fp8 and pa_decode_fp8).
+ * pools return PA_ERR_UNSUPPORTED (use pa_decode_append_fp8).
  * Everything else is as pa_decode.
  */
 pa_status_t pa_decode_append(const pa_cache_desc_t* cache, void* out, const void* q, void* k_pool, void* v_pool,
@@ -279,6 +279,28 @@ pa_status_t pa_decode_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* o
                           int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale, int32_t window,
                           int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* err_flag,
                           pa_stream_t stream);
+
+/*
+ * pa_decode_append_fp8 - pa_reshape_and_cache_fp8 of one new token per sequence followed by
+ * pa_decode_fp8 (no window), fused as pa_decode_append is.
+ *
+ * key/value: [batch][num_kv_heads][head_dim] in q_dtype (PA_F16 or PA_BF16), 16-byte
+ * aligned. The decode work-group that owns position context_lens[b] - 1 quantises the
+ * token's rows exactly as pa_reshape_and_cache_fp8 does (scale = max |x| / 448, codes nearest
+ * to x / scale; [BlockManager essay] §3 on quantised blocks), uses the codes and scales like
+ * every other row, and writes them, with the two scales, to the slot as its last act. The
+ * pool and scale arrays afterwards equal those of the two separate calls bit for bit, and the
+ * output equals pa_decode_fp8's up to the order of the fp32 sums (bit for bit on the
+ * matrix-core path). Slot checks, skipped slots, errors, shapes and workspace are those of
+ * pa_decode_append and pa_decode_fp8.
+ */
+pa_status_t pa_decode_append_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
+                                 void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale,
+                                 const void* key, const void* value, const int32_t* slot_mapping,
+                                 int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                 pa_stream_t stream);
 
 /*
  * pa_reblock - migrate a paged cache to another block size.

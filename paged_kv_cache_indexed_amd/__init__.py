@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     pa_copy_blocks_fp8,
     pa_decode,
     pa_decode_append,
+    pa_decode_append_fp8,
     pa_decode_fp8,
     pa_decode_partition_size,
     pa_decode_sliding_window,

@@ -30,7 +30,8 @@ EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_size"
             "pa_decode_workspace_bytes", "pa_decode", "pa_decode_sliding_window",
             "pa_decode_sliding_window_workspace_bytes", "pa_reshape_and_cache_fp8",
             "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_reblock", "pa_multi_token_attention",
-            "pa_multi_token_workspace_bytes", "pa_decode_append", "pa_status_string")
+            "pa_multi_token_workspace_bytes", "pa_decode_append", "pa_decode_append_fp8",
+            "pa_status_string")
 
 # 8-bit float pools are uint8 (or float8_e4m3fn) tensors of OCP E4M3 codes.
 _DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
@@ -115,6 +116,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_multi_token_workspace_bytes.restype = SZ
     lib.pa_decode_append.argtypes = [D, P, P, P, P, P, I32, P, I32, I32, I32, F, P, P, P, I32, P, SZ, P, P]
     lib.pa_decode_append.restype = ctypes.c_int
+    lib.pa_decode_append_fp8.argtypes = [D, I32, P, P, P, P, P, P, P, I32, P, I32, I32, I32, F, P, P, P, I32, P, SZ,
+                                         P, P]
+    lib.pa_decode_append_fp8.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -290,6 +294,19 @@ def pa_multi_token_attention(cache: CacheDesc, out, q, k_pool, v_pool, block_tab
         _ptr(query_start), int(context_lens.numel()), num_q_tokens, num_q_heads, int(max_context_len),
         int(max_query_len), float(scale), int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag),
         _stream(stream)))
+
+
+def pa_decode_append_fp8(cache: CacheDesc, out, q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                         max_context_len: int, scale: float, key, value, slot_mapping, partition_size: int = 0,
+                         workspace=None, err_flag=None, stream=None) -> None:
+    batch, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    desc = cache.c()
+    _check(load().pa_decode_append_fp8(
+        ctypes.byref(desc), dtype_code(q), _ptr(out), _ptr(q), _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), batch,
+        num_q_heads, int(max_context_len), float(scale), _ptr(key), _ptr(value), _ptr(slot_mapping),
+        int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream)))
 
 
 def pa_decode_append(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_lens, max_context_len: int,

@@ -420,9 +420,11 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out
     a.new_key = new_key;
     a.new_value = new_value;
     a.slot_mapping = slot_mapping;
-    // with a reduce pass, the new rows are written by it, after the decode has read the pool
-    a.ws_slot = (slot_mapping && parts > 1) ? reinterpret_cast<int32_t*>(a.ws_ml + (size_t)batch * num_q_heads * parts * 2)
-                                            : nullptr;
+    // with a reduce pass, 16-bit rows are written by it, after the decode has read the pool
+    // (8-bit rows are quantised by the decode and written by it)
+    a.ws_slot = (slot_mapping && parts > 1 && !is_fp8(cache))
+                    ? reinterpret_cast<int32_t*>(a.ws_ml + (size_t)batch * num_q_heads * parts * 2)
+                    : nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = decode_mfma_supported(cache->dtype, cache->head_dim, group, cache->block_size)
                        ? launch_decode_mfma(a, cache->dtype, q_dtype, cache->head_dim, group, batch,
@@ -473,6 +475,21 @@ pa_status_t pa_decode_append(const pa_cache_desc_t* cache, void* out, const void
     return decode_impl(cache, cache ? cache->dtype : 0, out, q, k_pool, v_pool, nullptr, nullptr, block_table,
                        max_blocks_per_seq, context_lens, batch, num_q_heads, max_context_len, scale, partition_size,
                        0, workspace, workspace_bytes, err_flag, stream, key, value, slot_mapping);
+}
+
+pa_status_t pa_decode_append_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
+                                 void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t batch, int32_t num_q_heads, int32_t max_context_len, float scale,
+                                 const void* key, const void* value, const int32_t* slot_mapping,
+                                 int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                 pa_stream_t stream) {
+    if (!cache || !is_fp8(cache)) return PA_ERR_INVALID_ARGUMENT;
+    if (batch > 0 && (!key || !value || !slot_mapping || !aligned16(key) || !aligned16(value)))
+        return PA_ERR_INVALID_ARGUMENT;
+    return decode_impl(cache, q_dtype, out, q, k_pool, v_pool, k_scale, v_scale, block_table, max_blocks_per_seq,
+                       context_lens, batch, num_q_heads, max_context_len, scale, partition_size, 0, workspace,
+                       workspace_bytes, err_flag, stream, key, value, slot_mapping);
 }
 
 pa_status_t pa_decode_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,

@@ -3,6 +3,8 @@
 // record). Every function here is called by all threads of the workgroup.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_kernels.h"
 
 namespace pagedkv {
@@ -65,10 +67,54 @@ __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
     for (int i = threadIdx.x; i < count; i += blockDim.x) store_elem(T{}, out, base + i, __builtin_nanf(""));
 }
 
+// Fused append: the record of one kv head's new rows in LDS holds the K row then the V row
+// in the pool's storage (KV), and for 8-bit pools their two float32 scales (16 bytes). The
+// prologue stages the rows as read (in q's type, NewRec<T, D>); over an 8-bit pool a wave
+// then quantises them into a record of its own (quantize_new_rows).
+template <typename KV, int D>
+struct NewRec {
+    static constexpr int kRowBytes = D * KV::kBytes;
+    static constexpr bool kScaled = KV::kBytes == 1;
+    static constexpr int kBytes = 2 * kRowBytes + (kScaled ? 16 : 0);
+};
+
+// Fused append into an 8-bit pool: one wave (all 64 lanes) quantises the new K and V rows of
+// one kv head, raw = the two rows in q's type T, into rec (E4M3 codes, then the two scales)
+// exactly as the quantising append does: s = max |x| / 448 and the code nearest x / s
+// clamped to +-448, IEEE float32 divisions; all codes 0 when s = 0.
+template <typename T, int D>
+__device__ void quantize_new_rows(const char* raw, char* rec) {
+    static_assert(T::kBytes == 2 && D % 64 == 0, "16-bit source rows of 64k elements");
+    constexpr int PL = D / 64;  // elements of a row per lane
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(raw + which * D * 2);
+        float x[PL];
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < PL; ++j) {
+            const uint16_t h = src[lane + 64 * j];
+            if constexpr (std::is_same_v<T, BF16>) x[j] = __uint_as_float((uint32_t)h << 16);
+            else x[j] = (float)__builtin_bit_cast(_Float16, h);
+            amax = fmaxf(amax, fabsf(x[j]));
+        }
+        amax = group_max<32>(amax);
+        amax = fmaxf(amax, shfl_xor(amax, 32));
+        const float sc = __fdiv_rn(amax, 448.f);
+#pragma unroll
+        for (int j = 0; j < PL; ++j) {
+            const uint32_t code = sc != 0.f ? e4m3_encode(fminf(fmaxf(__fdiv_rn(x[j], sc), -448.f), 448.f)) : 0u;
+            reinterpret_cast<uint8_t*>(rec)[which * D + lane + 64 * j] = (uint8_t)code;
+        }
+        if (lane == 0) reinterpret_cast<float*>(rec + 2 * D)[which] = sc;
+    }
+}
+
 // Fused append, step 1: the new token's K and V rows of kv heads [kv0, kv0 + nkv) in
-// registers (vector i of [nkv][K row, V row] held by thread i % NT in slot i / NT), read in
-// the prologue's first round trip where possible; the owner parks them in s_new before the
-// barrier. NKV bounds nkv.
+// registers, in q's type T (vector i of [nkv][K row, V row] held by thread i % NT in slot
+// i / NT), read in the prologue's first round trip where possible; the owner parks them in
+// s_new before the barrier, quantised for an 8-bit pool. NKV bounds nkv.
 template <typename T, int D, int NT, int NKV>
 struct NewRows {
     static constexpr int kRowVecs = D * T::kBytes / 16;
@@ -115,9 +161,10 @@ __device__ __forceinline__ bool check_new_slot(const DecodeArgs& a, int L, int j
 // stream; nothing waits for them.
 // The slot comes from the prologue's registers: reading slot_mapping again here would add a
 // memory round trip to the end of every owner workgroup.
-template <typename T, int D>
+template <typename KV, int D>
 __device__ void store_new_rows(const DecodeArgs& a, int slot, int kv0, int nkv, const char* s_new) {
-    constexpr int kRowVecs = D * T::kBytes / 16;
+    using R = NewRec<KV, D>;
+    constexpr int kRowVecs = R::kRowBytes / 16;
     const int lbs = a.log2_block_size;
     const int blk = slot >> lbs;
     const int off = slot & ((1 << lbs) - 1);
@@ -126,8 +173,15 @@ __device__ void store_new_rows(const DecodeArgs& a, int slot, int kv0, int nkv, 
         const int which = (i / kRowVecs) & 1;
         const int v = i % kRowVecs;
         char* dst = static_cast<char*>(const_cast<void*>(which ? a.v_pool : a.k_pool)) + (size_t)blk * a.block_stride +
-                    (((((size_t)kv0 + kv) << lbs) + off) * D) * T::kBytes + 16 * v;
-        store16(dst, load16(s_new + (size_t)i * 16));
+                    (((((size_t)kv0 + kv) << lbs) + off) * D) * KV::kBytes + 16 * v;
+        store16(dst, load16(s_new + (size_t)kv * R::kBytes + which * R::kRowBytes + 16 * v));
+    }
+    if constexpr (R::kScaled) {
+        for (int i = threadIdx.x; i < 2 * nkv; i += blockDim.x) {
+            const size_t srow = (((size_t)blk * a.num_kv_heads + kv0 + i / 2) << lbs) + off;
+            float* scales = const_cast<float*>((i & 1) ? a.v_scale : a.k_scale);
+            scales[srow] = reinterpret_cast<const float*>(s_new + (size_t)(i / 2) * R::kBytes + 2 * R::kRowBytes)[i & 1];
+        }
     }
 }
 

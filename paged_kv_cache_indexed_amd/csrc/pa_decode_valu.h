@@ -66,11 +66,14 @@ __device__ __forceinline__ float dot_frag(const QFrag<T, KV>& q, u32x4 k) {
 // weight in the weighted sum (not in the running sum, which normalises the weights).
 //
 // Fused append: the row at position part.npos (if >= 0) is taken from s_new (K row, then V
-// row, of this wave's kv head) instead of the pool.
+// row, of this wave's kv head, in the pool's storage) instead of the pool. Over an 8-bit pool
+// the wave that folds the token in first quantises the staged rows s_raw (q's type) into
+// s_new, while its first loads are in flight.
 template <typename T, typename KV, int D, int G, int UNROLL, int STRIDE>
 __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int* s_ids, const Partition& part,
                                                  int kvh, int slot, const QFrag<T, KV>* qv, float* m, float* l,
-                                                 float (*acc)[RowShape<KV, D>::E], const char* s_new = nullptr) {
+                                                 float (*acc)[RowShape<KV, D>::E], char* s_new = nullptr,
+                                                 const char* s_raw = nullptr) {
     constexpr bool kScaled = std::is_same_v<KV, FP8>;
     constexpr int E = RowShape<KV, D>::E;
     constexpr int LPR = RowShape<KV, D>::LPR;
@@ -179,6 +182,9 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
     float ksa[UNROLL], vsa[UNROLL], ksb[UNROLL], vsb[UNROLL];  // row scales (8-bit pools only)
     issue(0, ka, va, ksa, vsa);
     issue(1, kb, vb, ksb, vsb);
+    if constexpr (kScaled) {
+        if (npos >= 0 && slot == 0) quantize_new_rows<T, D>(s_raw, s_new);  // wave-uniform
+    }
     int it = 0;
     for (; it + 1 < niters; it += 2) {  // one latch: the wait state is the same on every entry
         __builtin_amdgcn_sched_barrier(0);
@@ -194,25 +200,32 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
     if (it < niters) compute(it, ka, va, ksa, vsa);
 
     // Fused append: the new token (masked in the loop above) joins the row-0 stream of the
-    // first wave that owns this head, its K and V rows read from s_new.
-    if constexpr (!kScaled) {
-        if (npos >= 0 && slot == 0) {
-            const u32x4 kx = *reinterpret_cast<const u32x4*>(s_new + 16 * col);
-            float vx[E];
-            unpack(KV{}, *reinterpret_cast<const u32x4*>(s_new + D * KV::kBytes + 16 * col), vx);
+    // first wave that owns this head, its K and V rows (and scales) read from s_new.
+    if (npos >= 0 && slot == 0) {
+        using R = NewRec<KV, D>;
+        const u32x4 kx = *reinterpret_cast<const u32x4*>(s_new + 16 * col);
+        float vx[E];
+        unpack(KV{}, *reinterpret_cast<const u32x4*>(s_new + R::kRowBytes + 16 * col), vx);
+        float kscale = 1.f, vscale = 1.f;
+        if constexpr (kScaled) {
+            kscale = reinterpret_cast<const float*>(s_new + 2 * R::kRowBytes)[0];
+            vscale = reinterpret_cast<const float*>(s_new + 2 * R::kRowBytes)[1];
+        }
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float d = group_sum<LPR>(dot_frag(qv[g], kx));
-                const float sc = (row == 0) ? d * a.scale_log2 : -INFINITY;
-                const float mn = fmaxf(m[g], sc);
-                const float ms = (mn == -INFINITY) ? 0.f : mn;
-                const float alpha = fast_exp2(m[g] - ms);
-                const float pr = fast_exp2(sc - ms);
-                m[g] = mn;
-                l[g] = l[g] * alpha + pr;
+        for (int g = 0; g < G; ++g) {
+            float d = group_sum<LPR>(dot_frag(qv[g], kx));
+            if constexpr (kScaled) d *= kscale;
+            const float sc = (row == 0) ? d * a.scale_log2 : -INFINITY;
+            const float mn = fmaxf(m[g], sc);
+            const float ms = (mn == -INFINITY) ? 0.f : mn;
+            const float alpha = fast_exp2(m[g] - ms);
+            const float pr = fast_exp2(sc - ms);
+            m[g] = mn;
+            l[g] = l[g] * alpha + pr;
+            float wv = pr;
+            if constexpr (kScaled) wv *= vscale;
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pr, vx[e], acc[g][e] * alpha);
-            }
+            for (int e = 0; e < E; ++e) acc[g][e] = fmaf(wv, vx[e], acc[g][e] * alpha);
         }
     }
 
@@ -266,9 +279,12 @@ __device__ __forceinline__ void split_item(const DecodeArgs& a, int p, int kvh, 
     load_q<T, KV, D, G>(a, b, kvh * G, qv);
     Partition part;
     if (!partition_prologue<T, D, G, NW * 64>(a, p, kvh, b, s_ids, part, s_new)) return;
+    // the rows in the pool's storage: the staged rows themselves, or after them the 8-bit
+    // record the folding wave quantises them into
+    char* s_rec = s_new + (std::is_same_v<KV, FP8> ? NewRec<T, D>::kBytes : 0);
 
     float m[G], l[G], acc[G][E];
-    stream_partition<T, KV, D, G, UNROLL, NW>(a, s_ids, part, kvh, wave, qv, m, l, acc, s_new);
+    stream_partition<T, KV, D, G, UNROLL, NW>(a, s_ids, part, kvh, wave, qv, m, l, acc, s_rec, s_new);
     if (row == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -284,7 +300,7 @@ __device__ __forceinline__ void split_item(const DecodeArgs& a, int p, int kvh, 
     }
     __syncthreads();
     partition_epilogue<T, D, G, NW>(a, p, kvh, b, part, s_m, s_l, s_acc);
-    if (part.npos >= 0 && !a.ws_slot) store_new_rows<KV, D>(a, part.slot, kvh, 1, s_new);
+    if (part.npos >= 0 && !a.ws_slot) store_new_rows<KV, D>(a, part.slot, kvh, 1, s_rec);
 }
 
 // Split mode: the NW waves of a workgroup share one kv head's partition. One workgroup per
@@ -295,10 +311,9 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
     __shared__ float s_m[NW][G];
     __shared__ float s_l[NW][G];
     __shared__ float s_acc[NW][G][D];
-    // the new token's K and V rows (fused append; 16/32-bit pools only)
-    __shared__ __align__(16) char s_new[std::is_same_v<KV, FP8> ? 16 : 2 * D * KV::kBytes];
-    split_item<T, KV, D, G, UNROLL, NW>(a, grid_partition(), blockIdx.x, blockIdx.y, s_ids, s_m, s_l, s_acc,
-                                    std::is_same_v<KV, FP8> ? nullptr : s_new);
+    // the new token's K and V rows as read, and their 8-bit record (fused append)
+    __shared__ __align__(16) char s_new[NewRec<T, D>::kBytes + (std::is_same_v<KV, FP8> ? NewRec<KV, D>::kBytes : 0)];
+    split_item<T, KV, D, G, UNROLL, NW>(a, grid_partition(), blockIdx.x, blockIdx.y, s_ids, s_m, s_l, s_acc, s_new);
 }
 
 // Head mode, for short partitions: a workgroup owns one (partition, sequence) and 4
@@ -322,21 +337,23 @@ __global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs 
     const int kvh = active ? kvh0 + wave : kvh0;
     const int h0 = kvh * G;
 
-    // the new token's K and V rows of the workgroup's kv heads (fused append; 16/32-bit pools)
-    constexpr int kRowBytes = D * KV::kBytes;
-    __shared__ __align__(16) char s_new[std::is_same_v<KV, FP8> ? 16 : kWaves * 2 * kRowBytes];
+    // the new token's K and V rows of the workgroup's kv heads as read, and for an 8-bit pool
+    // each wave's record of its own kv head (fused append)
+    using R = NewRec<KV, D>;
+    constexpr int kRaw = NewRec<T, D>::kBytes;
+    constexpr bool kRec8 = std::is_same_v<KV, FP8>;
+    __shared__ __align__(16) char s_new[kWaves * kRaw + (kRec8 ? kWaves * R::kBytes : 0)];
     if (partition_is_dead(a, p, b)) return;
     QFrag<T, KV> qv[G];
     load_q<T, KV, D, G>(a, b, h0, qv);
     Partition part;
-    if (!partition_prologue_heads<T, D, kThreads, kWaves>(a, p, kvh0 * G, nkv * G, b, s_ids, part,
-                                                  std::is_same_v<KV, FP8> ? nullptr : s_new))
+    if (!partition_prologue_heads<T, D, kThreads, kWaves>(a, p, kvh0 * G, nkv * G, b, s_ids, part, s_new))
         return;
     if (!active) return;  // no barrier follows
 
     float m[G], l[G], acc[G][E];
-    stream_partition<T, KV, D, G, UNROLL, 1>(a, s_ids, part, kvh, 0, qv, m, l, acc,
-                                             s_new + (std::is_same_v<KV, FP8> ? 0 : wave * 2 * kRowBytes));
+    char* s_rec = kRec8 ? s_new + kWaves * kRaw + wave * R::kBytes : s_new + wave * kRaw;
+    stream_partition<T, KV, D, G, UNROLL, 1>(a, s_ids, part, kvh, 0, qv, m, l, acc, s_rec, s_new + wave * kRaw);
     if (row == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -357,19 +374,25 @@ __global__ __launch_bounds__(kThreads) void decode_valu_heads_kernel(DecodeArgs 
         }
     }
     // each wave stores its own kv head's new rows (nothing to do when not appending)
-    if constexpr (!std::is_same_v<KV, FP8>) {
-        if (part.npos >= 0 && !a.ws_slot) {
-            constexpr int kVecs = 2 * kRowBytes / 16;
-            const int lbs = a.log2_block_size;
-            const int slot = part.slot;
-            char* base[2] = {static_cast<char*>(const_cast<void*>(a.k_pool)),
-                             static_cast<char*>(const_cast<void*>(a.v_pool))};
-            for (int i = lane; i < kVecs; i += 64) {
-                const int which = i / (kRowBytes / 16);
-                const int v = i % (kRowBytes / 16);
-                char* dst = base[which] + (size_t)(slot >> lbs) * a.block_stride +
-                            ((((size_t)kvh << lbs) + (slot & ((1 << lbs) - 1))) * kRowBytes) + 16 * v;
-                store16(dst, load16(s_new + (size_t)(wave * 2 * kRowBytes) + 16 * i));
+    if (part.npos >= 0 && !a.ws_slot) {
+        constexpr int kVecs = 2 * R::kRowBytes / 16;
+        const int lbs = a.log2_block_size;
+        const int slot = part.slot;
+        const int off = slot & ((1 << lbs) - 1);
+        char* base[2] = {static_cast<char*>(const_cast<void*>(a.k_pool)),
+                         static_cast<char*>(const_cast<void*>(a.v_pool))};
+        for (int i = lane; i < kVecs; i += 64) {
+            const int which = i / (R::kRowBytes / 16);
+            const int v = i % (R::kRowBytes / 16);
+            char* dst = base[which] + (size_t)(slot >> lbs) * a.block_stride +
+                        ((((size_t)kvh << lbs) + off) * R::kRowBytes) + 16 * v;
+            store16(dst, load16(s_rec + 16 * i));
+        }
+        if constexpr (R::kScaled) {
+            if (lane < 2) {
+                const size_t srow = (((size_t)(slot >> lbs) * a.num_kv_heads + kvh) << lbs) + off;
+                const_cast<float*>(lane ? a.v_scale : a.k_scale)[srow] =
+                    reinterpret_cast<const float*>(s_rec + 2 * R::kRowBytes)[lane];
             }
         }
     }

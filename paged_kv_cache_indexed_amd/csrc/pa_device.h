@@ -219,11 +219,12 @@ __device__ __forceinline__ float group_sum(float x) {
 // Maximum over aligned groups of N lanes (N <= 16); every lane of a group receives it.
 template <int N>
 __device__ __forceinline__ float group_max(float x) {
-    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group");
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32, "group");
     if constexpr (N >= 2) x = fmaxf(x, dpp<kDppQuadXor1>(x));
     if constexpr (N >= 4) x = fmaxf(x, dpp<kDppQuadXor2>(x));
     if constexpr (N >= 8) x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
     if constexpr (N >= 16) x = fmaxf(x, dpp<kDppRowMirror>(x));
+    if constexpr (N >= 32) x = fmaxf(x, shfl_xor(x, 16));
     return x;
 }
 

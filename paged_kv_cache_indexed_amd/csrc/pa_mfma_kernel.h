@@ -163,9 +163,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __shared__ float s_m[NW][NCOL];
     __shared__ float s_l[NW][NCOL];
     __shared__ float s_acc[NW][NCOL][D];
-    // the new token's K and V rows (fused append of the decode over 16-bit pools)
-    constexpr bool kAppendable = !kFp8 && !kMulti;
-    __shared__ __align__(16) char s_new[kAppendable ? 2 * D * 2 : 16];
+    // the new token's K and V rows as read, and for an 8-bit pool each wave's record of them
+    // (fused append of the decode)
+    constexpr bool kAppendable = !kMulti;
+    using R = NewRec<KV, D>;
+    constexpr int kRaw = NewRec<T, D>::kBytes;
+    __shared__ __align__(16) char s_new[kAppendable ? kRaw + (kFp8 ? NW * R::kBytes : 0) : 16];
 
     const int p = grid_partition();
     const int kvh = blockIdx.x;
@@ -219,7 +222,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                                                     s_ids, part))
             return;
     } else {
-        if (!partition_prologue<T, D, G, NW * 64>(a, p, kvh, b, s_ids, part, kAppendable ? s_new : nullptr)) return;
+        if (!partition_prologue<T, D, G, NW * 64>(a, p, kvh, b, s_ids, part, kAppendable ? s_new : nullptr))
+            return;
     }
     int ntok = part.ntok;
     int lim_col = ntok;  // tokens (relative to the partition) this lane's column may see
@@ -291,18 +295,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int s = 0; s < NS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int npos = part.npos;
-    auto compute = [&](int it, u32x4 (*kk)[NL], u32x4 (*vv)[NL], const u32x4* ks, const u32x4* vs) {
+    // this wave's record of the new rows in the pool's storage (8-bit: quantised below)
+    char* s_rec = s_new + (kFp8 ? kRaw + wave * R::kBytes : 0);
+    auto compute = [&](int it, u32x4 (*kk)[NL], u32x4 (*vv)[NL], u32x4* ks, u32x4* vs) {
         const int rel0 = (c0 + it * NW + wave) * kChunk;
         if constexpr (kAppendable) {
             if (npos >= 0) {  // fused append: the new token's rows come from s_new (wave-uniform test)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int d = npos - (rel0 + 16 * t);
-                    if (d >= 0 && d < 16 && n == d) {
+                    if (d >= 0 && d < 16) {
+                        if (n == d) {  // the A-operand row of the token
 #pragma unroll
-                        for (int c = 0; c < NL; ++c) {
-                            kk[t][c] = *reinterpret_cast<const u32x4*>(s_new + 64 * c + seg);
-                            vv[t][c] = *reinterpret_cast<const u32x4*>(s_new + D * 2 + 64 * c + seg);
+                            for (int c = 0; c < NL; ++c) {
+                                kk[t][c] = *reinterpret_cast<const u32x4*>(s_rec + 64 * c + seg);
+                                vv[t][c] = *reinterpret_cast<const u32x4*>(s_rec + R::kRowBytes + 64 * c + seg);
+                            }
+                        }
+                        if constexpr (kFp8) {  // the lanes whose scores include the token
+                            if (g == (d >> 2)) {
+                                const uint32_t* sc = reinterpret_cast<const uint32_t*>(s_rec + 2 * R::kRowBytes);
+                                ks[t][d & 3] = sc[0];
+                                vs[t][d & 3] = sc[1];
+                            }
                         }
                     }
                 }
@@ -428,6 +443,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         u32x4 kb[2][NL], vb[2][NL], ksb[2], vsb[2];
         issue(0, ka, va, ksa, vsa);
         issue(1, kb, vb, ksb, vsb);
+        if constexpr (kAppendable && kFp8) {
+            if (npos >= 0) quantize_new_rows<T, D>(s_new, s_rec);  // while the first loads fly
+        }
         int it = 0;
         for (; it + 1 < niters; it += 2) {
             __builtin_amdgcn_sched_barrier(0);
@@ -442,6 +460,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         __builtin_amdgcn_sched_barrier(0);
         if (it < niters) compute(it, ka, va, ksa, vsa);
     } else {
+        if constexpr (kAppendable && kFp8) {
+            if (npos >= 0) quantize_new_rows<T, D>(s_new, s_rec);
+        }
         for (int it = 0; it < niters; ++it) {
             issue(it, ka, va, ksa, vsa);
             compute(it, ka, va, ksa, vsa);
@@ -498,7 +519,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     } else {
         partition_epilogue<T, D, G, NW>(a, p, kvh, b, part, s_m, s_l, s_acc);
         if constexpr (kAppendable) {
-            if (part.npos >= 0 && !a.ws_slot) store_new_rows<T, D>(a, part.slot, kvh, 1, s_new);
+            // wave 0's record (every wave's is the same; the barrier above orders it)
+            if (part.npos >= 0 && !a.ws_slot) store_new_rows<KV, D>(a, part.slot, kvh, 1, s_new + (kFp8 ? kRaw : 0));
         }
     }
 }

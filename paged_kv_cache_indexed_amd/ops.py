@@ -7,8 +7,8 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (CacheDesc, pa_copy_blocks, pa_copy_blocks_fp8, pa_decode, pa_decode_append, pa_decode_fp8,
-                   pa_decode_sliding_window, pa_decode_sliding_window_workspace_bytes,
+from ._lib import (CacheDesc, pa_copy_blocks, pa_copy_blocks_fp8, pa_decode, pa_decode_append, pa_decode_append_fp8,
+                   pa_decode_fp8, pa_decode_sliding_window, pa_decode_sliding_window_workspace_bytes,
                    pa_decode_workspace_bytes, pa_multi_token_attention, pa_multi_token_workspace_bytes,
                    pa_reblock, pa_reshape_and_cache, pa_reshape_and_cache_fp8)
 
@@ -93,6 +93,20 @@ def decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, m
     pa_decode_fp8(CacheDesc.of(k_pool), out, q, k_pool, v_pool, k_scale, v_scale, block_table,
                   context_lens, max_context_len, scale, window, partition_size, workspace, err_flag,
                   stream)
+    return out
+
+
+def decode_append_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens, max_context_len: int,
+                      scale: float, key, value, slot_mapping, partition_size: int = 0, out=None, workspace=None,
+                      err_flag=None, stream=None):
+    """reshape_and_cache_fp8 of one token per sequence (rows in q's dtype), then decode_fp8 over
+    the grown contexts, in one launch."""
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = workspace_for(k_pool, q.shape[0], q.shape[1], max_context_len, partition_size)
+    pa_decode_append_fp8(CacheDesc.of(k_pool), out, q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
+                         max_context_len, scale, key, value, slot_mapping, partition_size, workspace, err_flag, stream)
     return out
 
 

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.fp8_cache as o8
 from paged_kv_cache_indexed_amd import ops
 from tests.gpu_util import assert_close, note, require_gpu
 from workloads import build_paged, config_workload
@@ -138,3 +139,83 @@ def test_fused_on_a_multilayer_view():
     ref = oracle.paged_decode(w.q, ka, va, w.block_table, w.lens_after_append, w.scale)
     assert_close(out.float().cpu().numpy(), ref, "f16", "decode_append multilayer")
     assert torch.all(cache[:, :, 0] == 0) and torch.all(cache[:, :, 2] == 0), "other layers were written"
+
+
+# ---- 8-bit pools: pa_decode_append_fp8 against pa_reshape_and_cache_fp8 + pa_decode_fp8 -----
+
+def _fp8_cache(w, dev):
+    """Device (k codes, v codes, k scales, v scales) of the workload's context, quantised by the
+    oracle's encoder; unwritten rows hold NaN codes and NaN scales."""
+    dead = np.isnan(w.k_pool).any(-1)
+    kc, ks = o8.quantize_rows(np.nan_to_num(w.k_pool))
+    vc, vs = o8.quantize_rows(np.nan_to_num(w.v_pool))
+    kc[dead], vc[dead] = o8.E4M3_NAN_CODE, o8.E4M3_NAN_CODE
+    ks[dead], vs[dead] = np.nan, np.nan
+    return [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (kc, vc, ks, vs)]
+
+
+def _both_fp8(w, dev, P=0, slots=None):
+    t = w.to_device(dev)
+    c1, c2 = _fp8_cache(w, dev), _fp8_cache(w, dev)
+    sl = t["slot_mapping"] if slots is None else torch.as_tensor(slots, dtype=torch.int32, device=dev)
+    L = int(w.lens_after_append.max())
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    fused = ops.decode_append_fp8(t["q"], *c1, t["block_table"], t["lens_after"], L, w.scale, t["new_key"],
+                                  t["new_value"], sl, partition_size=P, err_flag=err)
+    ops.reshape_and_cache_fp8(t["new_key"], t["new_value"], *c2, sl)
+    sep = ops.decode_fp8(t["q"], *c2, t["block_table"], t["lens_after"], L, w.scale, partition_size=P)
+    torch.cuda.synchronize()
+    return fused, sep, int(err.item()), c1, c2
+
+
+def _same_bits(a, b):
+    if a.dtype == torch.float32:
+        return torch.equal(a.view(torch.int32), b.view(torch.int32))
+    return torch.equal(a, b)
+
+
+@pytest.mark.parametrize("cfg,kw,P", [(2, dict(batch=16, heads=8), 0), (2, dict(batch=16, heads=8), 64),
+                                      (2, dict(batch=16, heads=8), 256), (3, dict(batch=64, heads=4), 0),
+                                      (4, dict(batch=8), 0), (4, dict(batch=8), 512)])
+def test_fused_fp8_equals_separate_calls(cfg, kw, P):
+    """Codes and scales bit for bit; outputs bit for bit on the matrix cores (config 4) and
+    within tolerance on the VALU kernels; and against the oracle's quantised append + decode."""
+    dev = require_gpu()
+    w = config_workload(cfg, seed=15, **kw)
+    note(f"decode_append_fp8 cfg={cfg} {kw} P={P}")
+    fused, sep, err, c1, c2 = _both_fp8(w, dev, P)
+    assert err == 0
+    for a, b in zip(c1, c2):
+        assert _same_bits(a, b), "fused fp8 append wrote different codes or scales"
+    if cfg == 4:
+        assert torch.equal(_bits(fused), _bits(sep)), "fused fp8 output differs from the separate calls"
+    else:
+        assert_close(fused.float().cpu().numpy(), sep.float().cpu().numpy().astype(np.float64), w.dtype,
+                     f"fused fp8 vs separate cfg {cfg} P={P}")
+    kc, vc, ks, vs = (x.cpu().numpy() for x in _fp8_cache(w, torch.device("cpu")))
+    kc, vc, ks, vs = o8.reshape_and_cache_fp8(kc, vc, ks, vs, w.new_key, w.new_value, w.slot_mapping)
+    ref = o8.paged_decode_fp8(w.q, kc, vc, ks, vs, w.block_table, w.lens_after_append, w.scale)
+    assert_close(fused.float().cpu().numpy(), ref, w.dtype, f"decode_append_fp8 cfg {cfg} P={P}")
+
+
+def test_fused_fp8_slots():
+    dev = require_gpu()
+    w = config_workload(2, seed=16, batch=8, heads=4)
+    slots = w.slot_mapping.copy()
+    slots[1] = -1
+    slots[2] = slots[3]
+    note("decode_append_fp8 slots")
+    fused, sep, err, c1, c2 = _both_fp8(w, dev, 0, slots)
+    assert err & 8
+    o = fused.float().cpu().numpy()
+    assert np.all(np.isnan(o[1])) and np.all(np.isnan(o[2]))
+    keep = [0] + list(range(3, 8))
+    kc, vc, ks, vs = (x.cpu().numpy() for x in _fp8_cache(w, torch.device("cpu")))
+    kc, vc, ks, vs = o8.reshape_and_cache_fp8(kc, vc, ks, vs, w.new_key[keep], w.new_value[keep],
+                                              w.slot_mapping[keep])
+    ref = o8.paged_decode_fp8(w.q, kc, vc, ks, vs, w.block_table, w.lens_after_append, w.scale)
+    assert_close(o[keep], ref[keep], "f16", "decode_append_fp8 next to skipped and bad slots")
+    got = [x.cpu().numpy() for x in c1]
+    for g_, r_ in zip(got, (kc, vc, ks, vs)):
+        assert np.array_equal(np.isnan(g_.astype(np.float64)), np.isnan(r_.astype(np.float64)))
+        assert np.array_equal(np.nan_to_num(g_.astype(np.float64)), np.nan_to_num(r_.astype(np.float64)))
