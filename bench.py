@@ -267,6 +267,18 @@ def _timed(step, first: int, steps: int):
     return time.perf_counter() - t0
 
 
+def _unique_slots(w, window: int) -> int:
+    """Distinct physical (block, offset) slots the decode attends to over the whole batch: a
+    slot shared by several sequences (a common prefix) counts once."""
+    bs = w.block_size
+    table = w.block_table if hasattr(w, "block_table") else w.table  # the beam workload's, after copy-on-write
+    slots = []
+    for b, L in enumerate(np.asarray(w.lens_after_append).tolist()):
+        pos = np.arange(max(0, L - window) if window > 0 else 0, L, dtype=np.int64)
+        slots.append(table[b, pos // bs].astype(np.int64) * bs + pos % bs)
+    return int(np.unique(np.concatenate(slots)).size)
+
+
 def _capture(fn, R: int) -> list:
     """fn(r) for r < R, each captured into its own HIP graph (the launches record their kernels
     on the capture stream; none of them allocates or clears memory)."""
@@ -605,10 +617,8 @@ def main() -> int:
     dec_avg = _event_pass(run_decode, args.warmup + args.steps, args.steps)
     ms_step = wall * 1e3 / args.steps
     # Blocks shared by several sequences (beams of one prompt) hold one copy of their bytes:
-    # the roofline counts each physical block once, the least the launch has to move.
-    roof_bytes = kv_bytes
-    if getattr(w, "unique_blocks", None) is not None and W == 0:
-        roof_bytes = min(kv_bytes, 2 * w.unique_blocks * w.block_size * w.num_kv_heads * row_bytes)
+    # the roofline counts each attended physical slot once, the least the launch has to move.
+    roof_bytes = 2 * w.num_kv_heads * row_bytes * _unique_slots(w, W)
     achieved = roof_bytes / (dec_avg * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     path = decode_path("fp8" if fp8 else w.dtype, w.head_dim, w.num_q_heads // w.num_kv_heads, w.block_size)
