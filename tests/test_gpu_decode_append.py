@@ -219,3 +219,28 @@ def test_fused_fp8_slots():
     for g_, r_ in zip(got, (kc, vc, ks, vs)):
         assert np.array_equal(np.isnan(g_.astype(np.float64)), np.isnan(r_.astype(np.float64)))
         assert np.array_equal(np.nan_to_num(g_.astype(np.float64)), np.nan_to_num(r_.astype(np.float64)))
+
+
+@pytest.mark.parametrize("cfg,kw", [(2, {}), (3, dict(median=87)), (3, dict(median=23)), (4, dict(block_size=16)),
+                                    (4, dict(block_size=256))])
+def test_fused_full_size(cfg, kw):
+    """The benchmark's step at full size, in its launch configuration (default partitions):
+    the fused append + decode against the oracle's append and decode, every output element,
+    and the appended rows bit for bit."""
+    dev = require_gpu()
+    w = config_workload(cfg, seed=0, **kw)
+    t = w.to_device(dev)
+    L = int(w.lens_after_append.max())
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    note(f"fused full size cfg={cfg} {kw}")
+    out = ops.decode_append(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["lens_after"], L, w.scale,
+                            t["new_key"], t["new_value"], t["slot_mapping"], err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ka, va = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.new_key, w.new_value, w.slot_mapping)
+    ref = oracle.paged_decode(w.q, ka, va, w.block_table, w.lens_after_append, w.scale)
+    assert_close(out.float().cpu().numpy(), ref, w.dtype, f"fused full size cfg {cfg} {kw}")
+    blk = torch.from_numpy(w.slot_mapping // w.block_size).long().to(dev)
+    off = torch.from_numpy(w.slot_mapping % w.block_size).long().to(dev)
+    for pool, new in ((t["k_pool"], t["new_key"]), (t["v_pool"], t["new_value"])):
+        assert torch.equal(_bits(pool[blk, :, off, :]), _bits(new)), "appended rows differ"

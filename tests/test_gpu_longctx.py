@@ -83,3 +83,32 @@ def test_config5_copy_on_write_append_decode():
     gk = t["k_pool"].index_select(0, ids).index_select(1, hs).float().cpu().numpy()
     gv = t["v_pool"].index_select(0, ids).index_select(1, hs).float().cpu().numpy()
     assert np.array_equal(gk, k2, equal_nan=True) and np.array_equal(gv, v2, equal_nan=True)
+
+
+def test_config5_fused_step():
+    """The benchmark's config 5 step: copy-on-write, then the append fused into the decode
+    (default partitions, so the reduce pass writes the rows), on sampled outputs."""
+    dev = require_gpu()
+    note("config 5 fused: building the 32K beam workload on the device")
+    w = beam_workload(dev)
+    t = w.tensors
+    host = host_subset(w, SEQS, HEADS)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    L = w.context
+    ops.copy_blocks(t["k_pool"], t["v_pool"], t["copy_pairs"], err_flag=err)
+    note("config 5 fused: decode_append at L + 1")
+    out = ops.decode_append(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["lens_after"], L + 1, w.scale,
+                            t["new_key"], t["new_value"], t["slot_mapping"], err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    blk = torch.from_numpy(w.slot_mapping // w.block_size).long().to(dev)
+    off = torch.from_numpy(w.slot_mapping % w.block_size).long().to(dev)
+    for pool, new in ((t["k_pool"], t["new_key"]), (t["v_pool"], t["new_value"])):
+        assert torch.equal(pool[blk, :, off, :].view(torch.int16), new.view(torch.int16)), "appended rows differ"
+    k1, v1 = oracle.copy_blocks(host["k_pool"], host["v_pool"], host["copy_pairs"])
+    k2, v2 = oracle.reshape_and_cache(k1, v1, host["new_key"], host["new_value"], host["slot_mapping"])
+    pairs = [(i, j) for i in range(len(SEQS)) for j in range(len(HEADS))]
+    ref = oracle.paged_decode_heads(host["q"], k2, v2, host["table"], np.full(len(SEQS), L + 1, np.int32), w.scale,
+                                    pairs)
+    got = out.float().cpu().numpy()[np.ix_(SEQS, HEADS)].reshape(len(pairs), -1).astype(np.float64)
+    assert_close(got, ref, "bf16", "config 5 fused sampled outputs")
