@@ -48,7 +48,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hbm_traffic.txt")
 # sources of the kernel that produced it are unchanged.
 _COMMON_SOURCES = ("pa_device.h", "pa_kernels.h", "pa_decode_common.h", "pa_api.hip")
 _PATH_SOURCES = {"valu": ("pa_decode_valu.h", "pa_decode.hip", "pa_decode_fp8.hip"),
-                 "mfma": ("pa_mfma_kernel.h", "pa_decode_mfma.hip")}
+                 "mfma": ("pa_mfma_kernel.h", "pa_decode_mfma.hip"),
+                 "multi": ("pa_mfma_kernel.h", "pa_multi_token.hip")}
 
 
 def decode_path(dtype: str, head_dim: int, group: int, block_size: int) -> str:
@@ -314,7 +315,8 @@ def _event_pass(launch, first: int, steps: int) -> float:
 
 def _bench_multi(args, dev) -> int:
     """Multi-token step: N new tokens per sequence appended after the workload's context, then
-    pa_multi_token_attention of those N causal queries over the grown context."""
+    pa_multi_token_attention of those N causal queries over the grown context (with --kv fp8
+    over 8-bit pools, appended by the quantising append)."""
     import torch
 
     from paged_kv_cache_indexed_amd import _lib, ops
@@ -342,29 +344,40 @@ def _bench_multi(args, dev) -> int:
     seq = np.repeat(np.arange(B), N)
     slots = torch.from_numpy((w.block_table[seq, tok // w.block_size] * w.block_size + tok % w.block_size)
                              .astype(np.int32)).to(dev)
-    pool_bytes = 2 * t["k_pool"].numel() * t["k_pool"].element_size()
+    fp8 = args.kv == "fp8"
+    if fp8:
+        pools = _fp8_pools(t["k_pool"], t["v_pool"])
+        del t["k_pool"], t["v_pool"]
+    else:
+        pools = (t["k_pool"], t["v_pool"], None, None)
+    pool_bytes = sum(x.numel() * x.element_size() for x in pools if x is not None)
     R = max(2, math.ceil(args.replica_bytes / pool_bytes))
-    kps = [t["k_pool"]] + [t["k_pool"].clone() for _ in range(R - 1)]
-    vps = [t["v_pool"]] + [t["v_pool"].clone() for _ in range(R - 1)]
+    reps = [pools] + [tuple(x.clone() if x is not None else None for x in pools) for _ in range(R - 1)]
     qs_d = torch.from_numpy(qs).to(dev)
     max_len = int(lens.max())
-    desc = _lib.CacheDesc.of(t["k_pool"])
+    desc = _lib.CacheDesc.of(pools[0])
     wsn = _lib.pa_multi_token_workspace_bytes(desc, B, B * N, Hq, max_len, N, args.partition_size)
     ws = torch.empty((wsn + 3) // 4, dtype=torch.float32, device=dev) if wsn else None
     out = torch.empty_like(q)
     def attend(i):
-        ops.multi_token_attention(q, kps[i % R], vps[i % R], t["block_table"], t["context_lens"], qs_d, max_len, N,
-                                  w.scale, partition_size=args.partition_size, out=out, workspace=ws)
+        kp, vp, ks, vs = reps[i % R]
+        ops.multi_token_attention(q, kp, vp, t["block_table"], t["context_lens"], qs_d, max_len, N, w.scale,
+                                  k_scale=ks, v_scale=vs, partition_size=args.partition_size, out=out, workspace=ws)
 
     def step(i):
-        ops.reshape_and_cache(keys, vals, kps[i % R], vps[i % R], slots)
+        kp, vp, ks, vs = reps[i % R]
+        if fp8:
+            ops.reshape_and_cache_fp8(keys, vals, kp, vp, ks, vs, slots)
+        else:
+            ops.reshape_and_cache(keys, vals, kp, vp, slots)
         attend(i)
 
     for i in range(args.warmup):
         step(i)
     wall = _timed(step, args.warmup, args.steps)
     ms = _event_pass(attend, args.warmup + args.steps, args.steps)
-    kv_bytes = 2 * w.num_kv_heads * d * t["k_pool"].element_size() * int(lens.sum())
+    row_bytes = d + 4 if fp8 else d * q.element_size()  # codes + scale, or elements
+    kv_bytes = 2 * w.num_kv_heads * row_bytes * int(lens.sum())
     visible = sum(int((L - N + np.arange(N) + 1).sum()) for L in lens)  # (query, key) pairs per head
     flops = 4.0 * Hq * d * visible
     sec = ms * 1e-3
@@ -372,20 +385,22 @@ def _bench_multi(args, dev) -> int:
     peak_t = MFMA_PEAK_TFLOPS[w.dtype]
     mfma_bound = flops / kv_bytes > peak_t * 1e12 / (HBM_PEAK_GBS * 1e9)
     cfg = _describe(w)
-    cfg.update({"workload": w.name, "queries_per_seq": N, "replicas": R,
+    if fp8:
+        cfg["workload"] = f"{w.name}-fp8"
+    cfg.update({"queries_per_seq": N, "replicas": R,
                 "step": f"append {N} tokens/seq + causal attention of those {N} queries"})
     result = {
         "metric": "multi-token paged attention: query tokens/s at 1 MI355X",
         "value": round(B * N / (wall / args.steps), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": cfg,
-        "attention_kernel_ms": round(ms, 5),
+        "scaling": "weak", "vs_baseline": None, "dtype": f"e4m3+{w.dtype}" if fp8 else w.dtype,
+        "data": "synthetic", "config": cfg, "attention_kernel_ms": round(ms, 5),
         "kv_gbs": round(gbs, 1), "tflops": round(tfl, 2),
         "roofline": ({"bound": "mfma", "achieved": round(tfl, 2), "peak": peak_t, "unit": "TFLOP/s",
                       "frac": round(tfl / peak_t, 4), "traffic": None} if mfma_bound else
                      {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}),
-        "kernel_source_hash": kernel_source_hash("mfma"),
+        "kernel_source_hash": kernel_source_hash("multi"),
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -98,18 +98,30 @@ struct RowTileNanSink {
     }
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
+// 8-byte buffer load (8 E4M3 codes).
+__device__ __forceinline__ u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)offset, 0, 0));
+}
+
+// T: type of q, out and the tiles in LDS; KV: the pool's storage (T, or FP8 codes that widen
+// exactly to T when parked, with the tile's K and V scales beside them in LDS).
+template <typename T, typename KV, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void prefill_kernel(DecodeArgs a) {
     static_assert(T::kBytes == 2 && (D == 64 || D == 128), "16-bit rows of 64 or 128 elements");
+    constexpr bool kFp8 = std::is_same_v<KV, FP8>;
     using M = mfma::Mma<T>;
-    constexpr int U = D / 8;                   // 16-byte units per row
+    constexpr int U = D / 8;                   // 16-byte units per 16-bit row (8 elements each)
     constexpr int NC = D / 32;                 // k-blocks of the score contraction
     constexpr int NS = D / 16;                 // 16-dim output slices
-    constexpr int kLoads = kTile * U / kThreads;  // 16-byte units per thread per tile, for K and for V
+    // Units of 8 elements per thread per tile, for K and for V (16 bytes each from 16-bit
+    // pools, 8 codes from 8-bit ones).
+    constexpr int kLoads = kTile * U / kThreads;
     static_assert(kLoads >= 1 && kLoads * kThreads == kTile * U, "tile split");
     __shared__ int s_ids[kMaxIdsPerPartition];
     __shared__ u32x4 s_k[2][kTile * U];
     __shared__ __align__(16) uint16_t s_vt[2][D * kVtStride];
+    __shared__ float s_ks[kFp8 ? 2 : 1][kFp8 ? kTile : 1];  // 8-bit pools: the tile's K and V row scales
+    __shared__ float s_vs[kFp8 ? 2 : 1][kFp8 ? kTile : 1];
 
     const int G = a.num_q_heads / a.num_kv_heads;
     const int row_tiles = (a.col_tiles + 3) / 4;
@@ -163,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
     const int xw = kRows * rt + 16 * wave;
     const int lim_wave = xw + 15 < nq * G ? min(ntok, first_pos + xw / G + 1 - part.t0) : 0;
 
-    const size_t head_bytes = (size_t)bs * D * 2;
+    const size_t head_bytes = (size_t)bs * D * KV::kBytes;
     const char* kpool = static_cast<const char*>(a.k_pool);
     const char* vpool = static_cast<const char*>(a.v_pool);
 
@@ -220,6 +232,45 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
         }
     };
 
+    // 8-bit pools: the same (token, unit) slots, each an 8-byte load of 8 codes; threads 0-31
+    // and 32-63 also load the K and V scales of the 32 tile tokens (whose blocks may differ
+    // from lane to lane).
+    float scale8 = 0.f;
+    auto issue8 = [&](int k, u32x2* kr, u32x2* vr) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            int t, u;
+            slot_of(i, t, u);
+            const int rel = (k0 + k) * kTile + t;
+            const int tw = kLoads == 2 ? 2 * (64 * wave / U) + i : (kThreads * i + 64 * wave) / U;
+            const int rel_w = (k0 + k) * kTile + tw;  // the wave's first token
+            const int id = __builtin_amdgcn_readfirstlane(s_ids[(rel_w < ntok ? rel_w : 0) >> lbs]);
+            const size_t slab = (size_t)id * a.block_stride + (size_t)kvh * head_bytes;
+            const uint32_t off = (rel < ntok && rel >= rel_lo) ? (uint32_t)((rel & (bs - 1)) * D + 8 * u) : kOutOfRange;
+            kr[i] = buffer_load8(make_rsrc(kpool + slab, (uint32_t)head_bytes), off);
+            vr[i] = buffer_load8(make_rsrc(vpool + slab, (uint32_t)head_bytes), off);
+        }
+        if (tid < 2 * kTile) {
+            const int rel = (k0 + k) * kTile + (tid & (kTile - 1));
+            scale8 = 0.f;
+            if (rel < ntok && rel >= rel_lo) {
+                const size_t srow = (((size_t)s_ids[rel >> lbs] * a.num_kv_heads + kvh) << lbs) + (rel & (bs - 1));
+                scale8 = (tid < kTile ? a.k_scale : a.v_scale)[srow];
+            }
+        }
+    };
+    auto park8 = [&](int buf, const u32x2* kr, const u32x2* vr) {
+        u32x4 kw[kLoads], vw[kLoads];
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {  // the codes widen exactly to T
+            kw[i] = mfma::widen8(T{}, kr[i].x, kr[i].y);
+            vw[i] = mfma::widen8(T{}, vr[i].x, vr[i].y);
+        }
+        park(buf, kw, vw);
+        if (tid < kTile) s_ks[buf][tid] = scale8;
+        else if (tid < 2 * kTile) s_vs[buf][tid - kTile] = scale8;
+    };
+
     float m = -INFINITY;  // running base-2 max of row n (same in the four lane groups)
     float l = 0.f;        // this lane's part of row n's running sum
     f32x4 acc[NS];        // acc[s][i] = O[row 4g + i][dim 16s + n]
@@ -236,6 +287,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
             const int r = 16 * t + n;
 #pragma unroll
             for (int c = 0; c < NC; ++c) st = M::k32(s_k[buf][r * U + ((4 * c + g) ^ (r & 7))], qb[c], st);
+            if constexpr (kFp8) {  // the K row scales multiply the scores
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st[i] *= s_ks[buf][16 * t + 4 * g + i];
+            }
             if (full) {  // every row of the wave sees the whole tile (wave-uniform)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[4 * t + i] = st[i] * a.scale_log2;
@@ -279,6 +334,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
             psum += pr[j];
         }
         l += psum;
+        if constexpr (kFp8) {  // the V row scales multiply the weights (not the running sum)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pr[j] *= s_vs[buf][16 * (j >> 2) + 4 * g + (j & 3)];
+        }
         u32x4 phi, plo;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -296,7 +355,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
         }
     };
 
-    if (ntiles > 0) {
+    if constexpr (kFp8) {
+        if (ntiles > 0) {
+            u32x2 kr[kLoads], vr[kLoads];
+            issue8(0, kr, vr);
+            park8(0, kr, vr);
+            __syncthreads();
+            if (ntiles > 1) issue8(1, kr, vr);
+            for (int k = 0; k < ntiles; ++k) {
+                compute(k, k & 1);
+                if (k + 1 < ntiles) park8((k + 1) & 1, kr, vr);
+                __syncthreads();
+                if (k + 2 < ntiles) issue8(k + 2, kr, vr);
+            }
+        }
+    } else if (ntiles > 0) {
         u32x4 kr[kLoads], vr[kLoads];
         issue(0, kr, vr);
         park(0, kr, vr);
@@ -338,11 +411,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(DecodeArgs a) {
     }
 }
 
-template <typename T, int D>
+template <typename T, typename KV, int D>
 hipError_t launch_prefill_td(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     const int row_tiles = (a.col_tiles + 3) / 4;
     dim3 grid(num_kv_heads, batch * row_tiles, a.max_partitions);
-    hipLaunchKernelGGL((prefill_kernel<T, D>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, KV, D>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -411,15 +484,22 @@ bool multi_token_supported(int kv_dtype, int head_dim, int group, int block_size
 
 hipError_t launch_multi_token(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream) {
-    // 64 or more (query, head) rows per kv head over 16-bit pools: the 64-row kernel (with
-    // fewer rows its tiles run mostly empty: 2 column tiles measured 30% slower there)
-    if (a.col_tiles >= 4 && kv_dtype == dtype && (head_dim == 64 || head_dim == 128)) {
-        if (dtype == PA_F16)
-            return head_dim == 64 ? prefill::launch_prefill_td<F16, 64>(a, batch, num_kv_heads, stream)
-                                  : prefill::launch_prefill_td<F16, 128>(a, batch, num_kv_heads, stream);
-        if (dtype == PA_BF16)
-            return head_dim == 64 ? prefill::launch_prefill_td<BF16, 64>(a, batch, num_kv_heads, stream)
-                                  : prefill::launch_prefill_td<BF16, 128>(a, batch, num_kv_heads, stream);
+    // 64 or more (query, head) rows per kv head: the 64-row kernel (with fewer rows its tiles
+    // run mostly empty: 2 column tiles measured 30% slower there)
+    if (a.col_tiles >= 4 && (head_dim == 64 || head_dim == 128) && (kv_dtype == dtype || kv_dtype == PA_FP8_E4M3)) {
+        const bool f8 = kv_dtype == PA_FP8_E4M3;
+        if (dtype == PA_F16) {
+            if (f8) return head_dim == 64 ? prefill::launch_prefill_td<F16, FP8, 64>(a, batch, num_kv_heads, stream)
+                                          : prefill::launch_prefill_td<F16, FP8, 128>(a, batch, num_kv_heads, stream);
+            return head_dim == 64 ? prefill::launch_prefill_td<F16, F16, 64>(a, batch, num_kv_heads, stream)
+                                  : prefill::launch_prefill_td<F16, F16, 128>(a, batch, num_kv_heads, stream);
+        }
+        if (dtype == PA_BF16) {
+            if (f8) return head_dim == 64 ? prefill::launch_prefill_td<BF16, FP8, 64>(a, batch, num_kv_heads, stream)
+                                          : prefill::launch_prefill_td<BF16, FP8, 128>(a, batch, num_kv_heads, stream);
+            return head_dim == 64 ? prefill::launch_prefill_td<BF16, BF16, 64>(a, batch, num_kv_heads, stream)
+                                  : prefill::launch_prefill_td<BF16, BF16, 128>(a, batch, num_kv_heads, stream);
+        }
     }
     if (kv_dtype == PA_FP8_E4M3) {
         switch (dtype) {

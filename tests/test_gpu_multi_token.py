@@ -72,12 +72,15 @@ def test_multi_token_one_query_is_the_decode_bitwise():
     assert torch.equal(out.view(torch.int16), dec.view(torch.int16))
 
 
-@pytest.mark.parametrize("q_dtype,group", [("bf16", 1), ("f16", 8)])
-def test_multi_token_fp8_cache(q_dtype, group):
+# group 1 takes the 16-column kernel; groups 4 and 8 bring 64 or more rows per kv head to
+# the 64-row kernel (head_dim 64 and 128, one or two units of 8 codes per thread)
+@pytest.mark.parametrize("q_dtype,group,d,bs", [("bf16", 1, 128, 16), ("f16", 8, 128, 16), ("bf16", 4, 64, 16),
+                                                ("bf16", 8, 128, 32), ("f16", 4, 64, 64)])
+def test_multi_token_fp8_cache(q_dtype, group, d, bs):
     dev = require_gpu()
-    lens = [20, 129, 64]
-    ns = [20, 7, 33]
-    w, qs, q = _case("mt-fp8", 720 + group, lens, ns, 16, 2, group, 128, q_dtype)
+    lens = [20, 129, 64, 300]
+    ns = [20, 7, 33, 50]
+    w, qs, q = _case("mt-fp8", 720 + group, lens, ns, bs, 2, group, d, q_dtype)
     dead_k = np.isnan(w.k_pool).any(-1)
     kc, ks = o8.quantize_rows(np.nan_to_num(w.k_pool))
     vc, vs = o8.quantize_rows(np.nan_to_num(w.v_pool))
@@ -86,8 +89,8 @@ def test_multi_token_fp8_cache(q_dtype, group):
     ref = oracle.paged_attention_multi(q, o8.dequantize(kc, ks), o8.dequantize(vc, vs), w.block_table,
                                        w.context_lens, qs, w.scale)
     fp8 = tuple(torch.from_numpy(x).to(dev) for x in (kc, vc, ks, vs))
-    for P in (0, 32):
-        note(f"multi-token fp8 q={q_dtype} G={group} P={P}")
+    for P in (0, 2 * bs):
+        note(f"multi-token fp8 q={q_dtype} G={group} d={d} bs={bs} P={P}")
         out, err = _run(w, qs, q, dev, max(ns), P, fp8=fp8)
         assert err == 0
         assert_close(out.float().cpu().numpy(), ref, q_dtype, f"multi-token fp8 G={group} P={P}")
@@ -105,6 +108,24 @@ def test_multi_token_chunked_prefill_size():
         out, err = _run(w, qs, q, dev, 128, P)
         assert err == 0
         assert_close(out.float().cpu().numpy(), ref, "bf16", f"chunked prefill P={P}")
+
+
+def test_multi_token_chunked_prefill_fp8():
+    """The same chunks over an 8-bit cache (the 64-row kernel widening codes into its tiles)."""
+    dev = require_gpu()
+    lens = [2048] * 4
+    ns = [128] * 4
+    w, qs, q = _case("mt-chunk8", 731, lens, ns, 16, 8, 4, 128, "bf16")
+    kc, ks = o8.quantize_rows(np.nan_to_num(w.k_pool))
+    vc, vs = o8.quantize_rows(np.nan_to_num(w.v_pool))
+    ref = oracle.paged_attention_multi(q, o8.dequantize(kc, ks), o8.dequantize(vc, vs), w.block_table,
+                                       w.context_lens, qs, w.scale)
+    fp8 = tuple(torch.from_numpy(x).to(dev) for x in (kc, vc, ks, vs))
+    for P in (0, 256):
+        note(f"chunked prefill fp8 P={P}")
+        out, err = _run(w, qs, q, dev, 128, P, fp8=fp8)
+        assert err == 0
+        assert_close(out.float().cpu().numpy(), ref, "bf16", f"chunked prefill fp8 P={P}")
 
 
 def test_multi_token_errors_poison_only_their_sequence():
