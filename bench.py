@@ -98,13 +98,21 @@ def _workload(cfg: int, block_size: int | None, median: float | None):
     return config_workload(cfg, seed=0, block_size=block_size, median=median)
 
 
+def padding_waste_pct(lens, block_size: int) -> float:
+    """Share of the allocated slots that hold no token: 1 - sum(L) / (bs * sum(ceil(L / bs)))."""
+    lens = np.asarray(lens, np.int64)
+    alloc = int((-(-lens // block_size)).sum()) * block_size
+    return 100.0 * (1.0 - float(lens.sum()) / alloc) if alloc else 0.0
+
+
 def _describe(w) -> dict:
     L = w.lens_after_append
     return {"workload": w.name, "dtype": w.dtype, "batch": w.batch,
             "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "block_size": w.block_size, "num_blocks": w.num_blocks,
             "context_len_min": int(L.min()), "context_len_max": int(L.max()),
-            "context_len_sum": int(L.sum()), "step": "append 1 token/seq + decode"}
+            "context_len_sum": int(L.sum()), "padding_waste_pct": round(padding_waste_pct(L, w.block_size), 2),
+            "step": "append 1 token/seq + decode"}
 
 
 def _cpu_baseline(w, budget_s: float, window: int = 0) -> dict:

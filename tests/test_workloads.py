@@ -33,6 +33,21 @@ def test_config1_layout():
     assert np.all(np.isfinite(w.k_pool[mask])) and np.all(np.isnan(w.k_pool[~mask]))
 
 
+def test_padding_waste_reported_by_the_bench():
+    """1 - sum(L) / (bs * sum(ceil(L / bs))): config 1 after its append holds 324 tokens in 24
+    blocks of 16 slots (15.625% empty); contents-only lengths that fill their blocks waste
+    nothing; the waste grows with the block size on the long-tail mix."""
+    import bench
+
+    w = config_workload(1, seed=0)
+    assert bench.padding_waste_pct(w.context_lens, 16) == 0.0
+    assert bench.padding_waste_pct(w.lens_after_append, 16) == 100.0 * (1 - 324 / 384)
+    assert bench.padding_waste_pct([1], 8) == 87.5
+    L = config_workload(3, seed=0, median=87).lens_after_append
+    waste = [bench.padding_waste_pct(L, bs) for bs in (8, 16, 32, 64)]
+    assert all(x < y for x, y in zip(waste, waste[1:]))
+
+
 def test_determinism_and_block_size_independence():
     a = config_workload(3, seed=5, batch=6, heads=2, block_size=8)
     b = config_workload(3, seed=5, batch=6, heads=2, block_size=32)
