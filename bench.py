@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hbm_traffic.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "gqa_mfma_busy.txt")
 
 
 # Sources each decode kernel is built from: a recorded counter figure stays valid while the
@@ -87,6 +88,23 @@ def recorded_traffic(workload: str, path: str):
             if len(cells) >= 5 and cells[0] == workload and cells[1] == cur:
                 try:
                     return int(cells[4])
+                except ValueError:
+                    return None
+    return None
+
+
+def recorded_mfma_busy(workload: str, path: str):
+    """Matrix-core busy % (rocprofv3 MfmaUtil) of the attention kernel for this workload, if
+    the table in profiles/ was taken from the current sources of its kernel; else None."""
+    if not os.path.exists(MFMA_FILE):
+        return None
+    cur = kernel_source_hash(path)
+    with open(MFMA_FILE) as f:
+        for line in f:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 8 and cells[0] == workload and cells[1] == cur:
+                try:
+                    return float(cells[7])
                 except ValueError:
                     return None
     return None
@@ -409,6 +427,7 @@ def _bench_multi(args, dev) -> int:
                      {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}),
         "kernel_source_hash": kernel_source_hash("multi"),
+        "mfma_busy_pct": recorded_mfma_busy(cfg["workload"], "multi"),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -691,6 +710,8 @@ def main() -> int:
         "kernel_source_hash": kernel_source_hash(path),
         "decode_kernel": path,
     }
+    if path == "mfma":
+        result["mfma_busy_pct"] = recorded_mfma_busy(cfg["workload"], path)
     if not args.no_cpu_baseline:
         if fp8:
             result["cpu_baseline"] = (_cpu_baseline_fp8_beams(w, host_sample, args.cpu_budget, W) if host_sample
