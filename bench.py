@@ -50,7 +50,8 @@ MFMA_FILE = os.path.join(ROOT, "profiles", "gqa_mfma_busy.txt")
 _COMMON_SOURCES = ("pa_device.h", "pa_kernels.h", "pa_decode_common.h", "pa_api.hip")
 _PATH_SOURCES = {"valu": ("pa_decode_valu.h", "pa_decode.hip", "pa_decode_fp8.hip"),
                  "mfma": ("pa_mfma_kernel.h", "pa_decode_mfma.hip"),
-                 "multi": ("pa_mfma_kernel.h", "pa_multi_token.hip")}
+                 "multi": ("pa_mfma_kernel.h", "pa_multi_token.hip"),
+                 "beams": ("pa_mfma_kernel.h", "pa_decode_beams.hip")}
 
 
 def decode_path(dtype: str, head_dim: int, group: int, block_size: int) -> str:
@@ -517,6 +518,8 @@ def main() -> int:
                     help="pool elements: the workload's dtype, or 8-bit floats with a scale per row")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per replica instead of launching from Python")
+    ap.add_argument("--beams", type=int, default=0,
+                    help="decode with pa_decode_beams, sequences grouped by this many beams (append separate)")
     ap.add_argument("--unfused", action="store_true",
                     help="append with pa_reshape_and_cache and decode with pa_decode (two launches)")
     ap.add_argument("--queries", type=int, default=0,
@@ -591,7 +594,16 @@ def main() -> int:
     max_len = int(w.lens_after_append.max())
     P = args.partition_size
     W = max(0, args.window)
-    ws = ops.workspace_for(t["k_pool"], w.batch, w.num_q_heads, max_len, P, window=W)
+    BW = max(0, args.beams)
+    if BW and W > 0:
+        print("--beams has no window", file=sys.stderr)
+        return 2
+    if BW:
+        nws = _lib.pa_decode_beams_workspace_bytes(_lib.CacheDesc.of(t["k_pool"]), w.batch, BW, w.num_q_heads,
+                                                   max_len, P)
+        ws = torch.empty((nws + 3) // 4, dtype=torch.float32, device=dev) if nws else None
+    else:
+        ws = ops.workspace_for(t["k_pool"], w.batch, w.num_q_heads, max_len, P, window=W)
     out = torch.empty_like(t["q"])
     pairs = t["copy_pairs"]
     esize = t["k_pool"].element_size()
@@ -600,12 +612,16 @@ def main() -> int:
     kv_bytes = 2 * w.num_kv_heads * row_bytes * int(attended.sum())
     stream = torch.cuda.current_stream()
 
-    # append and decode fused unless a window is set or asked not to
-    fused = not (W > 0 or args.unfused)
+    # append and decode fused unless a window or beam groups are set, or asked not to
+    fused = not (W > 0 or args.unfused or BW)
 
     def decode(i):  # the measured kernel: the decode launch of step i
         r = i % R
-        if fused and fp8:
+        if BW:
+            ops.decode_beams(t["q"], kps[r], vps[r], t["block_table"], lens, max_len, w.scale, BW,
+                             k_scale=kss[r] if fp8 else None, v_scale=vss[r] if fp8 else None, partition_size=P,
+                             out=out, workspace=ws)
+        elif fused and fp8:
             ops.decode_append_fp8(t["q"], kps[r], vps[r], kss[r], vss[r], t["block_table"], lens, max_len, w.scale,
                                   t["new_key"], t["new_value"], t["slot_mapping"], partition_size=P, out=out,
                                   workspace=ws)
@@ -663,10 +679,14 @@ def main() -> int:
     roof_bytes = 2 * w.num_kv_heads * row_bytes * _unique_slots(w, W)
     achieved = roof_bytes / (dec_avg * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
-    path = decode_path("fp8" if fp8 else w.dtype, w.head_dim, w.num_q_heads // w.num_kv_heads, w.block_size)
+    path = ("beams" if BW else
+            decode_path("fp8" if fp8 else w.dtype, w.head_dim, w.num_q_heads // w.num_kv_heads, w.block_size))
     span = min(max_len, W + w.block_size - 1) if W > 0 else max_len
-    part = _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, w.num_q_heads,
-                                         span, P)
+    if BW:
+        part = _lib.pa_decode_beams_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, BW, w.num_q_heads,
+                                                   max_len, P)
+    else:
+        part = _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, w.num_q_heads, span, P)
     cfg = _describe(w)
     if NL > 1:
         cfg["workload"] = f"{w.name}-layer{NL - 1}of{NL}"
@@ -682,7 +702,10 @@ def main() -> int:
                 "launch": "hip graph per replica" if args.graph else "eager",
                 "copy_pairs_per_step": int(pairs.shape[0]),
                 "step": ("copy-on-write + " if pairs.shape[0] else "") + "append 1 token/seq + decode"
-                        + (" (append fused into the decode: pa_decode_append)" if fused else "")})
+                        + (" (append fused into the decode: pa_decode_append)" if fused else "")
+                        + (f" (pa_decode_beams, groups of {BW} beams)" if BW else "")})
+    if BW:
+        cfg["workload"] = f"{cfg['workload']}-beamdecode{BW}"
     if roof_bytes != kv_bytes:
         cfg["roofline_bytes"] = roof_bytes  # unique K+V bytes: shared blocks counted once
     if args.config == 5:

@@ -303,6 +303,45 @@ pa_status_t pa_decode_append_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, 
                                  pa_stream_t stream);
 
 /*
+ * pa_decode_beams - pa_decode (or pa_decode_fp8) for batches of beam groups.
+ *
+ * Sequences g * beam_width .. g * beam_width + beam_width - 1 form group g (the last group
+ * may be smaller): beams or parallel samples forked from one prompt, whose block tables
+ * reference the same physical blocks for their common prefix ([BlockManager essay] §4.2,
+ * reference counts; copy-on-write, pa_copy_blocks, gives each its own blocks where they
+ * diverge). The output is that of pa_decode / pa_decode_fp8 on the same arguments, for every
+ * sequence and any tables: grouping changes only how blocks are read. One work-group per (kv
+ * head, group, partition) compares the group's table slices for the partition; where every
+ * beam that reaches the partition lists the same ids for the blocks it reads, each block is
+ * read once for all of them, else once per beam.
+ *
+ * Arguments as pa_decode_fp8 (q_dtype; k_scale/v_scale for PA_FP8_E4M3 pools, ignored for
+ * 16-bit ones, whose q_dtype must equal the pool's dtype), without a window, plus beam_width
+ * >= 1. Runs on the matrix cores: head_dim 64 or 128, num_q_heads / num_kv_heads in {1, 2, 4,
+ * 8} with beam_width * that group <= 16, block_size >= 16, else PA_ERR_UNSUPPORTED. Errors
+ * (status codes, err_flag bits, NaN rows of the affected sequence only) are those of
+ * pa_decode. The partition length is pa_decode_beams_partition_size(...) and the workspace
+ * must hold pa_decode_beams_workspace_bytes(...) (NULL when that is 0).
+ */
+pa_status_t pa_decode_beams(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
+                            const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t batch, int32_t beam_width, int32_t num_q_heads, int32_t max_context_len,
+                            float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                            int32_t* err_flag, pa_stream_t stream);
+
+/*
+ * Partition length pa_decode_beams uses: `requested` > 0 must be a multiple of block_size
+ * with beam_width * requested / block_size <= 2048 (else -1); 0 picks a default.
+ */
+int32_t pa_decode_beams_partition_size(const pa_cache_desc_t* cache, int32_t batch, int32_t beam_width,
+                                       int32_t num_q_heads, int32_t max_context_len, int32_t requested);
+
+/* Workspace bytes pa_decode_beams needs (0: none, or an invalid argument). */
+size_t pa_decode_beams_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, int32_t beam_width,
+                                       int32_t num_q_heads, int32_t max_context_len, int32_t partition_size);
+
+/*
  * pa_reblock - migrate a paged cache to another block size.
  *
  * A new block size invalidates every block table, so the contents move to the new layout

@@ -15,6 +15,9 @@ from ._lib import (  # noqa: F401
     pa_decode,
     pa_decode_append,
     pa_decode_append_fp8,
+    pa_decode_beams,
+    pa_decode_beams_partition_size,
+    pa_decode_beams_workspace_bytes,
     pa_decode_fp8,
     pa_decode_partition_size,
     pa_decode_sliding_window,

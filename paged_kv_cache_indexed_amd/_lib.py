@@ -31,6 +31,7 @@ EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_size"
             "pa_decode_sliding_window_workspace_bytes", "pa_reshape_and_cache_fp8",
             "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_reblock", "pa_multi_token_attention",
             "pa_multi_token_workspace_bytes", "pa_decode_append", "pa_decode_append_fp8",
+            "pa_decode_beams", "pa_decode_beams_partition_size", "pa_decode_beams_workspace_bytes",
             "pa_status_string")
 
 # 8-bit float pools are uint8 (or float8_e4m3fn) tensors of OCP E4M3 codes.
@@ -119,6 +120,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_append_fp8.argtypes = [D, I32, P, P, P, P, P, P, P, I32, P, I32, I32, I32, F, P, P, P, I32, P, SZ,
                                          P, P]
     lib.pa_decode_append_fp8.restype = ctypes.c_int
+    lib.pa_decode_beams.argtypes = [D, I32, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, I32, P, SZ, P, P]
+    lib.pa_decode_beams.restype = ctypes.c_int
+    lib.pa_decode_beams_partition_size.argtypes = [D, I32, I32, I32, I32, I32]
+    lib.pa_decode_beams_partition_size.restype = I32
+    lib.pa_decode_beams_workspace_bytes.argtypes = [D, I32, I32, I32, I32, I32]
+    lib.pa_decode_beams_workspace_bytes.restype = SZ
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -307,6 +314,33 @@ def pa_decode_append_fp8(cache: CacheDesc, out, q, k_pool, v_pool, k_scale, v_sc
         _ptr(k_scale), _ptr(v_scale), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), batch,
         num_q_heads, int(max_context_len), float(scale), _ptr(key), _ptr(value), _ptr(slot_mapping),
         int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream)))
+
+
+def pa_decode_beams_partition_size(cache: CacheDesc, batch: int, beam_width: int, num_q_heads: int,
+                                   max_context_len: int, requested: int = 0) -> int:
+    desc = cache.c()
+    return int(load().pa_decode_beams_partition_size(ctypes.byref(desc), batch, beam_width, num_q_heads,
+                                                      max_context_len, requested))
+
+
+def pa_decode_beams_workspace_bytes(cache: CacheDesc, batch: int, beam_width: int, num_q_heads: int,
+                                    max_context_len: int, partition_size: int = 0) -> int:
+    desc = cache.c()
+    return int(load().pa_decode_beams_workspace_bytes(ctypes.byref(desc), batch, beam_width, num_q_heads,
+                                                       max_context_len, partition_size))
+
+
+def pa_decode_beams(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_lens, max_context_len: int,
+                    scale: float, beam_width: int, k_scale=None, v_scale=None, partition_size: int = 0,
+                    workspace=None, err_flag=None, stream=None) -> None:
+    batch, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    desc = cache.c()
+    _check(load().pa_decode_beams(
+        ctypes.byref(desc), dtype_code(q), _ptr(out), _ptr(q), _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), batch,
+        int(beam_width), num_q_heads, int(max_context_len), float(scale), int(partition_size), _ptr(workspace),
+        ws_bytes, _ptr(err_flag), _stream(stream)))
 
 
 def pa_decode_append(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_lens, max_context_len: int,

@@ -505,3 +505,117 @@ pa_status_t pa_decode_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* o
 }
 
 }  // extern "C"
+
+namespace {
+
+int32_t beams_partition_size(const pa_cache_desc_t* c, int32_t batch, int32_t beam_width, int32_t num_q_heads,
+                             int32_t max_context_len, int32_t requested) {
+    if (check_cache(c) != PA_OK || batch < 0 || beam_width <= 0 || max_context_len <= 0 || num_q_heads <= 0)
+        return -1;
+    const int bs = c->block_size;
+    // every beam of a group stages its table slice: beam_width * P / bs entries
+    const int64_t max_p = (int64_t)(kMaxBeamIds / beam_width) * bs;
+    if (max_p < bs) return -1;
+    if (requested > 0) return (requested % bs != 0 || requested > max_p) ? -1 : requested;
+    // Measured defaults: 1024-token partitions (a block multiple; on 32K-token beams 512 and
+    // 2048 were 8% and 4% slower, 256 30%), shortened while the launch has fewer than 1024
+    // workgroups, never past one partition per context.
+    const int64_t pairs = ceil_div(batch, beam_width) * (int64_t)c->num_kv_heads;
+    int64_t P = ceil_div(1024 > bs ? 1024 : bs, bs) * bs;
+    if (pairs * ceil_div(max_context_len, P) < 1024) {
+        int64_t want = ceil_div((int64_t)max_context_len * pairs, 1024);
+        if (want < 64) want = 64;
+        P = ceil_div(want, bs) * bs;
+    }
+    const int64_t whole = ceil_div(max_context_len, bs) * bs;
+    if (P > whole) P = whole;
+    if (P > max_p) P = max_p;
+    return (int32_t)P;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_decode_beams_partition_size(const pa_cache_desc_t* cache, int32_t batch, int32_t beam_width,
+                                       int32_t num_q_heads, int32_t max_context_len, int32_t requested) {
+    return beams_partition_size(cache, batch, beam_width, num_q_heads, max_context_len, requested);
+}
+
+size_t pa_decode_beams_workspace_bytes(const pa_cache_desc_t* cache, int32_t batch, int32_t beam_width,
+                                       int32_t num_q_heads, int32_t max_context_len, int32_t partition_size) {
+    const int32_t P = beams_partition_size(cache, batch, beam_width, num_q_heads, max_context_len, partition_size);
+    if (P <= 0) return 0;
+    const int64_t parts = ceil_div(max_context_len, P);
+    if (parts <= 1) return 0;
+    // the partition records of pa_decode (no slot words: the beam decode has no fused append)
+    return (size_t)batch * num_q_heads * parts * (cache->head_dim + 2) * sizeof(float);
+}
+
+pa_status_t pa_decode_beams(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
+                            const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t batch, int32_t beam_width, int32_t num_q_heads, int32_t max_context_len,
+                            float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                            int32_t* err_flag, pa_stream_t stream) {
+    pa_status_t st = check_cache(cache);
+    if (st != PA_OK) return st;
+    if (batch < 0 || beam_width <= 0) return PA_ERR_INVALID_ARGUMENT;
+    if (batch == 0) return PA_OK;
+    if (ceil_div(batch, beam_width) > 65535) return PA_ERR_INVALID_ARGUMENT;
+    if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PA_ERR_INVALID_ARGUMENT;
+    if (is_fp8(cache)) {
+        if (q_dtype != PA_F16 && q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+        if (!k_scale || !v_scale || !aligned4(k_scale) || !aligned4(v_scale)) return PA_ERR_INVALID_ARGUMENT;
+    } else if (q_dtype != cache->dtype) {
+        return PA_ERR_INVALID_ARGUMENT;
+    }
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_INVALID_ARGUMENT;
+    if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+    const int group = num_q_heads / cache->num_kv_heads;
+    if (!decode_beams_supported(cache->dtype, cache->head_dim, group, cache->block_size, beam_width))
+        return PA_ERR_UNSUPPORTED;
+    if (max_blocks_per_seq <= 0 || max_context_len <= 0) return PA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * cache->block_size) return PA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+    const int32_t P = beams_partition_size(cache, batch, beam_width, num_q_heads, max_context_len, partition_size);
+    if (P <= 0) return PA_ERR_INVALID_ARGUMENT;
+    const int64_t parts = ceil_div(max_context_len, P);
+    if (parts > kMaxPartitionSlots) return PA_ERR_UNSUPPORTED;
+    const size_t need = pa_decode_beams_workspace_bytes(cache, batch, beam_width, num_q_heads, max_context_len, P);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_INVALID_ARGUMENT;
+
+    DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = need > 0 ? a.ws_o + (size_t)batch * num_q_heads * parts * cache->head_dim : nullptr;
+    a.err_flag = err_flag;
+    a.num_blocks = cache->num_blocks;
+    a.log2_block_size = log2_exact(cache->block_size);
+    a.num_kv_heads = cache->num_kv_heads;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.partition_size = P;
+    a.max_partitions = (int32_t)parts;
+    a.window = 0;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.block_stride = block_stride(cache);
+    a.batch = batch;
+    a.beam_width = beam_width;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_decode_beams(a, cache->dtype, q_dtype, cache->head_dim, group,
+                                       (int)ceil_div(batch, beam_width), cache->num_kv_heads, s);
+    if (e == hipSuccess && parts > 1) e = launch_reduce(a, q_dtype, cache->head_dim, batch, s);
+    return from_hip(e);
+}
+
+}  // extern "C"

@@ -12,6 +12,8 @@ namespace pagedkv {
 
 // Largest number of block-table entries one decode partition stages in LDS.
 constexpr int kMaxIdsPerPartition = 1024;
+// Beam groups: table entries staged per partition for all beams of a group together.
+constexpr int kMaxBeamIds = 2048;
 // Partition slots of one decode launch (the grid's z extent).
 constexpr int kMaxPartitionSlots = 65535;
 
@@ -52,6 +54,9 @@ struct DecodeArgs {
     int32_t col_tiles;
     int32_t batch;
     int32_t num_q_tokens;  // rows of q and out
+    // beam groups (pa_decode_beams): sequences g * beam_width .. + beam_width - 1 form group g,
+    // whose blocks a workgroup reads once for all its beams where their tables agree
+    int32_t beam_width;
 };
 
 struct CacheArgs {
@@ -77,6 +82,11 @@ hipError_t launch_decode_valu_fp8(const DecodeArgs& a, int dtype, int head_dim, 
 bool decode_mfma_supported(int kv_dtype, int head_dim, int group, int block_size);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream);
+// Beam-group decode on the matrix cores (16-bit or 8-bit pools, head_dim 64/128, group 1-8,
+// block_size >= 16, beam_width * group <= 16); `groups` = ceil(batch / beam_width).
+bool decode_beams_supported(int kv_dtype, int head_dim, int group, int block_size, int beam_width);
+hipError_t launch_decode_beams(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int groups,
+                               int num_kv_heads, hipStream_t stream);
 // Multi-token attention on the matrix cores (16-bit or 8-bit pools, any group, block_size
 // >= 16) and its log-sum-exp combine per query row.
 bool multi_token_supported(int kv_dtype, int head_dim, int group, int block_size);

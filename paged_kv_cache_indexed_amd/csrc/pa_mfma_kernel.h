@@ -142,16 +142,123 @@ struct MultiNanSink {
     }
 };
 
+// Prologue of a beam group's partition p for kv head kvh: the nb sequences b0 .. b0 + nb - 1
+// ([BlockManager essay] §4.2: sequences forked from one prompt hold references to the same
+// physical blocks). Validates every beam's length (flags and NaN outputs in partition 0, as
+// the decode does), stages each beam's table slice for the partition at s_bids[j * cap + i]
+// (cap = partition_size / block_size entries per beam) and validates the ids (a bad id
+// flags the beam and poisons its outputs or records of this partition, as the decode does).
+// After it s_blen[j] is beam j's length if it takes part in this partition, else <= t0;
+// ref is the beam that reads the most blocks and shared tells whether every other beam's
+// ids equal ref's over the blocks it reads (then one read of each block serves all beams).
+// Returns false (uniformly) when no beam of the group reaches the partition.
+template <typename T, int D, int G, int NT>
+__device__ bool beam_prologue(const DecodeArgs& a, int p, int kvh, int b0, int nb, int* s_bids, int* s_blen,
+                              int* s_bbad, Partition& part, int& ref, bool& shared) {
+    const int tid = threadIdx.x;
+    const int P = a.partition_size;
+    const int lbs = a.log2_block_size;
+    const int cap = P >> lbs;
+    const int t0 = p * P;
+    const int j0 = t0 >> lbs;
+    if (tid < nb) {
+        const int L = a.context_lens[b0 + tid];
+        int flag = 0;
+        if (L <= 0) flag = PA_FLAG_EMPTY_CONTEXT;
+        else if (L > a.max_context_len || ((L - 1) >> lbs) >= a.max_blocks_per_seq) flag = PA_FLAG_BAD_LENGTH;
+        if (flag && p == 0 && a.err_flag) atomicOr(a.err_flag, flag);
+        s_blen[tid] = flag ? -1 : L;
+        s_bbad[tid] = flag && p == 0;  // partition 0 writes the NaN outputs of a bad length
+    }
+    __syncthreads();
+    for (int i = tid; i < nb * G * D; i += NT) {
+        const int j = i / (G * D);
+        if (s_bbad[j]) store_elem(T{}, a.out, ((size_t)(b0 + j) * a.num_q_heads + kvh * G) * D + i % (G * D),
+                                  __builtin_nanf(""));
+    }
+    __syncthreads();
+    if (tid < nb) s_bbad[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < nb * cap; i += NT) {
+        const int j = i / cap;
+        const int k = i - j * cap;
+        const int L = s_blen[j];
+        if (L <= t0) continue;  // bad length, or the beam ends before this partition
+        const int nids = ((min(L, t0 + P) - 1) >> lbs) - j0 + 1;
+        if (k >= nids) continue;
+        int id = a.block_table[(size_t)(b0 + j) * a.max_blocks_per_seq + j0 + k];
+        if ((unsigned)id >= (unsigned)a.num_blocks) {
+            s_bbad[j] = 1;
+            id = 0;
+        }
+        s_bids[i] = id;
+    }
+    __syncthreads();
+    for (int i = tid; i < nb * G * (D + 2); i += NT) {
+        const int j = i / (G * (D + 2));
+        if (!s_bbad[j]) continue;
+        const int r = i - j * (G * (D + 2));
+        const int h = r / (D + 2);
+        const int e = r - h * (D + 2);
+        const size_t row = (size_t)(b0 + j) * a.num_q_heads + kvh * G + h;
+        if ((s_blen[j] + P - 1) / P == 1) {
+            if (e < D) store_elem(T{}, a.out, row * D + e, __builtin_nanf(""));
+        } else {
+            const size_t rec = row * a.max_partitions + p;
+            if (e < D) a.ws_o[rec * D + e] = __builtin_nanf("");
+            else a.ws_ml[rec * 2 + (e - D)] = (e == D) ? -INFINITY : __builtin_nanf("");
+        }
+    }
+    if (tid < nb && s_bbad[tid] && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_BLOCK_ID);
+    __syncthreads();
+    if (tid < nb && s_bbad[tid]) s_blen[tid] = -1;
+    __syncthreads();
+    ref = -1;
+    int end = t0;
+    for (int j = 0; j < nb; ++j) {
+        const int t1 = min(s_blen[j], t0 + P);
+        if (t1 > end) {
+            end = t1;
+            ref = j;
+        }
+    }
+    if (ref < 0) return false;
+    int mismatch = 0;
+    for (int i = tid; i < nb * cap; i += NT) {
+        const int j = i / cap;
+        const int k = i - j * cap;
+        const int L = s_blen[j];
+        if (L <= t0 || j == ref) continue;
+        if (k < ((min(L, t0 + P) - 1) >> lbs) - j0 + 1 && s_bids[i] != s_bids[ref * cap + k]) mismatch = 1;
+    }
+    shared = !__syncthreads_or(mismatch);
+    part.nparts = 0;
+    part.t0 = t0;
+    part.rel_lo = 0;
+    part.ntok = end - t0;
+    part.j0 = j0;
+    part.len = 0;
+    part.npos = -1;
+    part.slot = -1;
+    return true;
+}
+
 // kMulti = false: one query per sequence, column n of the B operand is head kvh * G + n.
 // kMulti = true: several queries per sequence (query_start), columns are (query, head)
 // pairs taken query-major, 16 per workgroup (column tile blockIdx.y % col_tiles); query i of
 // a sequence with n new tokens sits at position L - n + i and its column sees tokens up to
 // that position only (causal mask inside the valid range).
-template <typename T, typename KV, int D, int G, int NW, bool kDoubleBuffer, bool kMulti = false>
+// kBeams = true: one query per sequence, columns are (beam, head) pairs taken beam-major
+// over the beams of group blockIdx.y (beam_prologue); a partition whose blocks all beams
+// share is streamed once for all of them, else once per beam with the other beams' columns
+// masked.
+template <typename T, typename KV, int D, int G, int NW, bool kDoubleBuffer, bool kMulti = false,
+          bool kBeams = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(T::kBytes == 2, "matrix-core operands are 16-bit");
     static_assert(G >= 1 && G <= 16, "at most 16 query heads per kv head");
-    constexpr int NCOL = kMulti ? 16 : G;  // columns whose results this workgroup keeps
+    static_assert(!(kMulti && kBeams), "one column mapping");
+    constexpr int NCOL = (kMulti || kBeams) ? 16 : G;  // columns whose results this workgroup keeps
     constexpr bool kFp8 = std::is_same_v<KV, FP8>;
     constexpr int NC = D / 32;             // 32-dim k-blocks of the score contraction
     constexpr int NL = D * KV::kBytes / 64;  // 16-byte loads per lane per tile row (64 B of each row)
@@ -159,13 +266,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     constexpr int kChunk = 32;             // tokens per wave iteration (two 16-token tiles)
     using M = Mma<T>;
 
-    __shared__ int s_ids[kMaxIdsPerPartition];
+    __shared__ int s_ids[kBeams ? kMaxBeamIds : kMaxIdsPerPartition];
+    __shared__ int s_blen[kBeams ? 16 : 1];  // beam groups: lengths of the beams in this partition
+    __shared__ int s_bbad[kBeams ? 16 : 1];
     __shared__ float s_m[NW][NCOL];
     __shared__ float s_l[NW][NCOL];
     __shared__ float s_acc[NW][NCOL][D];
     // the new token's K and V rows as read, and for an 8-bit pool each wave's record of them
     // (fused append of the decode)
-    constexpr bool kAppendable = !kMulti;
+    constexpr bool kAppendable = !kMulti && !kBeams;
     using R = NewRec<KV, D>;
     constexpr int kRaw = NewRec<T, D>::kBytes;
     __shared__ __align__(16) char s_new[kAppendable ? kRaw + (kFp8 ? NW * R::kBytes : 0) : 16];
@@ -194,12 +303,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
         if (16 * ct >= nq * G) return;  // no query of this sequence in this tile (uniform)
     }
+    // beam groups: sequences b0 .. b0 + nb - 1; column n is head n % G of beam n / G
+    const int b0 = kBeams ? (int)blockIdx.y * a.beam_width : b;
+    const int nb = kBeams ? min(a.beam_width, a.batch - b0) : 1;
     const int col = 16 * ct + n;
     const int qi = kMulti ? col / G : 0;       // query of the column
-    const int qh = kMulti ? col - qi * G : n;  // head of the column inside the group
-    const bool col_valid = kMulti ? qi < nq : n < G;
+    const int qh = kMulti ? col - qi * G : (kBeams ? n % G : n);  // head of the column inside the group
+    const bool col_valid = kMulti ? qi < nq : (kBeams ? n < nb * G : n < G);
 
-    if constexpr (!kMulti) {
+    if constexpr (!kMulti && !kBeams) {
         if (partition_is_dead(a, p, b)) return;
     }
     // Q as the B operand of S^T = K Q^T (zero in invalid columns); k-block c of lane group g
@@ -207,8 +319,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // 8(c%2) .. +7 for 8-bit pools.
     u32x4 qb[NC];
     {
-        const size_t qrow_idx = kMulti ? (size_t)(q0 + (col_valid ? qi : 0)) * a.num_q_heads + kvh * G + qh
-                                       : (size_t)b * a.num_q_heads + kvh * G + (col_valid ? n : 0);
+        const size_t qrow_idx = kMulti   ? (size_t)(q0 + (col_valid ? qi : 0)) * a.num_q_heads + kvh * G + qh
+                                : kBeams ? (size_t)(b0 + (col_valid ? n / G : 0)) * a.num_q_heads + kvh * G + qh
+                                         : (size_t)b * a.num_q_heads + kvh * G + (col_valid ? n : 0);
         const char* qrow = static_cast<const char*>(a.q) + qrow_idx * D * 2;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -217,7 +330,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
     }
     Partition part;
-    if constexpr (kMulti) {
+    int bref = 0;        // beam groups: the beam whose table is streamed when all agree
+    bool bshared = true;
+    if constexpr (kBeams) {
+        if (!beam_prologue<T, D, G, NW * 64>(a, p, kvh, b0, nb, s_ids, s_blen, s_bbad, part, bref, bshared)) return;
+    } else if constexpr (kMulti) {
         if (!partition_prologue_sink<T, D, NW * 64>(a, p, b, max(nq, 1), MultiNanSink<T, D, G>{a, q0, nq, kvh, ct},
                                                     s_ids, part))
             return;
@@ -244,6 +361,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int first_pos = part.len - nq;
         lim_wave = 16 * ct + 15 < nq * G ? min(ntok, first_pos + (16 * ct) / G + 1 - part.t0) : 0;
     }
+    // the table slice streamed: the sequence's, or in a beam group the reference beam's
+    const int* ids = s_ids;
+    const int bcap = kBeams ? a.partition_size >> a.log2_block_size : 0;
+    // beam groups: a beam's column sees its own tokens of the partition; the wave's fast
+    // path needs the shortest beam of the partition
+    auto beam_end = [&](int j) { return min(s_blen[j], part.t0 + a.partition_size) - part.t0; };
+    if constexpr (kBeams) {
+        ids = s_ids + bref * bcap;
+        lim_col = col_valid && s_blen[n / G] > part.t0 ? beam_end(n / G) : 0;
+        for (int j = 0; j < nb; ++j)
+            if (s_blen[j] > part.t0) lim_wave = min(lim_wave, beam_end(j));
+    }
 
     // Identity B operand of the 16x16x16 transpose: k-slot (g, i) is 1 in column 4g + i.
     u32x2 ident;
@@ -256,7 +385,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const char* vpool = static_cast<const char*>(a.v_pool);
     const uint32_t slab_bytes = (uint32_t)head_bytes;
     const uint32_t seg = 16u * g;  // lane group g reads bytes 64c + 16g .. +15 of a row
-    const int niters = (ntok - c0 * kChunk + kChunk * NW - 1) / (kChunk * NW);
+    int niters = (ntok - c0 * kChunk + kChunk * NW - 1) / (kChunk * NW);
 
     // Loads of one chunk: tile t rows are tokens rel + 16t + n; lanes past the partition end
     // read zeros through an out-of-range offset. With 8-bit pools, ks/vs[t] are the scales
@@ -266,7 +395,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int rel = (c0 + it * NW + wave) * kChunk + 16 * t;  // wave-uniform
-            const int id = __builtin_amdgcn_readfirstlane(s_ids[(rel < ntok ? rel : 0) >> lbs]);  // partitions start on a block
+            const int id = __builtin_amdgcn_readfirstlane(ids[(rel < ntok ? rel : 0) >> lbs]);  // partitions start on a block
             const size_t slab = (size_t)id * block_bytes + (size_t)kvh * head_bytes;
             const uint32_t off = (rel + n < ntok && rel + n >= rel_lo)
                                      ? (uint32_t)(((rel & (bs - 1)) + n) * D * KV::kBytes) + seg
@@ -439,6 +568,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     };
 
     u32x4 ka[2][NL], va[2][NL], ksa[2], vsa[2];
+    // One pass over the partition; a beam group whose beams' blocks differ takes one pass per
+    // beam over its own blocks, with the other beams' columns seeing nothing.
+    const int npasses = kBeams && !bshared ? nb : 1;
+    if constexpr (kBeams) {
+        if (!bshared) lim_wave = 0;
+    }
+    for (int pass = 0; pass < npasses; ++pass) {
+    if constexpr (kBeams) {
+        if (!bshared) {
+            if (s_blen[pass] <= part.t0) continue;
+            ids = s_ids + pass * bcap;
+            ntok = beam_end(pass);
+            niters = (ntok + kChunk * NW - 1) / (kChunk * NW);
+            lim_col = col_valid && n / G == pass ? ntok : 0;
+        }
+    }
     if constexpr (kDoubleBuffer) {
         u32x4 kb[2][NL], vb[2][NL], ksb[2], vsb[2];
         issue(0, ka, va, ksa, vsa);
@@ -467,6 +612,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             issue(it, ka, va, ksa, vsa);
             compute(it, ka, va, ksa, vsa);
         }
+    }
     }
 
     // column n's sum over the four lane groups
@@ -506,6 +652,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
             const size_t r = rows.row(c);
             if (part.nparts == 1) {
+                store_elem(T{}, a.out, r * D + e, num / den);
+            } else {
+                const size_t rec = r * a.max_partitions + p;
+                a.ws_o[rec * D + e] = num / den;
+                if (e == 0) {
+                    a.ws_ml[rec * 2] = M;
+                    a.ws_ml[rec * 2 + 1] = den;
+                }
+            }
+        }
+    } else if constexpr (kBeams) {
+        // merge the waves per (beam, head) column: the output row (the beam's only partition)
+        // or the partition record
+        const int P = a.partition_size;
+        for (int i = threadIdx.x; i < 16 * D; i += NW * 64) {
+            const int c = i / D;
+            const int e = i % D;
+            if (c >= nb * G) continue;
+            const int L = s_blen[c / G];
+            if (L <= part.t0) continue;  // the beam does not reach this partition, or is poisoned
+            float M = s_m[0][c];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][c]);
+            const float Ms = (M == -INFINITY) ? 0.f : M;
+            float num = 0.f, den = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float f = __builtin_amdgcn_exp2f(s_m[w][c] - Ms);
+                num = fmaf(s_acc[w][c][e], f, num);
+                den = fmaf(s_l[w][c], f, den);
+            }
+            const size_t r = (size_t)(b0 + c / G) * a.num_q_heads + kvh * G + c % G;
+            if ((L + P - 1) / P == 1) {
                 store_elem(T{}, a.out, r * D + e, num / den);
             } else {
                 const size_t rec = r * a.max_partitions + p;

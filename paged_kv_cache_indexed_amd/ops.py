@@ -8,6 +8,7 @@ from __future__ import annotations
 import torch
 
 from ._lib import (CacheDesc, pa_copy_blocks, pa_copy_blocks_fp8, pa_decode, pa_decode_append, pa_decode_append_fp8,
+                   pa_decode_beams, pa_decode_beams_workspace_bytes,
                    pa_decode_fp8, pa_decode_sliding_window, pa_decode_sliding_window_workspace_bytes,
                    pa_decode_workspace_bytes, pa_multi_token_attention, pa_multi_token_workspace_bytes,
                    pa_reblock, pa_reshape_and_cache, pa_reshape_and_cache_fp8)
@@ -107,6 +108,22 @@ def decode_append_fp8(q, k_pool, v_pool, k_scale, v_scale, block_table, context_
         workspace = workspace_for(k_pool, q.shape[0], q.shape[1], max_context_len, partition_size)
     pa_decode_append_fp8(CacheDesc.of(k_pool), out, q, k_pool, v_pool, k_scale, v_scale, block_table, context_lens,
                          max_context_len, scale, key, value, slot_mapping, partition_size, workspace, err_flag, stream)
+    return out
+
+
+def decode_beams(q, k_pool, v_pool, block_table, context_lens, max_context_len: int, scale: float, beam_width: int,
+                 k_scale=None, v_scale=None, partition_size: int = 0, out=None, workspace=None, err_flag=None,
+                 stream=None):
+    """decode (or decode_fp8 when the scales are given) with sequences grouped by beam_width:
+    blocks that every beam of a group lists in a partition are read once for the group."""
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        n = pa_decode_beams_workspace_bytes(CacheDesc.of(k_pool), int(q.shape[0]), int(beam_width), int(q.shape[1]),
+                                            max_context_len, partition_size)
+        workspace = torch.empty((n + 3) // 4, dtype=torch.float32, device=q.device) if n else None
+    pa_decode_beams(CacheDesc.of(k_pool), out, q, k_pool, v_pool, block_table, context_lens, max_context_len, scale,
+                    beam_width, k_scale, v_scale, partition_size, workspace, err_flag, stream)
     return out
 
 
