@@ -112,3 +112,32 @@ def test_config5_fused_step():
                                     pairs)
     got = out.float().cpu().numpy()[np.ix_(SEQS, HEADS)].reshape(len(pairs), -1).astype(np.float64)
     assert_close(got, ref, "bf16", "config 5 fused sampled outputs")
+
+
+def test_config5_beam_decode_step():
+    """The benchmark's config 5 step with --beams 4: copy-on-write, append, then pa_decode_beams
+    (the shared prefix read once per group of 4 beams; the copied last shared block and the
+    tails per beam), on sampled outputs, for the default and the 512-token partitions."""
+    dev = require_gpu()
+    note("config 5 beams: building the 32K beam workload on the device")
+    w = beam_workload(dev)
+    t = w.tensors
+    host = host_subset(w, SEQS, HEADS)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    L = w.context
+    ops.copy_blocks(t["k_pool"], t["v_pool"], t["copy_pairs"], err_flag=err)
+    ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_pool"], t["v_pool"], t["slot_mapping"], err_flag=err)
+    k1, v1 = oracle.copy_blocks(host["k_pool"], host["v_pool"], host["copy_pairs"])
+    k2, v2 = oracle.reshape_and_cache(k1, v1, host["new_key"], host["new_value"], host["slot_mapping"])
+    pairs = [(i, j) for i in range(len(SEQS)) for j in range(len(HEADS))]
+    ref = oracle.paged_decode_heads(host["q"], k2, v2, host["table"], np.full(len(SEQS), L + 1, np.int32), w.scale,
+                                    pairs)
+    for P in (0, 512):
+        note(f"config 5 beams: decode_beams at L + 1, P={P}")
+        out = ops.decode_beams(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["lens_after"], L + 1, w.scale,
+                               w.beams, partition_size=P, err_flag=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert torch.isfinite(out.float()).all()
+        got = out.float().cpu().numpy()[np.ix_(SEQS, HEADS)].reshape(len(pairs), -1).astype(np.float64)
+        assert_close(got, ref, "bf16", f"config 5 beam decode sampled outputs P={P}")
