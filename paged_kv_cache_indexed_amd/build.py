@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -16,6 +17,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libpagedkv.so")
+# per-kernel registers, scratch, LDS and occupancy of the last build (from the compiler's
+# resource-usage remarks)
+RESOURCES_PATH = os.path.join(BUILD_DIR, "kernel_resources.tsv")
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of the generated code: every HIP compile disables the
@@ -38,17 +42,35 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, verbose: bool) -> str:
+_REMARK = re.compile(r"remark: .*?Function Name: (\S+)|remark: .*?(VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                     r"Occupancy \[waves/SIMD\]|LDS Size \[bytes/block\]): (\d+)")
+
+
+def _resources(stderr: str):
+    """(kernel, vgprs, agprs, scratch bytes per lane, occupancy, LDS bytes) from the remarks."""
+    rows, cur = [], None
+    for line in stderr.splitlines():
+        m = _REMARK.search(line)
+        if not m:
+            continue
+        if m.group(1):
+            cur = {"name": m.group(1)}
+            rows.append(cur)
+        elif cur is not None:
+            cur[m.group(2).split()[0]] = int(m.group(3))
+    return [(r["name"], r.get("VGPRs", -1), r.get("AGPRs", -1), r.get("ScratchSize", -1), r.get("Occupancy", -1),
+             r.get("LDS", -1)) for r in rows]
+
+
+def _compile(src: str, verbose: bool):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIP_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
-    if verbose and r.stderr.strip():
-        print(r.stderr, file=sys.stderr)
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
@@ -56,7 +78,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        done = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    objs = [o for o, _ in done]
+    with open(RESOURCES_PATH, "w") as f:
+        f.write("kernel\tvgprs\tagprs\tscratch_bytes_per_lane\toccupancy_waves_per_simd\tlds_bytes\n")
+        for _, rows in done:
+            for row in rows:
+                f.write("\t".join(str(x) for x in row) + "\n")
     tmp = LIB_PATH + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
