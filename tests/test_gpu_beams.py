@@ -102,6 +102,22 @@ def test_beams_bitwise_equal_to_grouped_decode(group):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_beams_degenerate_groups():
+    """beam_width 1 (every sequence its own group) and the largest partition the staged table
+    slices allow (beam_width x P / block_size = 2048 ids)."""
+    dev = require_gpu()
+    q, kp, vp, table, L = _beam_case(7, _LENS, 4, 2, 1, 64, 16, 256, "f16")
+    ref = oracle.paged_decode(q, kp, vp, table, L, 0.125)
+    tq, tk, tv, tt, tl = _device(dev, "f16", q, kp, vp, table, L)
+    for W, P in ((1, 0), (1, 16 * 2048), (4, 16 * 512), (4, 16)):
+        note(f"beams W={W} P={P}")
+        out = ops.decode_beams(tq, tk, tv, tt, tl, int(L.max()), 0.125, W, partition_size=P)
+        torch.cuda.synchronize()
+        assert_close(out.float().cpu().numpy(), ref, "f16", f"beams W={W} P={P}")
+    with pytest.raises(Exception):  # 4 beams x 513 ids of a partition: over the staged slices
+        ops.decode_beams(tq, tk, tv, tt, tl, int(L.max()), 0.125, 4, partition_size=16 * 513)
+
+
 def test_beams_private_tables():
     """No block is shared: every partition takes the per-beam passes."""
     dev = require_gpu()
