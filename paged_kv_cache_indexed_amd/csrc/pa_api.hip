@@ -63,6 +63,40 @@ int32_t window_span(const pa_cache_desc_t* c, int32_t max_context_len, int32_t w
     return span < max_context_len ? (int32_t)span : max_context_len;
 }
 
+// The launch arguments every attention entry point shares. `rows` are the rows of q and out
+// (sequences, or query tokens), which size the partition records; `need` is the workspace
+// the call requires (records follow their outputs: o first, then the (max, sum) pairs).
+DecodeArgs attention_args(const pa_cache_desc_t* c, void* out, const void* q, const void* k_pool, const void* v_pool,
+                          const float* k_scale, const float* v_scale, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch, int64_t rows,
+                          int32_t num_q_heads, int32_t max_context_len, float scale, int32_t P, int64_t parts,
+                          void* workspace, size_t need, int32_t* err_flag) {
+    DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = need > 0 ? a.ws_o + (size_t)rows * num_q_heads * parts * c->head_dim : nullptr;
+    a.err_flag = err_flag;
+    a.num_blocks = c->num_blocks;
+    a.log2_block_size = log2_exact(c->block_size);
+    a.num_kv_heads = c->num_kv_heads;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.partition_size = P;
+    a.max_partitions = (int32_t)parts;
+    a.scale_log2 = scale * 1.4426950408889634f;  // scores live in the base-2 exponent domain
+    a.block_stride = block_stride(c);
+    a.batch = batch;
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -312,32 +346,11 @@ pa_status_t pa_multi_token_attention(const pa_cache_desc_t* cache, int32_t q_dty
                                                        max_query_len, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_INVALID_ARGUMENT;
 
-    DecodeArgs a{};
-    a.out = out;
-    a.q = q;
-    a.k_pool = k_pool;
-    a.v_pool = v_pool;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
-    a.block_table = block_table;
-    a.context_lens = context_lens;
-    a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = need > 0 ? a.ws_o + (size_t)num_q_tokens * num_q_heads * parts * cache->head_dim : nullptr;
-    a.err_flag = err_flag;
-    a.num_blocks = cache->num_blocks;
-    a.log2_block_size = log2_exact(cache->block_size);
-    a.num_kv_heads = cache->num_kv_heads;
-    a.num_q_heads = num_q_heads;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.max_context_len = max_context_len;
-    a.partition_size = P;
-    a.max_partitions = (int32_t)parts;
-    a.window = 0;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    a.block_stride = block_stride(cache);
+    DecodeArgs a = attention_args(cache, out, q, k_pool, v_pool, k_scale, v_scale, block_table, max_blocks_per_seq,
+                                  context_lens, batch, num_q_tokens, num_q_heads, max_context_len, scale, P, parts,
+                                  workspace, need, err_flag);
     a.query_start = query_start;
     a.col_tiles = (int32_t)col_tiles;
-    a.batch = batch;
     a.num_q_tokens = num_q_tokens;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_multi_token(a, cache->dtype, q_dtype, cache->head_dim, group, batch, cache->num_kv_heads, s);
@@ -393,30 +406,10 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out
     const size_t need = pa_decode_workspace_bytes(cache, batch, num_q_heads, span, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_INVALID_ARGUMENT;
 
-    DecodeArgs a{};
-    a.out = out;
-    a.q = q;
-    a.k_pool = k_pool;
-    a.v_pool = v_pool;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
-    a.block_table = block_table;
-    a.context_lens = context_lens;
-    a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = need > 0 ? a.ws_o + (size_t)batch * num_q_heads * parts * cache->head_dim : nullptr;
-    a.err_flag = err_flag;
-    a.num_blocks = cache->num_blocks;
-    a.log2_block_size = log2_exact(cache->block_size);
-    a.num_kv_heads = cache->num_kv_heads;
-    a.num_q_heads = num_q_heads;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.max_context_len = max_context_len;
-    a.partition_size = P;
-    a.max_partitions = (int32_t)parts;
+    DecodeArgs a = attention_args(cache, out, q, k_pool, v_pool, k_scale, v_scale, block_table, max_blocks_per_seq,
+                                  context_lens, batch, batch, num_q_heads, max_context_len, scale, P, parts, workspace,
+                                  need, err_flag);
     a.window = window;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    a.block_stride = block_stride(cache);
-    a.batch = batch;
     a.new_key = new_key;
     a.new_value = new_value;
     a.slot_mapping = slot_mapping;
@@ -586,30 +579,9 @@ pa_status_t pa_decode_beams(const pa_cache_desc_t* cache, int32_t q_dtype, void*
     const size_t need = pa_decode_beams_workspace_bytes(cache, batch, beam_width, num_q_heads, max_context_len, P);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_INVALID_ARGUMENT;
 
-    DecodeArgs a{};
-    a.out = out;
-    a.q = q;
-    a.k_pool = k_pool;
-    a.v_pool = v_pool;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
-    a.block_table = block_table;
-    a.context_lens = context_lens;
-    a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = need > 0 ? a.ws_o + (size_t)batch * num_q_heads * parts * cache->head_dim : nullptr;
-    a.err_flag = err_flag;
-    a.num_blocks = cache->num_blocks;
-    a.log2_block_size = log2_exact(cache->block_size);
-    a.num_kv_heads = cache->num_kv_heads;
-    a.num_q_heads = num_q_heads;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.max_context_len = max_context_len;
-    a.partition_size = P;
-    a.max_partitions = (int32_t)parts;
-    a.window = 0;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    a.block_stride = block_stride(cache);
-    a.batch = batch;
+    DecodeArgs a = attention_args(cache, out, q, k_pool, v_pool, k_scale, v_scale, block_table, max_blocks_per_seq,
+                                  context_lens, batch, batch, num_q_heads, max_context_len, scale, P, parts, workspace,
+                                  need, err_flag);
     a.beam_width = beam_width;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_decode_beams(a, cache->dtype, q_dtype, cache->head_dim, group,
