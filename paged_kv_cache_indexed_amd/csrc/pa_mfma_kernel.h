@@ -314,6 +314,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if constexpr (!kMulti && !kBeams) {
         if (partition_is_dead(a, p, b)) return;
     }
+    if constexpr (kBeams) {  // a later partition no beam of the group reaches: leave before any load
+        if (PA_EARLY_DEAD_CHECK && p > 0) {
+            bool live = false;
+            for (int j = 0; j < nb; ++j) {
+                const int L = a.context_lens[b0 + j];
+                live |= L > p * a.partition_size && L <= a.max_context_len;
+            }
+            if (!live) return;
+        }
+    }
     // Q as the B operand of S^T = K Q^T (zero in invalid columns); k-block c of lane group g
     // holds the dims the K operand gives it: 32c + 8g .. +7 for 16-bit pools, 64(c/2) + 16g +
     // 8(c%2) .. +7 for 8-bit pools.

@@ -116,6 +116,13 @@ def test_beams_degenerate_groups():
         assert_close(out.float().cpu().numpy(), ref, "f16", f"beams W={W} P={P}")
     with pytest.raises(Exception):  # 4 beams x 513 ids of a partition: over the staged slices
         ops.decode_beams(tq, tk, tv, tt, tl, int(L.max()), 0.125, 4, partition_size=16 * 513)
+    # a loose max_context_len: most partitions of the launch lie past every beam of a group
+    wide = torch.full((tt.shape[0], 4 * tt.shape[1]), -1, dtype=torch.int32, device=dev)
+    wide[:, :tt.shape[1]] = tt
+    note("beams loose max_context_len")
+    out = ops.decode_beams(tq, tk, tv, wide, tl, 4 * int(L.max()), 0.125, 4, partition_size=64)
+    torch.cuda.synchronize()
+    assert_close(out.float().cpu().numpy(), ref, "f16", "beams loose max_context_len")
 
 
 def test_beams_private_tables():
