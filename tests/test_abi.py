@@ -58,6 +58,10 @@ def test_partition_policy(lib):
     # VALU path with few workgroups: partitions shrink toward ~2048 workgroups
     p = _lib.pa_decode_partition_size(_desc(hkv=8, dtype=_lib.PA_F32), 32, 64, 2049, 0)
     assert p % 16 == 0 and 32 * 8 * -(-2049 // p) >= 2048 - 256
+    # ... but not below 256 tokens: config 1 (4 sequences x 8 heads, 129 tokens) keeps one
+    # partition, one sequence of 4096 tokens at 32 heads gets 16
+    assert _lib.pa_decode_partition_size(_desc(hkv=8, d=64, dtype=_lib.PA_F32, nb=64), 4, 8, 129, 0) == 144
+    assert _lib.pa_decode_partition_size(c, 1, 32, 4096, 0) == 256
     # matrix-core path (bf16, 8 query heads per kv head): one partition for 256 pairs
     assert _lib.pa_decode_partition_size(_desc(hkv=8, dtype=_lib.PA_BF16), 32, 64, 2049, 0) == 2064
     # ... split to reach 256 workgroups, and at most 4096 tokens per partition
