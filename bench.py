@@ -24,6 +24,10 @@ With --window W the decode attends to the last W tokens of each sequence only
 With --kv fp8 the pools hold 8-bit floats (OCP E4M3) with a float32 scale per (token, kv
 head) row, filled by the library's own quantising append; the step uses the *_fp8 entry
 points and the algorithmic bytes are 2 x kv_heads x (head_dim + 4) per attended token.
+With --beams W the decode is pa_decode_beams with groups of W consecutive sequences (the
+append is a separate pa_reshape_and_cache[_fp8] call); config 5's groups of 4 beams share a
+30720-token prefix. With --queries N the step appends N tokens per sequence and runs
+pa_multi_token_attention over them (metric: query tokens/s).
 """
 
 from __future__ import annotations
