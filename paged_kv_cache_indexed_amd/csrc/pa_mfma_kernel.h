@@ -277,8 +277,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // region. The operand-layout loads give the L1 one access per lane; restaging measured
     // 23% faster with 4 queries per sequence (config 4) and 2% with beam groups (config 5),
     // but 3-4% slower for the one-query decode, which keeps the direct loads.
-    constexpr bool kStage = !kFp8 && D == 128 && (kMulti || kBeams);
-    constexpr int kCpr = D * 2 / 16;  // 16-byte chunks per row
+    constexpr bool kStage = D == 128 && (kMulti || kBeams);
+    constexpr int kCpr = D * KV::kBytes / 16;  // 16-byte chunks per row (16 or 8)
+    constexpr int kRpl = 64 / kCpr;            // rows per staged load instruction (4 or 8)
     __shared__ u32x4 s_stage[kStage ? NW : 1][kStage ? 2 * 16 * kCpr : 1];
     // the new token's K and V rows as read, and for an 8-bit pool each wave's record of them
     // (fused append of the decode)
@@ -422,11 +423,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + slab, slab_bytes);
 #pragma unroll
             for (int c = 0; c < NL; ++c) {
-                // staged: load c covers rows 4c .. 4c + 3 whole (lane: row 4c + lane / 16,
-                // chunk lane % 16); else 64 bytes of each of the 16 rows (the operand layout)
-                const int srow = 4 * c + (lane >> 4);
+                // staged: load c covers kRpl whole rows (lane: row kRpl c + lane / kCpr, chunk
+                // lane % kCpr); else 64 bytes of each of the 16 rows (the operand layout)
+                const int srow = kRpl * c + lane / kCpr;
                 const uint32_t so = (rel + srow < ntok && rel + srow >= rel_lo)
-                                        ? (uint32_t)(((rel & (bs - 1)) + srow) * D * 2 + 16 * (lane & 15))
+                                        ? (uint32_t)(((rel & (bs - 1)) + srow) * D * KV::kBytes + 16 * (lane % kCpr))
                                         : kOutOfRange;
                 const uint32_t o = kStage ? so : (off == kOutOfRange ? kOutOfRange : off + 64 * c);
                 kk[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rk, o);
@@ -450,10 +451,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int npos = part.npos;
     // this wave's record of the new rows in the pool's storage (8-bit: quantised below)
     char* s_rec = s_new + (kFp8 ? kRaw + wave * R::kBytes : 0);
-    // Staged tiles to the operand layout, in place: lane (n, g) gets row n, chunk 4c + g for
-    // k-block c. Chunk j of row r sits at j ^ r in LDS, so the writes (whole rows) and the
-    // reads (one chunk of 16 rows) both spread over all banks. The region is the wave's own
-    // and LDS operations of a wave complete in order: no barrier.
+    // Staged tiles to the operand layout, in place: lane (n, g) gets row n, chunk 4c + g of
+    // load c. Chunk j of row r sits at j ^ (r mod kCpr) in LDS, so the writes (whole rows) and
+    // the reads (one chunk of 16 rows) spread over the banks. The region is the wave's own and
+    // LDS operations of a wave complete in order: no barrier.
     auto restage = [&](u32x4 (*x)[NL]) {
         if constexpr (kStage) {
             u32x4* w = s_stage[wave];
@@ -461,13 +462,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int c = 0; c < NL; ++c) {
-                    const int r = 4 * c + (lane >> 4);
-                    w[(16 * t + r) * kCpr + ((lane & 15) ^ r)] = x[t][c];
+                    const int r = kRpl * c + lane / kCpr;
+                    w[(16 * t + r) * kCpr + ((lane % kCpr) ^ (r % kCpr))] = x[t][c];
                 }
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int c = 0; c < NL; ++c) x[t][c] = w[(16 * t + n) * kCpr + ((4 * c + g) ^ n)];
+                for (int c = 0; c < NL; ++c) x[t][c] = w[(16 * t + n) * kCpr + ((4 * c + g) ^ (n % kCpr))];
         }
     };
     auto compute = [&](int it, u32x4 (*kk)[NL], u32x4 (*vv)[NL], u32x4* ks, u32x4* vs) {
