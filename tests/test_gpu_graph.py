@@ -87,3 +87,41 @@ def test_fp8_step_graph_replays():
         torch.cuda.synchronize()
         for got, ref in zip((out, k8, ks), want):
             assert torch.equal(_bits(got), _bits(ref)), f"fp8 replay {k} differs from the eager step"
+
+
+def test_beam_step_graph_replays():
+    """Copy-on-write, append and the beam-group decode of a small beam workload (2 groups of 4
+    beams sharing a 2048-token prefix) captured and replayed."""
+    from workloads.longctx import beam_workload
+
+    dev = require_gpu()
+    w = beam_workload(dev, seed=3, groups=2, beams=4, heads=4, prefix=2048, context=2304)
+    t = w.tensors
+    L = w.context + 1
+    out = torch.empty_like(t["q"])
+    n = ops.pa_decode_beams_workspace_bytes(ops.CacheDesc.of(t["k_pool"]), w.batch, w.beams, w.num_q_heads, L, 512)
+    ws = torch.empty((n + 3) // 4, dtype=torch.float32, device=dev) if n else None
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+
+    def step():
+        ops.copy_blocks(t["k_pool"], t["v_pool"], t["copy_pairs"])
+        ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_pool"], t["v_pool"], t["slot_mapping"])
+        ops.decode_beams(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["lens_after"], L, w.scale, w.beams,
+                         partition_size=512, out=out, workspace=ws)
+
+    note("graph replay beam step")
+    step()
+    torch.cuda.synchronize()
+    want = [out.clone(), t["k_pool"].clone(), t["v_pool"].clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for k in range(3):
+        out.fill_(float("nan"))
+        t["k_pool"].copy_(k0)
+        t["v_pool"].copy_(v0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip((out, t["k_pool"], t["v_pool"]), want):
+            assert torch.equal(_bits(got), _bits(ref)), f"beam replay {k} differs from the eager step"
