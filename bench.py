@@ -53,7 +53,7 @@ MFMA_FILE = os.path.join(ROOT, "profiles", "gqa_mfma_busy.txt")
 # sources of the kernel that produced it are unchanged.
 _COMMON_SOURCES = ("pa_device.h", "pa_kernels.h", "pa_decode_common.h", "pa_api.hip")
 _PATH_SOURCES = {"valu": ("pa_decode_valu.h", "pa_decode.hip", "pa_decode_fp8.hip"),
-                 "mfma": ("pa_mfma_kernel.h", "pa_decode_mfma.hip"),
+                 "mfma": ("pa_mfma_kernel.h", "pa_decode_mfma.hip", "pa_decode_mfma_b8.hip"),
                  "multi": ("pa_mfma_kernel.h", "pa_multi_token.hip"),
                  "beams": ("pa_mfma_kernel.h", "pa_decode_beams.hip")}
 
@@ -61,8 +61,10 @@ _PATH_SOURCES = {"valu": ("pa_decode_valu.h", "pa_decode.hip", "pa_decode_fp8.hi
 def decode_path(dtype: str, head_dim: int, group: int, block_size: int) -> str:
     """Which decode kernel the library launches (its dispatch rule, restated for the record):
     the matrix cores for 4, 8 or 16 query heads per kv head over fp16/bf16/8-bit pools with
-    blocks of 16+ tokens (16 heads only up to head_dim 128), else the VALU kernel."""
-    ok = dtype in ("f16", "bf16", "fp8") and group in (4, 8, 16) and block_size >= 16
+    blocks of 16+ tokens, or of 8 tokens up to head_dim 128 (16 heads only up to head_dim
+    128), else the VALU kernel."""
+    ok = dtype in ("f16", "bf16", "fp8") and group in (4, 8, 16) and (
+        block_size >= 16 or (block_size == 8 and head_dim <= 128))
     return "mfma" if ok and not (group == 16 and head_dim > 128) else "valu"
 
 

@@ -46,12 +46,14 @@ hipError_t launch_t(const DecodeArgs& a, int head_dim, int group, int batch, int
 
 bool decode_mfma_supported(int kv_dtype, int head_dim, int group, int block_size) {
     return (kv_dtype == PA_F16 || kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) &&
-           (group == 4 || group == 8 || group == 16) && block_size >= 16 &&
+           (group == 4 || group == 8 || group == 16) && (block_size >= 16 || (block_size == 8 && head_dim <= 128)) &&
            (head_dim == 64 || head_dim == 128 || head_dim == 256) && !(group == 16 && head_dim == 256);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream) {
+    if (a.log2_block_size < 4)
+        return launch_decode_mfma_small_blocks(a, kv_dtype, dtype, head_dim, group, batch, num_kv_heads, stream);
     if (kv_dtype == PA_FP8_E4M3) {
         switch (dtype) {
             case PA_F16: return launch_t<F16, FP8>(a, head_dim, group, batch, num_kv_heads, stream);

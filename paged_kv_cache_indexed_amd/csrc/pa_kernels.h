@@ -78,10 +78,13 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int dtype, int 
 hipError_t launch_decode_valu_fp8(const DecodeArgs& a, int dtype, int head_dim, int group, int batch,
                                   int num_kv_heads, hipStream_t stream);
 // Matrix-core decode for grouped-query heads (fp16/bf16 or 8-bit pools, group 4/8/16,
-// block_size >= 16); dtype is the type of q and out.
+// block_size >= 16, or 8 with head_dim <= 128); dtype is the type of q and out.
 bool decode_mfma_supported(int kv_dtype, int head_dim, int group, int block_size);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream);
+// 8-token blocks (head_dim 64 or 128): the same kernel with a block lookup per row.
+hipError_t launch_decode_mfma_small_blocks(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group,
+                                           int batch, int num_kv_heads, hipStream_t stream);
 // Beam-group decode on the matrix cores (16-bit or 8-bit pools, head_dim 64/128, group 1-8,
 // block_size >= 16, beam_width * group <= 16); `groups` = ceil(batch / beam_width).
 bool decode_beams_supported(int kv_dtype, int head_dim, int group, int block_size, int beam_width);

@@ -253,11 +253,12 @@ __device__ bool beam_prologue(const DecodeArgs& a, int p, int kvh, int b0, int n
 // share is streamed once for all of them, else once per beam with the other beams' columns
 // masked.
 template <typename T, typename KV, int D, int G, int NW, bool kDoubleBuffer, bool kMulti = false,
-          bool kBeams = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
+          bool kBeams = false, bool kSmallBlocks = false>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallBlocks && D == 128 && KV::kBytes == 2 ? 1 : 2))) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(T::kBytes == 2, "matrix-core operands are 16-bit");
     static_assert(G >= 1 && G <= 16, "at most 16 query heads per kv head");
     static_assert(!(kMulti && kBeams), "one column mapping");
+    static_assert(!kSmallBlocks || (!kMulti && !kBeams && D <= 128), "8-token blocks: one-query decode");
     constexpr int NCOL = (kMulti || kBeams) ? 16 : G;  // columns whose results this workgroup keeps
     constexpr bool kFp8 = std::is_same_v<KV, FP8>;
     constexpr int NC = D / 32;             // 32-dim k-blocks of the score contraction
@@ -414,6 +415,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int rel = (c0 + it * NW + wave) * kChunk + 16 * t;  // wave-uniform
+            if constexpr (kSmallBlocks) {
+                // 8-token blocks: rows 0-7 and 8-15 of a tile lie in two blocks, so each lane
+                // looks up the block of its own row. A row past the partition reads the same
+                // offset in its first block (allocated memory; its V row is cleared and its
+                // score masked before use), so the loads need no lane masks.
+                const int tok = rel + n;
+                const int lid = ids[(tok < ntok ? tok : 0) >> lbs];
+                const size_t row = (size_t)lid * block_bytes + (size_t)kvh * head_bytes +
+                                   (size_t)((tok & (bs - 1)) * D * KV::kBytes) + seg;
+#pragma unroll
+                for (int c = 0; c < NL; ++c) {
+                    kk[t][c] = load16(kpool + row + 64 * c);
+                    vv[t][c] = load16(vpool + row + 64 * c);
+                }
+                if constexpr (kFp8) {  // scales of tokens rel + 4g .. +3, one block
+                    const int tok4 = rel + 4 * g;
+                    const int sid = ids[(tok4 < ntok ? tok4 : 0) >> lbs];
+                    const size_t srow = (((size_t)sid * a.num_kv_heads + kvh) << lbs) + (tok4 & (bs - 1));
+                    ks[t] = load16(a.k_scale + srow);
+                    vs[t] = load16(a.v_scale + srow);
+                }
+                continue;
+            }
             const int id = __builtin_amdgcn_readfirstlane(ids[(rel < ntok ? rel : 0) >> lbs]);  // partitions start on a block
             const size_t slab = (size_t)id * block_bytes + (size_t)kvh * head_bytes;
             const uint32_t off = (rel + n < ntok && rel + n >= rel_lo)
@@ -475,6 +499,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int rel0 = (c0 + it * NW + wave) * kChunk;
         restage(kk);
         restage(vv);
+        if constexpr (kSmallBlocks) {
+            // rows outside [rel_lo, ntok) were read from other slots: clear their V rows (their
+            // weights are 0, and 0 times a non-finite value is not)
+            if (!(rel0 >= rel_lo && rel0 + kChunk <= ntok)) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int tok = rel0 + 16 * t + n;
+                    if (tok >= ntok || tok < rel_lo) {
+#pragma unroll
+                        for (int c = 0; c < NL; ++c) vv[t][c] = u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+            }
+        }
         if constexpr (kAppendable) {
             if (npos >= 0) {  // fused append: the new token's rows come from s_new (wave-uniform test)
 #pragma unroll

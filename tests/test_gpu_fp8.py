@@ -244,9 +244,10 @@ def test_fp8_rejects_mismatched_calls():
     k8, v8, ks8, vs8 = ops.empty_fp8_cache(4, 2, 8, 64, dev)
     with pytest.raises(Exception):  # 8-token blocks of 64-byte rows: a wave load spans 2 blocks
         ops.decode_fp8(torch.zeros(1, 2, 64, dtype=torch.float16, device=dev), k8, v8, ks8, vs8, table, lens, 1, 1.0)
-    k9, v9, ks9, vs9 = ops.empty_fp8_cache(4, 2, 8, 128, dev)
-    q16 = torch.zeros(1, 32, 128, dtype=torch.float16, device=dev)
-    with pytest.raises(Exception):  # 16 query heads per kv head need the matrix cores: blocks >= 16
+    k9, v9, ks9, vs9 = ops.empty_fp8_cache(4, 2, 8, 256, dev)
+    q16 = torch.zeros(1, 32, 256, dtype=torch.float16, device=dev)
+    with pytest.raises(Exception):  # 16 query heads per kv head need the matrix cores, which take
+        # 8-token blocks up to head_dim 128 only
         ops.decode_fp8(q16, k9, v9, ks9, vs9, table, lens, 1, 1.0)
 
 

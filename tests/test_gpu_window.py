@@ -43,7 +43,7 @@ def _run(w, dev, window, P=0, lens=None):
 
 
 @pytest.mark.parametrize("dtype,group,bs", [("f16", 1, 16), ("bf16", 1, 8), ("f32", 2, 16),
-                                            ("bf16", 8, 16), ("f16", 4, 32)])
+                                            ("bf16", 8, 16), ("f16", 4, 32), ("bf16", 8, 8), ("f16", 16, 8)])
 def test_window_matches_oracle(dtype, group, bs):
     dev = require_gpu()
     lens = np.array([1, 9, 33, 64, 150, 400], np.int32)
