@@ -253,12 +253,17 @@ __device__ bool beam_prologue(const DecodeArgs& a, int p, int kvh, int b0, int n
 // share is streamed once for all of them, else once per beam with the other beams' columns
 // masked.
 template <typename T, typename KV, int D, int G, int NW, bool kDoubleBuffer, bool kMulti = false,
-          bool kBeams = false, bool kSmallBlocks = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallBlocks && D == 128 && KV::kBytes == 2 ? 1 : 2))) void decode_mfma_kernel(DecodeArgs a) {
+          bool kBeams = false, int kSmallBlocks = 0>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallBlocks == 1 && D == 128 && KV::kBytes == 2 ? 1 : 2))) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(T::kBytes == 2, "matrix-core operands are 16-bit");
     static_assert(G >= 1 && G <= 16, "at most 16 query heads per kv head");
     static_assert(!(kMulti && kBeams), "one column mapping");
-    static_assert(!kSmallBlocks || (!kMulti && !kBeams && D <= 128), "8-token blocks: one-query decode");
+    // 8-token blocks (kSmallBlocks != 0): a 16-row tile spans two blocks. Mode 1 addresses each
+    // row from its lane (a 64-bit address per lane: one wave per SIMD with 16-bit rows of 128
+    // dims); mode 2 loads the two 8-row halves from their blocks under lane masks (twice the
+    // load instructions, two waves per SIMD), the better choice for short partitions.
+    static_assert(kSmallBlocks == 0 || (!kMulti && !kBeams && D <= 128), "8-token blocks: one-query decode");
+    static_assert(kSmallBlocks != 2 || KV::kBytes == 2, "mode 2: 16-bit pools");
     constexpr int NCOL = (kMulti || kBeams) ? 16 : G;  // columns whose results this workgroup keeps
     constexpr bool kFp8 = std::is_same_v<KV, FP8>;
     constexpr int NC = D / 32;             // 32-dim k-blocks of the score contraction
@@ -415,11 +420,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int rel = (c0 + it * NW + wave) * kChunk + 16 * t;  // wave-uniform
-            if constexpr (kSmallBlocks) {
-                // 8-token blocks: rows 0-7 and 8-15 of a tile lie in two blocks, so each lane
-                // looks up the block of its own row. A row past the partition reads the same
-                // offset in its first block (allocated memory; its V row is cleared and its
-                // score masked before use), so the loads need no lane masks.
+            if constexpr (kSmallBlocks == 1) {
+                // rows 0-7 and 8-15 of a tile lie in two blocks: each lane looks up the block
+                // of its own row. A row past the partition reads the same offset in its first
+                // block (allocated memory; its V row is cleared and its score masked before
+                // use), so the loads need no lane masks.
                 const int tok = rel + n;
                 const int lid = ids[(tok < ntok ? tok : 0) >> lbs];
                 const size_t row = (size_t)lid * block_bytes + (size_t)kvh * head_bytes +
@@ -429,6 +434,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
                     kk[t][c] = load16(kpool + row + 64 * c);
                     vv[t][c] = load16(vpool + row + 64 * c);
                 }
+            } else if constexpr (kSmallBlocks == 2) {
+                // the tile's two blocks (wave-uniform); a half past the partition reads the
+                // first block again, cleared or masked before use as in mode 1
+                const int j0 = rel < ntok ? rel >> lbs : 0;
+                const int j1 = rel + 8 < ntok ? (rel >> lbs) + 1 : j0;
+                const int id0 = __builtin_amdgcn_readfirstlane(ids[j0]);
+                const int id1 = __builtin_amdgcn_readfirstlane(ids[j1]);
+                const uint32_t o8 = (uint32_t)((n & 7) * D * KV::kBytes) + seg;
+                if (n < 8) {
+                    const size_t s0 = (size_t)id0 * block_bytes + (size_t)kvh * head_bytes;
+                    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + s0, slab_bytes);
+                    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + s0, slab_bytes);
+#pragma unroll
+                    for (int c = 0; c < NL; ++c) {
+                        kk[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rk, o8 + 64 * c);
+                        vv[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rv, o8 + 64 * c);
+                    }
+                } else {
+                    const size_t s1 = (size_t)id1 * block_bytes + (size_t)kvh * head_bytes;
+                    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + s1, slab_bytes);
+                    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + s1, slab_bytes);
+#pragma unroll
+                    for (int c = 0; c < NL; ++c) {
+                        kk[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rk, o8 + 64 * c);
+                        vv[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rv, o8 + 64 * c);
+                    }
+                }
+            }
+            if constexpr (kSmallBlocks != 0) {
                 if constexpr (kFp8) {  // scales of tokens rel + 4g .. +3, one block
                     const int tok4 = rel + 4 * g;
                     const int sid = ids[(tok4 < ntok ? tok4 : 0) >> lbs];
@@ -499,7 +533,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
         const int rel0 = (c0 + it * NW + wave) * kChunk;
         restage(kk);
         restage(vv);
-        if constexpr (kSmallBlocks) {
+        if constexpr (kSmallBlocks != 0) {
             // rows outside [rel_lo, ntok) were read from other slots: clear their V rows (their
             // weights are 0, and 0 times a non-finite value is not)
             if (!(rel0 >= rel_lo && rel0 + kChunk <= ntok)) {

@@ -32,8 +32,8 @@ def test_no_kernel_spills():
 def test_decode_occupancy():
     for r in _rows():
         occ = int(r["occupancy_waves_per_simd"])
-        # the 8-token-block decode with 16-bit rows of 256 bytes holds a 64-bit address per
-        # lane and row; it asks for one wave per SIMD rather than spill
-        small16 = "Li128E" in r["kernel"] and "ELb0ELb0ELb1EE" in r["kernel"] and "FP8" not in r["kernel"]
+        # the 8-token-block decode with per-lane addresses over 16-bit rows of 128 dims holds a
+        # 64-bit address per lane and row; it asks for one wave per SIMD rather than spill
+        small16 = "Li128E" in r["kernel"] and "ELb0ELb0ELi1EE" in r["kernel"] and "FP8" not in r["kernel"]
         if "decode_mfma_kernel" in r["kernel"] or "prefill_kernel" in r["kernel"]:
             assert occ >= (1 if small16 else 2), (r["kernel"], occ)

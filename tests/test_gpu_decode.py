@@ -58,16 +58,17 @@ _GQA8 = [(dt, d, g) for dt in ("f16", "bf16") for d in (64, 128) for g in (4, 8,
 
 @pytest.mark.parametrize("dtype,head_dim,group", _GQA8, ids=lambda x: str(x))
 def test_grouped_heads_8_token_blocks(dtype, head_dim, group):
-    """Grouped heads over 8-token blocks run on the matrix cores with a block lookup per row
-    (a 16-row tile spans two blocks). Unused slots hold NaN; partitions of 8 and 24 tokens
-    start in the middle of a tile."""
+    """Grouped heads over 8-token blocks run on the matrix cores, a 16-row tile spanning two
+    blocks: per-lane row addresses for partitions over 1024 tokens, the tile's two block
+    halves under lane masks for shorter ones. Unused slots hold NaN; partitions of 8 and 24
+    tokens start in the middle of a tile."""
     dev = require_gpu()
     lens = np.array([1, 7, 8, 9, 15, 16, 17, 100, 250, 600], np.int32)
     w = build_paged(f"gqa-bs8-{dtype}-{head_dim}-{group}", 300 + group, head_dim, lens, 8, 2, 2 * group,
                     head_dim, dtype)
     ref = oracle_decode(w)
     t = w.to_device(dev)
-    for P in (0, 8, 24, 64, 512):
+    for P in (0, 8, 24, 64, 512, 2048):
         note(f"grouped heads bs=8 dtype={dtype} d={head_dim} G={group} P={P}")
         got, _ = gpu_decode(w, dev, partition_size=P, tensors=t)
         assert_close(got, ref, dtype, f"bs=8 {dtype} d={head_dim} G={group} P={P}")
