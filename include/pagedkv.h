@@ -380,7 +380,8 @@ pa_status_t pa_reblock(const pa_cache_desc_t* src, const void* src_k, const void
  * query_start[batch] <= num_q_tokens; rows outside every sequence are not written.
  *
  * Runs on the matrix cores: dtype f16/bf16 (q_dtype equal to it) or PA_FP8_E4M3 (q f16/bf16,
- * k_scale/v_scale as in pa_decode_fp8); block_size >= 16; num_q_heads / num_kv_heads in
+ * k_scale/v_scale as in pa_decode_fp8); block_size >= 16, or 8 with head_dim 64 or 128 (a
+ * 16-row tile then spans two blocks and each row looks up its own); num_q_heads / num_kv_heads in
  * {1, 2, 4, 8, 16} (16 only with head_dim <= 128); else PA_ERR_UNSUPPORTED. max_query_len
  * bounds every n_b and sizes the launch (batch * ceil(max_query_len * group / 16) <= 65535).
  * A sequence with n_b > context_len, a bad length or n_b > max_query_len sets

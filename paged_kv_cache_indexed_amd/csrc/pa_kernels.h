@@ -91,10 +91,13 @@ bool decode_beams_supported(int kv_dtype, int head_dim, int group, int block_siz
 hipError_t launch_decode_beams(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int groups,
                                int num_kv_heads, hipStream_t stream);
 // Multi-token attention on the matrix cores (16-bit or 8-bit pools, any group, block_size
-// >= 16) and its log-sum-exp combine per query row.
+// >= 16, or 8 up to head_dim 128) and its log-sum-exp combine per query row.
 bool multi_token_supported(int kv_dtype, int head_dim, int group, int block_size);
 hipError_t launch_multi_token(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream);
+// 8-token blocks (head_dim 64 or 128): the 16-column kernel with a block lookup per row.
+hipError_t launch_multi_token_small_blocks(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group,
+                                           int batch, int num_kv_heads, hipStream_t stream);
 hipError_t launch_reduce_multi(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 // Log-sum-exp combine of partition records (only when some sequence has > 1 partition).
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, int batch, hipStream_t stream);

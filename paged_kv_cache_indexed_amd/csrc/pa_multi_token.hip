@@ -478,12 +478,16 @@ hipError_t launch_reduce_t(const DecodeArgs& a, int head_dim, hipStream_t s) {
 
 bool multi_token_supported(int kv_dtype, int head_dim, int group, int block_size) {
     return (kv_dtype == PA_F16 || kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) &&
-           (group == 1 || group == 2 || group == 4 || group == 8 || group == 16) && block_size >= 16 &&
+           (group == 1 || group == 2 || group == 4 || group == 8 || group == 16) &&
+           (block_size >= 16 || (block_size == 8 && head_dim <= 128)) &&
            (head_dim == 64 || head_dim == 128 || head_dim == 256) && !(group == 16 && head_dim == 256);
 }
 
 hipError_t launch_multi_token(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream) {
+    // 8-token blocks: the 16-column kernel with a block lookup per row, for any number of rows
+    if (a.log2_block_size < 4)
+        return launch_multi_token_small_blocks(a, kv_dtype, dtype, head_dim, group, batch, num_kv_heads, stream);
     // 64 or more (query, head) rows per kv head: the 64-row kernel (with fewer rows its tiles
     // run mostly empty: 2 column tiles measured 30% slower there)
     if (a.col_tiles >= 4 && (head_dim == 64 || head_dim == 128) && (kv_dtype == dtype || kv_dtype == PA_FP8_E4M3)) {

@@ -1,0 +1,63 @@
+// Multi-token paged attention over 8-token blocks: the 16-column matrix-core kernel of
+// pa_mfma_kernel.h with a block lookup per tile row (a 16-row tile spans two blocks), for
+// every number of queries per sequence. The block size trade-off is [BlockManager essay] §3;
+// the causal mask of several new tokens is [Valid-length essay] §4.2.
+#include "pa_mfma_kernel.h"
+
+namespace pagedkv {
+
+namespace {
+
+constexpr int kSmallWaves = 4;
+
+template <typename T, typename KV, int D, int G>
+hipError_t launch_tdg(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
+    constexpr int NW = kSmallWaves;
+    dim3 grid(num_kv_heads, batch * a.col_tiles, a.max_partitions);
+    hipLaunchKernelGGL((mfma::decode_mfma_kernel<T, KV, D, G, NW, true, true, false, 1>), grid, dim3(NW * 64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, typename KV, int D>
+hipError_t launch_td(const DecodeArgs& a, int group, int batch, int num_kv_heads, hipStream_t s) {
+    switch (group) {
+        case 1: return launch_tdg<T, KV, D, 1>(a, batch, num_kv_heads, s);
+        case 2: return launch_tdg<T, KV, D, 2>(a, batch, num_kv_heads, s);
+        case 4: return launch_tdg<T, KV, D, 4>(a, batch, num_kv_heads, s);
+        case 8: return launch_tdg<T, KV, D, 8>(a, batch, num_kv_heads, s);
+        case 16: return launch_tdg<T, KV, D, 16>(a, batch, num_kv_heads, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, typename KV>
+hipError_t launch_t(const DecodeArgs& a, int head_dim, int group, int batch, int num_kv_heads, hipStream_t s) {
+    switch (head_dim) {
+        case 64: return launch_td<T, KV, 64>(a, group, batch, num_kv_heads, s);
+        case 128: return launch_td<T, KV, 128>(a, group, batch, num_kv_heads, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_multi_token_small_blocks(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group,
+                                           int batch, int num_kv_heads, hipStream_t stream) {
+    if (a.log2_block_size != 3) return hipErrorInvalidValue;
+    if (kv_dtype == PA_FP8_E4M3) {
+        switch (dtype) {
+            case PA_F16: return launch_t<F16, FP8>(a, head_dim, group, batch, num_kv_heads, stream);
+            case PA_BF16: return launch_t<BF16, FP8>(a, head_dim, group, batch, num_kv_heads, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (kv_dtype != dtype) return hipErrorInvalidValue;
+    switch (dtype) {
+        case PA_F16: return launch_t<F16, F16>(a, head_dim, group, batch, num_kv_heads, stream);
+        case PA_BF16: return launch_t<BF16, BF16>(a, head_dim, group, batch, num_kv_heads, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pagedkv

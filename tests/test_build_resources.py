@@ -32,8 +32,11 @@ def test_no_kernel_spills():
 def test_decode_occupancy():
     for r in _rows():
         occ = int(r["occupancy_waves_per_simd"])
-        # the 8-token-block decode with per-lane addresses over 16-bit rows of 128 dims holds a
-        # 64-bit address per lane and row; it asks for one wave per SIMD rather than spill
-        small16 = "Li128E" in r["kernel"] and "ELb0ELb0ELi1EE" in r["kernel"] and "FP8" not in r["kernel"]
-        if "decode_mfma_kernel" in r["kernel"] or "prefill_kernel" in r["kernel"]:
-            assert occ >= (1 if small16 else 2), (r["kernel"], occ)
+        # the 8-token-block kernels with per-lane addresses (last template argument 1) over
+        # rows of 128 dims hold a 64-bit address per lane and row; with 16-bit rows, or in the
+        # multi-token mode, they ask for one wave per SIMD rather than spill
+        k = r["kernel"]
+        per_lane = "Li128E" in k and k.endswith("ELi1EEEvNS_10DecodeArgsE")
+        small = per_lane and ("FP8" not in k or "ELb1ELb1ELb0ELi1EE" in k)
+        if "decode_mfma_kernel" in k or "prefill_kernel" in k:
+            assert occ >= (1 if small else 2), (k, occ)

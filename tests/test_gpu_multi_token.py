@@ -43,7 +43,8 @@ def _run(w, qs, q, dev, max_q, P=0, fp8=None, table=None):
 
 @pytest.mark.parametrize("dtype,group,bs,d", [("f16", 1, 16, 128), ("bf16", 2, 32, 128), ("f16", 4, 16, 64),
                                               ("bf16", 8, 16, 128), ("f16", 16, 16, 128), ("bf16", 1, 256, 256),
-                                              ("f16", 8, 64, 256)])
+                                              ("f16", 8, 64, 256), ("bf16", 8, 8, 128), ("f16", 1, 8, 64),
+                                              ("f16", 16, 8, 128)])
 def test_multi_token_matches_oracle(dtype, group, bs, d):
     dev = require_gpu()
     lens = [1, 16, 40, 17, 100, 300, 57]
@@ -75,7 +76,8 @@ def test_multi_token_one_query_is_the_decode_bitwise():
 # group 1 takes the 16-column kernel; groups 4 and 8 bring 64 or more rows per kv head to
 # the 64-row kernel (head_dim 64 and 128, one or two units of 8 codes per thread)
 @pytest.mark.parametrize("q_dtype,group,d,bs", [("bf16", 1, 128, 16), ("f16", 8, 128, 16), ("bf16", 4, 64, 16),
-                                                ("bf16", 8, 128, 32), ("f16", 4, 64, 64)])
+                                                ("bf16", 8, 128, 32), ("f16", 4, 64, 64), ("bf16", 8, 128, 8),
+                                                ("f16", 2, 64, 8)])
 def test_multi_token_fp8_cache(q_dtype, group, d, bs):
     dev = require_gpu()
     lens = [20, 129, 64, 300]
@@ -158,8 +160,8 @@ def test_multi_token_errors_poison_only_their_sequence():
 
 def test_multi_token_rejects_unsupported_shapes():
     dev = require_gpu()
-    k = torch.zeros(4, 2, 8, 128, dtype=torch.float16, device=dev)  # 8-token blocks
-    q = torch.zeros(3, 2, 128, dtype=torch.float16, device=dev)
+    k = torch.zeros(4, 2, 8, 256, dtype=torch.float16, device=dev)  # 8-token blocks of 256 dims
+    q = torch.zeros(3, 2, 256, dtype=torch.float16, device=dev)
     table = torch.zeros(1, 4, dtype=torch.int32, device=dev)
     lens = torch.tensor([3], dtype=torch.int32, device=dev)
     qs = torch.tensor([0, 3], dtype=torch.int32, device=dev)
@@ -167,4 +169,5 @@ def test_multi_token_rejects_unsupported_shapes():
         ops.multi_token_attention(q, k, k.clone(), table, lens, qs, 3, 3, 1.0)
     k32 = torch.zeros(4, 2, 16, 128, dtype=torch.float32, device=dev)
     with pytest.raises(Exception):
-        ops.multi_token_attention(q.float(), k32, k32.clone(), table, lens, qs, 3, 3, 1.0)
+        ops.multi_token_attention(torch.zeros(3, 2, 128, dtype=torch.float32, device=dev), k32, k32.clone(), table,
+                                  lens, qs, 3, 3, 1.0)
