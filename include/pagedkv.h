@@ -319,7 +319,7 @@ pa_status_t pa_decode_append_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, 
  * Arguments as pa_decode_fp8 (q_dtype; k_scale/v_scale for PA_FP8_E4M3 pools, ignored for
  * 16-bit ones, whose q_dtype must equal the pool's dtype), without a window, plus beam_width
  * >= 1. Runs on the matrix cores: head_dim 64 or 128, num_q_heads / num_kv_heads in {1, 2, 4,
- * 8} with beam_width * that group <= 16, block_size >= 16, else PA_ERR_UNSUPPORTED. Errors
+ * 8} with beam_width * that group <= 16, block_size >= 16 or 8, else PA_ERR_UNSUPPORTED. Errors
  * (status codes, err_flag bits, NaN rows of the affected sequence only) are those of
  * pa_decode. The partition length is pa_decode_beams_partition_size(...) and the workspace
  * must hold pa_decode_beams_workspace_bytes(...) (NULL when that is 0).

@@ -47,11 +47,13 @@ hipError_t launch_t(const DecodeArgs& a, int head_dim, int group, int groups, in
 bool decode_beams_supported(int kv_dtype, int head_dim, int group, int block_size, int beam_width) {
     return (kv_dtype == PA_F16 || kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3) &&
            (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8) &&
-           block_size >= 16 && beam_width >= 1 && beam_width * group <= 16;
+           (block_size >= 16 || (block_size == 8 && head_dim <= 128)) && beam_width >= 1 && beam_width * group <= 16;
 }
 
 hipError_t launch_decode_beams(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int groups,
                                int num_kv_heads, hipStream_t stream) {
+    if (a.log2_block_size < 4)  // 8-token blocks: a block lookup per tile row
+        return launch_decode_beams_small_blocks(a, kv_dtype, dtype, head_dim, group, groups, num_kv_heads, stream);
     if (kv_dtype == PA_FP8_E4M3) {
         switch (dtype) {
             case PA_F16: return launch_t<F16, FP8>(a, head_dim, group, groups, num_kv_heads, stream);

@@ -86,10 +86,13 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_dtype, int dtype, int 
 hipError_t launch_decode_mfma_small_blocks(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group,
                                            int batch, int num_kv_heads, hipStream_t stream);
 // Beam-group decode on the matrix cores (16-bit or 8-bit pools, head_dim 64/128, group 1-8,
-// block_size >= 16, beam_width * group <= 16); `groups` = ceil(batch / beam_width).
+// block_size >= 16 or 8, beam_width * group <= 16); `groups` = ceil(batch / beam_width).
 bool decode_beams_supported(int kv_dtype, int head_dim, int group, int block_size, int beam_width);
 hipError_t launch_decode_beams(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int groups,
                                int num_kv_heads, hipStream_t stream);
+// 8-token blocks: the beam-group kernel with a block lookup per row.
+hipError_t launch_decode_beams_small_blocks(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group,
+                                            int groups, int num_kv_heads, hipStream_t stream);
 // Multi-token attention on the matrix cores (16-bit or 8-bit pools, any group, block_size
 // >= 16, or 8 up to head_dim 128) and its log-sum-exp combine per query row.
 bool multi_token_supported(int kv_dtype, int head_dim, int group, int block_size);

@@ -254,15 +254,15 @@ __device__ bool beam_prologue(const DecodeArgs& a, int p, int kvh, int b0, int n
 // masked.
 template <typename T, typename KV, int D, int G, int NW, bool kDoubleBuffer, bool kMulti = false,
           bool kBeams = false, int kSmallBlocks = 0>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallBlocks == 1 && D == 128 && (KV::kBytes == 2 || kMulti) ? 1 : 2))) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallBlocks == 1 && D == 128 && (KV::kBytes == 2 || kMulti || kBeams) ? 1 : 2))) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(T::kBytes == 2, "matrix-core operands are 16-bit");
     static_assert(G >= 1 && G <= 16, "at most 16 query heads per kv head");
     static_assert(!(kMulti && kBeams), "one column mapping");
     // 8-token blocks (kSmallBlocks != 0): a 16-row tile spans two blocks. Mode 1 addresses each
     // row from its lane (a 64-bit address per lane: one wave per SIMD with 16-bit rows of 128
-    // dims, and with 128 dims in the multi-token mode); mode 2 loads the two 8-row halves from their blocks under lane masks (twice the
+    // dims, and with 128 dims in the multi-token and beam-group modes); mode 2 loads the two 8-row halves from their blocks under lane masks (twice the
     // load instructions, two waves per SIMD), the better choice for short partitions.
-    static_assert(kSmallBlocks == 0 || (!kBeams && D <= 128), "8-token blocks: decode and multi-token modes");
+    static_assert(kSmallBlocks == 0 || D <= 128, "8-token blocks: head_dim up to 128");
     static_assert(kSmallBlocks != 2 || KV::kBytes == 2, "mode 2: 16-bit pools");
     constexpr int NCOL = (kMulti || kBeams) ? 16 : G;  // columns whose results this workgroup keeps
     constexpr bool kFp8 = std::is_same_v<KV, FP8>;

@@ -34,9 +34,9 @@ def test_decode_occupancy():
         occ = int(r["occupancy_waves_per_simd"])
         # the 8-token-block kernels with per-lane addresses (last template argument 1) over
         # rows of 128 dims hold a 64-bit address per lane and row; with 16-bit rows, or in the
-        # multi-token mode, they ask for one wave per SIMD rather than spill
+        # multi-token and beam-group modes, they ask for one wave per SIMD rather than spill
         k = r["kernel"]
         per_lane = "Li128E" in k and k.endswith("ELi1EEEvNS_10DecodeArgsE")
-        small = per_lane and ("FP8" not in k or "ELb1ELb1ELb0ELi1EE" in k)
+        small = per_lane and ("FP8" not in k or "ELb1ELb1ELb0ELi1EE" in k or "ELb1ELb0ELb1ELi1EE" in k)
         if "decode_mfma_kernel" in k or "prefill_kernel" in k:
             assert occ >= (1 if small else 2), (k, occ)

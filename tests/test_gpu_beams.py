@@ -69,7 +69,8 @@ _LENS = [300, 290, 331, 257, 100, 200, 256, 270, 45, 333]
 
 @pytest.mark.parametrize("dtype,group,beams,d,bs", [("bf16", 1, 4, 128, 32), ("f16", 2, 4, 64, 16),
                                                      ("bf16", 4, 4, 128, 16), ("bf16", 8, 2, 128, 16),
-                                                     ("f16", 1, 16, 128, 16)])
+                                                     ("f16", 1, 16, 128, 16), ("bf16", 4, 4, 128, 8),
+                                                     ("f16", 2, 4, 64, 8)])
 def test_beams_match_oracle(dtype, group, beams, d, bs):
     dev = require_gpu()
     lens = _LENS if beams <= 4 else _LENS + [250, 256, 260, 261, 262, 263]
@@ -86,13 +87,14 @@ def test_beams_match_oracle(dtype, group, beams, d, bs):
         assert_close(out.float().cpu().numpy(), ref, dtype, f"beams G={group} W={beams} P={P}")
 
 
-@pytest.mark.parametrize("group", [4, 8])
-def test_beams_bitwise_equal_to_grouped_decode(group):
+@pytest.mark.parametrize("group,bs", [(4, 16), (8, 16), (8, 8)])
+def test_beams_bitwise_equal_to_grouped_decode(group, bs):
     """With 4 or 8 query heads per kv head pa_decode runs the same matrix-core arithmetic per
-    column, so for an explicit partition size the outputs agree bit for bit, shared or not."""
+    column, so for an explicit partition size the outputs agree bit for bit, shared or not
+    (with 8-token blocks too, where the two load the rows in different ways)."""
     dev = require_gpu()
     for share in (True, False):
-        q, kp, vp, table, L = _beam_case(2, _LENS, 2, 2, group, 128, 16, 256, "bf16", share=share)
+        q, kp, vp, table, L = _beam_case(2, _LENS, 2, 2, group, 128, bs, 256, "bf16", share=share)
         tq, tk, tv, tt, tl = _device(dev, "bf16", q, kp, vp, table, L)
         for P in (64, 256):
             note(f"beams vs decode G={group} share={share} P={P}")
@@ -138,10 +140,10 @@ def test_beams_private_tables():
         assert_close(out.float().cpu().numpy(), ref, "bf16", f"beams private tables P={P}")
 
 
-@pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
-def test_beams_fp8_cache(q_dtype):
+@pytest.mark.parametrize("q_dtype,bs", [("bf16", 32), ("f16", 32), ("bf16", 8)])
+def test_beams_fp8_cache(q_dtype, bs):
     dev = require_gpu()
-    q, kp, vp, table, L = _beam_case(4, _LENS, 4, 2, 1, 128, 32, 256, q_dtype)
+    q, kp, vp, table, L = _beam_case(4, _LENS, 4, 2, 1, 128, bs, 256, q_dtype)
     dead = np.isnan(kp).any(-1)
     kc, ks = o8.quantize_rows(np.nan_to_num(kp))
     vc, vs = o8.quantize_rows(np.nan_to_num(vp))
@@ -152,7 +154,7 @@ def test_beams_fp8_cache(q_dtype):
     tq = torch.from_numpy(q).to(_TORCH[q_dtype]).to(dev)
     tt, tl = torch.from_numpy(table).to(dev), torch.from_numpy(L).to(dev)
     for P in (0, 128):
-        note(f"beams fp8 q={q_dtype} P={P}")
+        note(f"beams fp8 q={q_dtype} bs={bs} P={P}")
         out = ops.decode_beams(tq, t8[0], t8[1], tt, tl, int(L.max()), 0.09, 4, k_scale=t8[2], v_scale=t8[3],
                                partition_size=P)
         torch.cuda.synchronize()
@@ -187,9 +189,9 @@ def test_beams_errors_poison_only_their_sequence():
 
 def test_beams_rejects_unsupported_shapes():
     dev = require_gpu()
-    q, kp, vp, table, L = _beam_case(6, [40, 50], 2, 2, 1, 128, 8, 16, "bf16")
+    q, kp, vp, table, L = _beam_case(6, [40, 50], 2, 2, 1, 256, 16, 16, "bf16")
     tq, tk, tv, tt, tl = _device(dev, "bf16", q, kp, vp, table, L)
-    with pytest.raises(Exception):  # 8-token blocks: below the matrix-core tile
+    with pytest.raises(Exception):  # head_dim 256
         ops.decode_beams(tq, tk, tv, tt, tl, 50, 0.1, 2)
     q, kp, vp, table, L = _beam_case(6, [40, 50], 2, 2, 8, 128, 16, 16, "bf16")
     tq, tk, tv, tt, tl = _device(dev, "bf16", q, kp, vp, table, L)
