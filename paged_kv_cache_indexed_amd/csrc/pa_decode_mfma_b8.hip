@@ -12,23 +12,19 @@ using mfma::decode_mfma_kernel;
 
 constexpr int kSmallWaves = 4;
 
-// Partitions up to this length take the lane-masked block halves (mode 2, two waves per
-// SIMD) when the pool rows are 16-bit and 128 dims wide; longer ones the per-lane addresses
-// (mode 1). Measured on grouped heads (8 per kv head, bf16): 2048-token partitions 54 against
-// 60 us for mode 1; 264-token partitions 87 against 111 us and 512-token ones 76 against
-// 88 us for mode 2.
-constexpr int kMode2MaxPartition = 1024;
-
 template <typename T, typename KV, int D, int G>
 hipError_t launch_tdg(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     constexpr int NW = kSmallWaves;
     dim3 grid(num_kv_heads, batch, a.max_partitions);
+    // 16-bit rows of 128 dims: the tile's two blocks through one buffer (mode 2), which keeps
+    // two waves per SIMD; per-lane row addresses (mode 1) need the registers of a second wave
+    // there. Measured with 8 query heads per kv head (bf16): B = 128 at 2049 tokens 200
+    // against 216 us, B = 256 at 257 tokens 82 against 111 us, B = 32 at 2049 tokens 55
+    // against 54 us.
     if constexpr (KV::kBytes == 2 && D == 128) {
-        if (a.partition_size <= kMode2MaxPartition) {
-            hipLaunchKernelGGL((decode_mfma_kernel<T, KV, D, G, NW, true, false, false, 2>), grid, dim3(NW * 64), 0,
-                               stream, a);
-            return hipGetLastError();
-        }
+        hipLaunchKernelGGL((decode_mfma_kernel<T, KV, D, G, NW, true, false, false, 2>), grid, dim3(NW * 64), 0, stream,
+                           a);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((decode_mfma_kernel<T, KV, D, G, NW, true, false, false, 1>), grid, dim3(NW * 64), 0, stream,
                        a);

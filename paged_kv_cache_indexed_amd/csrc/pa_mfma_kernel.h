@@ -259,9 +259,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
     static_assert(G >= 1 && G <= 16, "at most 16 query heads per kv head");
     static_assert(!(kMulti && kBeams), "one column mapping");
     // 8-token blocks (kSmallBlocks != 0): a 16-row tile spans two blocks. Mode 1 addresses each
-    // row from its lane (a 64-bit address per lane: one wave per SIMD with 16-bit rows of 128
-    // dims, and with 128 dims in the multi-token and beam-group modes); mode 2 loads the two 8-row halves from their blocks under lane masks (twice the
-    // load instructions, two waves per SIMD), the better choice for short partitions.
+    // row from its lane (a 64-bit address per lane: one wave per SIMD with 128 dims of 16-bit
+    // rows, and with 128 dims in the multi-token and beam-group modes). Mode 2 (16-bit pools)
+    // reads both blocks through one buffer when they lie within 2 GiB of each other, else the
+    // two 8-row halves under lane masks; it keeps two waves per SIMD.
     static_assert(kSmallBlocks == 0 || D <= 128, "8-token blocks: head_dim up to 128");
     static_assert(kSmallBlocks != 2 || KV::kBytes == 2, "mode 2: 16-bit pools");
     constexpr int NCOL = (kMulti || kBeams) ? 16 : G;  // columns whose results this workgroup keeps
@@ -442,7 +443,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
                 const int id0 = __builtin_amdgcn_readfirstlane(ids[j0]);
                 const int id1 = __builtin_amdgcn_readfirstlane(ids[j1]);
                 const uint32_t o8 = (uint32_t)((n & 7) * D * KV::kBytes) + seg;
-                if (n < 8) {
+                const int lo = min(id0, id1);
+                const size_t span = (size_t)(max(id0, id1) - lo) * block_bytes;
+                if (span <= (size_t)(0x7fffffffu - slab_bytes)) {
+                    // both blocks within one 2 GiB window: one buffer over them, 32-bit offsets
+                    const size_t base = (size_t)lo * block_bytes + (size_t)kvh * head_bytes;
+                    const uint32_t nrec = (uint32_t)span + slab_bytes;
+                    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + base, nrec);
+                    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + base, nrec);
+                    const uint32_t off = (uint32_t)((size_t)((n < 8 ? id0 : id1) - lo) * block_bytes) + o8;
+#pragma unroll
+                    for (int c = 0; c < NL; ++c) {
+                        kk[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rk, off + 64 * c);
+                        vv[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rv, off + 64 * c);
+                    }
+                } else if (n < 8) {
                     const size_t s0 = (size_t)id0 * block_bytes + (size_t)kvh * head_bytes;
                     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + s0, slab_bytes);
                     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + s0, slab_bytes);

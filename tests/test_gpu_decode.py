@@ -59,9 +59,9 @@ _GQA8 = [(dt, d, g) for dt in ("f16", "bf16") for d in (64, 128) for g in (4, 8,
 @pytest.mark.parametrize("dtype,head_dim,group", _GQA8, ids=lambda x: str(x))
 def test_grouped_heads_8_token_blocks(dtype, head_dim, group):
     """Grouped heads over 8-token blocks run on the matrix cores, a 16-row tile spanning two
-    blocks: per-lane row addresses for partitions over 1024 tokens, the tile's two block
-    halves under lane masks for shorter ones. Unused slots hold NaN; partitions of 8 and 24
-    tokens start in the middle of a tile."""
+    blocks (16-bit rows of 128 dims: one buffer over both blocks; otherwise per-lane row
+    addresses). Unused slots hold NaN; partitions of 8 and 24 tokens start in the middle of
+    a tile."""
     dev = require_gpu()
     lens = np.array([1, 7, 8, 9, 15, 16, 17, 100, 250, 600], np.int32)
     w = build_paged(f"gqa-bs8-{dtype}-{head_dim}-{group}", 300 + group, head_dim, lens, 8, 2, 2 * group,
@@ -72,6 +72,37 @@ def test_grouped_heads_8_token_blocks(dtype, head_dim, group):
         note(f"grouped heads bs=8 dtype={dtype} d={head_dim} G={group} P={P}")
         got, _ = gpu_decode(w, dev, partition_size=P, tensors=t)
         assert_close(got, ref, dtype, f"bs=8 {dtype} d={head_dim} G={group} P={P}")
+
+
+def test_grouped_heads_8_token_blocks_far_apart():
+    """A tile's two 8-token blocks more than 2 GiB apart in the pool (every other block of a
+    sequence moved up by 600000 ids, 2.3 GiB per pool): the kernel then loads the two 8-row
+    halves from their own blocks under lane masks."""
+    dev = require_gpu()
+    lens = np.array([1, 9, 100, 250], np.int32)
+    w = build_paged("gqa-bs8-far", 320, 0, lens, 8, 2, 16, 128, "bf16")
+    ref = oracle_decode(w)
+    far = 600_000
+    tab = w.block_table.copy()
+    odd = np.zeros_like(tab, dtype=bool)
+    odd[:, 1::2] = True
+    tab = np.where((tab >= 0) & odd, tab + far, tab).astype(np.int32)
+    used = np.unique(w.block_table[w.block_table >= 0])
+    t = w.to_device(dev)
+    shape = (far + w.num_blocks, 2, 8, 128)
+    kp = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    vp = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    ids = torch.from_numpy(np.where(np.isin(used, w.block_table[:, 1::2]), used + far, used)).long().to(dev)
+    src = torch.from_numpy(used).long().to(dev)
+    kp[ids] = t["k_pool"][src]
+    vp[ids] = t["v_pool"][src]
+    tt = torch.from_numpy(tab).to(dev)
+    for P in (0, 16, 2048):
+        note(f"grouped heads bs=8, blocks 2.3 GiB apart, P={P}")
+        out = ops.decode(t["q"], kp, vp, tt, t["context_lens"], int(lens.max()), w.scale, partition_size=P)
+        torch.cuda.synchronize()
+        assert_close(out.float().cpu().numpy().astype(np.float64), ref, "bf16", f"far blocks P={P}")
+    del kp, vp
 
 
 # ------------------------------------------------------------------ the five workloads
