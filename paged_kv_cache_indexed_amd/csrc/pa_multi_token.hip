@@ -485,9 +485,6 @@ bool multi_token_supported(int kv_dtype, int head_dim, int group, int block_size
 
 hipError_t launch_multi_token(const DecodeArgs& a, int kv_dtype, int dtype, int head_dim, int group, int batch,
                               int num_kv_heads, hipStream_t stream) {
-    // 8-token blocks: the 16-column kernel with a block lookup per row, for any number of rows
-    if (a.log2_block_size < 4)
-        return launch_multi_token_small_blocks(a, kv_dtype, dtype, head_dim, group, batch, num_kv_heads, stream);
     // 64 or more (query, head) rows per kv head: the 64-row kernel (with fewer rows its tiles
     // run mostly empty: 2 column tiles measured 30% slower there)
     if (a.col_tiles >= 4 && (head_dim == 64 || head_dim == 128) && (kv_dtype == dtype || kv_dtype == PA_FP8_E4M3)) {
@@ -505,6 +502,10 @@ hipError_t launch_multi_token(const DecodeArgs& a, int kv_dtype, int dtype, int 
                                   : prefill::launch_prefill_td<BF16, BF16, 128>(a, batch, num_kv_heads, stream);
         }
     }
+    // 8-token blocks, fewer rows: the 16-column kernel with a block lookup per row (the 64-row
+    // kernel's wave loads stay inside an aligned group of 8 tokens, so it takes any block size)
+    if (a.log2_block_size < 4)
+        return launch_multi_token_small_blocks(a, kv_dtype, dtype, head_dim, group, batch, num_kv_heads, stream);
     if (kv_dtype == PA_FP8_E4M3) {
         switch (dtype) {
             case PA_F16: return launch_t<F16, FP8>(a, head_dim, group, batch, num_kv_heads, stream);

@@ -58,6 +58,31 @@ def test_multi_token_matches_oracle(dtype, group, bs, d):
         assert_close(out.float().cpu().numpy(), ref, dtype, f"multi-token {dtype} G={group} d={d} P={P}")
 
 
+@pytest.mark.parametrize("dtype,group,d,fp8", [("bf16", 4, 128, False), ("f16", 1, 64, False), ("bf16", 8, 128, True)])
+def test_multi_token_few_queries_8_token_blocks(dtype, group, d, fp8):
+    """Fewer than 64 (query, head) rows per kv head over 8-token blocks: the 16-column kernel
+    with a block lookup per tile row (longer chunks take the 64-row kernel, covered above)."""
+    dev = require_gpu()
+    lens = [1, 9, 40, 17, 100, 300]
+    ns = [1, 2, 1, 0, 1, 2]
+    w, qs, q = _case(f"mt-few-bs8-{dtype}", 760 + group, lens, ns, 8, 2, group, d, dtype)
+    kp, vp, f8 = w.k_pool, w.v_pool, None
+    if fp8:
+        dead = np.isnan(w.k_pool).any(-1)
+        kc, ks = o8.quantize_rows(np.nan_to_num(w.k_pool))
+        vc, vs = o8.quantize_rows(np.nan_to_num(w.v_pool))
+        kc[dead], vc[dead] = o8.E4M3_NAN_CODE, o8.E4M3_NAN_CODE
+        ks[dead], vs[dead] = np.nan, np.nan
+        kp, vp = o8.dequantize(kc, ks), o8.dequantize(vc, vs)
+        f8 = tuple(torch.from_numpy(x).to(dev) for x in (kc, vc, ks, vs))
+    ref = oracle.paged_attention_multi(q, kp, vp, w.block_table, w.context_lens, qs, w.scale)
+    for P in (0, 8, 24, 128):
+        note(f"multi-token few queries bs=8 {dtype} G={group} d={d} fp8={fp8} P={P}")
+        out, err = _run(w, qs, q, dev, max(ns), P, fp8=f8)
+        assert err == 0, f"error flag {err}"
+        assert_close(out.float().cpu().numpy(), ref, dtype, f"few queries bs=8 G={group} d={d} P={P}")
+
+
 def test_multi_token_one_query_is_the_decode_bitwise():
     """With one query per sequence the (query, head) columns are the decode's head columns,
     the partition policy is the same, and so is every bit of the output."""
