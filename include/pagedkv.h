@@ -271,8 +271,8 @@ pa_status_t pa_copy_blocks_fp8(const pa_cache_desc_t* cache, void* k_pool, void*
  * Launch shape, partitions, workspace (pa_decode_workspace_bytes, or
  * pa_decode_sliding_window_workspace_bytes for a window) and error rules are those of the
  * unquantised calls. The cache dtype must be PA_FP8_E4M3, num_q_heads / num_kv_heads at
- * most 8 (or 16 with head_dim 64 or 128), and block_size >= 16 when head_dim is 64 (else
- * PA_ERR_UNSUPPORTED).
+ * most 8 (or 16 with head_dim 64 or 128), and block_size >= 16 when head_dim is 64 unless
+ * 4, 8 or 16 query heads per kv head run on the matrix cores (else PA_ERR_UNSUPPORTED).
  */
 pa_status_t pa_decode_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
                           const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,

@@ -380,8 +380,12 @@ pa_status_t decode_impl(const pa_cache_desc_t* cache, int32_t q_dtype, void* out
     if (batch < 0 || batch > 65535) return PA_ERR_INVALID_ARGUMENT;
     if (batch == 0) return PA_OK;
     if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens) return PA_ERR_INVALID_ARGUMENT;
-    // a VALU wave load covers 1 KiB of consecutive token rows, which must lie in one block
-    if ((int64_t)cache->head_dim * dtype_bytes(cache->dtype) * cache->block_size < 1024) return PA_ERR_UNSUPPORTED;
+    // a VALU wave load covers 1 KiB of consecutive token rows, which must lie in one block;
+    // grouped heads that run on the matrix cores take smaller slabs too
+    if ((int64_t)cache->head_dim * dtype_bytes(cache->dtype) * cache->block_size < 1024 &&
+        !(num_q_heads % cache->num_kv_heads == 0 &&
+          decode_mfma_supported(cache->dtype, cache->head_dim, num_q_heads / cache->num_kv_heads, cache->block_size)))
+        return PA_ERR_UNSUPPORTED;
     if (is_fp8(cache)) {
         if (q_dtype != PA_F16 && q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
         // the VALU kernel takes at most 8 query heads per kv head over 8-bit pools
