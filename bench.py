@@ -17,7 +17,14 @@ back-to-back launches of it alone (same inputs, same replica rotation) between o
 HIP events on its stream. An event pair around every launch would add 2-5 us to each measured launch, and one
 inside every step about 7 us to the step.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2] [--window W]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 3] [--median 87] [--block-size 16]
+
+The default workload is the long-tail block-size sweep's median-87, 16-token-block case
+(256 sequences, 32 heads, head_dim 128, fp16). With it the line also carries `sweep`: the
+fused step at medians 87 and 23 and block sizes 8, 16, 32 and 64, each with its decode
+launch time, GB/s and share of the 8 TB/s roofline. `roofline.ceiling` is the streaming-read
+rate this GPU reaches with the library's read kernel (pa_measure_stream_read over 4 GiB),
+and `*_per_launch_events` give the median, p10 and p90 of launches timed one by one.
 
 With --window W the decode attends to the last W tokens of each sequence only
 (pa_decode_sliding_window) and the algorithmic bytes count min(context_len, W) tokens.
@@ -165,7 +172,7 @@ def _cpu_baseline(w, budget_s: float, window: int = 0) -> dict:
             done += per_tok * int(L[seqs])
         seqs += 1
     dt = time.perf_counter() - t0
-    return {"value": round(done / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(done / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle", **_host_info(threads),
             "sample": f"oracle append of all {w.batch} tokens + float64 "
                       f"{'window-' + str(window) + ' ' if window > 0 else ''}decode of sequences "
                       f"0..{seqs - 1} (all heads, {done / 1e6:.1f} MB of KV) in {dt:.1f} s"}
@@ -194,7 +201,7 @@ def _cpu_baseline_beams(w, host, budget_s: float, window: int = 0) -> dict:
             oracle.paged_decode(host["q"], k2, v2, host["table"], L, w.scale)
         reps += 1
     dt = time.perf_counter() - t0
-    return {"value": round(reps * per_seq / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(reps * per_seq / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle", **_host_info(threads),
             "sample": f"{reps} x (copy-on-write + append + float64 "
                       f"{'window-' + str(window) + ' ' if window > 0 else ''}decode) of beam 0, all "
                       f"{w.num_kv_heads} heads, L={int(L[0])} ({per_seq / 1e6:.0f} MB of KV each) in {dt:.1f} s"}
@@ -232,7 +239,7 @@ def _cpu_baseline_fp8(w, budget_s: float, window: int = 0) -> dict:
         seqs += 1
         if timed >= budget_s:
             break
-    return {"value": round(done / timed / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(done / timed / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle", **_host_info(threads),
             "sample": f"oracle quantised append + float64 {'window-' + str(window) + ' ' if window > 0 else ''}"
                       f"decode of sequences 0..{seqs - 1} (all heads, {done / 1e6:.1f} MB of codes and "
                       f"scales) in {timed:.1f} s"}
@@ -261,7 +268,7 @@ def _cpu_baseline_fp8_beams(w, host, budget_s: float, window: int = 0) -> dict:
         o8.paged_decode_fp8(host["q"], *p2, host["table"], L, w.scale, window=window)
         reps += 1
     dt = time.perf_counter() - t0
-    return {"value": round(reps * per_seq / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(reps * per_seq / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle", **_host_info(threads),
             "sample": f"{reps} x (quantised copy-on-write + append + float64 decode) of beam 0, "
                       f"{heads} of {w.num_kv_heads} heads, L={int(L[0])} in {dt:.1f} s"}
 
@@ -327,6 +334,119 @@ def _capture(fn, R: int) -> list:
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
+
+
+def _host_info(threads: int) -> dict:
+    """CPU model, the cores this process may run on and the numpy BLAS threads."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": blas,
+            "threads_used": threads}
+
+
+def _event_each(launch, first: int, steps: int) -> list:
+    """Duration in us of each of `steps` launches, each between its own pair of HIP events on
+    the launch stream (the event packets add a little to each figure)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        launch(first + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+
+def _percentiles(xs) -> dict:
+    v = np.asarray(xs, np.float64)
+    return {"median": round(float(np.median(v)), 2), "p10": round(float(np.percentile(v, 10)), 2),
+            "p90": round(float(np.percentile(v, 90)), 2), "n": int(v.size)}
+
+
+def _stream_ceiling(dev, gib: float = 4.0, reps: int = 10) -> dict:
+    """Achievable streaming-read GB/s of this GPU: pa_measure_stream_read over `gib` GiB,
+    8 work-groups per compute unit, `reps` back-to-back reads between one event pair."""
+    import torch
+
+    from paged_kv_cache_indexed_amd import _lib
+
+    nbytes = int(gib * 2 ** 30)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wgs = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(wgs, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        _lib.pa_measure_stream_read(buf, sink, wgs)
+    ms = _event_pass(lambda i: _lib.pa_measure_stream_read(buf, sink, wgs), 0, reps)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes, "workgroups": wgs,
+            "kernel": "pa_measure_stream_read (16-byte non-temporal loads, 1 KiB per wave instruction)"}
+
+
+def _sweep_config3(args, dev, medians=(87, 23), block_sizes=(8, 16, 32, 64)) -> dict:
+    """The block-size sweep of the long-tail workload: for each median and block size, the
+    fused step (pa_decode_append) timed as the main line is, the decode launch from the event
+    pass, its share of the 8 TB/s roofline, and the padding waste."""
+    import torch
+
+    from paged_kv_cache_indexed_amd import _lib, ops
+    from workloads import config3_device_family
+
+    cases = {}
+    for med in medians:
+        fam = config3_device_family(med, block_sizes, dev)
+        for w in fam:
+            t = w.tensors
+            pool_bytes = 2 * t["k_pool"].numel() * t["k_pool"].element_size()
+            R = max(2, math.ceil(args.replica_bytes / pool_bytes))
+            kps = [t["k_pool"]] + [t["k_pool"].clone() for _ in range(R - 1)]
+            vps = [t["v_pool"]] + [t["v_pool"].clone() for _ in range(R - 1)]
+            lens = t["lens_after"]
+            max_len = int(w.lens_after_append.max())
+            ws = ops.workspace_for(t["k_pool"], w.batch, w.num_q_heads, max_len, 0)
+            out = torch.empty_like(t["q"])
+
+            def step(i, kps=kps, vps=vps, t=t, lens=lens, max_len=max_len, ws=ws, out=out, w=w, R=R):
+                ops.decode_append(t["q"], kps[i % R], vps[i % R], t["block_table"], lens, max_len, w.scale,
+                                  t["new_key"], t["new_value"], t["slot_mapping"], out=out, workspace=ws)
+
+            for i in range(args.warmup):
+                step(i)
+            wall = _timed(step, args.warmup, args.steps)
+            dec = _event_pass(step, args.warmup + args.steps, args.steps)
+            kv = 2 * w.num_kv_heads * w.head_dim * 2 * int(w.lens_after_append.sum())
+            gbs = kv / (dec * 1e-3) / 1e9
+            part = _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, w.num_q_heads, max_len, 0)
+            cases[f"med{med}-bs{w.block_size}"] = {
+                "decode_launch_us": round(dec * 1e3, 2), "decode_gbs": round(gbs, 1),
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "step_us": round(wall * 1e6 / args.steps, 2),
+                "step_gbs": round(kv / (wall / args.steps) / 1e9, 1), "kv_bytes": kv,
+                "context_len_sum": int(w.lens_after_append.sum()), "context_len_max": max_len,
+                "partition_size": part, "replicas": R,
+                "padding_waste_pct": round(padding_waste_pct(w.lens_after_append, w.block_size), 2)}
+            del kps, vps, t, ws, out, step
+        del fam
+        torch.cuda.empty_cache()
+    worst = min(cases, key=lambda k: cases[k]["frac"])
+    return {"workload": "cfg3-f16-longtail, fused step (append + decode), cold replicas",
+            "cases": cases, "worst": {"case": worst, "frac": cases[worst]["frac"]},
+            "all_at_least_70pct": all(c["frac"] >= 0.70 for c in cases.values())}
 
 
 def _event_pass(launch, first: int, steps: int) -> float:
@@ -453,7 +573,7 @@ def _bench_multi(args, dev) -> int:
             threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
         except Exception:  # noqa: BLE001
             threads = 1
-        result["cpu_baseline"] = {"value": round(done / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        result["cpu_baseline"] = {"value": round(done / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle", **_host_info(threads),
                                   "sample": f"float64 multi-token attention of sequences 0..{nseq - 1} "
                                             f"({done} query tokens, all heads) in {dt:.1f} s"}
     print(json.dumps(result), flush=True)
@@ -516,7 +636,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (default 2)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload 1-5 (default 3: the long-tail lengths, median 87, block size 16)")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--median", type=float, default=None)
     ap.add_argument("--partition-size", type=int, default=0)
@@ -540,6 +661,11 @@ def main() -> int:
                     help="pool bytes touched between reuses of one replica")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the block-size x median sweep that accompanies the default workload")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--variant", action="store_true",
+                    help="allow PAGEDKV_LIB to name a library other than the in-tree build")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -548,6 +674,13 @@ def main() -> int:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
+
+    if os.environ.get("PAGEDKV_LIB") and not args.variant:
+        print("PAGEDKV_LIB is set: bench.py measures the in-tree library unless --variant is given",
+              file=sys.stderr)
+        return 2
+    if args.config == 3 and args.median is None:
+        args.median = 87
 
     import torch
 
@@ -679,6 +812,8 @@ def main() -> int:
             run_step(i)
     wall = _timed(run_step, args.warmup, args.steps)
     dec_avg = _event_pass(run_decode, args.warmup + args.steps, args.steps)
+    dec_each = _event_each(run_decode, args.warmup + 2 * args.steps, args.steps)
+    step_each = _event_each(run_step, args.warmup + 3 * args.steps, args.steps)
     ms_step = wall * 1e3 / args.steps
     # Blocks shared by several sequences (beams of one prompt) hold one copy of their bytes:
     # the roofline counts each attended physical slot once, the least the launch has to move.
@@ -738,7 +873,20 @@ def main() -> int:
                      "traffic": recorded_traffic(cfg["workload"], path)},
         "kernel_source_hash": kernel_source_hash(path),
         "decode_kernel": path,
+        "decode_launch_us_per_launch_events": _percentiles(dec_each),
+        "step_us_per_step_events": _percentiles(step_each),
+        "library": _lib.library_identity(),
     }
+    if not args.no_ceiling:
+        ceil = _stream_ceiling(dev)
+        result["roofline"]["ceiling"] = ceil["gbs"]
+        result["roofline"]["frac_of_ceiling"] = round(achieved / ceil["gbs"], 4)
+        result["stream_read_ceiling"] = ceil
+    plain = not (fp8 or W or BW or args.unfused or args.graph or NL > 1)
+    if args.config == 3 and plain and not args.no_sweep:
+        del kps, vps
+        torch.cuda.empty_cache()
+        result["sweep"] = _sweep_config3(args, dev)
     if path == "mfma":
         result["mfma_busy_pct"] = recorded_mfma_busy(cfg["workload"], path)
     if not args.no_cpu_baseline:

@@ -15,8 +15,11 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# PAGEDKV_LIB selects another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_PKG, "libpagedkv.so")
+# The in-tree build. PAGEDKV_LIB selects another build of the same library (a tuning
+# variant); bench.py refuses it unless asked for one, and every record names the library
+# it loaded with its hash (library_identity()).
+DEFAULT_LIB_PATH = os.path.join(_PKG, "libpagedkv.so")
+LIB_PATH = os.environ.get("PAGEDKV_LIB") or DEFAULT_LIB_PATH
 
 PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, 1, 2, 3
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
@@ -32,7 +35,7 @@ EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_size"
             "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_reblock", "pa_multi_token_attention",
             "pa_multi_token_workspace_bytes", "pa_decode_append", "pa_decode_append_fp8",
             "pa_decode_beams", "pa_decode_beams_partition_size", "pa_decode_beams_workspace_bytes",
-            "pa_status_string")
+            "pa_status_string", "pa_measure_stream_read")
 
 # 8-bit float pools are uint8 (or float8_e4m3fn) tensors of OCP E4M3 codes.
 _DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
@@ -126,10 +129,26 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_beams_partition_size.restype = I32
     lib.pa_decode_beams_workspace_bytes.argtypes = [D, I32, I32, I32, I32, I32]
     lib.pa_decode_beams_workspace_bytes.restype = SZ
+    lib.pa_measure_stream_read.argtypes = [P, SZ, P, I32, P]
+    lib.pa_measure_stream_read.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
+
+
+def library_identity(path: str = LIB_PATH) -> dict:
+    """Path and sha256 (first 16 hex digits) of the library file, and whether it is the
+    in-tree build."""
+    import hashlib
+
+    h = hashlib.sha256()
+    with open(path, "rb") as f:
+        for chunk in iter(lambda: f.read(1 << 20), b""):
+            h.update(chunk)
+    return {"path": os.path.relpath(path, os.path.dirname(_PKG)) if path.startswith(os.path.dirname(_PKG))
+            else path, "sha256_16": h.hexdigest()[:16],
+            "in_tree": os.path.abspath(path) == os.path.abspath(DEFAULT_LIB_PATH)}
 
 
 def _ptr(t):
@@ -354,3 +373,12 @@ def pa_decode_append(cache: CacheDesc, out, q, k_pool, v_pool, block_table, cont
         int(block_table.shape[1]), _ptr(context_lens), batch, num_q_heads, int(max_context_len), float(scale),
         _ptr(key), _ptr(value), _ptr(slot_mapping), int(partition_size), _ptr(workspace), ws_bytes, _ptr(err_flag),
         _stream(stream)))
+
+
+def pa_measure_stream_read(buf, sink, num_workgroups: int, stream=None) -> None:
+    """One streaming read of the whole of ``buf`` (include/pagedkv_measure.h); ``sink`` holds
+    at least ``num_workgroups`` float32."""
+    if sink.numel() < num_workgroups or sink.dtype != torch.float32:
+        raise PagedKVError("sink must hold num_workgroups float32")
+    _check(load().pa_measure_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                         int(num_workgroups), _stream(stream)))

@@ -46,6 +46,10 @@ def max_err(a, b) -> float:
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
 
 
+# Every comparison of this process: (what, dtype, raw max-abs error, error beyond the output
+# rounding); the session summary lists them (tests/conftest.py).
+RESULTS: list = []
+
 # Half an ulp relative to |o| of the output type: the one rounding of the fp32 result.
 HALF_ULP = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
@@ -61,6 +65,7 @@ def assert_close(got, ref, dtype: str, what: str) -> float:
     excess = float(np.max(diff - np.abs(ref) * HALF_ULP[dtype])) if diff.size else 0.0
     print(f"[gpu-result] {what}: max abs err {err:.3e}, beyond output rounding {excess:.3e} "
           f"(tol {TOL[dtype]:.0e})", flush=True)
+    RESULTS.append((what, dtype, err, excess))
     assert excess <= TOL[dtype], f"{what}: error beyond output rounding {excess:.3e} > {TOL[dtype]}"
     return err
 

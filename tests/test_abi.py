@@ -10,13 +10,17 @@ import pytest
 from paged_kv_cache_indexed_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+    """Every function any include/*.h declares."""
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, f)).read(), flags=re.S)
+            names.update(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")

@@ -11,9 +11,15 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _bench(*args, timeout=600):
+def _bench(*args, timeout=600, env=None):
     return subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
-                          capture_output=True, text=True, timeout=timeout)
+                          capture_output=True, text=True, timeout=timeout, env=env)
+
+
+def test_bench_refuses_another_library_unless_asked():
+    env = dict(os.environ, PAGEDKV_LIB="/nonexistent/libpagedkv.so")
+    r = _bench("--steps", "1", timeout=120, env=env)
+    assert r.returncode == 2 and "PAGEDKV_LIB" in r.stderr and r.stdout.strip() == ""
 
 
 def test_bench_refuses_several_gpus():
@@ -25,8 +31,8 @@ def test_bench_refuses_several_gpus():
 
 @pytest.mark.gpu
 def test_bench_default_line():
-    print("[gpu-case] bench.py default workload, 3 steps", flush=True)
-    r = _bench("--steps", "3", "--warmup", "1", "--cpu-budget", "1")
+    print("[gpu-case] bench.py default workload, 3 steps, no sweep", flush=True)
+    r = _bench("--steps", "3", "--warmup", "1", "--cpu-budget", "1", "--no-sweep")
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [x for x in r.stdout.splitlines() if x.strip()]
     assert len(lines) == 1, r.stdout[-2000:]
@@ -51,3 +57,12 @@ def test_bench_default_line():
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["unit"]
     assert isinstance(cpu["sample"], str) and cpu["sample"]
+    assert cpu["cpu_model"] and cpu["affinity_cores"] >= 1
+    assert cfg["workload"].startswith("cfg3-f16-longtail-med87-bs16")
+    assert roof["ceiling"] > 1000 and roof["frac_of_ceiling"] == pytest.approx(roof["achieved"] / roof["ceiling"],
+                                                                                 abs=1e-3)
+    lib = d["library"]
+    assert lib["in_tree"] is True and len(lib["sha256_16"]) == 16
+    for k in ("decode_launch_us_per_launch_events", "step_us_per_step_events"):
+        p = d[k]
+        assert p["p10"] <= p["median"] <= p["p90"] and p["n"] == 3

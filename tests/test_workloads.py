@@ -84,3 +84,30 @@ def test_append_matches_oracle_cache_op():
         g = oracle.gather_sequence(k2, w.block_table[b], L + 1, 0)
         assert np.array_equal(g[-1], w.new_key[b, 0].astype(np.float64))
         assert np.array_equal(g[:-1], oracle.gather_sequence(w.k_pool, w.block_table[b], L, 0))
+
+
+def test_device_twin_matches_host_build():
+    """device_paged scatters the same contents through the same tables as build_paged: its
+    tensors equal build_paged(...).to_device() bit for bit (run here on the CPU device)."""
+    import torch
+
+    from workloads import build_paged, config3_lengths, device_paged, paged_contents
+
+    lens = config3_lengths(23)[:12]
+    for bs in (8, 16, 64):
+        host = build_paged("t", 30, 0, lens, bs, 4, 4, 64, "f16").to_device("cpu")
+        dev = device_paged("t", 30, 0, lens, bs, 4, 4, 64, "f16", "cpu").tensors
+        for k in ("q", "k_pool", "v_pool", "block_table", "context_lens", "lens_after", "new_key", "new_value",
+                  "slot_mapping"):
+            a, b = host[k], dev[k]
+            assert a.shape == b.shape and a.dtype == b.dtype, k
+            if a.is_floating_point():
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16)), k
+            else:
+                assert torch.equal(a, b), k
+    # shared contents across block sizes, as the sweep uses them
+    c = paged_contents(30, 0, lens, 4, 4, 64, "f16")
+    up: dict = {}
+    a = device_paged("t", 30, 0, lens, 16, 4, 4, 64, "f16", "cpu", contents=c, uploaded=up).tensors
+    b = build_paged("t", 30, 0, lens, 16, 4, 4, 64, "f16").to_device("cpu")
+    assert torch.equal(a["k_pool"].view(torch.int16), b["k_pool"].view(torch.int16))

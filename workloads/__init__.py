@@ -13,4 +13,9 @@ from .paged import (  # noqa: F401
     config_workload,
     cast_like,
     lognormal_lengths,
+    DevicePagedWorkload,
+    config3_device_family,
+    config3_lengths,
+    device_paged,
+    paged_contents,
 )

@@ -145,25 +145,38 @@ def _scatter(pool: np.ndarray, table: np.ndarray, lens: np.ndarray, starts: np.n
         pool[blk, :, off, :] = contents[int(starts[b]) + t]
 
 
-def build_paged(name: str, cfg_id: int, seed: int, lens: np.ndarray, block_size: int,
-                num_kv_heads: int, num_q_heads: int, head_dim: int, dtype: str,
-                scale: float | None = None, std: float = 1.0, num_blocks: int | None = None,
-                spare: float = 0.10, max_blocks_per_seq: int | None = None,
-                append: bool = True) -> PagedWorkload:
+def paged_contents(cfg_id: int, seed: int, lens: np.ndarray, num_kv_heads: int, num_q_heads: int,
+                   head_dim: int, dtype: str, std: float = 1.0):
+    """q and the contiguous K/V rows of every sequence, independent of the block size and of
+    the physical placement: (q, kc, vc, starts), sequence b's token t at row starts[b] + t
+    (L + 1 rows per sequence: its cached tokens, then the token the step appends)."""
     lens = np.asarray(lens, np.int32)
     B = len(lens)
-    if scale is None:
-        scale = 1.0 / math.sqrt(head_dim)
     rng_c = np.random.default_rng([cfg_id, seed, 0])
-    rng_l = np.random.default_rng([cfg_id, seed, 1, block_size])
-    table, nb = _allocate_tables(rng_l, lens, block_size, num_blocks, spare,
-                                 max_blocks_per_seq, append)
-    # Contents: q, then L+1 contiguous K rows per sequence, then the same for V.
     q = cast_like(rng_c.standard_normal((B, num_q_heads, head_dim), np.float32) * std, dtype)
     rows = int(lens.sum()) + B
     starts = np.concatenate([[0], np.cumsum(lens + 1)[:-1]]).astype(np.int64)
     kc = cast_like(rng_c.standard_normal((rows, num_kv_heads, head_dim), np.float32) * std, dtype)
     vc = cast_like(rng_c.standard_normal((rows, num_kv_heads, head_dim), np.float32) * std, dtype)
+    return q, kc, vc, starts
+
+
+def build_paged(name: str, cfg_id: int, seed: int, lens: np.ndarray, block_size: int,
+                num_kv_heads: int, num_q_heads: int, head_dim: int, dtype: str,
+                scale: float | None = None, std: float = 1.0, num_blocks: int | None = None,
+                spare: float = 0.10, max_blocks_per_seq: int | None = None,
+                append: bool = True, contents=None) -> PagedWorkload:
+    lens = np.asarray(lens, np.int32)
+    B = len(lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    rng_l = np.random.default_rng([cfg_id, seed, 1, block_size])
+    table, nb = _allocate_tables(rng_l, lens, block_size, num_blocks, spare,
+                                 max_blocks_per_seq, append)
+    # Contents: q, then L+1 contiguous K rows per sequence, then the same for V.
+    if contents is None:
+        contents = paged_contents(cfg_id, seed, lens, num_kv_heads, num_q_heads, head_dim, dtype, std)
+    q, kc, vc, starts = contents
     k_pool = np.full((nb, num_kv_heads, block_size, head_dim), np.nan, np.float32)
     v_pool = np.full_like(k_pool, np.nan)
     _scatter(k_pool, table, lens, starts, kc, block_size)
@@ -220,3 +233,96 @@ def config_workload(cfg: int, seed: int = 0, *, block_size: int | None = None,
         return build_paged(f"cfg4-bf16-gqa-bs{bs}", 4, seed, lens, bs, hkv, hkv * 8, 128,
                            "bf16")
     raise ValueError(f"unknown config {cfg}")
+
+
+@dataclass
+class DevicePagedWorkload:
+    """The device tensors of ``build_paged(...).to_device()`` built without the host pools: the
+    contents are drawn on the host by the same generator, uploaded once and scattered through
+    the tables on the device (for timing runs at full size; the oracle needs PagedWorkload)."""
+    name: str
+    dtype: str
+    block_size: int
+    num_kv_heads: int
+    num_q_heads: int
+    head_dim: int
+    scale: float
+    num_blocks: int
+    block_table: np.ndarray
+    context_lens: np.ndarray
+    slot_mapping: np.ndarray
+    tensors: dict
+
+    @property
+    def batch(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def lens_after_append(self) -> np.ndarray:
+        return (self.context_lens + 1).astype(np.int32)
+
+
+def device_paged(name: str, cfg_id: int, seed: int, lens: np.ndarray, block_size: int, num_kv_heads: int,
+                 num_q_heads: int, head_dim: int, dtype: str, device, scale: float | None = None,
+                 std: float = 1.0, spare: float = 0.10, contents=None, uploaded=None) -> DevicePagedWorkload:
+    """Device twin of build_paged (append=True, default pool size): the same tables, slots and
+    values bit for bit. ``contents`` (from paged_contents) and ``uploaded`` (their device
+    copies, a dict filled on first use) may be shared by several block sizes."""
+    lens = np.asarray(lens, np.int32)
+    B = len(lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    bs = block_size
+    rng_l = np.random.default_rng([cfg_id, seed, 1, bs])
+    table, nb = _allocate_tables(rng_l, lens, bs, None, spare, None, True)
+    if contents is None:
+        contents = paged_contents(cfg_id, seed, lens, num_kv_heads, num_q_heads, head_dim, dtype, std)
+    q, kc, vc, starts = contents
+    dt = _TORCH_DTYPES[dtype]
+    up = {} if uploaded is None else uploaded
+    if not up:
+        for key, x in (("q", q), ("kc", kc), ("vc", vc)):
+            up[key] = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dt).to(device)
+    seq = np.repeat(np.arange(B), lens)
+    tok = np.arange(int(lens.sum())) - np.repeat(np.cumsum(lens) - lens, lens)
+    blk = torch.from_numpy(table[seq, tok // bs].astype(np.int64)).to(device)
+    off = torch.from_numpy((tok % bs).astype(np.int64)).to(device)
+    rows = torch.from_numpy((starts[seq] + tok).astype(np.int64)).to(device)
+    pools = []
+    for src in (up["kc"], up["vc"]):
+        pool = torch.full((nb, num_kv_heads, bs, head_dim), float("nan"), dtype=dt, device=device)
+        pool[blk, :, off, :] = src.index_select(0, rows)
+        pools.append(pool)
+    new_rows = torch.from_numpy((starts + lens).astype(np.int64)).to(device)
+    slot = (table[np.arange(B), lens // bs].astype(np.int64) * bs + lens % bs).astype(np.int32)
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(device)
+
+    tensors = dict(q=up["q"], k_pool=pools[0], v_pool=pools[1], block_table=i32(table), context_lens=i32(lens),
+                   lens_after=i32(lens + 1), new_key=up["kc"].index_select(0, new_rows),
+                   new_value=up["vc"].index_select(0, new_rows), slot_mapping=i32(slot),
+                   copy_pairs=i32(np.zeros((0, 2), np.int32)))
+    return DevicePagedWorkload(name=name, dtype=dtype, block_size=bs, num_kv_heads=num_kv_heads,
+                               num_q_heads=num_q_heads, head_dim=head_dim, scale=float(scale), num_blocks=nb,
+                               block_table=table, context_lens=lens, slot_mapping=slot, tensors=tensors)
+
+
+def config3_lengths(median: float, seed: int = 0, sigma: float = 1.0, batch: int = 256) -> np.ndarray:
+    """The long-tail lengths of the block-size sweep (cached tokens before the step)."""
+    return lognormal_lengths(np.random.default_rng([3, seed, 2]), 256, median, sigma)[:batch]
+
+
+def config3_device_family(median: float, block_sizes, device, seed: int = 0):
+    """The block-size sweep at one median, on the device: one DevicePagedWorkload per block
+    size, all with the same contents (they equal config_workload(3, median=..., block_size=...)
+    uploaded)."""
+    lens = config3_lengths(median, seed)
+    cfg_id = 3 if median == 87 else 30
+    contents = paged_contents(cfg_id, seed, lens, 32, 32, 128, "f16")
+    up: dict = {}
+    out = []
+    for bs in block_sizes:
+        out.append(device_paged(f"cfg3-f16-longtail-med{median:g}-bs{bs}", cfg_id, seed, lens, bs, 32, 32, 128,
+                                "f16", device, contents=contents, uploaded=up))
+    return out
