@@ -54,7 +54,8 @@ typedef enum {
     PA_OK = 0,
     PA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, workspace too small */
     PA_ERR_UNSUPPORTED = 2,      /* dtype, head_dim, block_size or group not built */
-    PA_ERR_LAUNCH = 3            /* the HIP runtime refused a launch */
+    PA_ERR_LAUNCH = 3,           /* the HIP runtime refused a launch */
+    PA_ERR_SCRATCH_LIMIT = 4     /* pa_decode_append_noalloc: more workspace than its static scratch */
 } pa_status_t;
 
 /*
@@ -154,6 +155,29 @@ pa_status_t pa_decode_append(const pa_cache_desc_t* cache, void* out, const void
                              const void* key, const void* value, const int32_t* slot_mapping,
                              int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t* err_flag,
                              pa_stream_t stream);
+
+/*
+ * pa_decode_append_noalloc - pa_decode_append for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The same arguments and results as pa_decode_append, without the workspace: the partition
+ * records and slot words live in a static device array of PA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends. The caller still passes
+ * every input and output. A call whose pa_decode_workspace_bytes(cache, batch, num_q_heads,
+ * max_context_len, partition_size) exceeds PA_NOALLOC_SCRATCH_BYTES returns
+ * PA_ERR_SCRATCH_LIMIT and launches nothing. The call allocates and frees nothing (the
+ * first call on a device looks up the array's address there once). Nothing in the scratch
+ * needs to start at zero: every record the reduce pass reads is written by the same call's
+ * decode. All calls on one GPU share its array, so calls that can overlap on one GPU (on
+ * different streams without ordering between them) race and give undefined results.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64 << 20)
+pa_status_t pa_decode_append_noalloc(const pa_cache_desc_t* cache, void* out, const void* q, void* k_pool,
+                                     void* v_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                                     int32_t max_context_len, float scale, const void* key, const void* value,
+                                     const int32_t* slot_mapping, int32_t partition_size, int32_t* err_flag,
+                                     pa_stream_t stream);
 
 /*
  * pa_decode_partition_size - the context-partition length pa_decode will use.

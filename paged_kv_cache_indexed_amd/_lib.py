@@ -21,7 +21,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_LIB_PATH = os.path.join(_PKG, "libpagedkv.so")
 LIB_PATH = os.environ.get("PAGEDKV_LIB") or DEFAULT_LIB_PATH
 
-PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH = 0, 1, 2, 3
+PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH, PA_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/pagedkv.h
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_FLAG_BAD_BLOCK_ID = 1
 PA_FLAG_BAD_LENGTH = 2
@@ -35,7 +36,7 @@ EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_size"
             "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_reblock", "pa_multi_token_attention",
             "pa_multi_token_workspace_bytes", "pa_decode_append", "pa_decode_append_fp8",
             "pa_decode_beams", "pa_decode_beams_partition_size", "pa_decode_beams_workspace_bytes",
-            "pa_status_string", "pa_measure_stream_read")
+            "pa_status_string", "pa_measure_stream_read", "pa_decode_append_noalloc")
 
 # 8-bit float pools are uint8 (or float8_e4m3fn) tensors of OCP E4M3 codes.
 _DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
@@ -129,6 +130,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_beams_partition_size.restype = I32
     lib.pa_decode_beams_workspace_bytes.argtypes = [D, I32, I32, I32, I32, I32]
     lib.pa_decode_beams_workspace_bytes.restype = SZ
+    lib.pa_decode_append_noalloc.argtypes = [D, P, P, P, P, P, I32, P, I32, I32, I32, F, P, P, P, I32, P, P]
+    lib.pa_decode_append_noalloc.restype = ctypes.c_int
     lib.pa_measure_stream_read.argtypes = [P, SZ, P, I32, P]
     lib.pa_measure_stream_read.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -382,3 +385,15 @@ def pa_measure_stream_read(buf, sink, num_workgroups: int, stream=None) -> None:
         raise PagedKVError("sink must hold num_workgroups float32")
     _check(load().pa_measure_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                          int(num_workgroups), _stream(stream)))
+
+
+def pa_decode_append_noalloc(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_lens,
+                             max_context_len: int, scale: float, key, value, slot_mapping, partition_size: int = 0,
+                             err_flag=None, stream=None) -> None:
+    """pa_decode_append with the library's static scratch in place of a workspace."""
+    batch, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    desc = cache.c()
+    _check(load().pa_decode_append_noalloc(
+        ctypes.byref(desc), _ptr(out), _ptr(q), _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool), _ptr(block_table),
+        int(block_table.shape[1]), _ptr(context_lens), batch, num_q_heads, int(max_context_len), float(scale),
+        _ptr(key), _ptr(value), _ptr(slot_mapping), int(partition_size), _ptr(err_flag), _stream(stream)))

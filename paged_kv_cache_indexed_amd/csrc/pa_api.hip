@@ -2,6 +2,8 @@
 // No compute happens here; every step of the path runs in the HIP kernels.
 #include <math.h>
 
+#include <mutex>
+
 #include "pa_kernels.h"
 
 using namespace pagedkv;
@@ -107,6 +109,9 @@ const char* pa_status_string(pa_status_t s) {
         case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT: bad pointer, size or workspace";
         case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: dtype, head_dim, block_size or group not built";
         case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime refused a kernel launch";
+        case PA_ERR_SCRATCH_LIMIT:
+            return "PA_ERR_SCRATCH_LIMIT: the call needs more workspace than the static scratch of "
+                   "pa_decode_append_noalloc (PA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown pa_status_t";
     }
 }
@@ -476,6 +481,63 @@ pa_status_t pa_decode_append(const pa_cache_desc_t* cache, void* out, const void
     return decode_impl(cache, cache ? cache->dtype : 0, out, q, k_pool, v_pool, nullptr, nullptr, block_table,
                        max_blocks_per_seq, context_lens, batch, num_q_heads, max_context_len, scale, partition_size,
                        0, workspace, workspace_bytes, err_flag, stream, key, value, slot_mapping);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of pa_decode_append_noalloc: the partition records and slot words that the other
+// entry points take from the caller's workspace, in a static device array that every GPU the
+// library runs on holds until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: kernels get the address hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept in noalloc_scratch_ptr.
+static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (set-up on the first call per device).
+pa_status_t noalloc_scratch_ptr(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return PA_ERR_LAUNCH;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_decode_append_noalloc(const pa_cache_desc_t* cache, void* out, const void* q, void* k_pool,
+                                     void* v_pool, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                                     int32_t max_context_len, float scale, const void* key, const void* value,
+                                     const int32_t* slot_mapping, int32_t partition_size, int32_t* err_flag,
+                                     pa_stream_t stream) {
+    if (cache && is_fp8(cache)) return PA_ERR_UNSUPPORTED;
+    if (batch > 0 && (!key || !value || !slot_mapping || !aligned16(key) || !aligned16(value)))
+        return PA_ERR_INVALID_ARGUMENT;
+    // sizes first (no device call), so an oversized request is rejected before any set-up
+    if (check_cache(cache) == PA_OK && batch > 0 && max_context_len > 0 &&
+        pa_decode_workspace_bytes(cache, batch, num_q_heads, max_context_len, partition_size) >
+            (size_t)PA_NOALLOC_SCRATCH_BYTES)
+        return PA_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    if (batch > 0) {
+        const pa_status_t st = noalloc_scratch_ptr(&ws);
+        if (st != PA_OK) return st;
+    }
+    return decode_impl(cache, cache ? cache->dtype : 0, out, q, k_pool, v_pool, nullptr, nullptr, block_table,
+                       max_blocks_per_seq, context_lens, batch, num_q_heads, max_context_len, scale, partition_size,
+                       0, ws, ws ? (size_t)PA_NOALLOC_SCRATCH_BYTES : 0, err_flag, stream, key, value, slot_mapping);
 }
 
 pa_status_t pa_decode_append_fp8(const pa_cache_desc_t* cache, int32_t q_dtype, void* out, const void* q,
