@@ -162,20 +162,23 @@ def _cpu_baseline(w, budget_s: float, window: int = 0) -> dict:
     t0 = time.perf_counter()
     ek, ev = oracle.reshape_and_cache(w.k_pool, w.v_pool, w.new_key, w.new_value, w.slot_mapping)
     seqs = done = 0
-    while seqs < w.batch and (seqs == 0 or time.perf_counter() - t0 < budget_s):
-        sl = slice(seqs, seqs + 1)
+    # single-sequence decodes in batch order, cycling over the batch, until ~budget_s passed
+    while seqs == 0 or time.perf_counter() - t0 < budget_s:
+        b = seqs % w.batch
+        sl = slice(b, b + 1)
         if window > 0:
             oracle.paged_decode_window(w.q[sl], ek, ev, w.block_table[sl], L[sl], w.scale, window)
-            done += per_tok * min(int(L[seqs]), window)
+            done += per_tok * min(int(L[b]), window)
         else:
             oracle.paged_decode(w.q[sl], ek, ev, w.block_table[sl], L[sl], w.scale)
-            done += per_tok * int(L[seqs])
+            done += per_tok * int(L[b])
         seqs += 1
     dt = time.perf_counter() - t0
     return {"value": round(done / dt / 1e9, 5), "unit": "GB/s", "cores": threads, "kind": "oracle", **_host_info(threads),
             "sample": f"oracle append of all {w.batch} tokens + float64 "
-                      f"{'window-' + str(window) + ' ' if window > 0 else ''}decode of sequences "
-                      f"0..{seqs - 1} (all heads, {done / 1e6:.1f} MB of KV) in {dt:.1f} s"}
+                      f"{'window-' + str(window) + ' ' if window > 0 else ''}decode of {seqs} sequences in batch "
+                      f"order ({seqs / w.batch:.2f} passes over the batch; all heads, {done / 1e6:.1f} MB of KV) "
+                      f"in {dt:.1f} s"}
 
 
 def _cpu_baseline_beams(w, host, budget_s: float, window: int = 0) -> dict:
@@ -336,6 +339,11 @@ def _capture(fn, R: int) -> list:
     return graphs
 
 
+def _progress(msg: str) -> None:
+    """One line on stderr per finished stage (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def _host_info(threads: int) -> dict:
     """CPU model, the cores this process may run on and the numpy BLAS threads."""
     model = "unknown"
@@ -433,6 +441,7 @@ def _sweep_config3(args, dev, medians=(87, 23), block_sizes=(8, 16, 32, 64)) -> 
             kv = 2 * w.num_kv_heads * w.head_dim * 2 * int(w.lens_after_append.sum())
             gbs = kv / (dec * 1e-3) / 1e9
             part = _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, w.num_q_heads, max_len, 0)
+            _progress(f"sweep median {med} block size {w.block_size}: decode {dec * 1e3:.1f} us")
             cases[f"med{med}-bs{w.block_size}"] = {
                 "decode_launch_us": round(dec * 1e3, 2), "decode_gbs": round(gbs, 1),
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "step_us": round(wall * 1e6 / args.steps, 2),
@@ -701,6 +710,7 @@ def main() -> int:
     else:
         w = _workload(args.config, args.block_size, args.median)
         t = w.to_device(dev)
+        _progress(f"{w.name}: workload on the device")
     fp8 = args.kv == "fp8"
     if fp8 and w.dtype == "f32":
         print("--kv fp8 needs a workload with fp16 or bf16 queries", file=sys.stderr)
@@ -810,8 +820,10 @@ def main() -> int:
         run_step, run_decode = (lambda i: step_g[i % R].replay()), (lambda i: dec_g[i % R].replay())
         for i in range(2 * R):
             run_step(i)
+    _progress(f"{w.name}: warm-up done")
     wall = _timed(run_step, args.warmup, args.steps)
     dec_avg = _event_pass(run_decode, args.warmup + args.steps, args.steps)
+    _progress(f"{w.name}: {wall * 1e6 / args.steps:.1f} us per step, decode launch {dec_avg * 1e3:.1f} us")
     dec_each = _event_each(run_decode, args.warmup + 2 * args.steps, args.steps)
     step_each = _event_each(run_step, args.warmup + 3 * args.steps, args.steps)
     ms_step = wall * 1e3 / args.steps
@@ -890,6 +902,7 @@ def main() -> int:
     if path == "mfma":
         result["mfma_busy_pct"] = recorded_mfma_busy(cfg["workload"], path)
     if not args.no_cpu_baseline:
+        _progress("oracle timing on the host")
         if fp8:
             result["cpu_baseline"] = (_cpu_baseline_fp8_beams(w, host_sample, args.cpu_budget, W) if host_sample
                                       else _cpu_baseline_fp8(w, args.cpu_budget, W))
