@@ -62,6 +62,25 @@ __device__ __forceinline__ bool partition_is_dead(const DecodeArgs& a, int p, in
     return partition_base(a, L) + p * a.partition_size >= L;
 }
 
+// True on every thread when pred is true on any thread of the work-group of NT threads: one
+// ballot per wave, one LDS word per wave, one barrier. (The runtime's work-group OR reads the
+// dispatch packet for the group size, a dependent scalar load, and synchronises more than
+// once; on short work-groups that showed up as microseconds in the prologue.) Any LDS word
+// written here is read only before the next barrier of the caller, and callers reach a
+// barrier between two uses.
+template <int NT>
+__device__ __forceinline__ bool block_any(int pred) {
+    constexpr int NW = NT / 64;
+    __shared__ int s_any[NW];
+    const unsigned long long bal = __builtin_amdgcn_ballot_w64(pred != 0);
+    if ((threadIdx.x & 63) == 0) s_any[threadIdx.x >> 6] = bal != 0;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= s_any[w];
+    return any != 0;
+}
+
 template <typename T>
 __device__ __forceinline__ void store_nan(void* out, size_t base, int count) {
     for (int i = threadIdx.x; i < count; i += blockDim.x) store_elem(T{}, out, base + i, __builtin_nanf(""));
@@ -161,14 +180,14 @@ __device__ __forceinline__ bool check_new_slot(const DecodeArgs& a, int L, int j
 // stream; nothing waits for them.
 // The slot comes from the prologue's registers: reading slot_mapping again here would add a
 // memory round trip to the end of every owner workgroup.
-template <typename KV, int D>
+template <typename KV, int D, int NT>
 __device__ void store_new_rows(const DecodeArgs& a, int slot, int kv0, int nkv, const char* s_new) {
     using R = NewRec<KV, D>;
     constexpr int kRowVecs = R::kRowBytes / 16;
     const int lbs = a.log2_block_size;
     const int blk = slot >> lbs;
     const int off = slot & ((1 << lbs) - 1);
-    for (int i = threadIdx.x; i < 2 * nkv * kRowVecs; i += blockDim.x) {
+    for (int i = threadIdx.x; i < 2 * nkv * kRowVecs; i += NT) {
         const int kv = i / (2 * kRowVecs);
         const int which = (i / kRowVecs) & 1;
         const int v = i % kRowVecs;
@@ -177,7 +196,7 @@ __device__ void store_new_rows(const DecodeArgs& a, int slot, int kv0, int nkv, 
         store16(dst, load16(s_new + (size_t)kv * R::kBytes + which * R::kRowBytes + 16 * v));
     }
     if constexpr (R::kScaled) {
-        for (int i = threadIdx.x; i < 2 * nkv; i += blockDim.x) {
+        for (int i = threadIdx.x; i < 2 * nkv; i += NT) {
             const size_t srow = (((size_t)blk * a.num_kv_heads + kv0 + i / 2) << lbs) + off;
             float* scales = const_cast<float*>((i & 1) ? a.v_scale : a.k_scale);
             scales[srow] = reinterpret_cast<const float*>(s_new + (size_t)(i / 2) * R::kBytes + 2 * R::kRowBytes)[i & 1];
@@ -282,7 +301,7 @@ __device__ bool partition_prologue_sink(const DecodeArgs& a, int p, int b, int m
             s_ids[i] = id;
         }
     }
-    if (__syncthreads_or(bad)) {
+    if (block_any<NT>(bad)) {
         if (tid == 0 && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_BLOCK_ID);
         if (last && record) a.ws_slot[b] = -1;
         if (part.nparts == 1) sink.nan_outputs();

@@ -300,7 +300,7 @@ __device__ __forceinline__ void split_item(const DecodeArgs& a, int p, int kvh, 
     }
     __syncthreads();
     partition_epilogue<T, D, G, NW>(a, p, kvh, b, part, s_m, s_l, s_acc);
-    if (part.npos >= 0 && !a.ws_slot) store_new_rows<KV, D>(a, part.slot, kvh, 1, s_rec);
+    if (part.npos >= 0 && !a.ws_slot) store_new_rows<KV, D, NW * 64>(a, part.slot, kvh, 1, s_rec);
 }
 
 // Split mode: the NW waves of a workgroup share one kv head's partition. One workgroup per

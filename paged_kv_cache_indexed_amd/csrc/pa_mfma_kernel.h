@@ -231,7 +231,7 @@ __device__ bool beam_prologue(const DecodeArgs& a, int p, int kvh, int b0, int n
         if (L <= t0 || j == ref) continue;
         if (k < ((min(L, t0 + P) - 1) >> lbs) - j0 + 1 && s_bids[i] != s_bids[ref * cap + k]) mismatch = 1;
     }
-    shared = !__syncthreads_or(mismatch);
+    shared = !block_any<NT>(mismatch);
     part.nparts = 0;
     part.t0 = t0;
     part.rel_lo = 0;
@@ -833,7 +833,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
         partition_epilogue<T, D, G, NW>(a, p, kvh, b, part, s_m, s_l, s_acc);
         if constexpr (kAppendable) {
             // wave 0's record (every wave's is the same; the barrier above orders it)
-            if (part.npos >= 0 && !a.ws_slot) store_new_rows<KV, D>(a, part.slot, kvh, 1, s_new + (kFp8 ? kRaw : 0));
+            if (part.npos >= 0 && !a.ws_slot) store_new_rows<KV, D, NW * 64>(a, part.slot, kvh, 1, s_new + (kFp8 ? kRaw : 0));
         }
     }
 }
