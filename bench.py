@@ -33,7 +33,7 @@ head) row, filled by the library's own quantising append; the step uses the *_fp
 points and the algorithmic bytes are 2 x kv_heads x (head_dim + 4) per attended token.
 With --beams W the decode is pa_decode_beams with groups of W consecutive sequences (the
 append is a separate pa_reshape_and_cache[_fp8] call); config 5's groups of 4 beams share a
-30720-token prefix. With --queries N the step appends N tokens per sequence and runs
+30720-token prefix, and its step uses pa_decode_beams with W = 4 unless --beams 0 is given. With --queries N the step appends N tokens per sequence and runs
 pa_multi_token_attention over them (metric: query tokens/s).
 """
 
@@ -654,8 +654,9 @@ def main() -> int:
                     help="pool elements: the workload's dtype, or 8-bit floats with a scale per row")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per replica instead of launching from Python")
-    ap.add_argument("--beams", type=int, default=0,
-                    help="decode with pa_decode_beams, sequences grouped by this many beams (append separate)")
+    ap.add_argument("--beams", type=int, default=None,
+                    help="decode with pa_decode_beams, sequences grouped by this many beams (append separate); "
+                         "config 5 defaults to its beam width (4), --beams 0 decodes with pa_decode_append")
     ap.add_argument("--unfused", action="store_true",
                     help="append with pa_reshape_and_cache and decode with pa_decode (two launches)")
     ap.add_argument("--queries", type=int, default=0,
@@ -743,6 +744,8 @@ def main() -> int:
     max_len = int(w.lens_after_append.max())
     P = args.partition_size
     W = max(0, args.window)
+    if args.beams is None:
+        args.beams = w.beams if args.config == 5 and W <= 0 else 0
     BW = max(0, args.beams)
     if BW and W > 0:
         print("--beams has no window", file=sys.stderr)

@@ -1,6 +1,6 @@
 // Grouped-query paged decode on the gfx950 matrix cores for 8-token blocks: a 16-row operand
-// tile then spans two blocks, so the kernel of pa_mfma_kernel.h looks up each row's block per
-// lane instead of once per tile. The block size trade-off (smaller blocks waste less memory,
+// tile then spans two blocks, so the kernel of pa_mfma_kernel.h looks up the block of each
+// tile row. The block size trade-off (smaller blocks waste less memory,
 // at more table lookups) is [BlockManager essay] §3.
 #include "pa_mfma_kernel.h"
 
@@ -16,15 +16,17 @@ template <typename T, typename KV, int D, int G>
 hipError_t launch_tdg(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     constexpr int NW = kSmallWaves;
     dim3 grid(num_kv_heads, batch, a.max_partitions);
-    // 16-bit rows of 128 dims: the tile's two blocks through one buffer (mode 2), which keeps
-    // two waves per SIMD; per-lane row addresses (mode 1) need the registers of a second wave
-    // there. Measured with 8 query heads per kv head (bf16): B = 128 at 2049 tokens 200
-    // against 216 us, B = 256 at 257 tokens 82 against 111 us, B = 32 at 2049 tokens 55
-    // against 54 us.
+    // 16-bit rows of 128 dims in a pool within 2 GiB: the tile's two blocks through one buffer
+    // (mode 2), which keeps two waves per SIMD; per-lane row addresses (mode 1) need the
+    // registers of a second wave there. Measured with 8 query heads per kv head (bf16): B = 128
+    // at 2049 tokens 200 against 216 us, B = 256 at 257 tokens 82 against 111 us, B = 32 at
+    // 2049 tokens 55 against 54 us.
     if constexpr (KV::kBytes == 2 && D == 128) {
-        hipLaunchKernelGGL((decode_mfma_kernel<T, KV, D, G, NW, true, false, false, 2>), grid, dim3(NW * 64), 0, stream,
-                           a);
-        return hipGetLastError();
+        if (mfma::pool_within_2gib(a)) {
+            hipLaunchKernelGGL((decode_mfma_kernel<T, KV, D, G, NW, true, false, false, 2>), grid, dim3(NW * 64), 0,
+                               stream, a);
+            return hipGetLastError();
+        }
     }
     hipLaunchKernelGGL((decode_mfma_kernel<T, KV, D, G, NW, true, false, false, 1>), grid, dim3(NW * 64), 0, stream,
                        a);

@@ -24,9 +24,11 @@
 //     B operand (exact: products with 1 and sums with 0); its fp32 output (4 tokens of one
 //     dim per lane) packs back to 16-bit without rounding and is the B operand of
 //     v_mfma_f32_16x16x32 for O += P V.
-//   * Everything else (length checks, block ids staged and checked in LDS, branch-free
-//     masked buffer loads that never touch padding, base-2 online softmax in fp32, wave and
-//     partition merge) is shared with the VALU path.
+//   * Everything else (length checks, block ids staged and checked in LDS, masked loads
+//     that never touch padding, base-2 online softmax in fp32, wave and partition merge) is
+//     shared with the VALU path. A row outside the attended range gets an out-of-range
+//     buffer offset, or in the per-lane-address mode for 8-token blocks no load under its
+//     lane mask, and is zero.
 //
 // 8-bit float pools (OCP E4M3 codes, a float32 scale per (token, kv head) row): a lane's
 // 16-byte load holds 16 codes, dims 64c' + 16g .. +15 of token row n (still 64 contiguous
@@ -149,12 +151,13 @@ struct MultiNanSink {
 // (cap = partition_size / block_size entries per beam) and validates the ids (a bad id
 // flags the beam and poisons its outputs or records of this partition, as the decode does).
 // After it s_blen[j] is beam j's length if it takes part in this partition, else <= t0;
-// ref is the beam that reads the most blocks and shared tells whether every other beam's
-// ids equal ref's over the blocks it reads (then one read of each block serves all beams).
+// ref is the beam that reads the most blocks; ncommon counts the partition's leading blocks
+// on which every beam that reads the block has ref's id (one read of each serves all beams),
+// the whole slice (cap) when no beam's ids differ from ref's.
 // Returns false (uniformly) when no beam of the group reaches the partition.
 template <typename T, int D, int G, int NT>
 __device__ bool beam_prologue(const DecodeArgs& a, int p, int kvh, int b0, int nb, int* s_bids, int* s_blen,
-                              int* s_bbad, Partition& part, int& ref, bool& shared) {
+                              int* s_bbad, Partition& part, int& ref, int& ncommon) {
     const int tid = threadIdx.x;
     const int P = a.partition_size;
     const int lbs = a.log2_block_size;
@@ -211,7 +214,9 @@ __device__ bool beam_prologue(const DecodeArgs& a, int p, int kvh, int b0, int n
     }
     if (tid < nb && s_bbad[tid] && a.err_flag) atomicOr(a.err_flag, PA_FLAG_BAD_BLOCK_ID);
     __syncthreads();
+    __shared__ int s_first;  // the first block (of the slice) where some beam leaves ref's ids
     if (tid < nb && s_bbad[tid]) s_blen[tid] = -1;
+    if (tid == 0) s_first = cap;
     __syncthreads();
     ref = -1;
     int end = t0;
@@ -223,15 +228,17 @@ __device__ bool beam_prologue(const DecodeArgs& a, int p, int kvh, int b0, int n
         }
     }
     if (ref < 0) return false;
-    int mismatch = 0;
+    int first = cap;
     for (int i = tid; i < nb * cap; i += NT) {
         const int j = i / cap;
         const int k = i - j * cap;
         const int L = s_blen[j];
         if (L <= t0 || j == ref) continue;
-        if (k < ((min(L, t0 + P) - 1) >> lbs) - j0 + 1 && s_bids[i] != s_bids[ref * cap + k]) mismatch = 1;
+        if (k < ((min(L, t0 + P) - 1) >> lbs) - j0 + 1 && s_bids[i] != s_bids[ref * cap + k]) first = min(first, k);
     }
-    shared = !block_any<NT>(mismatch);
+    if (first < cap) atomicMin(&s_first, first);
+    __syncthreads();
+    ncommon = s_first;
     part.nparts = 0;
     part.t0 = t0;
     part.rel_lo = 0;
@@ -252,17 +259,22 @@ __device__ bool beam_prologue(const DecodeArgs& a, int p, int kvh, int b0, int n
 // over the beams of group blockIdx.y (beam_prologue); a partition whose blocks all beams
 // share is streamed once for all of them, else once per beam with the other beams' columns
 // masked.
+// True when every block of the pool lies within 2 GiB of the pool's start, so one buffer
+// resource with 32-bit offsets reaches any two blocks (8-token-block mode 2).
+inline bool pool_within_2gib(const DecodeArgs& a) {
+    return (uint64_t)a.num_blocks * (uint64_t)a.block_stride <= 0x7fffffffull;
+}
+
 template <typename T, typename KV, int D, int G, int NW, bool kDoubleBuffer, bool kMulti = false,
           bool kBeams = false, int kSmallBlocks = 0>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallBlocks == 1 && D == 128 && (KV::kBytes == 2 || kMulti || kBeams) ? 1 : 2))) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(T::kBytes == 2, "matrix-core operands are 16-bit");
     static_assert(G >= 1 && G <= 16, "at most 16 query heads per kv head");
     static_assert(!(kMulti && kBeams), "one column mapping");
-    // 8-token blocks (kSmallBlocks != 0): a 16-row tile spans two blocks. Mode 1 addresses each
-    // row from its lane (a 64-bit address per lane: one wave per SIMD with 128 dims of 16-bit
-    // rows, and with 128 dims in the multi-token and beam-group modes). Mode 2 (16-bit pools)
-    // reads both blocks through one buffer when they lie within 2 GiB of each other, else the
-    // two 8-row halves under lane masks; it keeps two waves per SIMD.
+    // 8-token blocks (kSmallBlocks != 0): a 16-row tile spans two blocks. Mode 1 addresses
+    // each row from its lane (64-bit addresses; 16-bit rows of 128 dims then need the registers
+    // of a second wave). Mode 2 (16-bit pools lying within 2 GiB) reads both blocks through one
+    // buffer and keeps two waves per SIMD.
     static_assert(kSmallBlocks == 0 || D <= 128, "8-token blocks: head_dim up to 128");
     static_assert(kSmallBlocks != 2 || KV::kBytes == 2, "mode 2: 16-bit pools");
     constexpr int NCOL = (kMulti || kBeams) ? 16 : G;  // columns whose results this workgroup keeps
@@ -356,10 +368,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
         }
     }
     Partition part;
-    int bref = 0;        // beam groups: the beam whose table is streamed when all agree
-    bool bshared = true;
+    int bref = 0;     // beam groups: the beam whose table is streamed over the shared blocks
+    int bcommon = 0;  // beam groups: leading blocks of the partition every beam shares
     if constexpr (kBeams) {
-        if (!beam_prologue<T, D, G, NW * 64>(a, p, kvh, b0, nb, s_ids, s_blen, s_bbad, part, bref, bshared)) return;
+        if (!beam_prologue<T, D, G, NW * 64>(a, p, kvh, b0, nb, s_ids, s_blen, s_bbad, part, bref, bcommon)) return;
     } else if constexpr (kMulti) {
         if (!partition_prologue_sink<T, D, NW * 64>(a, p, b, max(nq, 1), MultiNanSink<T, D, G>{a, q0, nq, kvh, ct},
                                                     s_ids, part))
@@ -378,8 +390,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
         ntok = min(ntok, tile_end);
         lim_col = col_valid ? min(ntok, first_pos + qi + 1 - part.t0) : 0;
     }
-    const int rel_lo = part.rel_lo;
-    const int c0 = rel_lo / kChunk;  // first chunk holding an attended token
+    int rel_lo = part.rel_lo;
+    int c0 = rel_lo / kChunk;  // first chunk holding an attended token
     // tokens every column of the wave sees: ntok for the decode; for several queries the
     // tile's first query's limit when all 16 columns are valid (else the masked path)
     int lim_wave = ntok;
@@ -390,15 +402,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
     // the table slice streamed: the sequence's, or in a beam group the reference beam's
     const int* ids = s_ids;
     const int bcap = kBeams ? a.partition_size >> a.log2_block_size : 0;
-    // beam groups: a beam's column sees its own tokens of the partition; the wave's fast
-    // path needs the shortest beam of the partition
+    // beam groups: a beam's column sees its own tokens of the partition
     auto beam_end = [&](int j) { return min(s_blen[j], part.t0 + a.partition_size) - part.t0; };
-    if constexpr (kBeams) {
-        ids = s_ids + bref * bcap;
-        lim_col = col_valid && s_blen[n / G] > part.t0 ? beam_end(n / G) : 0;
-        for (int j = 0; j < nb; ++j)
-            if (s_blen[j] > part.t0) lim_wave = min(lim_wave, beam_end(j));
-    }
 
     // Identity B operand of the 16x16x16 transpose: k-slot (g, i) is 1 in column 4g + i.
     u32x2 ident;
@@ -422,68 +427,56 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
         for (int t = 0; t < 2; ++t) {
             const int rel = (c0 + it * NW + wave) * kChunk + 16 * t;  // wave-uniform
             if constexpr (kSmallBlocks == 1) {
-                // rows 0-7 and 8-15 of a tile lie in two blocks: each lane looks up the block
-                // of its own row. A row past the partition reads the same offset in its first
-                // block (allocated memory; its V row is cleared and its score masked before
-                // use), so the loads need no lane masks.
+                // 8-token blocks, per-lane addresses: rows 0-7 and 8-15 of the tile lie in two
+                // blocks, and each lane looks up the block of its own row. A row outside
+                // [rel_lo, ntok) reads the partition's first attended row instead (a valid
+                // row whose line the workgroup reads anyway, never a padding slot); its score
+                // is masked, so its weight is 0 on finite values. The loads take no branch, so
+                // the waits of the double buffer stay exact.
                 const int tok = rel + n;
-                const int lid = ids[(tok < ntok ? tok : 0) >> lbs];
-                const size_t row = (size_t)lid * block_bytes + (size_t)kvh * head_bytes +
-                                   (size_t)((tok & (bs - 1)) * D * KV::kBytes) + seg;
+                const bool live = tok < ntok && tok >= rel_lo;
+                const int rt = live ? tok : rel_lo;
+                const size_t row = (size_t)ids[rt >> lbs] * block_bytes + (size_t)kvh * head_bytes +
+                                   (size_t)((rt & (bs - 1)) * D * KV::kBytes) + seg;
 #pragma unroll
                 for (int c = 0; c < NL; ++c) {
                     kk[t][c] = load16(kpool + row + 64 * c);
                     vv[t][c] = load16(vpool + row + 64 * c);
                 }
+                if constexpr (kFp8) {
+                    // scales of tokens rel + 4g .. +3 (one aligned 16-byte word of one block);
+                    // a word with none of the four attended reads the word of the first
+                    // attended token instead, and scales of unattended tokens are replaced by
+                    // 0 before use
+                    const int tok4 = rel + 4 * g;
+                    const int st = tok4 < ntok && tok4 + 3 >= rel_lo ? tok4 : (rel_lo & ~3);
+                    const size_t srow = (((size_t)ids[st >> lbs] * a.num_kv_heads + kvh) << lbs) + (st & (bs - 1));
+                    ks[t] = load16(a.k_scale + srow);
+                    vs[t] = load16(a.v_scale + srow);
+                }
+                continue;
             } else if constexpr (kSmallBlocks == 2) {
-                // the tile's two blocks (wave-uniform); a half past the partition reads the
-                // first block again, cleared or masked before use as in mode 1
+                // 8-token blocks, 16-bit pools, one buffer over the tile's two blocks (the host
+                // picks this mode only when the whole pool lies within 2 GiB, so any two
+                // blocks do): 32-bit offsets, and a row outside [rel_lo, ntok) gets an
+                // out-of-range offset and reads zeros without a memory access.
                 const int j0 = rel < ntok ? rel >> lbs : 0;
                 const int j1 = rel + 8 < ntok ? (rel >> lbs) + 1 : j0;
                 const int id0 = __builtin_amdgcn_readfirstlane(ids[j0]);
                 const int id1 = __builtin_amdgcn_readfirstlane(ids[j1]);
-                const uint32_t o8 = (uint32_t)((n & 7) * D * KV::kBytes) + seg;
+                const bool live = rel + n < ntok && rel + n >= rel_lo;
                 const int lo = min(id0, id1);
-                const size_t span = (size_t)(max(id0, id1) - lo) * block_bytes;
-                if (span <= (size_t)(0x7fffffffu - slab_bytes)) {
-                    // both blocks within one 2 GiB window: one buffer over them, 32-bit offsets
-                    const size_t base = (size_t)lo * block_bytes + (size_t)kvh * head_bytes;
-                    const uint32_t nrec = (uint32_t)span + slab_bytes;
-                    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + base, nrec);
-                    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + base, nrec);
-                    const uint32_t off = (uint32_t)((size_t)((n < 8 ? id0 : id1) - lo) * block_bytes) + o8;
+                const size_t base = (size_t)lo * block_bytes + (size_t)kvh * head_bytes;
+                const uint32_t nrec = (uint32_t)((size_t)(max(id0, id1) - lo) * block_bytes) + slab_bytes;
+                const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + base, nrec);
+                const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + base, nrec);
+                const uint32_t off = live ? (uint32_t)((size_t)((n < 8 ? id0 : id1) - lo) * block_bytes) +
+                                                (uint32_t)((n & 7) * D * KV::kBytes) + seg
+                                          : kOutOfRange;
 #pragma unroll
-                    for (int c = 0; c < NL; ++c) {
-                        kk[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rk, off + 64 * c);
-                        vv[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rv, off + 64 * c);
-                    }
-                } else if (n < 8) {
-                    const size_t s0 = (size_t)id0 * block_bytes + (size_t)kvh * head_bytes;
-                    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + s0, slab_bytes);
-                    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + s0, slab_bytes);
-#pragma unroll
-                    for (int c = 0; c < NL; ++c) {
-                        kk[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rk, o8 + 64 * c);
-                        vv[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rv, o8 + 64 * c);
-                    }
-                } else {
-                    const size_t s1 = (size_t)id1 * block_bytes + (size_t)kvh * head_bytes;
-                    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + s1, slab_bytes);
-                    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + s1, slab_bytes);
-#pragma unroll
-                    for (int c = 0; c < NL; ++c) {
-                        kk[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rk, o8 + 64 * c);
-                        vv[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rv, o8 + 64 * c);
-                    }
-                }
-            }
-            if constexpr (kSmallBlocks != 0) {
-                if constexpr (kFp8) {  // scales of tokens rel + 4g .. +3, one block
-                    const int tok4 = rel + 4 * g;
-                    const int sid = ids[(tok4 < ntok ? tok4 : 0) >> lbs];
-                    const size_t srow = (((size_t)sid * a.num_kv_heads + kvh) << lbs) + (tok4 & (bs - 1));
-                    ks[t] = load16(a.k_scale + srow);
-                    vs[t] = load16(a.v_scale + srow);
+                for (int c = 0; c < NL; ++c) {
+                    kk[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rk, off + 64 * c);
+                    vv[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rv, off + 64 * c);
                 }
                 continue;
             }
@@ -507,8 +500,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
                 vv[t][c] = buffer_load16<PA_MFMA_LOAD_POLICY>(rv, o);
             }
             if constexpr (kFp8) {
+                // scales of tokens rel + 4g .. +3 (the rows of this lane's scores): one aligned
+                // 16-byte word, not read when none of the four is attended
                 const size_t srow = ((size_t)id * a.num_kv_heads + kvh) << lbs;  // this slab's scales
-                const uint32_t so = rel < ntok ? (uint32_t)(((rel & (bs - 1)) + 4 * g) * 4) : kOutOfRange;
+                const int tok4 = rel + 4 * g;
+                const uint32_t so = tok4 < ntok && tok4 + 3 >= rel_lo ? (uint32_t)(((rel & (bs - 1)) + 4 * g) * 4)
+                                                                       : kOutOfRange;
                 ks[t] = buffer_load16<PA_MFMA_LOAD_POLICY>(make_rsrc(a.k_scale + srow, (uint32_t)bs * 4), so);
                 vs[t] = buffer_load16<PA_MFMA_LOAD_POLICY>(make_rsrc(a.v_scale + srow, (uint32_t)bs * 4), so);
             }
@@ -548,20 +545,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
         const int rel0 = (c0 + it * NW + wave) * kChunk;
         restage(kk);
         restage(vv);
-        if constexpr (kSmallBlocks != 0) {
-            // rows outside [rel_lo, ntok) were read from other slots: clear their V rows (their
-            // weights are 0, and 0 times a non-finite value is not)
-            if (!(rel0 >= rel_lo && rel0 + kChunk <= ntok)) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int tok = rel0 + 16 * t + n;
-                    if (tok >= ntok || tok < rel_lo) {
-#pragma unroll
-                        for (int c = 0; c < NL; ++c) vv[t][c] = u32x4{0u, 0u, 0u, 0u};
-                    }
-                }
-            }
-        }
         if constexpr (kAppendable) {
             if (npos >= 0) {  // fused append: the new token's rows come from s_new (wave-uniform test)
 #pragma unroll
@@ -702,21 +685,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
     };
 
     u32x4 ka[2][NL], va[2][NL], ksa[2], vsa[2];
-    // One pass over the partition; a beam group whose beams' blocks differ takes one pass per
-    // beam over its own blocks, with the other beams' columns seeing nothing.
-    const int npasses = kBeams && !bshared ? nb : 1;
-    if constexpr (kBeams) {
-        if (!bshared) lim_wave = 0;
-    }
+    // One pass over the partition. A beam group takes pass 0 over the leading blocks all its
+    // beams share (read once, through the reference beam's ids, for every beam's columns; the
+    // wave's fast path needs the shortest beam), then pass 1 + j over beam j's tokens after
+    // them (its own blocks), the other beams' columns seeing nothing.
+    const int npasses = kBeams ? 1 + nb : 1;
     for (int pass = 0; pass < npasses; ++pass) {
     if constexpr (kBeams) {
-        if (!bshared) {
-            if (s_blen[pass] <= part.t0) continue;
-            ids = s_ids + pass * bcap;
-            ntok = beam_end(pass);
-            niters = (ntok + kChunk * NW - 1) / (kChunk * NW);
-            lim_col = col_valid && n / G == pass ? ntok : 0;
+        const int cend = min(bcommon << lbs, part.ntok);  // tokens in the shared blocks
+        if (pass == 0) {
+            if (cend == 0) continue;
+            ids = s_ids + bref * bcap;
+            ntok = cend;
+            rel_lo = 0;
+            lim_col = col_valid && s_blen[n / G] > part.t0 ? min(beam_end(n / G), cend) : 0;
+            lim_wave = cend;
+            for (int j = 0; j < nb; ++j)
+                if (s_blen[j] > part.t0) lim_wave = min(lim_wave, beam_end(j));
+        } else {
+            const int j = pass - 1;
+            if (s_blen[j] <= part.t0 || beam_end(j) <= cend) continue;
+            ids = s_ids + j * bcap;
+            ntok = beam_end(j);
+            rel_lo = cend;
+            lim_col = col_valid && n / G == j ? ntok : 0;
+            lim_wave = 0;
         }
+        c0 = rel_lo / kChunk;
+        niters = (ntok - c0 * kChunk + kChunk * NW - 1) / (kChunk * NW);
     }
     if constexpr (kDoubleBuffer) {
         u32x4 kb[2][NL], vb[2][NL], ksb[2], vsb[2];

@@ -14,9 +14,16 @@ template <typename T, typename KV, int D, int G>
 hipError_t launch_tdg(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     constexpr int NW = kSmallWaves;
     dim3 grid(num_kv_heads, batch * a.col_tiles, a.max_partitions);
-    // 16-bit rows of 128 dims: one buffer over the tile's two blocks (mode 2, two waves per SIMD)
-    constexpr int kMode = KV::kBytes == 2 && D == 128 ? 2 : 1;
-    hipLaunchKernelGGL((mfma::decode_mfma_kernel<T, KV, D, G, NW, true, true, false, kMode>), grid, dim3(NW * 64), 0,
+    // 16-bit rows of 128 dims in a pool within 2 GiB: one buffer over the tile's two blocks
+    // (mode 2, two waves per SIMD); else per-lane row addresses (mode 1)
+    if constexpr (KV::kBytes == 2 && D == 128) {
+        if (mfma::pool_within_2gib(a)) {
+            hipLaunchKernelGGL((mfma::decode_mfma_kernel<T, KV, D, G, NW, true, true, false, 2>), grid, dim3(NW * 64), 0,
+                               stream, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((mfma::decode_mfma_kernel<T, KV, D, G, NW, true, true, false, 1>), grid, dim3(NW * 64), 0,
                        stream, a);
     return hipGetLastError();
 }
