@@ -33,6 +33,10 @@ namespace valu {
 constexpr int kWaves = kDecodeWaves;
 constexpr int kThreads = kDecodeThreads;
 
+// Lazy rescaling of the online softmax (8-bit pools): the running reference moves only when a
+// score exceeds it by more than this (base-2 exponent), so weights stay below 2^8 in fp32.
+constexpr float kLazyRescale = 8.f;
+
 // KV is the pool's element type: a lane's 16-byte load holds E elements of a token row.
 template <typename KV, int D>
 struct RowShape {
@@ -146,29 +150,74 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
                 s[g][u] = valid ? d * a.scale_log2 : -INFINITY;
             }
         }
-        float vf[UNROLL][E];
+        if constexpr (kScaled) {
+            // 8-bit pools: m[g] is a reference the state is scaled to, moved only when a score
+            // passes it by more than kLazyRescale (base 2), so every weight 2^(s - m) stays
+            // below 2^kLazyRescale and the 16 accumulators of a lane are rescaled rarely, not
+            // once per row group. The rows are then folded in one at a time, each V row
+            // widened just before its FMAs (16 values a row: widening all UNROLL rows first
+            // would hold UNROLL x 16 more registers).
+            float ms[G];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) unpack(KV{}, vv[u], vf[u]);
+            for (int g = 0; g < G; ++g) {
+                float cm = s[g][0];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float cm = s[g][0];
+                for (int u = 1; u < UNROLL; ++u) cm = fmaxf(cm, s[g][u]);
+                if (cm > m[g] + kLazyRescale) {  // -inf + k is -inf: the first finite score moves it
+                    const float alpha = fast_exp2(m[g] - cm);
+                    m[g] = cm;
+                    l[g] *= alpha;
 #pragma unroll
-            for (int u = 1; u < UNROLL; ++u) cm = fmaxf(cm, s[g][u]);
-            const float mn = fmaxf(m[g], cm);
-            const float ms = (mn == -INFINITY) ? 0.f : mn;
-            const float alpha = fast_exp2(m[g] - ms);
-            m[g] = mn;
-            l[g] *= alpha;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
+                    for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
+                }
+                ms[g] = (m[g] == -INFINITY) ? 0.f : m[g];
+            }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
-                const float pr = fast_exp2(s[g][u] - ms);
-                l[g] += pr;
-                float wv = pr;
-                if constexpr (kScaled) wv *= vsc[u];
+                float wv[G];
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[g][e] = fmaf(wv, vf[u][e], acc[g][e]);
+                for (int g = 0; g < G; ++g) {
+                    const float pr = fast_exp2(s[g][u] - ms[g]);
+                    l[g] += pr;
+                    wv[g] = pr * vsc[u];
+                }
+                // two codes at a time: each widened pair feeds its FMAs at once
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vv[u][w], 1.f, false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vv[u][w], 1.f, true);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        acc[g][4 * w] = fmaf(wv[g], lo.x, acc[g][4 * w]);
+                        acc[g][4 * w + 1] = fmaf(wv[g], lo.y, acc[g][4 * w + 1]);
+                        acc[g][4 * w + 2] = fmaf(wv[g], hi.x, acc[g][4 * w + 2]);
+                        acc[g][4 * w + 3] = fmaf(wv[g], hi.y, acc[g][4 * w + 3]);
+                    }
+                }
+            }
+        } else {
+            float vf[UNROLL][E];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) unpack(KV{}, vv[u], vf[u]);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float cm = s[g][0];
+#pragma unroll
+                for (int u = 1; u < UNROLL; ++u) cm = fmaxf(cm, s[g][u]);
+                const float mn = fmaxf(m[g], cm);
+                const float ms = (mn == -INFINITY) ? 0.f : mn;
+                const float alpha = fast_exp2(m[g] - ms);
+                m[g] = mn;
+                l[g] *= alpha;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    const float pr = fast_exp2(s[g][u] - ms);
+                    l[g] += pr;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pr, vf[u][e], acc[g][e]);
+                }
             }
         }
     };
@@ -423,10 +472,16 @@ hipError_t launch_decode_tgdu(const DecodeArgs& a, int batch, int num_kv_heads, 
 // Groups per iteration per wave: 4 for long partitions (and for head mode, where one wave
 // streams a whole partition); 2 for short split-mode partitions (<= 384 tokens), where a
 // 4-deep iteration would leave most lanes idle and the smaller register footprint lets 8
-// waves share a SIMD. Grouped-query heads multiply the registers per group.
+// waves share a SIMD. Grouped-query heads multiply the registers per group. 8-bit pools
+// take 1 everywhere: a lane's 16-byte load is 16 codes (1 KiB per wave load is 8 rows, as
+// many tokens as 2 groups of 16-bit rows), and at 72 VGPRs 7 waves share a SIMD, against
+// 3 with 4 groups (145 VGPRs). Measured with lazy rescaling: config 3 (median 87) 83 against
+// 115 us, median 23 42 against 56 us, config 2 50 against 58 us.
 template <typename T, typename KV, int D, int G>
 hipError_t launch_decode_tgd(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
-    if constexpr (G <= 2) {
+    if constexpr (G <= 2 && std::is_same_v<KV, FP8>) {
+        return launch_decode_tgdu<T, KV, D, G, 1>(a, batch, num_kv_heads, stream);
+    } else if constexpr (G <= 2) {
         if (a.partition_size > PA_HEAD_MODE_MAX_P && a.partition_size <= 384)
             return launch_decode_tgdu<T, KV, D, G, 2>(a, batch, num_kv_heads, stream);
         return launch_decode_tgdu<T, KV, D, G, 4>(a, batch, num_kv_heads, stream);
