@@ -885,7 +885,8 @@ def main() -> int:
         "decode_kernel_ms": round(dec_avg, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(cfg["workload"], path)},
+                     "traffic": recorded_traffic(cfg["workload"], path),
+                     "algorithmic_bytes": int(roof_bytes)},
         "kernel_source_hash": kernel_source_hash(path),
         "decode_kernel": path,
         "decode_launch_us_per_launch_events": _percentiles(dec_each),

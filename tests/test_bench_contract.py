@@ -54,6 +54,9 @@ def test_bench_default_line():
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert 0 < roof["frac"] < 1 and roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-4)
     assert roof["traffic"] is None or (isinstance(roof["traffic"], int) and roof["traffic"] > 0)
+    # achieved is the algorithmic bytes of one decode launch over its average duration
+    assert roof["algorithmic_bytes"] == step_bytes
+    assert roof["achieved"] * d["decode_kernel_ms"] * 1e6 == pytest.approx(step_bytes, rel=2e-3)
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["unit"]
     assert isinstance(cpu["sample"], str) and cpu["sample"]
