@@ -240,10 +240,13 @@ int32_t pa_decode_partition_size(const pa_cache_desc_t* cache, int32_t batch, in
         int64_t parts = wgs >= 256 ? 1 : ceil_div(256, wgs > 0 ? wgs : 1);
         if (parts < ceil_div(max_context_len, 4096)) parts = ceil_div(max_context_len, 4096);
         P = ceil_div(ceil_div(max_context_len, parts), bs) * bs;
-    } else if (max_context_len <= 1024 && wgs >= 128) {
+    } else if (max_context_len <= (is_fp8(cache) ? 2048 : 1024) && wgs >= 128) {
         // VALU path, short contexts and at least half a workgroup per compute unit: no split
         // (the reduce launch costs more than the extra parallelism gains; equal lengths of
         // 600 tokens at 8 x 32 heads: 16.0 us whole against 18.6 us in 256-token partitions).
+        // 8-bit rows stream in half the time, so contexts twice as long stay whole (config 3
+        // at median 87, lengths up to 1197: 85.7 against 90.8 us at P = 512; 16-bit pools
+        // there: 126.9 against 124.1 us).
         P = whole;
     } else {
         // VALU path: 512-token partitions, shortened until the launch has about 2048
