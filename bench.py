@@ -124,10 +124,10 @@ def recorded_mfma_busy(workload: str, path: str):
     return None
 
 
-def _workload(cfg: int, block_size: int | None, median: float | None):
+def _workload(cfg: int, block_size: int | None, median: float | None, contiguous: bool = False):
     from workloads import config_workload
 
-    return config_workload(cfg, seed=0, block_size=block_size, median=median)
+    return config_workload(cfg, seed=0, block_size=block_size, median=median, contiguous=contiguous)
 
 
 def padding_waste_pct(lens, block_size: int) -> float:
@@ -657,6 +657,9 @@ def main() -> int:
     ap.add_argument("--beams", type=int, default=None,
                     help="decode with pa_decode_beams, sequences grouped by this many beams (append separate); "
                          "config 5 defaults to its beam width (4), --beams 0 decodes with pa_decode_append")
+    ap.add_argument("--contiguous-pool", action="store_true",
+                    help="configs 2-4: each sequence's blocks consecutive in id order (same lengths and contents), "
+                         "to measure what scattered blocks and their table lookups cost")
     ap.add_argument("--unfused", action="store_true",
                     help="append with pa_reshape_and_cache and decode with pa_decode (two launches)")
     ap.add_argument("--queries", type=int, default=0,
@@ -691,6 +694,9 @@ def main() -> int:
         return 2
     if args.config == 3 and args.median is None:
         args.median = 87
+    if args.contiguous_pool and args.config not in (2, 3, 4):
+        print("--contiguous-pool applies to configs 2-4", file=sys.stderr)
+        return 2
 
     import torch
 
@@ -709,7 +715,7 @@ def main() -> int:
         if not args.no_cpu_baseline:
             host_sample = host_subset(w, [0], range(4 if args.kv == "fp8" else w.num_kv_heads))
     else:
-        w = _workload(args.config, args.block_size, args.median)
+        w = _workload(args.config, args.block_size, args.median, args.contiguous_pool)
         t = w.to_device(dev)
         _progress(f"{w.name}: workload on the device")
     fp8 = args.kv == "fp8"
@@ -898,7 +904,7 @@ def main() -> int:
         result["roofline"]["ceiling"] = ceil["gbs"]
         result["roofline"]["frac_of_ceiling"] = round(achieved / ceil["gbs"], 4)
         result["stream_read_ceiling"] = ceil
-    plain = not (fp8 or W or BW or args.unfused or args.graph or NL > 1)
+    plain = not (fp8 or W or BW or args.unfused or args.graph or NL > 1 or args.contiguous_pool)
     if args.config == 3 and plain and not args.no_sweep:
         del kps, vps
         torch.cuda.empty_cache()

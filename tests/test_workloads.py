@@ -111,3 +111,21 @@ def test_device_twin_matches_host_build():
     a = device_paged("t", 30, 0, lens, 16, 4, 4, 64, "f16", "cpu", contents=c, uploaded=up).tensors
     b = build_paged("t", 30, 0, lens, 16, 4, 4, 64, "f16").to_device("cpu")
     assert torch.equal(a["k_pool"].view(torch.int16), b["k_pool"].view(torch.int16))
+
+
+def test_contiguous_pool_is_a_relabelling():
+    """The contiguous variant gives each sequence consecutive ids in order and holds the same
+    tokens: the oracle's decode is bitwise that of the shuffled pool."""
+    import oracle
+
+    a = config_workload(3, median=23, block_size=16, batch=8, heads=2)
+    b = config_workload(3, median=23, block_size=16, batch=8, heads=2, contiguous=True)
+    assert b.name.endswith("-contiguous") and np.array_equal(a.context_lens, b.context_lens)
+    nxt = 0
+    for row, L in zip(b.block_table, b.lens_after_append):
+        n = -(-int(L) // 16)
+        assert np.array_equal(row[:n], np.arange(nxt, nxt + n)) and np.all(row[n:] == -1)
+        nxt += n
+    ra = oracle.paged_decode(a.q, a.k_pool, a.v_pool, a.block_table, a.context_lens, a.scale)
+    rb = oracle.paged_decode(b.q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale)
+    assert np.array_equal(ra, rb)

@@ -107,12 +107,14 @@ class PagedWorkload:
 
 def _allocate_tables(rng_layout: np.random.Generator, lens: np.ndarray, bs: int,
                      num_blocks: int | None, spare: float, max_blocks_per_seq: int | None,
-                     append: bool):
+                     append: bool, contiguous: bool = False):
     """Hand out physical ids from one seeded permutation of the pool.
 
     Every sequence first receives the blocks its current tokens occupy (sequence 0 first),
     then the sequences whose append starts a new block receive one more id each, taken
-    from the ids that remain.
+    from the ids that remain. ``contiguous``: ids in order instead, each sequence's blocks
+    (its append block included) consecutive, as if the cache were one dense array per
+    sequence; for measuring what scattered blocks cost.
     """
     need_now = (lens + bs - 1) // bs
     need_after = (lens + (1 if append else 0) + bs - 1) // bs
@@ -124,6 +126,11 @@ def _allocate_tables(rng_layout: np.random.Generator, lens: np.ndarray, bs: int,
     mbs = int(need_after.max()) if max_blocks_per_seq is None else int(max_blocks_per_seq)
     perm = rng_layout.permutation(num_blocks).astype(np.int32)
     table = np.full((len(lens), mbs), -1, np.int32)
+    if contiguous:
+        first = np.concatenate([[0], np.cumsum(need_after)[:-1]]).astype(np.int32)
+        for b, n in enumerate(need_after):
+            table[b, :n] = first[b] + np.arange(n, dtype=np.int32)
+        return table, num_blocks
     cur = 0
     for b, n in enumerate(need_now):
         table[b, :n] = perm[cur:cur + n]
@@ -165,14 +172,14 @@ def build_paged(name: str, cfg_id: int, seed: int, lens: np.ndarray, block_size:
                 num_kv_heads: int, num_q_heads: int, head_dim: int, dtype: str,
                 scale: float | None = None, std: float = 1.0, num_blocks: int | None = None,
                 spare: float = 0.10, max_blocks_per_seq: int | None = None,
-                append: bool = True, contents=None) -> PagedWorkload:
+                append: bool = True, contents=None, contiguous: bool = False) -> PagedWorkload:
     lens = np.asarray(lens, np.int32)
     B = len(lens)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     rng_l = np.random.default_rng([cfg_id, seed, 1, block_size])
     table, nb = _allocate_tables(rng_l, lens, block_size, num_blocks, spare,
-                                 max_blocks_per_seq, append)
+                                 max_blocks_per_seq, append, contiguous)
     # Contents: q, then L+1 contiguous K rows per sequence, then the same for V.
     if contents is None:
         contents = paged_contents(cfg_id, seed, lens, num_kv_heads, num_q_heads, head_dim, dtype, std)
@@ -200,11 +207,13 @@ def build_paged(name: str, cfg_id: int, seed: int, lens: np.ndarray, block_size:
 
 def config_workload(cfg: int, seed: int = 0, *, block_size: int | None = None,
                     median: float | None = None, batch: int | None = None,
-                    heads: int | None = None, sigma: float = 1.0) -> PagedWorkload:
+                    heads: int | None = None, sigma: float = 1.0,
+                    contiguous: bool = False) -> PagedWorkload:
     """The five seeded synthetic workloads (configs 1-4 here; 5 lives in ``longctx``).
 
     ``batch``/``heads`` shrink a configuration for quick tests while keeping its dtype,
-    head_dim, block size and length distribution.
+    head_dim, block size and length distribution. ``contiguous`` places each sequence's
+    blocks consecutively in id order (same lengths and contents; name suffix -contiguous).
     """
     rng_len = np.random.default_rng([cfg, seed, 2])
     if cfg == 1:
@@ -215,23 +224,23 @@ def config_workload(cfg: int, seed: int = 0, *, block_size: int | None = None,
         B = batch or 64
         H = heads or 32
         lens = rng_len.integers(450, 521, size=64).astype(np.int32)[:B]
-        return build_paged("cfg2-f16-mha", 2, seed, lens, block_size or 16, H, H, 128, "f16",
-                           std=0.5)
+        return build_paged("cfg2-f16-mha" + ("-contiguous" if contiguous else ""), 2, seed, lens,
+                           block_size or 16, H, H, 128, "f16", std=0.5, contiguous=contiguous)
     if cfg == 3:
         B = batch or 256
         H = heads or 32
         med = median or 87
         lens = lognormal_lengths(rng_len, 256, med, sigma)[:B]
         bs = block_size or 16
-        return build_paged(f"cfg3-f16-longtail-med{med:g}-bs{bs}", 3 if med == 87 else 30,
-                           seed, lens, bs, H, H, 128, "f16")
+        return build_paged(f"cfg3-f16-longtail-med{med:g}-bs{bs}" + ("-contiguous" if contiguous else ""),
+                           3 if med == 87 else 30, seed, lens, bs, H, H, 128, "f16", contiguous=contiguous)
     if cfg == 4:
         B = batch or 32
         hkv = heads or 8
         lens = np.full(B, 2048, np.int32)
         bs = block_size or 16
-        return build_paged(f"cfg4-bf16-gqa-bs{bs}", 4, seed, lens, bs, hkv, hkv * 8, 128,
-                           "bf16")
+        return build_paged(f"cfg4-bf16-gqa-bs{bs}" + ("-contiguous" if contiguous else ""), 4, seed, lens, bs,
+                           hkv, hkv * 8, 128, "bf16", contiguous=contiguous)
     raise ValueError(f"unknown config {cfg}")
 
 
