@@ -22,7 +22,8 @@ inside every step about 7 us to the step.
 The default workload is the long-tail block-size sweep's median-87, 16-token-block case
 (256 sequences, 32 heads, head_dim 128, fp16). With it the line also carries `sweep`: the
 fused step at medians 87 and 23 and block sizes 8, 16, 32 and 64, each with its decode
-launch time, GB/s and share of the 8 TB/s roofline. `roofline.ceiling` is the streaming-read
+launch time, GB/s and share of the 8 TB/s roofline, and `config1`: the tiny fp32 workload's
+step, decode launch and roofline share, with its own oracle baseline. `roofline.ceiling` is the streaming-read
 rate this GPU reaches with the library's read kernel (pa_measure_stream_read over 4 GiB),
 and `*_per_launch_events` give the median, p10 and p90 of launches timed one by one.
 
@@ -456,6 +457,47 @@ def _sweep_config3(args, dev, medians=(87, 23), block_sizes=(8, 16, 32, 64)) -> 
     return {"workload": "cfg3-f16-longtail, fused step (append + decode), cold replicas",
             "cases": cases, "worst": {"case": worst, "frac": cases[worst]["frac"]},
             "all_at_least_70pct": all(c["frac"] >= 0.70 for c in cases.values())}
+
+
+def _config1_line(args, dev) -> dict:
+    """Config 1, the tiny fp32 workload (4 sequences, 1.3 MB of K+V): the fused step and its
+    decode launch timed as the main line is, the launch's share of the 8 TB/s roofline, and
+    the oracle on the host (a few seconds). At this size a launch is its fixed costs."""
+    import torch
+
+    from paged_kv_cache_indexed_amd import _lib, ops
+
+    w = _workload(1, None, None)
+    t = w.to_device(dev)
+    pool_bytes = 2 * t["k_pool"].numel() * t["k_pool"].element_size()
+    R = max(2, math.ceil(args.replica_bytes / pool_bytes))
+    kps = [t["k_pool"]] + [t["k_pool"].clone() for _ in range(R - 1)]
+    vps = [t["v_pool"]] + [t["v_pool"].clone() for _ in range(R - 1)]
+    lens = t["lens_after"]
+    max_len = int(w.lens_after_append.max())
+    ws = ops.workspace_for(t["k_pool"], w.batch, w.num_q_heads, max_len, 0)
+    out = torch.empty_like(t["q"])
+
+    def step(i):
+        ops.decode_append(t["q"], kps[i % R], vps[i % R], t["block_table"], lens, max_len, w.scale,
+                          t["new_key"], t["new_value"], t["slot_mapping"], out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    wall = _timed(step, args.warmup, args.steps)
+    dec = _event_pass(step, args.warmup + args.steps, args.steps)
+    kv = 2 * w.num_kv_heads * w.head_dim * 4 * int(w.lens_after_append.sum())
+    gbs = kv / (dec * 1e-3) / 1e9
+    _progress(f"config 1: decode {dec * 1e3:.1f} us")
+    line = {"workload": w.name, "decode_launch_us": round(dec * 1e3, 2), "decode_gbs": round(gbs, 2),
+            "frac": round(gbs / HBM_PEAK_GBS, 5), "step_us": round(wall * 1e6 / args.steps, 2),
+            "kv_bytes": kv, "decode_tokens_per_s": round(w.batch / wall * args.steps, 1), "replicas": R,
+            "partition_size": _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch,
+                                                            w.num_q_heads, max_len, 0)}
+    del kps, vps
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = _cpu_baseline(w, min(3.0, args.cpu_budget))
+    return line
 
 
 def _event_pass(launch, first: int, steps: int) -> float:
@@ -909,6 +951,7 @@ def main() -> int:
         del kps, vps
         torch.cuda.empty_cache()
         result["sweep"] = _sweep_config3(args, dev)
+        result["config1"] = _config1_line(args, dev)
     if path == "mfma":
         result["mfma_busy_pct"] = recorded_mfma_busy(cfg["workload"], path)
     if not args.no_cpu_baseline:
