@@ -26,6 +26,9 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     const int hpw = (a.num_q_heads + (int)gridDim.x - 1) / (int)gridDim.x;
     const int h0 = blockIdx.x * hpw;
     const int h1 = min(h0 + hpw, a.num_q_heads);
+    // the length is read with the slot and the first rows: read after the row stores (which
+    // the compiler cannot prove leave it alone), it would wait for them to be acknowledged
+    const int L = a.context_lens[b];
     if (a.ws_slot) {
         constexpr int kRowVecs = D * T::kBytes / 16;
         const int group = a.num_q_heads / a.num_kv_heads;
@@ -52,7 +55,6 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
             for (int i = tid + kReduceThreads; i < nvec; i += kReduceThreads) store16(dst(i), load16(src(i)));
         }
     }
-    const int L = a.context_lens[b];
     if (L <= 0 || L > a.max_context_len || (L - 1) >> a.log2_block_size >= a.max_blocks_per_seq) return;
     const int nparts = (L - partition_base(a, L) + a.partition_size - 1) / a.partition_size;
     if (nparts <= 1) return;
