@@ -22,10 +22,14 @@ inside every step about 7 us to the step.
 The default workload is the long-tail block-size sweep's median-87, 16-token-block case
 (256 sequences, 32 heads, head_dim 128, fp16). With it the line also carries `sweep`: the
 fused step at medians 87 and 23 and block sizes 8, 16, 32 and 64, each with its decode
-launch time, GB/s and share of the 8 TB/s roofline, and `config1`: the tiny fp32 workload's
-step, decode launch and roofline share, with its own oracle baseline. `roofline.ceiling` is the streaming-read
-rate this GPU reaches with the library's read kernel (pa_measure_stream_read over 4 GiB),
-and `*_per_launch_events` give the median, p10 and p90 of launches timed one by one.
+launch time, GB/s, share of the 8 TB/s roofline and the time of the same cache's reads
+alone (pa_measure_gather_read: the split decode's loads through the table, no arithmetic);
+and `config1`: the tiny fp32 workload's step, decode launch and roofline share, with its own
+oracle baseline. `roofline.ceiling` is the streaming-read rate this GPU reaches with the
+library's read kernel (pa_measure_stream_read over 4 GiB), `roofline.gather_ceiling` the
+rate of the decode's own reads of this cache alone (16-bit pools without a window or beam
+groups), and `*_per_launch_events` give the median, p10 and p90 of launches timed one by
+one.
 
 With --window W the decode attends to the last W tokens of each sequence only
 (pa_decode_sliding_window) and the algorithmic bytes count min(context_len, W) tokens.
@@ -439,13 +443,15 @@ def _sweep_config3(args, dev, medians=(87, 23), block_sizes=(8, 16, 32, 64)) -> 
                 step(i)
             wall = _timed(step, args.warmup, args.steps)
             dec = _event_pass(step, args.warmup + args.steps, args.steps)
+            gat = _gather_ms(args, w, t, kps, vps, R)
             kv = 2 * w.num_kv_heads * w.head_dim * 2 * int(w.lens_after_append.sum())
             gbs = kv / (dec * 1e-3) / 1e9
             part = _lib.pa_decode_partition_size(_lib.CacheDesc.of(t["k_pool"]), w.batch, w.num_q_heads, max_len, 0)
             _progress(f"sweep median {med} block size {w.block_size}: decode {dec * 1e3:.1f} us")
             cases[f"med{med}-bs{w.block_size}"] = {
                 "decode_launch_us": round(dec * 1e3, 2), "decode_gbs": round(gbs, 1),
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "step_us": round(wall * 1e6 / args.steps, 2),
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "gather_us": round(gat * 1e3, 2),
+                "frac_of_gather": round(gat / dec, 4), "step_us": round(wall * 1e6 / args.steps, 2),
                 "step_gbs": round(kv / (wall / args.steps) / 1e9, 1), "kv_bytes": kv,
                 "context_len_sum": int(w.lens_after_append.sum()), "context_len_max": max_len,
                 "partition_size": part, "replicas": R,
@@ -457,6 +463,26 @@ def _sweep_config3(args, dev, medians=(87, 23), block_sizes=(8, 16, 32, 64)) -> 
     return {"workload": "cfg3-f16-longtail, fused step (append + decode), cold replicas",
             "cases": cases, "worst": {"case": worst, "frac": cases[worst]["frac"]},
             "all_at_least_70pct": all(c["frac"] >= 0.70 for c in cases.values())}
+
+
+def _gather_ms(args, w, t, kps, vps, R: int) -> float:
+    """Average duration in ms of pa_measure_gather_read over the step's replicas: the split
+    decode's reads of this cache (K and V below the lengths, through the table) alone."""
+    import torch
+
+    from paged_kv_cache_indexed_amd import _lib
+
+    lens = t["lens_after"]
+    max_len = int(w.lens_after_append.max())
+    sink = torch.empty(w.batch * w.num_kv_heads, dtype=torch.float32, device=lens.device)
+    desc = _lib.CacheDesc.of(t["k_pool"])
+
+    def gather(i):
+        _lib.pa_measure_gather_read(desc, kps[i % R], vps[i % R], t["block_table"], lens, max_len, sink)
+
+    for i in range(args.warmup):
+        gather(i)
+    return _event_pass(gather, args.warmup, args.steps)
 
 
 def _config1_line(args, dev) -> dict:
@@ -946,6 +972,11 @@ def main() -> int:
         result["roofline"]["ceiling"] = ceil["gbs"]
         result["roofline"]["frac_of_ceiling"] = round(achieved / ceil["gbs"], 4)
         result["stream_read_ceiling"] = ceil
+    if not (fp8 or W or BW or NL > 1):
+        # the same cache read by the split decode's loads alone, in its decomposition
+        gat = _gather_ms(args, w, t, kps, vps, R)
+        result["roofline"]["gather_ceiling"] = round(roof_bytes / (gat * 1e-3) / 1e9, 1)
+        result["roofline"]["frac_of_gather_ceiling"] = round(gat / dec_avg, 4)
     plain = not (fp8 or W or BW or args.unfused or args.graph or NL > 1 or args.contiguous_pool)
     if args.config == 3 and plain and not args.no_sweep:
         del kps, vps

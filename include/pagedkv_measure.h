@@ -30,6 +30,31 @@ extern "C" {
 pa_status_t pa_measure_stream_read(const void* buf, size_t bytes, float* sink, int32_t num_workgroups,
                                    pa_stream_t stream);
 
+/*
+ * Enqueues the reads a split decode (pa_decode's VALU kernel, one work-group of 4 waves per
+ * (sequence, kv head)) makes of a paged cache, and nothing else: each work-group reads the
+ * sequence's context_len (tokens 0 .. L-1), stages its block_table row, and reads every K and
+ * V row of its kv head below L, a wave load being 1 KiB of consecutive rows of one block.
+ * The address translation ([BlockManager essay] §2) and the scattered blocks are those of the
+ * decode; the attention arithmetic, the queries and the outputs are left out. Timed with
+ * events on `stream`, the K+V bytes below the lengths over the time give the rate this
+ * cache layout and decomposition allow, a ceiling for the decode on the same cache.
+ * Arguments are pa_decode's (one partition per sequence): cache describes both pools; k_pool
+ * and v_pool are device memory, 16-byte aligned; block_table is int32 [batch][max_blocks_per_seq];
+ * context_lens int32 [batch]; sink is device memory of batch x num_kv_heads floats (written
+ * only with negligible probability, to keep the loads alive). A sequence with a length
+ * outside [1, max_context_len] or more than max_blocks_per_seq (or 4096) blocks is skipped;
+ * ids outside the pool are not read. 8-bit pools: the codes only. Returns
+ * PA_ERR_INVALID_ARGUMENT for null or misaligned pointers and bad sizes, PA_ERR_UNSUPPORTED
+ * for a cache whose rows exceed 1 KiB or whose blocks hold less than 1 KiB per kv head
+ * (or a cache pa_decode rejects), PA_ERR_LAUNCH if the launch fails. Allocates nothing
+ * and does not synchronise.
+ */
+pa_status_t pa_measure_gather_read(const pa_cache_desc_t* cache, const void* k_pool, const void* v_pool,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                                   float* sink, pa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ EXPORTED = ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_partition_size"
             "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_reblock", "pa_multi_token_attention",
             "pa_multi_token_workspace_bytes", "pa_decode_append", "pa_decode_append_fp8",
             "pa_decode_beams", "pa_decode_beams_partition_size", "pa_decode_beams_workspace_bytes",
-            "pa_status_string", "pa_measure_stream_read", "pa_decode_append_noalloc")
+            "pa_status_string", "pa_measure_stream_read", "pa_measure_gather_read", "pa_decode_append_noalloc")
 
 # 8-bit float pools are uint8 (or float8_e4m3fn) tensors of OCP E4M3 codes.
 _DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
@@ -134,6 +134,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_append_noalloc.restype = ctypes.c_int
     lib.pa_measure_stream_read.argtypes = [P, SZ, P, I32, P]
     lib.pa_measure_stream_read.restype = ctypes.c_int
+    lib.pa_measure_gather_read.argtypes = [D, P, P, P, I32, P, I32, I32, P, P]
+    lib.pa_measure_gather_read.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -385,6 +387,19 @@ def pa_measure_stream_read(buf, sink, num_workgroups: int, stream=None) -> None:
         raise PagedKVError("sink must hold num_workgroups float32")
     _check(load().pa_measure_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                          int(num_workgroups), _stream(stream)))
+
+
+def pa_measure_gather_read(cache: CacheDesc, k_pool, v_pool, block_table, context_lens, max_context_len: int,
+                           sink, stream=None) -> None:
+    """The split decode's K/V reads of a paged cache without its arithmetic
+    (include/pagedkv_measure.h); ``sink`` holds at least batch x num_kv_heads float32."""
+    batch = int(context_lens.shape[0])
+    if sink.numel() < batch * cache.num_kv_heads or sink.dtype != torch.float32:
+        raise PagedKVError("sink must hold batch x num_kv_heads float32")
+    desc = cache.c()
+    _check(load().pa_measure_gather_read(ctypes.byref(desc), _pool_ptr(k_pool), _pool_ptr(v_pool, k_pool),
+                                         _ptr(block_table), int(block_table.shape[1]), _ptr(context_lens), batch,
+                                         int(max_context_len), _ptr(sink), _stream(stream)))
 
 
 def pa_decode_append_noalloc(cache: CacheDesc, out, q, k_pool, v_pool, block_table, context_lens,

@@ -4,6 +4,7 @@
 
 #include <mutex>
 
+#include "../../include/pagedkv_measure.h"
 #include "pa_kernels.h"
 
 using namespace pagedkv;
@@ -661,6 +662,26 @@ pa_status_t pa_decode_beams(const pa_cache_desc_t* cache, int32_t q_dtype, void*
                                        (int)ceil_div(batch, beam_width), cache->num_kv_heads, s);
     if (e == hipSuccess && parts > 1) e = launch_reduce(a, q_dtype, cache->head_dim, batch, s);
     return from_hip(e);
+}
+
+pa_status_t pa_measure_gather_read(const pa_cache_desc_t* cache, const void* k_pool, const void* v_pool,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                                   float* sink, pa_stream_t stream) {
+    pa_status_t st = check_cache(cache);
+    if (st != PA_OK) return st;
+    if (batch < 0 || batch > 65535) return PA_ERR_INVALID_ARGUMENT;
+    if (batch == 0) return PA_OK;
+    if (!k_pool || !v_pool || !block_table || !context_lens || !sink) return PA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_INVALID_ARGUMENT;
+    if (max_blocks_per_seq <= 0 || max_context_len <= 0) return PA_ERR_INVALID_ARGUMENT;
+    // a wave load is 1 KiB of consecutive rows, which must lie in one block
+    const int row_bytes = cache->head_dim * dtype_bytes(cache->dtype);
+    if (row_bytes > 1024 || (int64_t)cache->block_size * row_bytes < 1024) return PA_ERR_UNSUPPORTED;
+    GatherReadArgs a{static_cast<const char*>(k_pool), static_cast<const char*>(v_pool), block_table, context_lens,
+                     sink, block_stride(cache), cache->num_blocks, max_blocks_per_seq, max_context_len,
+                     log2_exact(cache->block_size), row_bytes};
+    return from_hip(launch_gather_read(a, batch, cache->num_kv_heads, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -141,6 +141,24 @@ struct ReblockArgs {
 };
 hipError_t launch_reblock(const ReblockArgs& a, int batch, hipStream_t stream);
 
+// Measurement: the decode's K/V reads alone (pa_measure_gather_read): 4 waves per (kv head,
+// sequence) read every token row of K and V below the length through the staged table, with
+// the split decode's 1 KiB wave loads, and compute nothing.
+struct GatherReadArgs {
+    const char* k_pool;
+    const char* v_pool;
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    float* sink;           // one float per work-group, written with negligible probability
+    int64_t block_stride;  // bytes from one physical block to the next
+    int32_t num_blocks;
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;
+    int32_t log2_block_size;
+    int32_t row_bytes;  // head_dim x element bytes: 64 .. 1024, a power of two
+};
+hipError_t launch_gather_read(const GatherReadArgs& a, int batch, int num_kv_heads, hipStream_t stream);
+
 // Quantising append into 8-bit pools: src_dtype is the type of key/value rows.
 hipError_t launch_reshape_and_cache_fp8(const CacheArgs& a, int src_dtype, int head_dim, const void* key,
                                         const void* value, float* k_scale, float* v_scale,

@@ -64,6 +64,9 @@ def test_bench_default_line():
     assert cfg["workload"].startswith("cfg3-f16-longtail-med87-bs16")
     assert roof["ceiling"] > 1000 and roof["frac_of_ceiling"] == pytest.approx(roof["achieved"] / roof["ceiling"],
                                                                                  abs=1e-3)
+    # the same cache's reads alone: at least as fast as the decode that also computes on them,
+    # within launch-to-launch noise
+    assert roof["gather_ceiling"] > 1000 and 0 < roof["frac_of_gather_ceiling"] < 1.15
     lib = d["library"]
     assert lib["in_tree"] is True and len(lib["sha256_16"]) == 16
     for k in ("decode_launch_us_per_launch_events", "step_us_per_step_events"):
