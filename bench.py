@@ -65,7 +65,7 @@ MFMA_FILE = os.path.join(ROOT, "profiles", "gqa_mfma_busy.txt")
 # sources of the kernel that produced it are unchanged.
 _COMMON_SOURCES = ("pa_device.h", "pa_kernels.h", "pa_decode_common.h", "pa_api.hip")
 _PATH_SOURCES = {"valu": ("pa_decode_valu.h", "pa_decode.hip", "pa_decode_fp8.hip"),
-                 "mfma": ("pa_mfma_kernel.h", "pa_decode_mfma.hip", "pa_decode_mfma_b8.hip"),
+                 "mfma": ("pa_mfma_kernel.h", "pa_mfma_lds.h", "pa_decode_mfma.hip", "pa_decode_mfma_b8.hip"),
                  "multi": ("pa_mfma_kernel.h", "pa_multi_token.hip", "pa_multi_token_b8.hip"),
                  "beams": ("pa_mfma_kernel.h", "pa_decode_beams.hip", "pa_decode_beams_b8.hip")}
 

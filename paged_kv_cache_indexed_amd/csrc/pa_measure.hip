@@ -84,8 +84,10 @@ __global__ __launch_bounds__(kGatherThreads) void gather_read_kernel(GatherReadA
             kk[u] = buffer_load16(make_rsrc(a.k_pool + base, slab), off);
             vv[u] = buffer_load16(make_rsrc(a.v_pool + base, slab), off);
         }
+        // every dword of every load feeds x: with some unused the compiler narrows the loads
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) x ^= kk[u][0] ^ kk[u][3] ^ vv[u][1] ^ vv[u][2];
+        for (int u = 0; u < kGatherUnroll; ++u)
+            x ^= kk[u][0] ^ kk[u][1] ^ kk[u][2] ^ kk[u][3] ^ vv[u][0] ^ vv[u][1] ^ vv[u][2] ^ vv[u][3];
     }
     if (x == 0x9e3779b9u) a.sink[(size_t)b * gridDim.x + kvh] = __uint_as_float(x);
 }

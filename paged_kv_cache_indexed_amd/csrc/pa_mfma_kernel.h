@@ -23,7 +23,8 @@
 //     16-token x 16-dim slice is transposed by one v_mfma_f32_16x16x16 against an identity
 //     B operand (exact: products with 1 and sums with 0); its fp32 output (4 tokens of one
 //     dim per lane) packs back to 16-bit without rounding and is the B operand of
-//     v_mfma_f32_16x16x32 for O += P V.
+//     v_mfma_f32_16x16x32 for O += P V. Where 16-bit tiles pass through LDS anyway (several
+//     queries, beam groups) the B operand is read from there with transpose reads instead.
 //   * Everything else (length checks, block ids staged and checked in LDS, masked loads
 //     that never touch padding, base-2 online softmax in fp32, wave and partition merge) is
 //     shared with the VALU path. A row outside the attended range gets an out-of-range
@@ -297,6 +298,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
     // 23% faster with 4 queries per sequence (config 4) and 2% with beam groups (config 5),
     // but 3-4% slower for the one-query decode, which keeps the direct loads.
     constexpr bool kStage = D == 128 && (kMulti || kBeams) && kSmallBlocks == 0;
+    // Staged 16-bit V tiles stay in LDS, and the B operand of P V comes from transpose reads
+    // (ds_read_b64_tr_b16) instead of identity-MFMA transposes: 12% faster with 4 queries per
+    // sequence on config 4, equal elsewhere. The one-query decode measured the same with it
+    // (staged, 4 or 8 waves), so it keeps the direct loads.
+    constexpr bool kTrV = kStage && KV::kBytes == 2;
     constexpr int kCpr = D * KV::kBytes / 16;  // 16-byte chunks per row (16 or 8)
     constexpr int kRpl = 64 / kCpr;            // rows per staged load instruction (4 or 8)
     __shared__ u32x4 s_stage[kStage ? NW : 1][kStage ? 2 * 16 * kCpr : 1];
@@ -541,10 +547,48 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
                 for (int c = 0; c < NL; ++c) x[t][c] = w[(16 * t + n) * kCpr + ((4 * c + g) ^ (n % kCpr))];
         }
     };
+    // V tiles for transpose reads: whole rows written as loaded, chunk j of row r at
+    // j ^ (2r mod kCpr), so that the transpose reads (four rows, two chunks per lane group)
+    // and the row writes both spread over the banks.
+    auto vswz = [&](int r) { return (2 * r) & (kCpr - 1); };
+    auto stage_v = [&](u32x4 (*x)[NL]) {
+        if constexpr (kTrV) {
+            u32x4* w = s_stage[wave];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int c = 0; c < NL; ++c) {
+                    const int r = kRpl * c + lane / kCpr;
+                    w[(16 * t + r) * kCpr + ((lane % kCpr) ^ vswz(r))] = x[t][c];
+                }
+        }
+    };
+    // B operand of P V for output slice s from the staged V tiles: lane (n, g) gets dim
+    // 16s + n at tokens 4g .. 4g+3 of tile 0, then of tile 1 (the k-slots of P's A operand).
+    // ds_read_b64_tr_b16 gives lane i of a 16-lane group, as its value k (k = 0..3), 16-bit
+    // element i % 4 of the 8-byte piece that lane i / 4 + 4k of the group addresses. So lane n
+    // addresses row 4g + n / 4, dims 16s + 4 (n % 4) .. +3.
+    auto tr_v = [&](int s) {
+        const u32x4* w = s_stage[wave];
+        const int r = 4 * g + (n >> 2);
+        const int j = 2 * s + ((n & 3) >> 1);  // 16-byte chunk of dims 16s + 4 (n % 4) ..
+        u32x4 vb;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const char* piece = reinterpret_cast<const char*>(w + (16 * t + r) * kCpr + (j ^ vswz(r))) + 8 * (n & 1);
+            const mf_s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) mf_s16x4*)(const_cast<char*>(piece)));
+            const u32x2 y = __builtin_bit_cast(u32x2, x);
+            vb[2 * t] = y.x;
+            vb[2 * t + 1] = y.y;
+        }
+        return vb;
+    };
     auto compute = [&](int it, u32x4 (*kk)[NL], u32x4 (*vv)[NL], u32x4* ks, u32x4* vs) {
         const int rel0 = (c0 + it * NW + wave) * kChunk;
         restage(kk);
-        restage(vv);
+        if constexpr (kTrV) stage_v(vv);
+        else restage(vv);
         if constexpr (kAppendable) {
             if (npos >= 0) {  // fused append: the new token's rows come from s_new (wave-uniform test)
 #pragma unroll
@@ -555,8 +599,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
 #pragma unroll
                             for (int c = 0; c < NL; ++c) {
                                 kk[t][c] = *reinterpret_cast<const u32x4*>(s_rec + 64 * c + seg);
-                                vv[t][c] = *reinterpret_cast<const u32x4*>(s_rec + R::kRowBytes + 64 * c + seg);
+                                if constexpr (!kTrV)
+                                    vv[t][c] = *reinterpret_cast<const u32x4*>(s_rec + R::kRowBytes + 64 * c + seg);
                             }
+                        }
+                        if constexpr (kTrV) {  // the staged V row of the token
+                            if (lane < kCpr)
+                                s_stage[wave][(16 * t + d) * kCpr + (lane ^ vswz(d))] =
+                                    *reinterpret_cast<const u32x4*>(s_rec + R::kRowBytes + 16 * lane);
                         }
                         if constexpr (kFp8) {  // the lanes whose scores include the token
                             if (g == (d >> 2)) {
@@ -653,6 +703,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
             const uint32_t h = M::pack_round(pr[2 * w], pr[2 * w + 1]);
             phi[w] = h;
             plo[w] = M::pack_round(pr[2 * w] - M::lo(h), pr[2 * w + 1] - M::hi(h));
+        }
+        if constexpr (kTrV) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const u32x4 vb = tr_v(s);
+                acc[s] = M::k32(phi, vb, acc[s]);
+                acc[s] = M::k32(plo, vb, acc[s]);
+            }
+            return;
         }
         // V rows as 16-bit words: vw[t][c] holds the 8 dims of token row n that k-block c of
         // lane group g covers
@@ -755,8 +814,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int c = s >> 1;  // column n of slice s
-        const int dim = (kFp8 ? 64 * (c >> 1) + 16 * (n >> 2) + 8 * (c & 1) : 32 * c + 8 * (n >> 2)) + 4 * (s & 1) +
-                        (n & 3);
+        const int dim = kTrV ? 16 * s + n
+                             : (kFp8 ? 64 * (c >> 1) + 16 * (n >> 2) + 8 * (c & 1) : 32 * c + 8 * (n >> 2)) +
+                                   4 * (s & 1) + (n & 3);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (4 * g + i < NCOL) s_acc[wave][4 * g + i][dim] = acc[s][i];

@@ -43,21 +43,22 @@ __global__ __launch_bounds__(D) void reduce_multi_kernel(DecodeArgs a) {
 // transposes V once per tile and wave. This one gives a work-group 64 rows (16 per wave) of
 // one kv head and streams the partition's K/V once for all of them:
 //   * 32-token tiles are loaded by the whole work-group with whole-row loads (1 KiB
-//     contiguous per wave instruction) into LDS, double-buffered, one barrier per tile. K is
-//     stored row-major (16-byte unit u of token r at u ^ (r & 7), so the operand reads below
-//     hit distinct banks); V is stored transposed, [dim][token], in 80-byte rows whose 8-byte
-//     chunks of 4 tokens are permuted by the dim (chunk c of dim d at c ^ ((d / 8) % 8)):
-//     the transposing 16-bit writes then spread over the banks, and the 8-byte operand reads
-//     stay conflict-free.
+//     contiguous per wave instruction) into LDS, double-buffered, one barrier per tile. K and
+//     V are stored row-major as loaded (16-byte unit u of token r at u ^ (r & 7) for K, so
+//     the operand reads below hit distinct banks; at u ^ vsw(r) for V, so the transpose reads
+//     do).
 //   * Each wave computes S^T = K Q^T for its 16 rows (K tile rows from LDS as the A operand,
 //     Q^T in registers as B), runs the same base-2 online softmax as the decode (P stays in
 //     the lanes that computed it, split into rounded high and low parts), and accumulates
-//     O = P V with V^T rows from LDS as the B operand: lane (n, g) reads tokens 4g..4g+3 and
-//     16+4g..16+4g+3 of dim n of the slice, the tokens its k-slots stand for.
+//     O = P V with the B operand read from the V tile by ds_read_b64_tr_b16, which transposes
+//     4 x 16 pieces across each 16-lane group: lane (n, g) receives dim n of the slice at
+//     tokens 4g..4g+3 and 16+4g..16+4g+3, the tokens its k-slots stand for. (A transposed
+//     [dim][token] copy written with 16-bit stores was 1-7% slower and took more registers.)
 //   * Rows belong to one wave from start to end, so there is no cross-wave merge: each wave
 //     writes its rows' outputs, or their partition records for the log-sum-exp reduce.
 // 16-bit pools, head_dim 64 or 128; the group size is a run-time value.
 namespace prefill {
+
 
 using mfma::f32x4;
 using mfma::u32x2;
@@ -66,12 +67,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 16 * kWaves;  // (query, head) rows per work-group
 constexpr int kTile = 32;           // tokens per K/V tile
-constexpr int kVtStride = kTile + 8;  // V^T row in 16-bit elements (80 bytes)
-
-// Position (16-bit elements) of token t of dim d in a V^T tile.
-__device__ __forceinline__ int vt_pos(int d, int t) {
-    return d * kVtStride + 4 * ((t >> 2) ^ ((d >> 3) & 7)) + (t & 3);
-}
 
 // NaN sink: the rows of row tile rt of sequence b (query-major (query, head) rows).
 template <typename T, int D>
@@ -119,7 +114,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     static_assert(kLoads >= 1 && kLoads * kThreads == kTile * U, "tile split");
     __shared__ int s_ids[kMaxIdsPerPartition];
     __shared__ u32x4 s_k[2][kTile * U];
-    __shared__ __align__(16) uint16_t s_vt[2][D * kVtStride];
+    __shared__ u32x4 s_v[2][kTile * U];
+    // V rows as loaded; unit u of token r at u ^ vsw(r), so that the transpose reads (4 rows,
+    // 2 units per 16-lane group) and the row writes spread over the banks
+    auto vsw = [](int r) { return (r * (U / 8)) & (U - 1); };
     __shared__ float s_ks[kFp8 ? 2 : 1][kFp8 ? kTile : 1];  // 8-bit pools: the tile's K and V row scales
     __shared__ float s_vs[kFp8 ? 2 : 1][kFp8 ? kTile : 1];
 
@@ -179,18 +177,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const char* kpool = static_cast<const char*>(a.k_pool);
     const char* vpool = static_cast<const char*>(a.v_pool);
 
-    // Load i of thread tid covers 16-byte unit u of tile token t: with two loads per thread
-    // (head_dim 128) tokens 2 (tid / U) and 2 (tid / U) + 1 at the same unit, so that the
-    // transposed V writes pair two tokens per 32-bit word; with one, unit tid. The tokens of a
-    // wave instruction lie in one aligned group of 8, so in one block: the id is wave-uniform.
+    // Load i of thread tid covers 16-byte unit u of tile token t, unit kThreads i + tid of the
+    // tile in row order: a wave instruction reads 4 (head_dim 128) or 8 (head_dim 64) whole
+    // consecutive rows, which lie in one aligned group of 8 tokens, so in one block: the id is
+    // wave-uniform.
     auto slot_of = [&](int i, int& t, int& u) {
-        if constexpr (kLoads == 2) {
-            t = 2 * (tid / U) + i;
-            u = tid % U;
-        } else {
-            t = (kThreads * i + tid) / U;
-            u = (kThreads * i + tid) % U;
-        }
+        t = (kThreads * i + tid) / U;
+        u = (kThreads * i + tid) % U;
     };
     auto issue = [&](int k, u32x4* kr, u32x4* vr) {
 #pragma unroll
@@ -198,7 +191,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             int t, u;
             slot_of(i, t, u);
             const int rel = (k0 + k) * kTile + t;
-            const int tw = kLoads == 2 ? 2 * (64 * wave / U) + i : (kThreads * i + 64 * wave) / U;
+            const int tw = (kThreads * i + 64 * wave) / U;
             const int rel_w = (k0 + k) * kTile + tw;  // the wave's first token
             const int id = __builtin_amdgcn_readfirstlane(s_ids[(rel_w < ntok ? rel_w : 0) >> lbs]);
             const size_t slab = (size_t)id * a.block_stride + (size_t)kvh * head_bytes;
@@ -214,21 +207,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             int t, u;
             slot_of(i, t, u);
             s_k[buf][t * U + (u ^ (t & 7))] = kr[i];
-        }
-        int t, u;
-        slot_of(0, t, u);
-        if constexpr (kLoads == 2) {
-            // dims 8u .. 8u + 7 of tokens t (even) and t + 1: one 32-bit word per dim
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (vr[0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                const uint32_t hi = (vr[1][e >> 1] >> (16 * (e & 1))) << 16;
-                *reinterpret_cast<uint32_t*>(&s_vt[buf][vt_pos(8 * u + e, t)]) = hi | lo;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                s_vt[buf][vt_pos(8 * u + e, t)] = (uint16_t)(vr[0][e >> 1] >> (16 * (e & 1)));
+            s_v[buf][t * U + (u ^ vsw(t))] = vr[i];
         }
     };
 
@@ -242,7 +221,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             int t, u;
             slot_of(i, t, u);
             const int rel = (k0 + k) * kTile + t;
-            const int tw = kLoads == 2 ? 2 * (64 * wave / U) + i : (kThreads * i + 64 * wave) / U;
+            const int tw = (kThreads * i + 64 * wave) / U;
             const int rel_w = (k0 + k) * kTile + tw;  // the wave's first token
             const int id = __builtin_amdgcn_readfirstlane(s_ids[(rel_w < ntok ? rel_w : 0) >> lbs]);
             const size_t slab = (size_t)id * a.block_stride + (size_t)kvh * head_bytes;
@@ -347,9 +326,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const u32x2 lo4 = *reinterpret_cast<const u32x2*>(&s_vt[buf][vt_pos(16 * s + n, 4 * g)]);
-            const u32x2 hi4 = *reinterpret_cast<const u32x2*>(&s_vt[buf][vt_pos(16 * s + n, 16 + 4 * g)]);
-            const u32x4 vb = {lo4.x, lo4.y, hi4.x, hi4.y};
+            // lane n addresses row 4g + n / 4 (of each 16-token half), dims 16s + 4 (n % 4) .. +3;
+            // the transpose read hands it dim 16s + n of rows 4g .. 4g+3
+            u32x4 vb;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = 16 * h + 4 * g + (n >> 2);
+                const int uu = 2 * s + ((n & 3) >> 1);
+                const char* piece = reinterpret_cast<const char*>(&s_v[buf][r * U + (uu ^ vsw(r))]) + 8 * (n & 1);
+                const u32x2 y = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) mfma::mf_s16x4*)(const_cast<char*>(piece))));
+                vb[2 * h] = y.x;
+                vb[2 * h + 1] = y.y;
+            }
             acc[s] = M::k32(phi, vb, acc[s]);
             acc[s] = M::k32(plo, vb, acc[s]);
         }

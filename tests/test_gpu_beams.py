@@ -91,7 +91,9 @@ def test_beams_match_oracle(dtype, group, beams, d, bs):
 def test_beams_bitwise_equal_to_grouped_decode(group, bs):
     """With 4 or 8 query heads per kv head pa_decode runs the same matrix-core arithmetic per
     column, so for an explicit partition size the outputs agree bit for bit, shared or not
-    (with 8-token blocks too, where the two load the rows in different ways)."""
+    (with 8-token blocks too, where the two load the rows in different ways). This holds below
+    1152-token partitions: longer ones take pa_decode's LDS path, which sums P V in 16-token
+    steps."""
     dev = require_gpu()
     for share in (True, False):
         q, kp, vp, table, L = _beam_case(2, _LENS, 2, 2, group, 128, bs, 256, "bf16", share=share)

@@ -41,7 +41,8 @@ def _bits(x):
                                       (2, dict(batch=16, heads=8), 64), (2, dict(batch=16, heads=8), 256),
                                       (3, dict(batch=64, heads=4), 0), (4, dict(batch=8), 0), (4, dict(batch=8), 512),
                                       (3, dict(batch=64, heads=4, block_size=8), 0),
-                                      (4, dict(batch=8, block_size=8), 0), (4, dict(batch=8, block_size=8), 24)])
+                                      (4, dict(batch=8, block_size=8), 0), (4, dict(batch=8, block_size=8), 24),
+                                      (4, dict(batch=8), 1152), (4, dict(batch=8, block_size=256), 2304)])
 def test_fused_equals_separate_calls_bitwise(cfg, kw, P):
     dev = require_gpu()
     w = config_workload(cfg, seed=11, **kw)
