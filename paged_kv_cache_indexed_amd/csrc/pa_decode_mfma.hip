@@ -13,24 +13,13 @@ using mfma::decode_mfma_kernel;
 #define PA_MFMA_WAVES 4
 #endif
 
-// Partitions of at least this many tokens take the kernel that loads its tiles straight into
-// LDS (pa_mfma_lds.h; 16-bit pools, head_dim 128, G <= 8). Measured on MI355X, bf16, 8 kv
-// heads: 5-8% faster from 1.3K to 4K tokens per partition (B = 32 at 2049 tokens: 49.8
-// against 54.3 us), 12% at 4096-token partitions of 32K contexts; at 1040 tokens within 2%
-// either way, and shorter partitions lose up to 15% (B = 128 at 513 tokens: 66.7 against
-// 58.0 us): its 152 KB of LDS leave one work-group per compute unit.
-constexpr int kLdsPathMinPartition = 1152;
-
 template <typename T, typename KV, int D, int G>
 hipError_t launch_tdg(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     constexpr int NW = PA_MFMA_WAVES;
     dim3 grid(num_kv_heads, batch, a.max_partitions);
-    if constexpr (std::is_same_v<KV, T> && D == 128 && G <= 8) {
-        if (a.partition_size >= kLdsPathMinPartition) {
-            hipLaunchKernelGGL((mfma::decode_mfma_lds_kernel<T, G>), grid, dim3(256), 0, stream, a);
-            return hipGetLastError();
-        }
-    }
+    // 16-bit rows of 128 dims and up to 8 heads per kv head: the LDS path (faster on every
+    // shape measured, short contexts included)
+    if constexpr (std::is_same_v<KV, T> && D == 128 && G <= 8) return mfma::launch_decode_lds<T, G>(a, batch, num_kv_heads, stream);
     hipLaunchKernelGGL((decode_mfma_kernel<T, KV, D, G, NW, (D <= 128)>), grid, dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }

@@ -2,7 +2,7 @@
 // tile then spans two blocks, so the kernel of pa_mfma_kernel.h looks up the block of each
 // tile row. The block size trade-off (smaller blocks waste less memory,
 // at more table lookups) is [BlockManager essay] §3.
-#include "pa_mfma_kernel.h"
+#include "pa_mfma_lds.h"
 
 namespace pagedkv {
 
@@ -16,6 +16,9 @@ template <typename T, typename KV, int D, int G>
 hipError_t launch_tdg(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     constexpr int NW = kSmallWaves;
     dim3 grid(num_kv_heads, batch, a.max_partitions);
+    // 16-bit rows of 128 dims, up to 8 heads per kv head: the LDS path, whose load
+    // instructions cover four rows of one block each
+    if constexpr (std::is_same_v<KV, T> && D == 128 && G <= 8) return mfma::launch_decode_lds<T, G>(a, batch, num_kv_heads, stream);
     // 16-bit rows of 128 dims in a pool within 2 GiB: the tile's two blocks through one buffer
     // (mode 2), which keeps two waves per SIMD; per-lane row addresses (mode 1) need the
     // registers of a second wave there. Measured with 8 query heads per kv head (bf16): B = 128

@@ -4,17 +4,18 @@
 //
 // The matrix-core decode of pa_mfma_kernel.h loads its tiles straight into the MFMA operand
 // layout: each load instruction covers a 64-byte strip of 16 rows, which the L1 serves one
-// lane at a time, and its two register buffers keep one 32-token chunk in flight while the
-// other is computed. Here each wave owns a ring of kLdsRing 16-token tiles in LDS, filled by
+// lane at a time. Here each wave stages one 16-token tile at a time in LDS, filled by
 // buffer_load_dwordx4 ... lds: every load instruction reads four whole rows (1 KiB of
-// consecutive memory) and needs no registers, so three tiles are in flight while the fourth
-// is computed. Per tile and wave:
+// consecutive memory) and needs no registers, and the other waves of the compute unit (two
+// to four per SIMD) keep loads in flight while a wave computes. Per tile and wave:
 //   * Loads. Instruction i of the K tile gives lane l row r = 4i + l / 16; the hardware
 //     writes lane l's 16 bytes to position l % 16 of the row in LDS, so the lane fetches the
 //     row's 16-byte chunk (l % 16) ^ r: chunk j of row r sits at position j ^ r. (XOR keeps each
 //     quad of lanes inside one aligned 64-byte segment, so the loads stay coalesced.) V rows
-//     put chunk j at j ^ (2r mod 16). A row outside the attended range gets an out-of-range
-//     offset: no memory access, and the hardware writes zeros to its LDS slot.
+//     put chunk j at j ^ (2r mod 16). Each instruction's four rows lie in one block (blocks
+//     hold a multiple of 8 tokens) and it takes that block's id. A row outside the attended
+//     range gets an out-of-range offset: no memory access, and the hardware writes zeros to
+//     its LDS slot.
 //   * Scores. S^T = K Q^T with v_mfma_f32_16x16x32: lane (n, g) reads chunk 4c + g of row n
 //     (dims 32c + 8g .. +7) as the A operand of k-block c, from position (4c + g) ^ n: the 16
 //     rows of a lane group hit distinct banks. Q is the B operand with the same dims.
@@ -24,9 +25,15 @@
 //     comes from one ds_read_b64_tr_b16 per 16-dim slice: in each 16-lane group, lane i
 //     receives element i % 4 of the 8-byte pieces that lanes i / 4 + 4k (k = 0..3) address, so
 //     lane n addresses row 4g + n / 4, dims 16s + 4 (n % 4) .. +3.
-//   * The ring buffers are four distinct LDS arrays, and the loop is written out four times
-//     with scheduling barriers between the phases, so the compiler's wait counts cover only
-//     the tile being read (three tiles' loads stay outstanding).
+//   * After the last tile the work-group meets at a barrier and the waves' softmax states are
+//     merged through the tile buffers' memory: 8 KiB of LDS per wave in all (plus the table
+//     slice), so two 8-wave or four 4-wave work-groups fit a compute unit.
+// Measured against the direct-load kernel (bf16, 8 kv heads of 8 query heads, decode launch):
+// B = 32 at 2049 tokens 45.2 against 48.7-54.3 us, B = 128 at 2049 173.8 against 186.5, B = 8
+// at 32769 194.5 against 210.2, B = 256 at 129 tokens (4 waves) 32.6 against 48.2 us. Keeping
+// two or four tiles per wave in flight instead (a ring of distinct LDS arrays, one work-group
+// per compute unit) measured 46.9-48.4 us at B = 32, 2049 tokens: more bytes in flight per
+// wave, fewer waves, slower.
 // Everything else (length and table checks in the prologue, the base-2 online softmax with
 // the lazy rescale, the wave merge and the records for the log-sum-exp reduce, the fused
 // append) is the decode's.
@@ -35,7 +42,6 @@
 namespace pagedkv {
 namespace mfma {
 
-constexpr int kLdsRing = 4;              // tiles per wave: one computed, three in flight
 constexpr int kLdsTileVecs = 2 * 16 * 16;  // 16-byte vectors per tile buffer: 16 K rows, 16 V rows
 
 #define PA_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -43,24 +49,24 @@ constexpr int kLdsTileVecs = 2 * 16 * 16;  // 16-byte vectors per tile buffer: 1
 // Byte address in LDS of a pointer to a __shared__ object (the low half of its flat address).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
 
-template <typename T, int G>
-__global__ __launch_bounds__(256) void decode_mfma_lds_kernel(DecodeArgs a) {
+// Registers for four waves per SIMD (at most 128 per lane): two 8-wave or four 4-wave
+// work-groups per compute unit, as many as the LDS allows.
+template <typename T, int G, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void decode_mfma_lds_kernel(DecodeArgs a) {
     static_assert(T::kBytes == 2 && G >= 1 && G <= 8, "16-bit pools, at most 8 heads per kv head");
     constexpr int D = 128;
-    constexpr int NW = 4;
     constexpr int NC = D / 32;  // k-blocks of the score contraction
     constexpr int NS = D / 16;  // 16-dim output slices
     constexpr int kRowBytes = D * 2;
     using M = Mma<T>;
 
-    __shared__ u32x4 s_ring0[NW][kLdsTileVecs];
-    __shared__ u32x4 s_ring1[NW][kLdsTileVecs];
-    __shared__ u32x4 s_ring2[NW][kLdsTileVecs];
-    __shared__ u32x4 s_ring3[NW][kLdsTileVecs];
+    __shared__ u32x4 s_tile[NW][kLdsTileVecs];
     __shared__ int s_ids[kMaxIdsPerPartition];
     __shared__ float s_m[NW][G];
     __shared__ float s_l[NW][G];
-    __shared__ float s_acc[NW][G][D];
+    // the waves' weighted sums, merged after the loop, in the tile buffers' memory
+    static_assert(sizeof(float) * G * D <= sizeof(u32x4) * kLdsTileVecs, "one wave's sums fit its tile");
+    float (*const s_acc)[G][D] = reinterpret_cast<float (*)[G][D]>(&s_tile[0][0]);
     __shared__ __align__(16) char s_new[NewRec<T, D>::kBytes];
 
     const int p = grid_partition();
@@ -96,26 +102,26 @@ __global__ __launch_bounds__(256) void decode_mfma_lds_kernel(DecodeArgs a) {
     const char* vpool = static_cast<const char*>(a.v_pool);
     auto vswz = [](int r) { return (2 * r) & 15; };
 
-    // Loads of this wave's tile k into buf (masked whole when k >= nt). Tiles start on a
-    // multiple of 16 tokens, so a tile lies in one block (block_size >= 16).
+    // Loads of this wave's tile k into buf. Instruction i reads
+    // rows 4i .. 4i+3 of the tile, which lie in one block: its id is looked up for the
+    // instruction (clamped to the last attended row, so the entry is one the prologue staged).
     auto issue = [&](int k, u32x4* buf) {
         const int rel = (tile0 + wave + NW * k) << 4;  // wave-uniform
-        const bool any = k < nt;
-        const int id = __builtin_amdgcn_readfirstlane(s_ids[(any ? rel : 0) >> lbs]);
-        const size_t slab = (size_t)id * a.block_stride + (size_t)kvh * head_bytes;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + slab, (uint32_t)head_bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + slab, (uint32_t)head_bytes);
         const int pos = lane & 15;
-        // attended rows of the tile: [lo, hi) relative to rel, empty for a tile past the wave's
-        // last (one unsigned compare per row, and selects rather than branches, so that both
-        // sides of every load are the same instruction stream and the waits stay exact)
+        // attended rows of the tile: [lo, lo + span) relative to rel (one unsigned compare per
+        // row and selects rather than branches: a load under a lane branch would leave the
+        // compiler's wait counts unsure of what is outstanding)
         const int lo = rel_lo - rel;
-        const uint32_t span = any ? (uint32_t)(ntok - rel_lo) : 0u;
+        const uint32_t span = (uint32_t)(ntok - rel_lo);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const int id = __builtin_amdgcn_readfirstlane(s_ids[min(rel + 4 * i, ntok - 1) >> lbs]);
+            const size_t slab = (size_t)id * a.block_stride + (size_t)kvh * head_bytes;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kpool + slab, (uint32_t)head_bytes);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vpool + slab, (uint32_t)head_bytes);
             const int r = 4 * i + (lane >> 4);
             const bool live = (uint32_t)(r - lo) < span;
-            const uint32_t row = (uint32_t)(((rel & (bs - 1)) + r) * kRowBytes);
+            const uint32_t row = (uint32_t)((((rel + 4 * i) & (bs - 1)) + (lane >> 4)) * kRowBytes);
             const uint32_t ok = live ? row + 16u * (uint32_t)(pos ^ r) : kOutOfRange;
             const uint32_t ov = live ? row + 16u * (uint32_t)(pos ^ vswz(r)) : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, PA_LDS_PTR(buf + 64 * i), 16, ok, 0, 0, PA_KV_LOAD_POLICY);
@@ -218,34 +224,13 @@ __global__ __launch_bounds__(256) void decode_mfma_lds_kernel(DecodeArgs a) {
         }
     };
 
-    u32x4* const r0 = s_ring0[wave];
-    u32x4* const r1 = s_ring1[wave];
-    u32x4* const r2 = s_ring2[wave];
-    u32x4* const r3 = s_ring3[wave];
-    issue(0, r0);
-    issue(1, r1);
-    issue(2, r2);
-    for (int k = 0; k < nt; k += kLdsRing) {
-        __builtin_amdgcn_sched_barrier(0);
-        issue(k + 3, r3);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(k, r0);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(k + 4, r0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (k + 1 < nt) compute(k + 1, r1);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(k + 5, r1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (k + 2 < nt) compute(k + 2, r2);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(k + 6, r2);
-        __builtin_amdgcn_sched_barrier(0);
-        if (k + 3 < nt) compute(k + 3, r3);
+    u32x4* const buf = s_tile[wave];
+    for (int k = 0; k < nt; ++k) {
+        issue(k, buf);
+        compute(k, buf);
     }
-    // the masked loads past the wave's last tile still write their LDS slots: drain them
-    // before the work-group can end
-    __builtin_amdgcn_s_waitcnt(0);
+    // every wave done with its tiles before the sums take their memory
+    __syncthreads();
 
     // column n's sum over the four lane groups
     l += shfl_xor(l, 16);
@@ -265,6 +250,20 @@ __global__ __launch_bounds__(256) void decode_mfma_lds_kernel(DecodeArgs a) {
 }
 
 #undef PA_LDS_PTR
+
+// Launch of the LDS path: 8 waves per work-group (two work-groups per compute unit, two waves
+// per SIMD), or 4 for partitions of up to 512 tokens in a grid of 1024 or more work-groups,
+// where four work-groups per unit hide each one's prologue (B = 256 at 129 tokens: 32.6
+// against 40.2 us; B = 32 at 2049 tokens, one 4-wave work-group per unit: 52.2 against 45.2).
+template <typename T, int G>
+hipError_t launch_decode_lds(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
+    const dim3 grid(num_kv_heads, batch, a.max_partitions);
+    if (a.partition_size <= 512 && (int64_t)num_kv_heads * batch * a.max_partitions >= 1024)
+        hipLaunchKernelGGL((decode_mfma_lds_kernel<T, G, 4>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_mfma_lds_kernel<T, G, 8>), grid, dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
 
 }  // namespace mfma
 }  // namespace pagedkv

@@ -89,14 +89,14 @@ def test_beams_match_oracle(dtype, group, beams, d, bs):
 
 @pytest.mark.parametrize("group,bs", [(4, 16), (8, 16), (8, 8)])
 def test_beams_bitwise_equal_to_grouped_decode(group, bs):
-    """With 4 or 8 query heads per kv head pa_decode runs the same matrix-core arithmetic per
-    column, so for an explicit partition size the outputs agree bit for bit, shared or not
-    (with 8-token blocks too, where the two load the rows in different ways). This holds below
-    1152-token partitions: longer ones take pa_decode's LDS path, which sums P V in 16-token
-    steps."""
+    """With 4 or 8 query heads per kv head at head_dim 64 pa_decode runs the same matrix-core
+    arithmetic per column, so for an explicit partition size the outputs agree bit for bit,
+    shared or not (with 8-token blocks too, where the two load the rows in different ways).
+    (At head_dim 128 pa_decode takes its LDS path, which sums P V in 16-token steps; the beam
+    kernel is checked against the oracle there.)"""
     dev = require_gpu()
     for share in (True, False):
-        q, kp, vp, table, L = _beam_case(2, _LENS, 2, 2, group, 128, bs, 256, "bf16", share=share)
+        q, kp, vp, table, L = _beam_case(2, _LENS, 2, 2, group, 64, bs, 256, "bf16", share=share)
         tq, tk, tv, tt, tl = _device(dev, "bf16", q, kp, vp, table, L)
         for P in (64, 256):
             note(f"beams vs decode G={group} share={share} P={P}")

@@ -74,13 +74,15 @@ def test_grouped_heads_8_token_blocks(dtype, head_dim, group):
         assert_close(got, ref, dtype, f"bs=8 {dtype} d={head_dim} G={group} P={P}")
 
 
-def test_grouped_heads_8_token_blocks_far_apart():
+@pytest.mark.parametrize("group", [8, 16])
+def test_grouped_heads_8_token_blocks_far_apart(group):
     """A tile's two 8-token blocks more than 2 GiB apart in the pool (every other block of a
-    sequence moved up by 600000 ids, 2.3 GiB per pool): the kernel then loads the two 8-row
-    halves from their own blocks under lane masks."""
+    sequence moved up by 600000 ids, 2.3 GiB per pool). With 8 heads per kv head the LDS path
+    gives each 4-row load its own block's buffer; with 16 the direct-load kernel loads the two
+    8-row halves from their own blocks through per-lane addresses."""
     dev = require_gpu()
     lens = np.array([1, 9, 100, 250], np.int32)
-    w = build_paged("gqa-bs8-far", 320, 0, lens, 8, 2, 16, 128, "bf16")
+    w = build_paged("gqa-bs8-far", 320, 0, lens, 8, 2, 2 * group, 128, "bf16")
     ref = oracle_decode(w)
     far = 600_000
     tab = w.block_table.copy()
@@ -98,7 +100,7 @@ def test_grouped_heads_8_token_blocks_far_apart():
     vp[ids] = t["v_pool"][src]
     tt = torch.from_numpy(tab).to(dev)
     for P in (0, 16, 2048):
-        note(f"grouped heads bs=8, blocks 2.3 GiB apart, P={P}")
+        note(f"grouped heads bs=8 G={group}, blocks 2.3 GiB apart, P={P}")
         out = ops.decode(t["q"], kp, vp, tt, t["context_lens"], int(lens.max()), w.scale, partition_size=P)
         torch.cuda.synchronize()
         assert_close(out.float().cpu().numpy().astype(np.float64), ref, "bf16", f"far blocks P={P}")

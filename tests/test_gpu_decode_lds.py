@@ -1,10 +1,11 @@
-"""GPU: the grouped-query decode on its LDS path (partitions of 1152 tokens or more, fp16/bf16
-pools, head_dim 128, 4 or 8 query heads per kv head: tiles reach LDS through direct buffer
-loads, and the P V operand comes from transpose reads) against the float64 oracle.
+"""GPU: the grouped-query decode on its LDS path (fp16/bf16 pools, head_dim 128, 4 or 8 query
+heads per kv head: tiles reach LDS through direct buffer loads, and the P V operand comes
+from transpose reads) against the float64 oracle.
 
-Every case runs with explicit partition sizes that take the LDS path (the default policy
-splits these small batches to fill the grid); the full-size case checks that the policy's
-own choice takes it too. Unused pool slots hold NaN, so a read of padding would show.
+Partition sizes from 64 tokens to whole sequences: short partitions in grids of 1024 or more
+work-groups run the 4-wave form, the rest the 8-wave form. Unused pool slots hold NaN, so a
+read of padding would show. (The other decode tests at head_dim 128 with 4 or 8 heads per kv
+head run on this path too.)
 """
 
 import dataclasses
@@ -22,22 +23,22 @@ from workloads import build_paged
 
 pytestmark = pytest.mark.gpu
 
-LDS_MIN_PARTITION = 1152
-
 # short and long sequences in one batch: tiles that start past the length, a last tile with
 # one token, lengths one past and one short of a tile and of a partition
 _LENS = np.array([1, 15, 16, 17, 300, 1151, 1152, 1153, 2049, 2500, 3000, 4100], np.int32)
 
 
 @pytest.mark.parametrize("dtype,group,bs", [("bf16", 8, 16), ("f16", 8, 16), ("bf16", 4, 16), ("f16", 4, 32),
-                                            ("bf16", 8, 64), ("bf16", 8, 256), ("f16", 8, 512)])
+                                            ("bf16", 8, 64), ("bf16", 8, 256), ("f16", 8, 512), ("bf16", 8, 8),
+                                            ("f16", 4, 8)])
 def test_lds_path_matches_oracle(dtype, group, bs):
     dev = require_gpu()
     w = build_paged(f"lds-{dtype}-{group}-{bs}", 500 + group, bs, _LENS, bs, 2, 2 * group, 128, dtype)
     ref = oracle_decode(w)
     t = w.to_device(dev)
     whole = -(-int(_LENS.max()) // bs) * bs
-    for P in (-(-LDS_MIN_PARTITION // bs) * bs, 2048, 4096, whole):
+    # 64 and 128: 1560 and 792 work-groups of 2 kv heads x 12 sequences (4- and 8-wave forms)
+    for P in sorted({max(64, bs), max(128, bs), 1152 if bs <= 128 else 1536, 2048, 4096, whole}):
         note(f"lds path dtype={dtype} G={group} bs={bs} P={P}")
         got, _ = gpu_decode(w, dev, partition_size=P, tensors=t)
         assert_close(got, ref, dtype, f"lds path {dtype} G={group} bs={bs} P={P}")
@@ -53,7 +54,7 @@ def test_lds_path_one_partition_per_sequence_at_full_size():
     w = build_paged("lds-full", 510, 16, lens, 16, 8, 64, 128, "bf16")
     ref = oracle_decode(w)
     t = w.to_device(dev)
-    assert pa_decode_partition_size(CacheDesc.of(t["k_pool"]), 32, 64, 2049, 0) >= LDS_MIN_PARTITION
+    assert pa_decode_partition_size(CacheDesc.of(t["k_pool"]), 32, 64, 2049, 0) == 2064
     note("lds path B=32 ragged up to 2049")
     got, _ = gpu_decode(w, dev)
     assert_close(got, ref, "bf16", "lds path B=32 ragged up to 2049")
@@ -80,7 +81,7 @@ def test_lds_path_sliding_window(window):
     w = _release_before_window(base, window)
     ref = oracle.paged_decode_window(w.q, w.k_pool, w.v_pool, w.block_table, w.context_lens, w.scale, window)
     t = w.to_device(dev)
-    for P in (1152, 2048):
+    for P in (64, 1152, 2048):
         note(f"lds path window={window} P={P}")
         err = torch.zeros(1, dtype=torch.int32, device=dev)
         out = ops.decode(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["context_lens"], int(_LENS.max()),
@@ -90,7 +91,7 @@ def test_lds_path_sliding_window(window):
         assert_close(out.float().cpu().numpy().astype(np.float64), ref, "bf16", f"lds window={window} P={P}")
 
 
-@pytest.mark.parametrize("P", [1152, 2048, 4112])
+@pytest.mark.parametrize("P", [64, 1152, 2048, 4112])
 def test_lds_path_fused_append(P):
     """pa_decode_append: the new token's rows replace their slot in the staged tile. Outputs
     bit for bit those of the separate append and decode, pools bit for bit, and the oracle."""
@@ -130,7 +131,7 @@ def test_lds_path_bad_inputs():
     bad_lens = torch.from_numpy(lens.copy()).to(dev)
     bad_lens[0] = 0
     bad_lens[1] = ml + 1  # past max_context_len
-    for P in (1152, 2048):
+    for P in (64, 1152, 2048):
         note(f"lds path bad inputs P={P}")
         err = torch.zeros(1, dtype=torch.int32, device=dev)
         out = ops.decode(t["q"], t["k_pool"], t["v_pool"], t["block_table"], bad_lens, ml, w.scale,

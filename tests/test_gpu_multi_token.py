@@ -85,11 +85,11 @@ def test_multi_token_few_queries_8_token_blocks(dtype, group, d, fp8):
 
 def test_multi_token_one_query_is_the_decode_bitwise():
     """With one query per sequence the (query, head) columns are the decode's head columns,
-    the partition policy is the same, and so is every bit of the output (for partitions below
-    the 1152 tokens from which the decode takes its LDS path, as here)."""
+    the partition policy is the same, and so is every bit of the output (at head_dim 64: at
+    128 the decode takes its LDS path, which sums P V in 16-token steps)."""
     dev = require_gpu()
     lens = [5, 64, 333, 1000]
-    w, qs, q = _case("mt-decode", 710, lens, [1, 1, 1, 1], 16, 4, 8, 128, "bf16")
+    w, qs, q = _case("mt-decode", 710, lens, [1, 1, 1, 1], 16, 4, 8, 64, "bf16")
     t = w.to_device(dev)
     qd = torch.from_numpy(q).to(torch.bfloat16).to(dev)
     note("multi-token n=1 vs decode")
