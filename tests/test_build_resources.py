@@ -40,3 +40,60 @@ def test_decode_occupancy():
         small = per_lane and ("FP8" not in k or "ELb1ELb1ELb0ELi1EE" in k or "ELb1ELb0ELb1ELi1EE" in k)
         if "decode_mfma_kernel" in k or "prefill_kernel" in k:
             assert occ >= (1 if small else 2), (k, occ)
+
+
+def test_lds_path_occupancy():
+    """The LDS-path decode keeps four waves per SIMD, and its work-groups fit the LDS that
+    occupancy needs: two 8-wave or four 4-wave work-groups per compute unit (160 KB)."""
+    rows = [r for r in _rows() if "decode_mfma_lds_kernel" in r["kernel"]]
+    assert rows
+    for r in rows:
+        nw = 8 if "ELi8EEEvNS_10DecodeArgsE" in r["kernel"] else 4
+        assert int(r["occupancy_waves_per_simd"]) == 4, r["kernel"]
+        assert int(r["lds_bytes"]) * (16 // nw) <= 160 * 1024, (r["kernel"], r["lds_bytes"])
+
+
+def _device_asm(src: str) -> str:
+    """The device assembly of one source file of the library (compiled here, for gfx950)."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    from paged_kv_cache_indexed_amd import build
+
+    if shutil.which(build._hipcc()) is None and not os.path.exists(build._hipcc()):
+        pytest.skip("no hipcc")
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "k.s")
+        cmd = [build._hipcc(), *[f for f in build.HIP_FLAGS if f != "-fPIC"], "--cuda-device-only", "-S",
+               os.path.join(build.CSRC, src), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        with open(out) as f:
+            return f.read()
+
+
+def _function(asm: str, name_part: str) -> str:
+    start = next(i for i, line in enumerate(asm.splitlines())
+                 if line.split(";")[0].strip().endswith(":") and name_part in line and not line.startswith((".", "\t")))
+    body = []
+    for line in asm.splitlines()[start + 1:]:
+        body.append(line)
+        if "s_endpgm" in line:
+            break
+    return "\n".join(body)
+
+
+def test_measurement_kernels_load_full_width():
+    """The read-rate kernels must move the bytes they claim to: every buffer load of the
+    gather and every load of the streaming loop is 16 bytes per lane. (If some dwords of a
+    load feed nothing, the compiler narrows it, and the measured rate is of another access.)"""
+    import re
+
+    asm = _device_asm("pa_measure.hip")
+    gather = _function(asm, "gather_read_kernel")
+    loads = re.findall(r"buffer_load_dword\w*", gather)
+    assert loads and set(loads) == {"buffer_load_dwordx4"}, sorted(set(loads))
+    stream = _function(asm, "stream_read_kernel")
+    assert len(re.findall(r"global_load_dwordx4", stream)) >= 8
+    assert not re.findall(r"global_load_dword(?:x2|x3)?\s", stream)
