@@ -53,6 +53,29 @@ def test_lds_path_occupancy():
         assert int(r["lds_bytes"]) * (16 // nw) <= 160 * 1024, (r["kernel"], r["lds_bytes"])
 
 
+def test_valu_occupancy():
+    """The VALU stream kernels at one query head per kv head keep the waves per SIMD they were
+    measured at: with 16-bit pools at head_dim 128, 8 for fp16 (64 registers) and 7 for bf16;
+    with 8-bit pools, 7 (a lane's 16 codes per load, 72 registers)."""
+    import re
+
+    pat = re.compile(r"decode_valu_kernelINS_(3F16|4BF16)E(NS_3FP8E|S2_)Li(\d+)ELi1ELi(\d)ELi4E")
+    seen = set()
+    for r in _rows():
+        m = pat.search(r["kernel"])
+        if not m:
+            continue
+        q, kv, d, unroll = m.group(1), m.group(2), int(m.group(3)), int(m.group(4))
+        occ = int(r["occupancy_waves_per_simd"])
+        if kv == "NS_3FP8E":
+            seen.add("fp8")
+            assert occ >= 7, (r["kernel"], occ)
+        elif d == 128 and unroll == 2:
+            seen.add(q)
+            assert occ >= (8 if q == "3F16" else 7), (r["kernel"], occ)
+    assert seen == {"fp8", "3F16", "4BF16"}, seen
+
+
 def _device_asm(src: str) -> str:
     """The device assembly of one source file of the library (compiled here, for gfx950)."""
     import shutil
