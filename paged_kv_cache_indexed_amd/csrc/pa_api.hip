@@ -250,9 +250,13 @@ int32_t pa_decode_partition_size(const pa_cache_desc_t* cache, int32_t batch, in
         // there: 126.9 against 124.1 us).
         P = whole;
     } else {
-        // VALU path: 512-token partitions, shortened until the launch has about 2048
-        // workgroups (8 per compute unit).
-        P = ceil_div(512 > bs ? 512 : bs, bs) * bs;
+        // VALU path: partitions of 256 tokens up to 2048-token contexts (a long-tailed batch
+        // ends sooner when its longest sequences come in short pieces: config 3 at median 87,
+        // lengths up to 1197, was 1-2% faster per step at every block size than at 512), and
+        // of 512 beyond (32K contexts: 7% slower at 256); shortened until the launch has about
+        // 2048 workgroups (8 per compute unit).
+        const int base_p = max_context_len <= 2048 ? 256 : 512;
+        P = ceil_div(base_p > bs ? base_p : bs, bs) * bs;
         if (wgs * ceil_div(max_context_len, P) < 2048) {
             int64_t want = ceil_div((int64_t)max_context_len * wgs, 2048);
             // not below 256 tokens: shorter partitions lost 15-40% on small launches

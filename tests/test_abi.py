@@ -57,9 +57,12 @@ def test_partition_policy(lib):
     assert _lib.pa_decode_workspace_bytes(c, 64, 32, 521, 0) == 0
     # long contexts: 512-token partitions
     assert _lib.pa_decode_partition_size(_desc(bs=32), 32, 32, 32769, 0) == 512
-    # the long-tail batch (256 x 32 heads, up to 1197 tokens): 512-token partitions for
-    # 16-bit rows, one whole partition for 8-bit rows (twice the tokens per byte)
-    assert _lib.pa_decode_partition_size(c, 256, 32, 1197, 0) == 512
+    # the long-tail batch (256 x 32 heads, up to 1197 tokens): 256-token partitions for
+    # 16-bit rows (up to 2048-token contexts; 2049 and beyond: 512), one whole partition for
+    # 8-bit rows (twice the tokens per byte)
+    assert _lib.pa_decode_partition_size(c, 256, 32, 1197, 0) == 256
+    assert _lib.pa_decode_partition_size(c, 256, 32, 2048, 0) == 256
+    assert _lib.pa_decode_partition_size(c, 256, 32, 2049, 0) == 512
     assert _lib.pa_decode_partition_size(_desc(dtype=_lib.PA_FP8_E4M3), 256, 32, 1197, 0) == 1200
     assert _lib.pa_decode_partition_size(_desc(dtype=_lib.PA_FP8_E4M3), 256, 32, 2049, 0) == 512
     # partition records (head_dim + 2 floats) and one int32 slot per sequence
