@@ -245,14 +245,14 @@ int32_t pa_decode_partition_size(const pa_cache_desc_t* cache, int32_t batch, in
         // VALU path, short contexts and at least half a workgroup per compute unit: no split
         // (the reduce launch costs more than the extra parallelism gains; equal lengths of
         // 600 tokens at 8 x 32 heads: 16.0 us whole against 18.6 us in 256-token partitions).
-        // 8-bit rows stream in half the time, so contexts twice as long stay whole (config 3
-        // at median 87, lengths up to 1197: 85.7 against 90.8 us at P = 512; 16-bit pools
-        // there: 126.9 against 124.1 us).
+        // 8-bit rows stream in half the time, so contexts twice as long stay whole (256
+        // sequences x 32 heads of long-tailed lengths, median 87, up to 1197 tokens: 85.7
+        // against 90.8 us at P = 512; 16-bit pools there: 126.9 against 124.1 us).
         P = whole;
     } else {
         // VALU path: partitions of 256 tokens up to 2048-token contexts (a long-tailed batch
-        // ends sooner when its longest sequences come in short pieces: config 3 at median 87,
-        // lengths up to 1197, was 1-2% faster per step at every block size than at 512), and
+        // ends sooner when its longest sequences come in short pieces: that 256 x 32-head
+        // batch was 1-2% faster per step at every block size than at 512), and
         // of 512 beyond (32K contexts: 7% slower at 256); shortened until the launch has about
         // 2048 workgroups (8 per compute unit).
         const int base_p = max_context_len <= 2048 ? 256 : 512;

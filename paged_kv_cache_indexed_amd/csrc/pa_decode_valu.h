@@ -130,7 +130,8 @@ __device__ __forceinline__ void stream_partition(const DecodeArgs& a, const int*
             vv[u] = buffer_load16(make_rsrc(vpool + slab, slab_bytes), off);
             if constexpr (kScaled) {
                 // cached, unlike the streamed codes: with 16-token blocks two kv heads' scales
-                // share a 128-byte line (1-2.5% faster than streaming loads on configs 2 and 3)
+                // share a 128-byte line (2-3% faster than streamed loads on 64 x 32 heads of
+                // 450-520 tokens and on 256 x 32 heads of long-tailed lengths)
                 const size_t srow = ((size_t)id * a.num_kv_heads + kvh) << lbs;  // this slab's scales
                 const uint32_t soff = live ? (uint32_t)(((rel & (bs - 1)) + row) * 4) : kOutOfRange;
                 ksc[u] = buffer_load_f32<0>(make_rsrc(a.k_scale + srow, (uint32_t)bs * 4), soff);
@@ -477,8 +478,9 @@ hipError_t launch_decode_tgdu(const DecodeArgs& a, int batch, int num_kv_heads, 
 // waves share a SIMD. Grouped-query heads multiply the registers per group. 8-bit pools
 // take 1 everywhere: a lane's 16-byte load is 16 codes (1 KiB per wave load is 8 rows, as
 // many tokens as 2 groups of 16-bit rows), and at 72 VGPRs 7 waves share a SIMD, against
-// 3 with 4 groups (145 VGPRs). Measured with lazy rescaling: config 3 (median 87) 83 against
-// 115 us, median 23 42 against 56 us, config 2 50 against 58 us.
+// 3 with 4 groups (145 VGPRs). Measured with lazy rescaling on 256 sequences x 32 heads of
+// long-tailed lengths: median 87, 83 against 115 us; median 23, 42 against 56 us; on 64 x 32
+// heads of 450-520 tokens, 50 against 58 us.
 template <typename T, typename KV, int D, int G>
 hipError_t launch_decode_tgd(const DecodeArgs& a, int batch, int num_kv_heads, hipStream_t stream) {
     if constexpr (G <= 2 && std::is_same_v<KV, FP8>) {

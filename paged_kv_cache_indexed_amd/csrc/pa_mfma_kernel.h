@@ -295,13 +295,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kSmallB
     // 16-bit rows of 256 bytes, several queries or beams: tiles are loaded with whole rows per
     // lane group (coalesced) and turned into the operand layout through this wave-private LDS
     // region. The operand-layout loads give the L1 one access per lane; restaging measured
-    // 23% faster with 4 queries per sequence (config 4) and 2% with beam groups (config 5),
+    // 23% faster with 4 queries per sequence (32 sequences of 2049 tokens, 64 query / 8 kv
+    // heads) and 2% with beam groups (8 groups of 4 beams at 32K tokens),
     // but 3-4% slower for the one-query decode, which keeps the direct loads.
     constexpr bool kStage = D == 128 && (kMulti || kBeams) && kSmallBlocks == 0;
     // Staged 16-bit V tiles stay in LDS, and the B operand of P V comes from transpose reads
     // (ds_read_b64_tr_b16) instead of identity-MFMA transposes: 12% faster with 4 queries per
-    // sequence on config 4, equal elsewhere. The one-query decode measured the same with it
-    // (staged, 4 or 8 waves), so it keeps the direct loads.
+    // sequence on that 64 / 8-head batch, equal elsewhere. The one-query decode measured the
+    // same with it (staged, 4 or 8 waves), so it keeps the direct loads.
     constexpr bool kTrV = kStage && KV::kBytes == 2;
     constexpr int kCpr = D * KV::kBytes / 16;  // 16-byte chunks per row (16 or 8)
     constexpr int kRpl = 64 / kCpr;            // rows per staged load instruction (4 or 8)
